@@ -1,0 +1,294 @@
+"""Python binding of libtwell.so, the MI355X TwELL sparse-FFN library.
+
+Thin ctypes marshalling over the C ABI declared in ``include/twell.h``: torch
+tensors supply device memory and the current HIP stream; every step of the
+computation runs in the library's HIP kernels.  The functions carry the same
+names as the C entry points.  Importing this package fails loudly when the
+library has not been built (``python activation_sparse_transformer_bf16_amd/build.py``).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtwell.so")
+
+TWELL_OK, TWELL_ERR_INVALID_ARG, TWELL_ERR_UNSUPPORTED, TWELL_ERR_WORKSPACE, TWELL_ERR_HIP = range(5)
+TWELL_F32, TWELL_BF16 = 0, 1
+
+
+class TwellMatrixC(ctypes.Structure):
+    """Mirror of ``twell_matrix`` (include/twell.h)."""
+
+    _fields_ = [
+        ("rows", ctypes.c_int32), ("cols", ctypes.c_int32), ("tile", ctypes.c_int32),
+        ("cap", ctypes.c_int32), ("dtype", ctypes.c_int), ("cnt", ctypes.c_void_p),
+        ("val", ctypes.c_void_p), ("idx", ctypes.c_void_p), ("ovf_rows", ctypes.c_void_p),
+        ("n_ovf", ctypes.c_void_p), ("dense", ctypes.c_void_p), ("ovf_cap", ctypes.c_int32),
+    ]
+
+
+class TwellError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+def _load():
+    # torch ships its own libamdhip64.so.7; importing it first makes libtwell.so
+    # bind to that same HIP runtime instead of loading a second one.
+    import torch  # noqa: F401
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python activation_sparse_transformer_bf16_amd/build.py`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    M = ctypes.POINTER(TwellMatrixC)
+    sig = {
+        "twell_abi_version": (I, []),
+        "twell_status_str": (ctypes.c_char_p, [I]),
+        "twell_last_error": (ctypes.c_char_p, []),
+        "twell_pack": (I, [P, M, P]),
+        "twell_ffn_workspace_size": (Z, [I, I, I, I, I, I]),
+        "twell_ffn_forward": (I, [P, P, P, P, P, P, I, M, P, Z, P]),
+        "twell_gate_pack": (I, [P, P, P, I, M, P, P]),
+        "twell_overflow_scan": (I, [M, P]),
+        "twell_sparse_ffn": (I, [M, P, P, P, P, P, P, I, P, Z, P]),
+        "dense_ffn_workspace_size": (Z, [I, I, I, I]),
+        "dense_ffn_forward": (I, [P, P, P, P, P, P, I, I, I, I, P, Z, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype, fn.argtypes = res, args
+    return lib
+
+
+_lib = _load()
+
+# Names every build of the library must export (checked by the CPU tests).
+EXPORTS = ("twell_abi_version", "twell_status_str", "twell_last_error", "twell_pack",
+           "twell_ffn_workspace_size", "twell_ffn_forward", "twell_gate_pack", "twell_overflow_scan",
+           "twell_sparse_ffn",
+           "dense_ffn_workspace_size", "dense_ffn_forward")
+
+
+def lib():
+    return _lib
+
+
+def twell_abi_version() -> int:
+    return _lib.twell_abi_version()
+
+
+def twell_status_str(status: int) -> str:
+    return _lib.twell_status_str(status).decode()
+
+
+def twell_last_error() -> str:
+    return _lib.twell_last_error().decode()
+
+
+def _check(status: int):
+    if status != TWELL_OK:
+        raise TwellError(status, f"{twell_status_str(status)}: {twell_last_error()}")
+
+
+# --------------------------------------------------------------------------- torch glue
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t == torch.float32:
+        return TWELL_F32
+    if t == torch.bfloat16:
+        return TWELL_BF16
+    raise TypeError(f"unsupported dtype {t} (float32 or bfloat16)")
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _need(t, name, device, dtype=None, shape=None):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+@dataclass
+class TwellMatrix:
+    """Device buffers of one TwELL matrix (see ``twell_matrix`` in include/twell.h)."""
+
+    rows: int
+    cols: int
+    tile: int
+    cap: int
+    dtype: object        # torch dtype of the values
+    cnt: object          # int16 [rows, cols/tile] (uint16 bit patterns)
+    val: object          # dtype [rows, cols/tile, cap]
+    idx: object          # uint8 [rows, cols/tile, cap]
+    ovf_rows: object     # int32 [ovf_cap]
+    n_ovf: object        # int32 [1]
+    dense: object        # dtype [ovf_cap, cols] or None
+    ovf_cap: int
+
+    @classmethod
+    def empty(cls, rows: int, cols: int, tile: int, cap: int, dtype, device,
+              ovf_cap: Optional[int] = None, dense: bool = True) -> "TwellMatrix":
+        torch = _torch()
+        nt = cols // tile
+        ovf_cap = rows if ovf_cap is None else ovf_cap
+        return cls(rows, cols, tile, cap, dtype,
+                   torch.empty((rows, nt), dtype=torch.int16, device=device),
+                   torch.empty((rows, nt, cap), dtype=dtype, device=device),
+                   torch.empty((rows, nt, cap), dtype=torch.uint8, device=device),
+                   torch.empty((max(ovf_cap, 1),), dtype=torch.int32, device=device),
+                   torch.empty((1,), dtype=torch.int32, device=device),
+                   torch.empty((max(ovf_cap, 1), cols), dtype=dtype, device=device) if dense else None,
+                   ovf_cap)
+
+    def c_struct(self) -> TwellMatrixC:
+        return TwellMatrixC(self.rows, self.cols, self.tile, self.cap, _dtype_code(self.dtype),
+                            _ptr(self.cnt), _ptr(self.val), _ptr(self.idx), _ptr(self.ovf_rows),
+                            _ptr(self.n_ovf), _ptr(self.dense), self.ovf_cap)
+
+    @property
+    def device(self):
+        return self.cnt.device
+
+
+def twell_pack(pre, tile: int, cap: int, ovf_cap: Optional[int] = None, dense: bool = True,
+               out: Optional[TwellMatrix] = None) -> TwellMatrix:
+    """Pack a pre-activation matrix [T, F] (fp32 or bf16, on the GPU) into TwELL."""
+    device = pre.device
+    _need(pre, "pre", device)
+    T, F = pre.shape
+    if out is None:
+        out = TwellMatrix.empty(T, F, tile, cap, pre.dtype, device, ovf_cap, dense)
+    m = out.c_struct()
+    _check(_lib.twell_pack(_ptr(pre), ctypes.byref(m), _stream(device)))
+    return out
+
+
+def twell_ffn_workspace_size(T: int, d: int, F: int, tile: int, cap: int, dtype) -> int:
+    return int(_lib.twell_ffn_workspace_size(T, d, F, tile, cap, _dtype_code(dtype)))
+
+
+def dense_ffn_workspace_size(T: int, d: int, F: int, dtype) -> int:
+    return int(_lib.dense_ffn_workspace_size(T, d, F, _dtype_code(dtype)))
+
+
+def _ffn_checks(x, w_gate, w_up, w_down, gate_bias):
+    torch = _torch()
+    device = x.device
+    T, d = x.shape
+    F = w_gate.shape[0]
+    _need(x, "x", device)
+    for name, w in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
+        _need(w, name, device, x.dtype, (F, d))
+    if gate_bias is not None:
+        _need(gate_bias, "gate_bias", device, torch.float32, (T,))
+    return device, T, d, F
+
+
+def _workspace(nbytes: int, device, workspace=None):
+    torch = _torch()
+    if workspace is not None and workspace.numel() * workspace.element_size() >= nbytes:
+        return workspace
+    return torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=device)
+
+
+def twell_ffn_forward(x, w_gate, w_up, w_down, gate_bias=None, tile: int = 256, cap: int = 16,
+                      packed: Optional[TwellMatrix] = None, y=None, workspace=None
+                      ) -> Tuple[object, TwellMatrix]:
+    """y = (ReLU(x W_g^T + beta) * (x W_u^T)) W_d through TwELL; returns (y, packed)."""
+    torch = _torch()
+    device, T, d, F = _ffn_checks(x, w_gate, w_up, w_down, gate_bias)
+    if packed is None:
+        packed = TwellMatrix.empty(T, F, tile, cap, x.dtype, device, T, dense=False)
+    if y is None:
+        y = torch.empty((T, d), dtype=x.dtype, device=device)
+    ws = _workspace(twell_ffn_workspace_size(T, d, F, packed.tile, packed.cap, x.dtype), device, workspace)
+    m = packed.c_struct()
+    _check(_lib.twell_ffn_forward(_ptr(x), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(gate_bias),
+                                  _ptr(y), d, ctypes.byref(m), _ptr(ws),
+                                  ws.numel(), _stream(device)))
+    return y, packed
+
+
+def twell_gate_pack(x, w_gate, gate_bias=None, tile: int = 256, cap: int = 16,
+                    packed: Optional[TwellMatrix] = None, pre_out: bool = False, scan: bool = True):
+    """Gate matmul + TwELL epilogue (one kernel), then, with ``scan``, the overflow
+    scan; returns (packed, pre or None)."""
+    torch = _torch()
+    device = x.device
+    T, d = x.shape
+    F = w_gate.shape[0]
+    _need(x, "x", device)
+    _need(w_gate, "w_gate", device, x.dtype, (F, d))
+    if gate_bias is not None:
+        _need(gate_bias, "gate_bias", device, torch.float32, (T,))
+    if packed is None:
+        packed = TwellMatrix.empty(T, F, tile, cap, x.dtype, device, T, dense=False)
+    pre = torch.empty((T, F), dtype=x.dtype, device=device) if pre_out else None
+    m = packed.c_struct()
+    _check(_lib.twell_gate_pack(_ptr(x), _ptr(w_gate), _ptr(gate_bias), d, ctypes.byref(m),
+                                _ptr(pre), _stream(device)))
+    if scan:
+        twell_overflow_scan(packed)
+    return packed, pre
+
+
+def twell_overflow_scan(packed: TwellMatrix) -> TwellMatrix:
+    """List the overflowing rows of a packed matrix (fills ovf_rows and n_ovf)."""
+    m = packed.c_struct()
+    _check(_lib.twell_overflow_scan(ctypes.byref(m), _stream(packed.device)))
+    return packed
+
+
+def twell_sparse_ffn(packed: TwellMatrix, x, w_gate, w_up, w_down, gate_bias=None, y=None,
+                     workspace=None):
+    """Up / down projections over TwELL plus the dense fallback; returns y."""
+    torch = _torch()
+    device, T, d, F = _ffn_checks(x, w_gate, w_up, w_down, gate_bias)
+    if y is None:
+        y = torch.empty((T, d), dtype=x.dtype, device=device)
+    ws = _workspace(twell_ffn_workspace_size(T, d, F, packed.tile, packed.cap, x.dtype), device, workspace)
+    m = packed.c_struct()
+    _check(_lib.twell_sparse_ffn(ctypes.byref(m), _ptr(x), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+                                 _ptr(gate_bias), _ptr(y), d, _ptr(ws), ws.numel(),
+                                 _stream(device)))
+    return y
+
+
+def dense_ffn_forward(x, w_gate, w_up, w_down, gate_bias=None, y=None, workspace=None):
+    """The same layer computed densely on the matrix cores (baseline)."""
+    torch = _torch()
+    device, T, d, F = _ffn_checks(x, w_gate, w_up, w_down, gate_bias)
+    if y is None:
+        y = torch.empty((T, d), dtype=x.dtype, device=device)
+    ws = _workspace(dense_ffn_workspace_size(T, d, F, x.dtype), device, workspace)
+    _check(_lib.dense_ffn_forward(_ptr(x), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(gate_bias),
+                                  _ptr(y), T, d, F, _dtype_code(x.dtype), _ptr(ws), ws.numel(),
+                                  _stream(device)))
+    return y

@@ -1,0 +1,285 @@
+// C ABI of libtwell.so: argument validation, workspace layout and the launch
+// sequence of every entry point declared in include/twell.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "launch.hpp"
+#include "twell.h"
+
+using namespace twell;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+void set_err(const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+}
+
+twell_status fail(twell_status st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+twell_status hip_check(hipError_t e, const char *what) {
+  if (e == hipSuccess) return TWELL_OK;
+  set_err("%s: %s", what, hipGetErrorString(e));
+  return TWELL_ERR_HIP;
+}
+
+#define TW_TRY(expr, what)                           \
+  do {                                               \
+    twell_status st_ = hip_check((expr), (what));    \
+    if (st_ != TWELL_OK) return st_;                 \
+  } while (0)
+
+constexpr size_t ALIGN_WS = 256;
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int dt_size(twell_dtype dt) { return dt == TWELL_BF16 ? 2 : 4; }
+
+Dt to_dt(twell_dtype dt) { return dt == TWELL_BF16 ? Dt::BF16 : Dt::F32; }
+
+bool valid_dtype(int dt) { return dt == TWELL_F32 || dt == TWELL_BF16; }
+
+// Format parameters shared by every entry point.
+twell_status check_format(int tile, int cap, int F, int dtype) {
+  if (!valid_dtype(dtype)) return fail(TWELL_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (tile <= 0 || F <= 0 || cap <= 0) return fail(TWELL_ERR_INVALID_ARG, "tile, cols and cap must be positive");
+  if (F % tile != 0) return fail(TWELL_ERR_INVALID_ARG, "cols (%d) must be a multiple of the tile (%d)", F, tile);
+  if (tile != 128 && tile != 256) return fail(TWELL_ERR_UNSUPPORTED, "tile %d not built (128 or 256)", tile);
+  if (cap > std::min(tile, 64)) return fail(TWELL_ERR_UNSUPPORTED, "cap %d not built (1..%d)", cap, std::min(tile, 64));
+  if (F > (1 << 24)) return fail(TWELL_ERR_UNSUPPORTED, "cols %d too large", F);
+  return TWELL_OK;
+}
+
+twell_status check_d(int d, int dtype) {
+  if (d <= 0) return fail(TWELL_ERR_INVALID_ARG, "d must be positive");
+  const int q = dtype == TWELL_BF16 ? 512 : 256;
+  if (d % q != 0 || d > 8192) return fail(TWELL_ERR_UNSUPPORTED, "d %d not built (multiple of %d, <= 8192)", d, q);
+  return TWELL_OK;
+}
+
+twell_status check_matrix(const twell_matrix *m, bool need_ovf_all) {
+  if (m == nullptr) return fail(TWELL_ERR_INVALID_ARG, "null twell_matrix");
+  if (m->rows < 0) return fail(TWELL_ERR_INVALID_ARG, "rows must be >= 0");
+  if (m->ovf_cap < 0) return fail(TWELL_ERR_INVALID_ARG, "ovf_cap must be >= 0");
+  twell_status st = check_format(m->tile, m->cap, m->cols, (int)m->dtype);
+  if (st != TWELL_OK) return st;
+  if (m->n_ovf == nullptr) return fail(TWELL_ERR_INVALID_ARG, "null n_ovf");
+  if (m->rows > 0 && (m->cnt == nullptr || m->val == nullptr || m->idx == nullptr))
+    return fail(TWELL_ERR_INVALID_ARG, "null cnt/val/idx");
+  if (m->ovf_cap > 0 && m->ovf_rows == nullptr) return fail(TWELL_ERR_INVALID_ARG, "null ovf_rows with ovf_cap > 0");
+  if (need_ovf_all && m->ovf_cap < m->rows)
+    return fail(TWELL_ERR_INVALID_ARG, "ovf_cap (%d) must be >= rows (%d)", m->ovf_cap, m->rows);
+  if (!aligned(m->cnt, 2) || !aligned(m->val, dt_size(m->dtype)) || !aligned(m->ovf_rows, 4) ||
+      !aligned(m->n_ovf, 4) || !aligned(m->dense, 16))
+    return fail(TWELL_ERR_UNSUPPORTED, "misaligned twell_matrix buffer");
+  return TWELL_OK;
+}
+
+struct FfnWs {
+  size_t flag, v, a, total;
+};
+
+FfnWs ffn_ws_layout(int T, int F, int tile, int cap, twell_dtype dt) {
+  FfnWs w;
+  const size_t nt = (size_t)F / tile;
+  w.flag = 0;
+  w.v = align_up((size_t)T, ALIGN_WS);
+  w.a = align_up(w.v + (size_t)T * nt * cap * 4, ALIGN_WS);
+  w.total = std::max(align_up(w.a + (size_t)T * F * dt_size(dt), ALIGN_WS), ALIGN_WS);
+  return w;
+}
+
+twell_status check_ffn_ptrs(const void *x, const void *wg, const void *wu, const void *wd, const float *beta,
+                            const void *y) {
+  if (!x || !wg || !wu || !wd || !y) return fail(TWELL_ERR_INVALID_ARG, "null x/w_gate/w_up/w_down/y");
+  if (!aligned(x, 16) || !aligned(wg, 16) || !aligned(wu, 16) || !aligned(wd, 16) || !aligned(y, 16) ||
+      !aligned(beta, 4))
+    return fail(TWELL_ERR_UNSUPPORTED, "x, weights and y must be 16-byte aligned");
+  return TWELL_OK;
+}
+
+twell_status run_sparse(const twell_matrix *m, const void *x, const void *wg, const void *wu, const void *wd,
+                        const float *beta, void *y, int d, void *ws, hipStream_t s) {
+  const int T = m->rows, F = m->cols;
+  const FfnWs L = ffn_ws_layout(T, F, m->tile, m->cap, m->dtype);
+  char *base = static_cast<char *>(ws);
+  uint8_t *row_flag = reinterpret_cast<uint8_t *>(base + L.flag);
+  float *vbuf = reinterpret_cast<float *>(base + L.v);
+  void *a_ws = base + L.a;
+  const Dt D = to_dt(m->dtype);
+
+  ScanArgs sc{m->cnt, T, F / m->tile, m->cap, row_flag, m->ovf_rows, m->ovf_cap, m->n_ovf};
+  TW_TRY(overflow_scan(sc, s), "overflow scan");
+
+  SparseArgs sa{D, T, d, F, m->tile, m->cap, m->cnt, m->val, m->idx, row_flag, x, wu, wd, vbuf, y};
+  TW_TRY(sparse_up(sa, s), "sparse up projection");
+  TW_TRY(sparse_down(sa, s), "sparse down projection");
+
+  DenseArgs da{D, x, wg, wu, wd, beta, y, T, d, F, m->ovf_rows, m->n_ovf, a_ws, m->dense, m->ovf_cap};
+  TW_TRY(dense_gate_up(da, s), "fallback gate/up matmul");
+  TW_TRY(dense_down(da, s), "fallback down matmul");
+  return TWELL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int twell_abi_version(void) { return TWELL_ABI_VERSION; }
+
+const char *twell_status_str(twell_status s) {
+  switch (s) {
+    case TWELL_OK: return "ok";
+    case TWELL_ERR_INVALID_ARG: return "invalid argument";
+    case TWELL_ERR_UNSUPPORTED: return "unsupported configuration";
+    case TWELL_ERR_WORKSPACE: return "workspace too small";
+    case TWELL_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char *twell_last_error(void) { return g_err; }
+
+twell_status twell_pack(const void *pre, twell_matrix *out, void *stream) {
+  g_err[0] = 0;
+  twell_status st = check_matrix(out, false);
+  if (st != TWELL_OK) return st;
+  if (out->rows > 0 && pre == nullptr) return fail(TWELL_ERR_INVALID_ARG, "null pre");
+  if (!aligned(pre, 16)) return fail(TWELL_ERR_UNSUPPORTED, "pre must be 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int T = out->rows;
+  if (T == 0) return hip_check(zero_int(out->n_ovf, s), "zero n_ovf");
+  const Dt D = to_dt(out->dtype);
+  PackArgs pa{D, out->tile, out->cap, pre, T, out->cols, out->cnt, out->val, out->idx};
+  TW_TRY(pack_tiles(pa, s), "pack");
+  ScanArgs sc{out->cnt, T, out->cols / out->tile, out->cap, nullptr, out->ovf_rows, out->ovf_cap, out->n_ovf};
+  TW_TRY(overflow_scan(sc, s), "overflow scan");
+  DenseRowsArgs dr{D, pre, T, out->cols, out->ovf_rows, out->n_ovf, out->ovf_cap, out->dense};
+  TW_TRY(pack_dense_rows(dr, s), "dense rows");
+  return TWELL_OK;
+}
+
+size_t twell_ffn_workspace_size(int T, int d, int F, int tile, int cap, twell_dtype dtype) {
+  if (T < 0 || check_format(tile, cap, F, (int)dtype) != TWELL_OK || check_d(d, (int)dtype) != TWELL_OK) return 0;
+  return ffn_ws_layout(T, F, tile, cap, dtype).total;
+}
+
+twell_status twell_gate_pack(const void *x, const void *w_gate, const float *gate_bias, int d, twell_matrix *packed,
+                             void *pre_out, void *stream) {
+  g_err[0] = 0;
+  twell_status st = check_matrix(packed, false);
+  if (st != TWELL_OK) return st;
+  if ((st = check_d(d, (int)packed->dtype)) != TWELL_OK) return st;
+  if (packed->rows == 0) return TWELL_OK;
+  if (!x || !w_gate) return fail(TWELL_ERR_INVALID_ARG, "null x/w_gate");
+  if (!aligned(x, 16) || !aligned(w_gate, 16) || !aligned(gate_bias, 4) || !aligned(pre_out, 16))
+    return fail(TWELL_ERR_UNSUPPORTED, "misaligned x/w_gate/gate_bias/pre_out");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int T = packed->rows, F = packed->cols;
+  if (T == 0) return TWELL_OK;
+  GateArgs ga{to_dt(packed->dtype), packed->tile, x, w_gate, gate_bias, T, d, F, packed->cap,
+              packed->cnt, packed->val, packed->idx, pre_out};
+  TW_TRY(gate_twell(ga, s), "gate matmul");
+  return TWELL_OK;
+}
+
+twell_status twell_overflow_scan(twell_matrix *packed, void *stream) {
+  g_err[0] = 0;
+  twell_status st = check_matrix(packed, false);
+  if (st != TWELL_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (packed->rows == 0) return hip_check(zero_int(packed->n_ovf, s), "zero n_ovf");
+  ScanArgs sc{packed->cnt, packed->rows, packed->cols / packed->tile, packed->cap, nullptr, packed->ovf_rows,
+              packed->ovf_cap, packed->n_ovf};
+  TW_TRY(overflow_scan(sc, s), "overflow scan");
+  return TWELL_OK;
+}
+
+twell_status twell_sparse_ffn(const twell_matrix *packed, const void *x, const void *w_gate, const void *w_up,
+                              const void *w_down, const float *gate_bias, void *y, int d, void *workspace,
+                              size_t ws_bytes, void *stream) {
+  g_err[0] = 0;
+  twell_status st = check_matrix(packed, true);
+  if (st != TWELL_OK) return st;
+  if ((st = check_d(d, (int)packed->dtype)) != TWELL_OK) return st;
+  if (packed->rows == 0) return hip_check(zero_int(packed->n_ovf, static_cast<hipStream_t>(stream)), "zero n_ovf");
+  if ((st = check_ffn_ptrs(x, w_gate, w_up, w_down, gate_bias, y)) != TWELL_OK) return st;
+  const size_t need = ffn_ws_layout(packed->rows, packed->cols, packed->tile, packed->cap, packed->dtype).total;
+  if (workspace == nullptr || ws_bytes < need)
+    return fail(TWELL_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : 0);
+  if (!aligned(workspace, ALIGN_WS)) return fail(TWELL_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (packed->rows == 0) return hip_check(zero_int(packed->n_ovf, s), "zero n_ovf");
+  return run_sparse(packed, x, w_gate, w_up, w_down, gate_bias, y, d, workspace, s);
+}
+
+twell_status twell_ffn_forward(const void *x, const void *w_gate, const void *w_up, const void *w_down,
+                               const float *gate_bias, void *y, int d, twell_matrix *packed, void *workspace,
+                               size_t ws_bytes, void *stream) {
+  g_err[0] = 0;
+  twell_status st = check_matrix(packed, true);
+  if (st != TWELL_OK) return st;
+  if ((st = check_d(d, (int)packed->dtype)) != TWELL_OK) return st;
+  if (packed->rows == 0) return hip_check(zero_int(packed->n_ovf, static_cast<hipStream_t>(stream)), "zero n_ovf");
+  if ((st = check_ffn_ptrs(x, w_gate, w_up, w_down, gate_bias, y)) != TWELL_OK) return st;
+  const size_t need = ffn_ws_layout(packed->rows, packed->cols, packed->tile, packed->cap, packed->dtype).total;
+  if (workspace == nullptr || ws_bytes < need)
+    return fail(TWELL_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : 0);
+  if (!aligned(workspace, ALIGN_WS)) return fail(TWELL_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int T = packed->rows, F = packed->cols;
+  if (T == 0) return hip_check(zero_int(packed->n_ovf, s), "zero n_ovf");
+  GateArgs ga{to_dt(packed->dtype), packed->tile, x, w_gate, gate_bias, T, d, F, packed->cap,
+              packed->cnt, packed->val, packed->idx, nullptr};
+  TW_TRY(gate_twell(ga, s), "gate matmul");
+  return run_sparse(packed, x, w_gate, w_up, w_down, gate_bias, y, d, workspace, s);
+}
+
+size_t dense_ffn_workspace_size(int T, int d, int F, twell_dtype dtype) {
+  if (T < 0 || !valid_dtype((int)dtype) || F <= 0 || F % 128 != 0 || F > (1 << 24) ||
+      check_d(d, (int)dtype) != TWELL_OK)
+    return 0;
+  return std::max(align_up((size_t)T * F * dt_size(dtype), ALIGN_WS), ALIGN_WS);
+}
+
+twell_status dense_ffn_forward(const void *x, const void *w_gate, const void *w_up, const void *w_down,
+                               const float *gate_bias, void *y, int T, int d, int F, twell_dtype dtype,
+                               void *workspace, size_t ws_bytes, void *stream) {
+  g_err[0] = 0;
+  if (!valid_dtype((int)dtype)) return fail(TWELL_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (T < 0 || F <= 0) return fail(TWELL_ERR_INVALID_ARG, "T must be >= 0 and F > 0");
+  if (F % 128 != 0 || F > (1 << 24)) return fail(TWELL_ERR_UNSUPPORTED, "F %d not built (multiple of 128)", F);
+  twell_status st = check_d(d, (int)dtype);
+  if (st != TWELL_OK) return st;
+  if (T == 0) return TWELL_OK;
+  if ((st = check_ffn_ptrs(x, w_gate, w_up, w_down, gate_bias, y)) != TWELL_OK) return st;
+  const size_t need = dense_ffn_workspace_size(T, d, F, dtype);
+  if (workspace == nullptr || ws_bytes < need)
+    return fail(TWELL_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : 0);
+  if (!aligned(workspace, ALIGN_WS)) return fail(TWELL_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+  if (T == 0) return TWELL_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  DenseArgs da{to_dt(dtype), x, w_gate, w_up, w_down, gate_bias, y, T, d, F, nullptr, nullptr, workspace,
+               nullptr, 0};
+  TW_TRY(dense_gate_up(da, s), "dense gate/up matmul");
+  TW_TRY(dense_down(da, s), "dense down matmul");
+  return TWELL_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,170 @@
+// Dense ReGLU FFN on the matrix cores: the dense-backup path of the hybrid
+// format (rows whose TwELL tiles overflowed; gist.science "Sparser, Faster,
+// Lighter Transformer Language Models", Resumen Técnico §2.A, and the
+// q2bstudio post on TwELL, third paragraph) and the dense baseline layer.
+//
+//   k_gate_up: one matmul over [W_g rows | W_u rows] of the same 128 hidden
+//              units; epilogue a = ReLU(round(pre)) * u, rounded to the
+//              storage dtype (and optionally h = ReLU(round(pre)) stored).
+//   k_down:    y = a W_d with W_d [F][d] read n-contiguous and transposed into
+//              the k-contiguous LDS layout of the mainloop.
+// Rows may be gathered through an index list whose length lives on the device;
+// workgroups past that length return before loading anything.
+#include "gemm.hpp"
+#include "launch.hpp"
+
+namespace twell {
+
+template <Dt D>
+__global__ __launch_bounds__(GEMM_THREADS) void k_gate_up(
+    const typename DtT<D>::T *__restrict__ x, const typename DtT<D>::T *__restrict__ wg,
+    const typename DtT<D>::T *__restrict__ wu, const float *__restrict__ beta, int M, int K, int F,
+    const int *__restrict__ rows, const int *__restrict__ n_rows_dev, typename DtT<D>::T *__restrict__ a_ws,
+    typename DtT<D>::T *__restrict__ h_out, int h_cap) {
+  using T = typename DtT<D>::T;
+  constexpr int BN = 256, HALF = 128;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int mt = (M + GEMM_BM - 1) / GEMM_BM, ntl = F / HALF;
+  int tm, tn;
+  tile_coords(blockIdx.x, mt, ntl, tm, tn);
+  const int m0 = tm * GEMM_BM, n0 = tn * HALF;
+  const int n_eff = n_rows_dev ? min(*n_rows_dev, M) : M;
+  if (m0 >= n_eff) return;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const size_t ldk = (size_t)K * sizeof(T);
+  auto phys = [&](int r) { return rows ? rows[r] : r; };
+
+  KRowLoader<GEMM_BM> la;
+  la.init(tid, [&](int r) {
+    int lr = m0 + r;
+    int row = lr < n_eff ? phys(lr) : phys(0);
+    return reinterpret_cast<const char *>(x) + (size_t)row * ldk;
+  });
+  KRowLoader<BN> lb;
+  lb.init(tid, [&](int r) {
+    const T *w = r < HALF ? wg : wu;
+    return reinterpret_cast<const char *>(w) + (size_t)(n0 + (r & (HALF - 1))) * ldk;
+  });
+
+  f32x16_t acc[2][8];
+#pragma unroll
+  for (int bm = 0; bm < 2; ++bm) {
+    f32x16_t b0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      int lr = m0 + acc_row(wave, bm, i, lane);
+      b0[i] = (beta != nullptr && lr < n_eff) ? beta[phys(lr)] : 0.0f;
+    }
+#pragma unroll
+    for (int bn = 0; bn < 4; ++bn) acc[bm][bn] = b0;
+#pragma unroll
+    for (int bn = 4; bn < 8; ++bn) acc[bm][bn] = f32x16_t{};
+  }
+
+  gemm_mainloop<D, BN>(acc, la, lb, K / (KCHUNK_BYTES / (int)sizeof(T)), smem);
+
+  const int col = lane & 31;
+#pragma unroll
+  for (int bm = 0; bm < 2; ++bm) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int lr = m0 + acc_row(wave, bm, i, lane);
+      if (lr >= n_eff) continue;
+#pragma unroll
+      for (int bn = 0; bn < 4; ++bn) {
+        const T hb = from_f32<D>(acc[bm][bn][i]);
+        const bool act = active_bits(hb);
+        const float h = act ? to_f32(hb) : 0.0f;
+        const size_t j = (size_t)n0 + 32 * bn + col;
+        a_ws[(size_t)lr * F + j] = from_f32<D>(h * acc[bm][bn + 4][i]);
+        if (h_out != nullptr && lr < h_cap) h_out[(size_t)lr * F + j] = act ? hb : T(0);
+      }
+    }
+  }
+}
+
+template <Dt D>
+__global__ __launch_bounds__(GEMM_THREADS) void k_down(
+    const typename DtT<D>::T *__restrict__ a_ws, const typename DtT<D>::T *__restrict__ wd, int M, int K,
+    int N, const int *__restrict__ rows, const int *__restrict__ n_rows_dev,
+    typename DtT<D>::T *__restrict__ y) {
+  using T = typename DtT<D>::T;
+  constexpr int BN = 256;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int mt = (M + GEMM_BM - 1) / GEMM_BM, ntl = N / BN;
+  int tm, tn;
+  tile_coords(blockIdx.x, mt, ntl, tm, tn);
+  const int m0 = tm * GEMM_BM, n0 = tn * BN;
+  const int n_eff = n_rows_dev ? min(*n_rows_dev, M) : M;
+  if (m0 >= n_eff) return;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const size_t ldk = (size_t)K * sizeof(T);
+
+  KRowLoader<GEMM_BM> la;
+  la.init(tid, [&](int r) {
+    int lr = min(m0 + r, n_eff - 1);
+    return reinterpret_cast<const char *>(a_ws) + (size_t)lr * ldk;
+  });
+  NColLoader<D, BN> lb;
+  lb.init(tid, wd, (size_t)N * sizeof(T), n0);
+
+  f32x16_t acc[2][8];
+#pragma unroll
+  for (int bm = 0; bm < 2; ++bm)
+#pragma unroll
+    for (int bn = 0; bn < 8; ++bn) acc[bm][bn] = f32x16_t{};
+
+  gemm_mainloop<D, BN>(acc, la, lb, K / (KCHUNK_BYTES / (int)sizeof(T)), smem);
+
+  const int col = lane & 31;
+#pragma unroll
+  for (int bm = 0; bm < 2; ++bm) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int lr = m0 + acc_row(wave, bm, i, lane);
+      if (lr >= n_eff) continue;
+      const size_t prow = rows ? (size_t)rows[lr] : (size_t)lr;
+#pragma unroll
+      for (int bn = 0; bn < 8; ++bn) y[prow * N + n0 + 32 * bn + col] = from_f32<D>(acc[bm][bn][i]);
+    }
+  }
+}
+
+template <Dt D>
+static hipError_t launch_gate_up(const DenseArgs &a, hipStream_t s) {
+  using T = typename DtT<D>::T;
+  auto kern = k_gate_up<D>;
+  const int lds = gemm_lds_bytes(256);
+  hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (e != hipSuccess) return e;
+  const int mt = (a.M + GEMM_BM - 1) / GEMM_BM, ntl = a.F / 128;
+  hipLaunchKernelGGL(kern, dim3(mt * ntl), dim3(GEMM_THREADS), lds, s, (const T *)a.x, (const T *)a.wg,
+                     (const T *)a.wu, a.beta, a.M, a.d, a.F, a.rows, a.n_rows_dev, (T *)a.a_ws,
+                     (T *)a.h_out, a.h_cap);
+  return hipGetLastError();
+}
+
+template <Dt D>
+static hipError_t launch_down(const DenseArgs &a, hipStream_t s) {
+  using T = typename DtT<D>::T;
+  auto kern = k_down<D>;
+  const int lds = gemm_lds_bytes(256);
+  hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (e != hipSuccess) return e;
+  const int mt = (a.M + GEMM_BM - 1) / GEMM_BM, ntl = a.d / 256;
+  hipLaunchKernelGGL(kern, dim3(mt * ntl), dim3(GEMM_THREADS), lds, s, (const T *)a.a_ws, (const T *)a.wd,
+                     a.M, a.F, a.d, a.rows, a.n_rows_dev, (T *)a.y);
+  return hipGetLastError();
+}
+
+hipError_t dense_gate_up(const DenseArgs &a, hipStream_t s) {
+  if (a.M <= 0) return hipSuccess;
+  return a.dtype == Dt::BF16 ? launch_gate_up<Dt::BF16>(a, s) : launch_gate_up<Dt::F32>(a, s);
+}
+
+hipError_t dense_down(const DenseArgs &a, hipStream_t s) {
+  if (a.M <= 0) return hipSuccess;
+  return a.dtype == Dt::BF16 ? launch_down<Dt::BF16>(a, s) : launch_down<Dt::F32>(a, s);
+}
+
+}  // namespace twell

@@ -1,0 +1,247 @@
+// MFMA GEMM mainloop for gfx950 shared by the gate, gate+up and down kernels.
+//
+// C[m][n] = sum_k A[m][k] * B(k, n), accumulated in fp32 on the matrix cores:
+// bf16 operands use v_mfma_f32_32x32x16_bf16, fp32 operands v_mfma_f32_32x32x2_f32.
+//
+// Workgroup tile: BM = 256 rows x BN (128 or 256) columns, 4 waves.  Wave w
+// owns rows [64w, 64w + 64) and every column of the tile, i.e. 2 x BN/32
+// blocks of 32x32 accumulators (a whole TwELL tile row sits in one wave,
+// which lets the TwELL epilogue run without any cross-wave exchange).
+//
+// K is consumed 128 bytes at a time (64 bf16 / 32 fp32).  Each stage keeps
+// A [256][128 B] and B [BN][128 B] in LDS; every 128-byte row is 8 chunks of
+// 16 bytes, and chunk c of row r sits at physical chunk c ^ ((r >> 1) & 7),
+// which makes the 16-lane phases of ds_read_b128 conflict-free on the 64-bank
+// gfx950 LDS (two consecutive rows fill the 256-byte bank width).  Two stages
+// are double-buffered; the next stage's global loads are issued before the
+// current stage's MFMAs and written to LDS after them.
+#pragma once
+
+#include "common.hpp"
+
+namespace twell {
+
+constexpr int GEMM_BM = 256;
+constexpr int GEMM_THREADS = 256;
+constexpr int KCHUNK_BYTES = 128;  // K bytes per stage and LDS row
+
+__host__ __device__ constexpr int gemm_lds_bytes(int bn) { return 2 * (GEMM_BM + bn) * KCHUNK_BYTES; }
+
+__device__ __forceinline__ int lds_off(int row, int chunk) {
+  return row * KCHUNK_BYTES + ((chunk ^ ((row >> 1) & 7)) << 4);
+}
+
+// ---- operand loaders -------------------------------------------------------
+// Each loader moves one 128-byte K slab of its operand for the workgroup tile:
+// issue(kt) reads global memory into registers, commit(dst) writes LDS.
+
+// K-contiguous operand rows (A = activations; B = weight rows W[n][k]).
+// Row r of the tile comes from row_ptr(r).  NR = rows in the tile.
+template <int NR>
+struct KRowLoader {
+  static constexpr int PER_THREAD = NR * 8 / GEMM_THREADS;
+  const char *ptr[PER_THREAD];
+  u32x4_t reg[PER_THREAD];
+  int row0, chunk;
+
+  template <class RowPtr>
+  __device__ __forceinline__ void init(int tid, RowPtr row_ptr) {
+    row0 = tid >> 3;
+    chunk = tid & 7;
+#pragma unroll
+    for (int i = 0; i < PER_THREAD; ++i) ptr[i] = row_ptr(row0 + 32 * i) + chunk * 16;
+  }
+  __device__ __forceinline__ void issue(int kt) {
+#pragma unroll
+    for (int i = 0; i < PER_THREAD; ++i)
+      reg[i] = *reinterpret_cast<const u32x4_t *>(ptr[i] + (size_t)kt * KCHUNK_BYTES);
+  }
+  __device__ __forceinline__ void commit(char *dst) {
+#pragma unroll
+    for (int i = 0; i < PER_THREAD; ++i)
+      *reinterpret_cast<u32x4_t *>(dst + lds_off(row0 + 32 * i, chunk)) = reg[i];
+  }
+};
+
+// N-contiguous B operand (W[k][n] row-major, e.g. W_d [F][d] in the down
+// projection): loaded as small k x n blocks and transposed in registers so
+// that LDS holds the same [n][k] layout as a K-contiguous operand.
+template <Dt D, int BN> struct NColLoader;
+
+// bf16: 8 (k) x 8 (n) blocks, 16 bytes per k row; 8 x 8 transpose with v_perm.
+template <int BN>
+struct NColLoader<Dt::BF16, BN> {
+  static constexpr int BLOCKS = BN / 8 * 8;  // (BN/8 n-blocks) x (8 k-blocks of 8)
+  static constexpr int PER_THREAD = BLOCKS / GEMM_THREADS;
+  const char *base;
+  size_t ld;  // bytes per k row
+  int kb[PER_THREAD], nb[PER_THREAD];
+  u32x4_t reg[PER_THREAD][8];
+
+  __device__ __forceinline__ void init(int tid, const void *b, size_t ld_bytes, int n0) {
+    ld = ld_bytes;
+    base = reinterpret_cast<const char *>(b) + (size_t)n0 * 2;
+#pragma unroll
+    for (int p = 0; p < PER_THREAD; ++p) {
+      int blk = tid + GEMM_THREADS * p;
+      kb[p] = blk & 7;
+      nb[p] = blk >> 3;
+    }
+  }
+  __device__ __forceinline__ void issue(int kt) {
+#pragma unroll
+    for (int p = 0; p < PER_THREAD; ++p) {
+      const char *src = base + (size_t)(kt * 64 + kb[p] * 8) * ld + nb[p] * 16;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) reg[p][i] = *reinterpret_cast<const u32x4_t *>(src + i * ld);
+    }
+  }
+  __device__ __forceinline__ void commit(char *dst) {
+#pragma unroll
+    for (int p = 0; p < PER_THREAD; ++p) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        // output row n = 8*nb + j holds k = 8*kb .. 8*kb+7: pair (k=2m, 2m+1) per dword
+        const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+        u32x4_t o;
+        o.x = __builtin_amdgcn_perm(reg[p][1][j >> 1], reg[p][0][j >> 1], sel);
+        o.y = __builtin_amdgcn_perm(reg[p][3][j >> 1], reg[p][2][j >> 1], sel);
+        o.z = __builtin_amdgcn_perm(reg[p][5][j >> 1], reg[p][4][j >> 1], sel);
+        o.w = __builtin_amdgcn_perm(reg[p][7][j >> 1], reg[p][6][j >> 1], sel);
+        *reinterpret_cast<u32x4_t *>(dst + lds_off(nb[p] * 8 + j, kb[p])) = o;
+      }
+    }
+  }
+};
+
+// fp32: 4 (k) x 4 (n) blocks; 4 x 4 transpose is a register renaming.
+template <int BN>
+struct NColLoader<Dt::F32, BN> {
+  static constexpr int BLOCKS = BN / 4 * 8;
+  static constexpr int PER_THREAD = BLOCKS / GEMM_THREADS;
+  const char *base;
+  size_t ld;
+  int kb[PER_THREAD], nb[PER_THREAD];
+  u32x4_t reg[PER_THREAD][4];
+
+  __device__ __forceinline__ void init(int tid, const void *b, size_t ld_bytes, int n0) {
+    ld = ld_bytes;
+    base = reinterpret_cast<const char *>(b) + (size_t)n0 * 4;
+#pragma unroll
+    for (int p = 0; p < PER_THREAD; ++p) {
+      int blk = tid + GEMM_THREADS * p;
+      kb[p] = blk & 7;
+      nb[p] = blk >> 3;
+    }
+  }
+  __device__ __forceinline__ void issue(int kt) {
+#pragma unroll
+    for (int p = 0; p < PER_THREAD; ++p) {
+      const char *src = base + (size_t)(kt * 32 + kb[p] * 4) * ld + nb[p] * 16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) reg[p][i] = *reinterpret_cast<const u32x4_t *>(src + i * ld);
+    }
+  }
+  __device__ __forceinline__ void commit(char *dst) {
+#pragma unroll
+    for (int p = 0; p < PER_THREAD; ++p) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        u32x4_t o = {reg[p][0][j], reg[p][1][j], reg[p][2][j], reg[p][3][j]};
+        *reinterpret_cast<u32x4_t *>(dst + lds_off(nb[p] * 4 + j, kb[p])) = o;
+      }
+    }
+  }
+};
+
+// ---- MFMA step ----------------------------------------------------------------
+
+template <Dt D> struct Mfma;
+template <> struct Mfma<Dt::BF16> {
+  __device__ __forceinline__ static void step(f32x16_t &acc, const u32x4_t &a, const u32x4_t &b) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
+  }
+};
+template <> struct Mfma<Dt::F32> {
+  // One 16-byte chunk per lane holds 4 k values; lanes 0-31 and 32-63 carry
+  // different k, and A and B use the same assignment, so 4 rank-2 MFMAs cover
+  // the 8 k values of the chunk pair.
+  __device__ __forceinline__ static void step(f32x16_t &acc, const u32x4_t &a, const u32x4_t &b) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[j]), __uint_as_float(b[j]), acc, 0, 0, 0);
+  }
+};
+
+// Accumulate one LDS stage into acc[2][BN/32].
+template <Dt D, int BN>
+__device__ __forceinline__ void mfma_stage(f32x16_t (&acc)[2][BN / 32], const char *stage, int wave, int lane) {
+  const char *As = stage;
+  const char *Bs = stage + GEMM_BM * KCHUNK_BYTES;
+  const int r = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    u32x4_t a[2], b[BN / 32];
+#pragma unroll
+    for (int bm = 0; bm < 2; ++bm)
+      a[bm] = *reinterpret_cast<const u32x4_t *>(As + lds_off(64 * wave + 32 * bm + r, 2 * g + h));
+#pragma unroll
+    for (int bn = 0; bn < BN / 32; ++bn)
+      b[bn] = *reinterpret_cast<const u32x4_t *>(Bs + lds_off(32 * bn + r, 2 * g + h));
+#pragma unroll
+    for (int bm = 0; bm < 2; ++bm)
+#pragma unroll
+      for (int bn = 0; bn < BN / 32; ++bn) Mfma<D>::step(acc[bm][bn], a[bm], b[bn]);
+  }
+}
+
+// The double-buffered mainloop over nk K-slabs.
+template <Dt D, int BN, class LA, class LB>
+__device__ __forceinline__ void gemm_mainloop(f32x16_t (&acc)[2][BN / 32], LA &la, LB &lb, int nk, char *smem) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  constexpr int STAGE = (GEMM_BM + BN) * KCHUNK_BYTES;
+  la.issue(0);
+  lb.issue(0);
+  la.commit(smem);
+  lb.commit(smem + GEMM_BM * KCHUNK_BYTES);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    char *cur = smem + (kt & 1) * STAGE;
+    char *nxt = smem + ((kt + 1) & 1) * STAGE;
+    const bool more = kt + 1 < nk;
+    if (more) {
+      la.issue(kt + 1);
+      lb.issue(kt + 1);
+    }
+    mfma_stage<D, BN>(acc, cur, wave, lane);
+    if (more) {
+      la.commit(nxt);
+      lb.commit(nxt + GEMM_BM * KCHUNK_BYTES);
+    }
+    __syncthreads();
+  }
+}
+
+// Accumulator element (bm, bn, i) of lane l sits at tile row
+//   64*wave + 32*bm + 8*(i/4) + 4*(l/32) + (i%4)   and tile column 32*bn + (l%32).
+__device__ __forceinline__ int acc_row(int wave, int bm, int i, int lane) {
+  return 64 * wave + 32 * bm + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+}
+
+// Grouped, XCD-aware order of (m-tile, n-tile) pairs: the tiles that run at the
+// same time on one XCD share GROUP_M row panels of A and a run of B panels.
+__device__ __forceinline__ void tile_coords(int bid, int mt, int nt, int &tm, int &tn) {
+  const int total = mt * nt;
+  const int L = xcd_linear(bid, total);
+  constexpr int GROUP_M = 4;
+  const int per_group = GROUP_M * nt;
+  const int g = L / per_group;
+  const int first_m = g * GROUP_M;
+  const int gm = min(GROUP_M, mt - first_m);
+  const int in = L - g * per_group;
+  tm = first_m + in % gm;
+  tn = in / gm;
+}
+
+}  // namespace twell

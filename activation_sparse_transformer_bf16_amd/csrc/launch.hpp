@@ -1,0 +1,100 @@
+// Internal launcher interface between the C ABI (api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace twell {
+
+// Gate matmul + TwELL epilogue (tile == matmul N tile).
+struct GateArgs {
+  Dt dtype;
+  int tile;
+  const void *x;      // [M][K]
+  const void *wg;     // [N][K]
+  const float *beta;  // [M] or null
+  int M, K, N, cap;
+  uint16_t *cnt;      // [M][N/tile]
+  void *val;          // [M][N/tile][cap]
+  uint8_t *idx;       // [M][N/tile][cap]
+  void *pre_out;      // [M][N] or null
+};
+hipError_t gate_twell(const GateArgs &a, hipStream_t s);
+
+// Overflow scan: row flags, ascending overflow row list, its true length.
+struct ScanArgs {
+  const uint16_t *cnt;  // [T][nt]
+  int T, nt, cap;
+  uint8_t *row_flag;    // [T] or null
+  int *ovf_rows;        // [ovf_cap] (may be null when ovf_cap == 0)
+  int ovf_cap;
+  int *n_ovf;           // [1]
+};
+hipError_t overflow_scan(const ScanArgs &a, hipStream_t s);
+
+// Sparse up / down projections over the TwELL entries of non-overflow rows.
+struct SparseArgs {
+  Dt dtype;
+  int T, d, F, tile, cap;
+  const uint16_t *cnt;
+  const void *val;
+  const uint8_t *idx;
+  const uint8_t *row_flag;  // [T], 1 = overflow row (handled by the dense fallback)
+  const void *x;            // [T][d]
+  const void *wu;           // [F][d]
+  const void *wd;           // [F][d]
+  float *vbuf;              // [T][nt][cap] fp32: h * u per TwELL slot
+  void *y;                  // [T][d]
+};
+hipError_t sparse_up(const SparseArgs &a, hipStream_t s);
+hipError_t sparse_down(const SparseArgs &a, hipStream_t s);
+
+// Dense ReGLU FFN on the matrix cores over a (possibly gathered) set of rows:
+// logical row r < n_rows reads x[rows ? rows[r] : r] and writes y at the same
+// physical row.  n_rows_dev (device int) overrides M when non-null; the grid
+// is sized for M and workgroups past the device count exit at once.
+struct DenseArgs {
+  Dt dtype;
+  const void *x, *wg, *wu, *wd;
+  const float *beta;   // indexed by physical row, or null
+  void *y;             // [T][d]
+  int M, d, F;         // M = grid rows (T)
+  const int *rows;     // [M] or null (identity)
+  const int *n_rows_dev;
+  void *a_ws;          // [M][F] storage dtype, logical rows
+  void *h_out;         // [h_cap][F] storage dtype (ReLU'd gate rows) or null
+  int h_cap;
+};
+hipError_t dense_gate_up(const DenseArgs &a, hipStream_t s);
+hipError_t dense_down(const DenseArgs &a, hipStream_t s);
+
+// Standalone TwELL packing of an explicit pre-activation matrix.
+struct PackArgs {
+  Dt dtype;
+  int tile, cap;
+  const void *pre;  // [T][F]
+  int T, F;
+  uint16_t *cnt;
+  void *val;
+  uint8_t *idx;
+};
+hipError_t pack_tiles(const PackArgs &a, hipStream_t s);
+
+// dense[r] = ReLU(pre[ovf_rows[r]]) for r < min(*n_ovf, ovf_cap).
+struct DenseRowsArgs {
+  Dt dtype;
+  const void *pre;
+  int T, F;
+  const int *ovf_rows;
+  const int *n_ovf;
+  int ovf_cap;
+  void *dense;
+};
+hipError_t pack_dense_rows(const DenseRowsArgs &a, hipStream_t s);
+
+// *p = 0 with a one-thread kernel (safe under stream capture).
+hipError_t zero_int(int *p, hipStream_t s);
+
+}  // namespace twell

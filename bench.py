@@ -1,0 +1,286 @@
+#!/usr/bin/env python3
+"""Benchmark of the TwELL sparse-FFN forward on one MI355X.
+
+One step = one call of twell_ffn_forward (gate matmul + TwELL epilogue,
+overflow scan, sparse up and down projections, dense fallback) over the whole
+token batch of the workload, with inputs resident in HBM.  Prints ONE JSON
+line on stdout:
+
+  value        tokens/s of the sparse forward (T * steps / timed seconds)
+  roofline     the dominant kernel (the gate matmul with the TwELL epilogue)
+               against the bf16 matrix-core peak
+  cpu_baseline the float64 CPU oracle timed on a bounded sample of the batch
+  speedups     against the library's dense matrix-core FFN and against a
+               torch (hipBLASLt) dense FFN on the same inputs
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload NAME]
+                       [--no-cpu-baseline] [--sweep] [--sweep-out FILE]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "sparse-FFN tokens/s at 99% sparsity; achieved HBM GB/s vs peak; speedup vs dense"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+MFMA_F32_PEAK_TFLOPS = 157.3
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="layer_1p5b_bf16")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work to aim for")
+    p.add_argument("--sweep", action="store_true", help="also run the density sweep (stderr / --sweep-out)")
+    p.add_argument("--sweep-out", default=None)
+    p.add_argument("--no-torch", action="store_true", help="skip the torch (hipBLASLt) dense FFN")
+    return p.parse_args()
+
+
+def to_dev(a, dtype, dev):
+    import numpy as np
+    import torch
+    if dtype == "f32":
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+
+def event_time(fn, steps, warmup):
+    """Average ms per call over exactly `steps` calls, HIP events on the current stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    e0.record(s)
+    for _ in range(steps):
+        fn()
+    e1.record(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    return e0.elapsed_time(e1) / steps, wall
+
+
+def cold_time(fn, reps, flush_buf):
+    """Median ms of single calls, each after overwriting a 1 GiB buffer (evicts L2 and MALL)."""
+    import torch
+    s = torch.cuda.current_stream()
+    times = []
+    for _ in range(reps):
+        flush_buf.add_(1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        fn()
+        e1.record(s)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    times.sort()
+    return times[len(times) // 2]
+
+
+def gather_bytes(T, d, F, tile, cap, s, nnz_kept, rows_sparse):
+    """Algorithmic bytes of the up + down stages: one W_u^T row and one W_d row per
+    active entry of the non-overflow rows, the x row read and y row written per
+    such token, and the TwELL row (counts, values, indices) it reads."""
+    nt = F // tile
+    return (nnz_kept * 2 * d * s + rows_sparse * d * (s + s)
+            + rows_sparse * nt * (2 + cap * (s + 1)))
+
+
+def measure(w, steps, warmup, want_torch=True, want_cold=True):
+    import numpy as np
+    import torch
+    import activation_sparse_transformer_bf16_amd as tw
+
+    dev = torch.device("cuda:0")
+    t0 = time.perf_counter()
+    inp = w.inputs()
+    log(f"[bench] inputs for {w.name} generated in {time.perf_counter() - t0:.1f}s")
+    x, wg, wu, wd = (to_dev(a, w.dtype, dev) for a in (inp.x, inp.w_gate, inp.w_up, inp.w_down))
+    b = torch.from_numpy(inp.gate_bias).to(dev)
+    T, d, F = w.T, w.d, w.F
+    s = 2 if w.dtype == "bf16" else 4
+
+    packed = tw.TwellMatrix.empty(T, F, w.tile, w.cap, x.dtype, dev, T, dense=False)
+    y = torch.empty((T, d), dtype=x.dtype, device=dev)
+    ws = torch.empty((tw.twell_ffn_workspace_size(T, d, F, w.tile, w.cap, x.dtype),), dtype=torch.uint8,
+                     device=dev)
+    yd = torch.empty_like(y)
+    wsd = torch.empty((tw.dense_ffn_workspace_size(T, d, F, x.dtype),), dtype=torch.uint8, device=dev)
+
+    sparse = lambda: tw.twell_ffn_forward(x, wg, wu, wd, b, packed=packed, y=y, workspace=ws)
+    gate = lambda: tw.twell_gate_pack(x, wg, b, packed=packed, scan=False)
+    rest = lambda: tw.twell_sparse_ffn(packed, x, wg, wu, wd, b, y=y, workspace=ws)
+    dense = lambda: tw.dense_ffn_forward(x, wg, wu, wd, b, y=yd, workspace=wsd)
+
+    ms_sparse, wall = event_time(sparse, steps, warmup)
+    log(f"[bench] sparse forward: {ms_sparse * 1e3:.1f} us/step ({wall:.2f}s wall for {steps} steps)")
+    ms_gate, _ = event_time(gate, steps, warmup)
+    ms_rest, _ = event_time(rest, steps, warmup)
+    ms_dense, _ = event_time(dense, steps, warmup)
+    log(f"[bench] gate {ms_gate * 1e3:.1f} us, scan+up+down+fallback {ms_rest * 1e3:.1f} us, "
+        f"dense {ms_dense * 1e3:.1f} us")
+
+    ms_torch = None
+    if want_torch:
+        import torch.nn.functional as Fn
+
+        def torch_dense():
+            pre = torch.addmm(b[:, None].to(x.dtype), x, wg.t())  # bias in the activation dtype
+            a = torch.relu(pre) * Fn.linear(x, wu)
+            return a @ wd
+
+        ms_torch, _ = event_time(torch_dense, steps, warmup)
+        log(f"[bench] torch (hipBLASLt) dense {ms_torch * 1e3:.1f} us")
+
+    cold = {}
+    if want_cold:
+        flush = torch.empty((1 << 28,), dtype=torch.float32, device=dev)
+        cold = {"sparse_ms": cold_time(sparse, 7, flush), "dense_ms": cold_time(dense, 7, flush)}
+        del flush
+
+    # one more forward to read the statistics of this batch
+    sparse()
+    torch.cuda.synchronize()
+    cnt = packed.cnt.cpu().numpy().view(np.uint16).astype(np.int64)
+    n_ovf = int(packed.n_ovf.item())
+    ovf = (cnt > w.cap).any(axis=1)
+    nnz = int(cnt.sum())
+    nnz_kept = int(cnt[~ovf].sum())
+    rows_sparse = int((~ovf).sum())
+    B_alg = gather_bytes(T, d, F, w.tile, w.cap, s, nnz_kept, rows_sparse)
+    flops_gate = 2.0 * T * d * F
+    peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
+    res = {
+        "T": T, "ms_sparse": ms_sparse, "ms_gate": ms_gate, "ms_rest": ms_rest, "ms_dense": ms_dense,
+        "ms_torch": ms_torch, "cold": cold, "n_ovf": n_ovf, "density": nnz / (T * F),
+        "nnz": nnz, "nnz_kept": nnz_kept, "rows_sparse": rows_sparse, "gather_bytes": B_alg,
+        "gate_tflops": flops_gate / (ms_gate * 1e-3) / 1e12, "peak": peak,
+        "dense_tflops": 3 * flops_gate / (ms_dense * 1e-3) / 1e12,
+        "gather_gbs": B_alg / (ms_rest * 1e-3) / 1e9,
+    }
+    del x, wg, wu, wd, b, packed, y, ws, yd, wsd
+    torch.cuda.empty_cache()
+    return res, inp
+
+
+def cpu_baseline(w, inp, budget_s):
+    """The float64 oracle (gate, TwELL pack, dense FFN) on the first n tokens."""
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    from oracle import ffn, gate_pre, pack, round_to_storage
+
+    cores = len(os.sched_getaffinity(0))
+
+    def run(n):
+        r = slice(0, n)
+        t0 = time.perf_counter()
+        pre = gate_pre(inp.x[r], inp.w_gate, inp.gate_bias[r], w.dtype)
+        pack(round_to_storage(pre, w.dtype), w.dtype, w.tile, w.cap)
+        ffn(inp.x[r], inp.w_gate, inp.w_up, inp.w_down, inp.gate_bias[r], w.dtype)
+        return time.perf_counter() - t0
+
+    with threadpool_limits(limits=cores):
+        used = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        run(min(w.T, 64))                       # warm up numpy / BLAS
+        n0 = min(w.T, 512)
+        t_cal = run(n0)
+        n = int(min(w.T, max(n0, n0 * budget_s / max(t_cal, 1e-6))) // 256 * 256) or n0
+        t = run(n)
+    return {"value": n / t, "unit": "tokens/s", "cores": int(used), "kind": "oracle",
+            "sample": f"first {n} of {w.T} tokens of the same batch, one float64 pass "
+                      f"(gate, TwELL pack, dense FFN) in {t:.1f}s; cpu threads available {cores}"}
+
+
+def sweep(args):
+    from workloads.configs import SWEEP_DENSITIES
+    from workloads import workload
+    out = []
+    for rho in SWEEP_DENSITIES:
+        w = workload(f"sweep@{rho}")
+        r, _ = measure(w, max(5, args.steps // 2), 2, want_torch=False, want_cold=False)
+        rec = {"density_target": rho, "density": r["density"], "n_ovf": r["n_ovf"],
+               "sparse_tokens_per_s": w.T / (r["ms_sparse"] * 1e-3),
+               "dense_tokens_per_s": w.T / (r["ms_dense"] * 1e-3),
+               "speedup_vs_dense": r["ms_dense"] / r["ms_sparse"]}
+        log("[sweep] " + json.dumps(rec))
+        out.append(rec)
+    if args.sweep_out:
+        with open(args.sweep_out, "w") as f:
+            json.dump(out, f, indent=1)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU: --gpus {args.gpus} is not supported "
+              "(the TwELL forward shards by tokens with no exchange; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    from workloads import workload
+
+    w = workload(args.workload)
+    r, inp = measure(w, args.steps, args.warmup, want_torch=not args.no_torch)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, inp, args.cpu_budget)
+    if args.sweep:
+        sweep(args)
+
+    ach = r["gate_tflops"]
+    record = {
+        "metric": METRIC,
+        "value": w.T / (r["ms_sparse"] * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["ms_sparse"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic: seeded Gaussian x and weights (var 1/fan_in), per-token gate bias for the density",
+        "config": {**w.summary(), "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": ach, "peak": r["peak"], "unit": "TFLOP/s",
+                     "frac": ach / r["peak"], "traffic": None,
+                     "kernel": "k_gate_twell (gate matmul + TwELL epilogue)"},
+        "cpu_baseline": cpu,
+        "speedup_vs_dense": r["ms_dense"] / r["ms_sparse"],
+        "speedup_vs_torch_dense": (r["ms_torch"] / r["ms_sparse"]) if r["ms_torch"] else None,
+        "stages_us": {"gate_twell": r["ms_gate"] * 1e3, "scan_up_down_fallback": r["ms_rest"] * 1e3,
+                      "forward": r["ms_sparse"] * 1e3, "dense_ffn": r["ms_dense"] * 1e3,
+                      "torch_dense_ffn": r["ms_torch"] * 1e3 if r["ms_torch"] else None},
+        "cold_us": {k: v * 1e3 for k, v in r["cold"].items()},
+        "gather": {"bytes_alg": r["gather_bytes"], "achieved_GBps": r["gather_gbs"],
+                   "frac_of_hbm_peak": r["gather_gbs"] / HBM_PEAK_GBS,
+                   "note": "scan+up+down+fallback stage time; bytes per active entry = one W_u^T row + one W_d row"},
+        "dense_mfma_tflops": r["dense_tflops"],
+        "density": r["density"],
+        "n_ovf": r["n_ovf"],
+    }
+    print(json.dumps(record), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,213 @@
+/*
+ * twell.h -- C ABI of the MI355X (gfx950) TwELL sparse-FFN library (libtwell.so).
+ *
+ * The library computes the forward pass of one ReLU-gated ("ReGLU")
+ * transformer feed-forward layer
+ *
+ *     pre = x W_g^T + beta,   h = ReLU(pre),   u = x W_u^T,   y = (h * u) W_d
+ *
+ * where the gate activations h are about 99% zero and are carried in the
+ * TwELL (tile-wise ELLPACK) format, with a dense backup for rows that do not
+ * fit.  Sources: gist.science "Sparser, Faster, Lighter Transformer Language
+ * Models", Resumen Técnico §2.A (TwELL: hidden columns cut into tiles, the
+ * non-zeros of each tile packed in the epilogue of the dense gate matmul, no
+ * separate conversion pass; hybrid format with a dense backup matrix for
+ * overflowing rows) and §2.B (inference kernel: up and down projections driven
+ * by the TwELL gate activations); q2bstudio post on TwELL, third and fourth
+ * paragraphs (ReLU in place of SiLU; compact ELL plus dense backup for rows
+ * with many non-zeros); estadored.mx news item on the same paper (TwELL cuts
+ * index management and memory traffic).  The pages fix no layout, precision
+ * or tile size; every such choice below is this library's own definition.
+ *
+ * General rules for every entry point
+ * -----------------------------------
+ * - Pointers inside arguments are DEVICE pointers unless stated otherwise.
+ *   Structures passed by pointer (twell_matrix) live in HOST memory.
+ * - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
+ *   NULL = the default stream).  The library never allocates device memory,
+ *   never synchronises the host and keeps no pointer after returning.
+ * - Arguments are validated on the host before any HIP call.  On any error
+ *   status nothing has been launched and every output is untouched.
+ * - Device buffers must be 16-byte aligned (torch allocations are).
+ * - Dtypes: TWELL_F32 (IEEE binary32) or TWELL_BF16 (bfloat16, bit pattern
+ *   in a uint16).  All dot products accumulate in fp32; stored values are
+ *   rounded to the storage dtype with round-to-nearest-even.
+ * - Shapes: T tokens (T >= 0; T == 0 is a no-op apart from *n_ovf = 0, and
+ *   x and y may then be NULL),
+ *   d = d_model, F = d_ff.  d must be a multiple of 256 (fp32) or 512 (bf16)
+ *   and at most 8192; F must be a multiple of the TwELL tile width.
+ * - Weights are rows per hidden unit, row-major: w_gate [F][d] (= W_g^T, the
+ *   nn.Linear weight layout), w_up [F][d] (= W_u^T), w_down [F][d] (= W_d,
+ *   transposed once at load time so that every hidden unit's down row is
+ *   contiguous).  x and y are [T][d] row-major.  gate_bias is one fp32 value
+ *   per token ([T]) or NULL for none.
+ * - Thread safety: every entry point is reentrant; calls on different
+ *   streams do not interact.  twell_last_error() is thread-local.
+ */
+#ifndef TWELL_H
+#define TWELL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TWELL_ABI_VERSION 1
+
+typedef enum {
+  TWELL_OK = 0,
+  TWELL_ERR_INVALID_ARG = 1, /* NULL required pointer, bad enum, negative or inconsistent size */
+  TWELL_ERR_UNSUPPORTED = 2, /* valid but not built: tile, cap, d, dtype or alignment */
+  TWELL_ERR_WORKSPACE = 3,   /* ws_bytes smaller than the *_workspace_size() value */
+  TWELL_ERR_HIP = 4          /* a HIP call or kernel launch failed; see twell_last_error() */
+} twell_status;
+
+typedef enum { TWELL_F32 = 0, TWELL_BF16 = 1 } twell_dtype;
+
+/*
+ * One TwELL matrix [rows][cols] (token-major), described by caller-owned
+ * device buffers.  Definition (this library's reading of the TwELL format,
+ * gist.science Resumen Técnico §2.A):
+ *
+ *   A value v is ACTIVE iff IEEE v > 0, decided on the stored bits: fp32
+ *   0 < bits <= 0x7F800000, bf16 0 < bits <= 0x7F80 (bits read as signed).
+ *   +denormals and +inf are active; +-0, negatives and NaNs are not.
+ *
+ *   For row t and tile k (columns [k*tile, (k+1)*tile)):
+ *     cnt[t][k]          number of active columns in the tile (NOT capped).
+ *     val[t][k][s],      for s < min(cnt, cap): the bits of the s-th active
+ *     idx[t][k][s]       column in ascending column order, and its offset
+ *                        inside the tile (0..tile-1).  Slots s >= cnt hold
+ *                        +0 and 0.
+ *   Row t OVERFLOWS iff cnt[t][k] > cap for some k (cnt == cap still fits).
+ *   Its TwELL slots still hold the first min(cnt, cap) entries per tile.
+ *     ovf_rows[r]        the overflowing rows in ascending order, r < n_ovf.
+ *     *n_ovf             the true number of overflowing rows (may exceed
+ *                        ovf_cap, in which case only ovf_cap are listed).
+ *     dense[r][:]        ReLU of overflow row ovf_rows[r] (active values bit
+ *                        for bit, +0 elsewhere), r < min(n_ovf, ovf_cap);
+ *                        the dense backup of the hybrid format.
+ */
+typedef struct {
+  int32_t rows, cols;   /* T, F; cols % tile == 0 */
+  int32_t tile;         /* W: 128 or 256 */
+  int32_t cap;          /* C: 1 <= cap <= min(tile, 64) */
+  twell_dtype dtype;    /* value dtype == activation dtype */
+  uint16_t *cnt;        /* [rows][cols/tile] */
+  void *val;            /* [rows][cols/tile][cap], dtype */
+  uint8_t *idx;         /* [rows][cols/tile][cap] */
+  int32_t *ovf_rows;    /* [ovf_cap] */
+  int32_t *n_ovf;       /* [1] */
+  void *dense;          /* [ovf_cap][cols], dtype; may be NULL (not written) */
+  int32_t ovf_cap;      /* rows available in ovf_rows (and dense when non-NULL) */
+} twell_matrix;
+
+/* ABI version of the loaded library (TWELL_ABI_VERSION). */
+int twell_abi_version(void);
+
+/* Static text for a status code. */
+const char *twell_status_str(twell_status s);
+
+/* Text of the last TWELL_ERR_HIP (or validation) error on this thread; "" if none. */
+const char *twell_last_error(void);
+
+/*
+ * twell_pack -- pack a given pre-activation tensor into TwELL.
+ *
+ * pre: [out->rows][out->cols] device buffer in out->dtype.  Fills every field
+ * of *out as defined above: cnt, val, idx, ovf_rows (first ovf_cap),
+ * *n_ovf, and dense (when non-NULL).  This is the format of gist.science
+ * Resumen Técnico §2.A applied to an explicit matrix; twell_ffn_forward
+ * produces the same TwELL matrix inside the gate matmul.
+ * Errors: INVALID_ARG (NULL pre/out/cnt/val/idx/n_ovf, ovf_rows NULL with
+ * ovf_cap > 0, rows < 0, ovf_cap < 0, cols <= 0, cols % tile != 0),
+ * UNSUPPORTED (tile, cap, dtype, alignment), HIP.
+ */
+twell_status twell_pack(const void *pre, twell_matrix *out, void *stream);
+
+/*
+ * Workspace bytes needed by twell_ffn_forward / twell_sparse_ffn for the
+ * given shape and format (0 on invalid arguments).
+ */
+size_t twell_ffn_workspace_size(int T, int d, int F, int tile, int cap, twell_dtype dtype);
+
+/*
+ * twell_ffn_forward -- the sparse ReGLU FFN forward:
+ *   y = (ReLU(x W_g^T + beta) * (x W_u^T)) W_d
+ * computed as (1) the dense gate matmul on the matrix cores whose epilogue
+ * adds beta, rounds to the storage dtype, applies ReLU and writes TwELL into
+ * *packed directly (no dense pre-activation matrix is stored); (2) a scan that
+ * lists the overflowing rows; (3) the up projection for the active entries of
+ * non-overflowing rows only; (4) the down projection as a weighted sum of
+ * w_down rows, fp32 accumulation, one rounding to the storage dtype; (5) the
+ * dense fallback (gate, up and down matmuls) for the overflowing rows, which
+ * also writes packed->dense when it is non-NULL.
+ * Sources: gist.science Resumen Técnico §2.A and §2.B.
+ *
+ * packed: caller-owned TwELL buffers with rows == T, cols == F; tile, cap and
+ * dtype select the format and the arithmetic.  packed->ovf_cap must be >= T so
+ * that no overflowing row can be dropped.  On return (after the stream
+ * completes) *packed describes round(pre) exactly as twell_pack would.
+ * y: [T][d] in the storage dtype, fully written.
+ * workspace: device buffer of at least twell_ffn_workspace_size() bytes,
+ * 256-byte aligned; its contents on entry do not matter.
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP.
+ */
+twell_status twell_ffn_forward(const void *x, const void *w_gate, const void *w_up,
+                               const void *w_down, const float *gate_bias, void *y, int d,
+                               twell_matrix *packed, void *workspace, size_t ws_bytes,
+                               void *stream);
+
+/*
+ * Stage entry points (for profiling and parity).  twell_ffn_forward performs
+ * twell_gate_pack followed by twell_sparse_ffn on the same arguments.
+ *
+ * twell_gate_pack: step (1) alone -- one kernel, the gate matmul with the
+ * TwELL epilogue.  Writes packed->cnt, val and idx; ovf_rows, n_ovf and dense
+ * are not touched (twell_overflow_scan completes them).  pre_out, when
+ * non-NULL, receives the rounded pre-activations [T][F] in the storage dtype
+ * (a debugging dump; the fused path itself never stores them).
+ * Errors: INVALID_ARG, UNSUPPORTED, HIP.
+ */
+twell_status twell_gate_pack(const void *x, const void *w_gate, const float *gate_bias, int d,
+                             twell_matrix *packed, void *pre_out, void *stream);
+
+/*
+ * twell_overflow_scan: step (2) alone.  Reads packed->cnt and writes the
+ * ascending list of overflowing rows (first ovf_cap of them) and *n_ovf.
+ * Errors: INVALID_ARG, UNSUPPORTED, HIP.
+ */
+twell_status twell_overflow_scan(twell_matrix *packed, void *stream);
+
+/*
+ * twell_sparse_ffn: steps (2)-(5) from the cnt/val/idx written by
+ * twell_gate_pack (or by twell_pack of the rounded gate pre-activations).  It
+ * rebuilds the overflow list itself; the overflow rows' gate is recomputed from
+ * x, w_gate and gate_bias, and packed->dense is written when non-NULL.
+ */
+twell_status twell_sparse_ffn(const twell_matrix *packed, const void *x, const void *w_gate,
+                              const void *w_up, const void *w_down, const float *gate_bias,
+                              void *y, int d, void *workspace, size_t ws_bytes, void *stream);
+
+/* Workspace bytes needed by dense_ffn_forward (0 on invalid arguments). */
+size_t dense_ffn_workspace_size(int T, int d, int F, twell_dtype dtype);
+
+/*
+ * dense_ffn_forward -- the same layer computed densely on the matrix cores
+ * (the baseline the sparse path is measured against): a fused gate+up matmul
+ * whose epilogue forms a = ReLU(round(pre)) * u rounded to the storage dtype,
+ * then the down matmul y = a W_d.  Same argument conventions as
+ * twell_ffn_forward.  Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP.
+ */
+twell_status dense_ffn_forward(const void *x, const void *w_gate, const void *w_up,
+                               const void *w_down, const float *gate_bias, void *y, int T,
+                               int d, int F, twell_dtype dtype, void *workspace,
+                               size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TWELL_H */

@@ -1,0 +1,128 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad
+arguments before any HIP call (CPU only: no kernel is ever launched here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "twell.h")
+
+twell = pytest.importorskip("activation_sparse_transformer_bf16_amd")
+
+FAKE = 0x100000  # a non-null, 256-byte aligned address that must never be dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "defined")))
+
+
+def test_header_declares_the_binding_exports():
+    assert set(declared_functions()) == set(twell.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(twell.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_and_status_strings():
+    assert twell.twell_abi_version() == 1
+    assert twell.twell_status_str(twell.TWELL_OK) == "ok"
+    assert "workspace" in twell.twell_status_str(twell.TWELL_ERR_WORKSPACE)
+    assert twell.twell_status_str(99) == "unknown status"
+
+
+def _matrix(rows=8, cols=512, tile=256, cap=16, dtype=twell.TWELL_BF16, ovf_cap=None, **kw):
+    m = twell.TwellMatrixC(rows, cols, tile, cap, dtype, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                           rows if ovf_cap is None else ovf_cap)
+    for k, v in kw.items():
+        setattr(m, k, v)
+    return m
+
+
+L = twell.lib()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cols=500), twell.TWELL_ERR_INVALID_ARG),        # cols % tile != 0
+    (dict(tile=64, cols=512), twell.TWELL_ERR_UNSUPPORTED),
+    (dict(cap=0), twell.TWELL_ERR_INVALID_ARG),
+    (dict(cap=65), twell.TWELL_ERR_UNSUPPORTED),
+    (dict(dtype=7), twell.TWELL_ERR_INVALID_ARG),
+    (dict(rows=-1), twell.TWELL_ERR_INVALID_ARG),
+    (dict(ovf_cap=-2), twell.TWELL_ERR_INVALID_ARG),
+    (dict(cnt=None), twell.TWELL_ERR_INVALID_ARG),
+    (dict(n_ovf=None), twell.TWELL_ERR_INVALID_ARG),
+    (dict(ovf_rows=None), twell.TWELL_ERR_INVALID_ARG),  # ovf_cap > 0
+    (dict(dense=FAKE + 8), twell.TWELL_ERR_UNSUPPORTED),  # misaligned dense
+])
+def test_pack_validation(kw, status):
+    m = _matrix(**kw)
+    assert L.twell_pack(FAKE, ctypes.byref(m), None) == status
+    assert twell.twell_last_error() != ""
+
+
+def test_pack_null_pre_and_misaligned_pre():
+    m = _matrix()
+    assert L.twell_pack(None, ctypes.byref(m), None) == twell.TWELL_ERR_INVALID_ARG
+    assert L.twell_pack(FAKE + 2, ctypes.byref(m), None) == twell.TWELL_ERR_UNSUPPORTED
+    assert L.twell_pack(FAKE, None, None) == twell.TWELL_ERR_INVALID_ARG
+
+
+def _ffn(m, d=512, ws=FAKE, ws_bytes=1 << 40, x=FAKE, y=FAKE, bias=None):
+    return L.twell_ffn_forward(x, FAKE, FAKE, FAKE, bias, y, d, ctypes.byref(m), ws, ws_bytes, None)
+
+
+def test_ffn_forward_validation():
+    assert _ffn(_matrix(), d=256) == twell.TWELL_ERR_UNSUPPORTED     # bf16 needs d % 512
+    assert _ffn(_matrix(), d=0) == twell.TWELL_ERR_INVALID_ARG
+    assert _ffn(_matrix(), d=16384) == twell.TWELL_ERR_UNSUPPORTED
+    assert _ffn(_matrix(ovf_cap=4)) == twell.TWELL_ERR_INVALID_ARG   # ovf_cap < rows
+    assert _ffn(_matrix(), x=None) == twell.TWELL_ERR_INVALID_ARG
+    assert _ffn(_matrix(), y=FAKE + 4) == twell.TWELL_ERR_UNSUPPORTED
+    assert _ffn(_matrix(), bias=FAKE + 2) == twell.TWELL_ERR_UNSUPPORTED
+    assert _ffn(_matrix(), ws_bytes=16) == twell.TWELL_ERR_WORKSPACE
+    assert _ffn(_matrix(), ws=None) == twell.TWELL_ERR_WORKSPACE
+    assert _ffn(_matrix(), ws=FAKE + 16) == twell.TWELL_ERR_UNSUPPORTED
+    # fp32 accepts d % 256
+    assert _ffn(_matrix(dtype=twell.TWELL_F32), d=384) == twell.TWELL_ERR_UNSUPPORTED
+
+
+def test_sparse_ffn_and_gate_pack_validation():
+    m = _matrix(ovf_cap=1)
+    assert L.twell_sparse_ffn(ctypes.byref(m), FAKE, FAKE, FAKE, FAKE, None, FAKE, 512, FAKE, 1 << 40,
+                              None) == twell.TWELL_ERR_INVALID_ARG
+    m = _matrix()
+    assert L.twell_sparse_ffn(ctypes.byref(m), FAKE, FAKE, FAKE, FAKE, None, FAKE, 512, FAKE, 8,
+                              None) == twell.TWELL_ERR_WORKSPACE
+    assert L.twell_gate_pack(None, FAKE, None, 512, ctypes.byref(m), None, None) == twell.TWELL_ERR_INVALID_ARG
+    assert L.twell_gate_pack(FAKE, FAKE, None, 512, ctypes.byref(m), FAKE + 8,
+                             None) == twell.TWELL_ERR_UNSUPPORTED
+
+
+def test_dense_validation():
+    D = L.dense_ffn_forward
+    assert D(FAKE, FAKE, FAKE, FAKE, None, FAKE, 8, 512, 500, 1, FAKE, 1 << 40, None) == twell.TWELL_ERR_UNSUPPORTED
+    assert D(FAKE, FAKE, FAKE, FAKE, None, FAKE, -1, 512, 512, 1, FAKE, 1 << 40, None) == twell.TWELL_ERR_INVALID_ARG
+    assert D(FAKE, FAKE, FAKE, FAKE, None, FAKE, 8, 512, 512, 3, FAKE, 1 << 40, None) == twell.TWELL_ERR_INVALID_ARG
+    assert D(FAKE, FAKE, FAKE, FAKE, None, FAKE, 8, 512, 512, 1, FAKE, 10, None) == twell.TWELL_ERR_WORKSPACE
+
+
+def test_workspace_sizes():
+    ws = twell.twell_ffn_workspace_size
+    import torch
+    n = ws(8192, 2048, 8192, 256, 16, torch.bfloat16)
+    # row flags + fp32 v per slot + bf16 fallback activations, 256-byte aligned pieces
+    assert n >= 8192 + 8192 * 32 * 16 * 4 + 8192 * 8192 * 2
+    assert n % 256 == 0
+    assert ws(8, 2048, 8192, 100, 16, torch.bfloat16) == 0
+    assert ws(8, 300, 8192, 256, 16, torch.bfloat16) == 0
+    assert ws(0, 512, 512, 256, 16, torch.bfloat16) >= 256
+    assert twell.dense_ffn_workspace_size(64, 256, 1024, torch.float32) == 64 * 1024 * 4

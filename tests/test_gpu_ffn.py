@@ -1,0 +1,115 @@
+"""GPU parity: the sparse TwELL FFN forward and the dense baseline against the
+float64 oracle (relative L2 error <= 1e-5 for fp32, <= 1e-2 for bf16, on all
+rows of small cases that span several tiles and a ragged tail)."""
+
+import numpy as np
+import pytest
+
+from oracle.numerics import decode
+from workloads.synth import ffn_inputs
+
+from gpu_util import (TOL, check_fused_pack, check_y, dev_inputs, exact_gate_inputs, from_dev, gate_bound,
+                      packed_to_host)
+
+pytestmark = pytest.mark.gpu
+
+tw = pytest.importorskip("activation_sparse_transformer_bf16_amd")
+
+SMALL = [
+    # dtype, T, d, F, tile, cap, bias (None = no bias; "hot" = skewed rows)
+    ("f32", 64, 256, 1024, 128, 8, -2.326),        # the tiny fp32 layer
+    ("f32", 100, 512, 512, 256, 4, -1.5),
+    ("bf16", 300, 512, 1024, 256, 16, -2.3263),
+    ("bf16", 130, 1024, 2048, 128, 8, -2.0537),
+    ("bf16", 257, 2048, 2048, 256, 16, "hot"),      # overflow rows -> dense fallback
+    ("bf16", 1, 512, 512, 256, 16, -1.0),
+    ("bf16", 64, 512, 512, 256, 16, 6.0),          # everything active: every row overflows
+    ("bf16", 70, 512, 768, 256, 16, -1e30),        # nothing active: y == 0
+]
+
+
+def _bias(spec, T):
+    if isinstance(spec, str):
+        b = np.full(T, -2.3263, np.float32)
+        b[(np.arange(T) % 128) < 8] = -0.8416   # first 8 tokens of every 128: ~20% active
+        return b
+    return spec
+
+
+@pytest.mark.parametrize("dtype,T,d,F,tile,cap,bias", SMALL)
+def test_twell_ffn_forward(dtype, T, d, F, tile, cap, bias):
+    print(f"ffn {dtype} T={T} d={d} F={F} tile={tile} cap={cap} bias={bias if np.isscalar(bias) else 'hot'}",
+          flush=True)
+    inp = ffn_inputs(T, d, F, dtype, seed=T, gate_bias=_bias(bias, T))
+    x, wg, wu, wd, b = dev_inputs(inp)
+    packed = tw.TwellMatrix.empty(T, F, tile, cap, x.dtype, x.device, T, dense=True)
+    y, packed = tw.twell_ffn_forward(x, wg, wu, wd, b, packed=packed)
+    yh = from_dev(y, dtype)
+    check_y(yh, inp, dtype)
+    if isinstance(bias, float) and bias < -1e20:
+        assert not decode(yh, dtype).any()
+    # the TwELL side output is the gate's TwELL matrix
+    host = packed_to_host(packed, dtype)
+    pre64, bound = gate_bound(inp)
+    check_fused_pack(host, pre64, bound, dtype, tile, cap)
+    # dense backup rows hold ReLU(round(pre)) of the overflow rows
+    rel = 2.0 ** -8 if dtype == "bf16" else 0.0
+    for r, t in enumerate(host["ovf_rows"]):
+        h = decode(host["dense"][r], dtype)
+        want = np.where(pre64[t] > 0, pre64[t], 0.0)
+        assert np.all(np.abs(h - want) <= bound[t] + rel * (np.abs(pre64[t]) + bound[t]))
+    if bias == "hot":
+        assert host["n_ovf"] > 0
+    if bias == 6.0:
+        assert host["n_ovf"] == T
+
+
+@pytest.mark.parametrize("dtype,T,d,F,tile,cap,bias", SMALL)
+def test_dense_ffn_forward(dtype, T, d, F, tile, cap, bias):
+    print(f"dense {dtype} T={T} d={d} F={F}", flush=True)
+    inp = ffn_inputs(T, d, F, dtype, seed=T, gate_bias=_bias(bias, T))
+    x, wg, wu, wd, b = dev_inputs(inp)
+    y = tw.dense_ffn_forward(x, wg, wu, wd, b)
+    check_y(from_dev(y, dtype), inp, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_exact_inputs_sparse_equals_dense_up_to_rounding(dtype):
+    # integer-valued operands: the gate decisions are exact on both paths
+    T, d, F = 200, 512, 1024
+    inp = exact_gate_inputs(T, d, F, dtype, seed=1, density=0.02)
+    inp.w_up = inp.w_up.copy()
+    x, wg, wu, wd, b = dev_inputs(inp)
+    ys, _ = tw.twell_ffn_forward(x, wg, wu, wd, b, tile=256, cap=16)
+    yd = tw.dense_ffn_forward(x, wg, wu, wd, b)
+    check_y(from_dev(ys, dtype), inp, dtype)
+    check_y(from_dev(yd, dtype), inp, dtype)
+
+
+def test_stage_entry_points_compose():
+    T, d, F = 300, 512, 1024
+    inp = ffn_inputs(T, d, F, "bf16", seed=4, gate_bias=_bias("hot", T))
+    x, wg, wu, wd, b = dev_inputs(inp)
+    y1, _ = tw.twell_ffn_forward(x, wg, wu, wd, b, tile=256, cap=16)
+    p, _ = tw.twell_gate_pack(x, wg, b, tile=256, cap=16)
+    y2 = tw.twell_sparse_ffn(p, x, wg, wu, wd, b)
+    assert np.array_equal(from_dev(y1, "bf16"), from_dev(y2, "bf16"))
+
+
+def test_deterministic():
+    T, d, F = 257, 1024, 2048
+    inp = ffn_inputs(T, d, F, "bf16", seed=6, gate_bias=_bias("hot", T))
+    x, wg, wu, wd, b = dev_inputs(inp)
+    outs = [from_dev(tw.twell_ffn_forward(x, wg, wu, wd, b)[0], "bf16") for _ in range(3)]
+    outs += [from_dev(tw.dense_ffn_forward(x, wg, wu, wd, b), "bf16") for _ in range(2)]
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+    assert np.array_equal(outs[3], outs[4])
+
+
+def test_zero_tokens():
+    import torch
+    x = torch.empty((0, 512), dtype=torch.bfloat16, device="cuda:0")
+    w = torch.zeros((512, 512), dtype=torch.bfloat16, device="cuda:0")
+    y, p = tw.twell_ffn_forward(x, w, w, w, None)
+    assert y.shape == (0, 512) and int(p.n_ovf.item()) == 0
+    assert tw.dense_ffn_forward(x, w, w, w, None).shape == (0, 512)
