@@ -61,13 +61,24 @@ def _load():
         "dense_ffn_workspace_size": (Z, [I, I, I, I]),
         "dense_ffn_forward": (I, [P, P, P, P, P, P, I, I, I, I, P, Z, P]),
     }
+    # Private function objects: changing argtypes on the public handle (lib())
+    # cannot make this binding pass truncated pointers.
+    fns = {}
     for name, (res, args) in sig.items():
-        fn = getattr(lib, name)
-        fn.restype, fn.argtypes = res, args
-    return lib
+        for fn in (lib._FuncPtr((name, lib)), getattr(lib, name)):
+            fn.restype, fn.argtypes = res, args
+        fns[name] = lib._FuncPtr((name, lib))
+        fns[name].restype, fns[name].argtypes = res, args
+    return lib, fns
 
 
-_lib = _load()
+class _Fns:
+    def __init__(self, fns):
+        self.__dict__.update(fns)
+
+
+_public_lib, _private = _load()
+_lib = _Fns(_private)
 
 # Names every build of the library must export (checked by the CPU tests).
 EXPORTS = ("twell_abi_version", "twell_status_str", "twell_last_error", "twell_pack",
@@ -77,7 +88,8 @@ EXPORTS = ("twell_abi_version", "twell_status_str", "twell_last_error", "twell_p
 
 
 def lib():
-    return _lib
+    """The ctypes handle of libtwell.so (its functions have argtypes set)."""
+    return _public_lib
 
 
 def twell_abi_version() -> int:

@@ -34,17 +34,15 @@ __global__ __launch_bounds__(GEMM_THREADS) void k_gate_up(
   const size_t ldk = (size_t)K * sizeof(T);
   auto phys = [&](int r) { return rows ? rows[r] : r; };
 
-  KRowLoader<GEMM_BM> la;
-  la.init(tid, [&](int r) {
-    int lr = m0 + r;
-    int row = lr < n_eff ? phys(lr) : phys(0);
+  auto rowA = [&](int r) {
+    const int lr = m0 + r;
+    const int row = lr < n_eff ? phys(lr) : phys(0);
     return reinterpret_cast<const char *>(x) + (size_t)row * ldk;
-  });
-  KRowLoader<BN> lb;
-  lb.init(tid, [&](int r) {
+  };
+  auto rowB = [&](int r) {
     const T *w = r < HALF ? wg : wu;
     return reinterpret_cast<const char *>(w) + (size_t)(n0 + (r & (HALF - 1))) * ldk;
-  });
+  };
 
   f32x16_t acc[2][8];
 #pragma unroll
@@ -61,14 +59,16 @@ __global__ __launch_bounds__(GEMM_THREADS) void k_gate_up(
     for (int bn = 4; bn < 8; ++bn) acc[bm][bn] = f32x16_t{};
   }
 
-  gemm_mainloop<D, BN>(acc, la, lb, K / (KCHUNK_BYTES / (int)sizeof(T)), smem);
+  gemm_mainloop_dma<D, BN>(acc, rowA, rowB, (int)(ldk / SLAB), smem);
 
   const int col = lane & 31;
+  int row_base = m0 + 64 * wave + 4 * (lane >> 5);  // opaque: keep row math after the mainloop
+  asm volatile("" : "+v"(row_base));
 #pragma unroll
   for (int bm = 0; bm < 2; ++bm) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int lr = m0 + acc_row(wave, bm, i, lane);
+      const int lr = row_base + 32 * bm + 8 * (i >> 2) + (i & 3);
       if (lr >= n_eff) continue;
 #pragma unroll
       for (int bn = 0; bn < 4; ++bn) {
@@ -117,11 +117,13 @@ __global__ __launch_bounds__(GEMM_THREADS) void k_down(
   gemm_mainloop<D, BN>(acc, la, lb, K / (KCHUNK_BYTES / (int)sizeof(T)), smem);
 
   const int col = lane & 31;
+  int row_base = m0 + 64 * wave + 4 * (lane >> 5);  // opaque: keep row math after the mainloop
+  asm volatile("" : "+v"(row_base));
 #pragma unroll
   for (int bm = 0; bm < 2; ++bm) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int lr = m0 + acc_row(wave, bm, i, lane);
+      const int lr = row_base + 32 * bm + 8 * (i >> 2) + (i & 3);
       if (lr >= n_eff) continue;
       const size_t prow = rows ? (size_t)rows[lr] : (size_t)lr;
 #pragma unroll
@@ -134,7 +136,7 @@ template <Dt D>
 static hipError_t launch_gate_up(const DenseArgs &a, hipStream_t s) {
   using T = typename DtT<D>::T;
   auto kern = k_gate_up<D>;
-  const int lds = gemm_lds_bytes(256);
+  const int lds = gemm_dma_lds_bytes(256);
   hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
   const int mt = (a.M + GEMM_BM - 1) / GEMM_BM, ntl = a.F / 128;

@@ -223,6 +223,137 @@ __device__ __forceinline__ void gemm_mainloop(f32x16_t (&acc)[2][BN / 32], LA &l
   }
 }
 
+// ---- mainloop with direct-to-LDS loads (k-contiguous operands) ------------
+//
+// global_load_lds_dwordx4 moves 16 bytes per lane from global memory straight
+// into LDS (M0 + 16 * lane), with no VGPR staging, so several stages can be in
+// flight at once.  K is consumed in 64-byte slabs (32 bf16 / 16 fp32) through a
+// ring of DMA_STAGES LDS stages; the loads of stage kt+3 are issued while stage
+// kt is multiplied.  The loads are written as inline assembly and their
+// completion is tracked with explicit s_waitcnt vmcnt: the compiler otherwise
+// assumes every LDS read may alias an in-flight direct load and waits for all
+// of them, which would serialise the ring.
+//
+// Each 64-byte LDS row holds 4 chunks of 16 bytes; chunk c of row r sits at
+// physical chunk c ^ ((r >> 2) & 3), so the 16 lanes of one ds_read_b128 phase
+// (16 consecutive rows, one chunk) hit 16 distinct 4-bank groups of the 64-bank
+// LDS.
+
+constexpr int DMA_STAGES = 4;
+constexpr int SLAB = 64;  // K bytes per stage
+
+__host__ __device__ constexpr int gemm_dma_lds_bytes(int bn) { return DMA_STAGES * (GEMM_BM + bn) * SLAB; }
+
+__device__ __forceinline__ int lds_off64(int row, int chunk) {
+  return row * SLAB + ((chunk ^ ((row >> 2) & 3)) << 4);
+}
+
+__device__ __forceinline__ uint32_t lds_address(const void *p) {
+  return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char *)p);
+}
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// One wave-wide 16-byte-per-lane copy global -> LDS [lds, lds + 1024).
+__device__ __forceinline__ void dma16(const void *g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Rows of one operand tile loaded by DMA.  NR rows x 4 chunks = NR*4 lane
+// slots = NR/16 wave instructions, spread over the 4 waves.
+template <int NR>
+struct DmaRows {
+  static constexpr int PER_WAVE = NR / 64;  // instructions per wave per stage
+  const char *ptr[PER_WAVE];
+  uint32_t lds_off[PER_WAVE];  // byte offset of the wave's 1 KB block in the stage
+
+  template <class RowPtr>
+  __device__ __forceinline__ void init(int wave_u, int lane, int region_off, RowPtr row_ptr) {
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const int blk = wave_u * PER_WAVE + j;  // 1 KB block = 16 rows
+      const int row = blk * 16 + (lane >> 2);
+      const int c = (lane & 3) ^ ((row >> 2) & 3);
+      ptr[j] = row_ptr(row) + c * 16;
+      lds_off[j] = region_off + blk * 1024;
+    }
+  }
+  __device__ __forceinline__ void issue(int kt, uint32_t stage_base) {
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) dma16(ptr[j] + (size_t)kt * SLAB, stage_base + lds_off[j]);
+  }
+};
+
+template <Dt D, int BN>
+__device__ __forceinline__ void mfma_slab(f32x16_t (&acc)[2][BN / 32], const char *stage, int wave, int lane) {
+  const char *As = stage;
+  const char *Bs = stage + GEMM_BM * SLAB;
+  const int r = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    u32x4_t a[2], b[BN / 32];
+#pragma unroll
+    for (int bm = 0; bm < 2; ++bm)
+      a[bm] = *reinterpret_cast<const u32x4_t *>(As + lds_off64(64 * wave + 32 * bm + r, 2 * g + h));
+#pragma unroll
+    for (int bn = 0; bn < BN / 32; ++bn)
+      b[bn] = *reinterpret_cast<const u32x4_t *>(Bs + lds_off64(32 * bn + r, 2 * g + h));
+#pragma unroll
+    for (int bm = 0; bm < 2; ++bm)
+#pragma unroll
+      for (int bn = 0; bn < BN / 32; ++bn) Mfma<D>::step(acc[bm][bn], a[bm], b[bn]);
+  }
+}
+
+// Mainloop over nk 64-byte K slabs; A rows from rowA(r), B rows from rowB(r).
+template <Dt D, int BN, class RA, class RB>
+__device__ __forceinline__ void gemm_mainloop_dma(f32x16_t (&acc)[2][BN / 32], RA rowA, RB rowB, int nk,
+                                                  char *smem) {
+  constexpr int STAGE = (GEMM_BM + BN) * SLAB;
+  constexpr int OPS = DmaRows<GEMM_BM>::PER_WAVE + DmaRows<BN>::PER_WAVE;  // DMA ops per stage per lane
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t base = lds_address(smem);
+  DmaRows<GEMM_BM> da;
+  DmaRows<BN> db;
+  da.init(wave_u, lane, 0, rowA);
+  db.init(wave_u, lane, GEMM_BM * SLAB, rowB);
+#pragma unroll
+  for (int s = 0; s < DMA_STAGES - 1; ++s) {
+    if (s < nk) {
+      da.issue(s, base + s * STAGE);
+      db.issue(s, base + s * STAGE);
+    }
+  }
+  for (int kt = 0; kt < nk; ++kt) {
+    // stage kt landed once at most the younger stages' loads are outstanding
+    if (kt + 2 < nk)
+      wait_vmcnt<2 * OPS>();
+    else if (kt + 1 < nk)
+      wait_vmcnt<OPS>();
+    else
+      wait_vmcnt<0>();
+    __syncthreads();
+    const int nxt = kt + DMA_STAGES - 1;
+    if (nxt < nk) {
+      const uint32_t sb = base + (nxt % DMA_STAGES) * STAGE;
+      da.issue(nxt, sb);
+      db.issue(nxt, sb);
+    }
+    mfma_slab<D, BN>(acc, smem + (kt % DMA_STAGES) * STAGE, wave, lane);
+  }
+  // no DMA is left in flight; make the last stage's LDS reads complete before
+  // the caller reuses LDS
+  __syncthreads();
+}
+
 // Accumulator element (bm, bn, i) of lane l sits at tile row
 //   64*wave + 32*bm + 8*(i/4) + 4*(l/32) + (i%4)   and tile column 32*bn + (l%32).
 __device__ __forceinline__ int acc_row(int wave, int bm, int i, int lane) {

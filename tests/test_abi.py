@@ -126,3 +126,17 @@ def test_workspace_sizes():
     assert ws(8, 300, 8192, 256, 16, torch.bfloat16) == 0
     assert ws(0, 512, 512, 256, 16, torch.bfloat16) >= 256
     assert twell.dense_ffn_workspace_size(64, 256, 1024, torch.float32) == 64 * 1024 * 4
+
+
+def test_binding_keeps_its_own_argtypes():
+    # Reconfiguring the public ctypes handle must not change how the binding
+    # marshals pointers (without argtypes ctypes would pass 64-bit device
+    # pointers as 32-bit ints).
+    pub = twell.lib().twell_pack
+    saved = pub.argtypes
+    try:
+        pub.argtypes = None
+        assert twell._lib.twell_pack.argtypes is not None
+        assert ctypes.c_void_p in twell._lib.twell_ffn_forward.argtypes
+    finally:
+        pub.argtypes = saved
