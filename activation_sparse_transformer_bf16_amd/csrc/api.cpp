@@ -73,6 +73,13 @@ twell_status check_d(int d, int dtype) {
   return TWELL_OK;
 }
 
+// The gather kernels address weight rows with 32-bit byte offsets.
+twell_status check_weight_bytes(int F, int d, int dtype) {
+  if ((size_t)F * (size_t)d * (size_t)dt_size((twell_dtype)dtype) >= ((size_t)1 << 31))
+    return fail(TWELL_ERR_UNSUPPORTED, "weight matrices of F*d = %zu elements are too large", (size_t)F * d);
+  return TWELL_OK;
+}
+
 twell_status check_matrix(const twell_matrix *m, bool need_ovf_all) {
   if (m == nullptr) return fail(TWELL_ERR_INVALID_ARG, "null twell_matrix");
   if (m->rows < 0) return fail(TWELL_ERR_INVALID_ARG, "rows must be >= 0");
@@ -176,7 +183,9 @@ twell_status twell_pack(const void *pre, twell_matrix *out, void *stream) {
 }
 
 size_t twell_ffn_workspace_size(int T, int d, int F, int tile, int cap, twell_dtype dtype) {
-  if (T < 0 || check_format(tile, cap, F, (int)dtype) != TWELL_OK || check_d(d, (int)dtype) != TWELL_OK) return 0;
+  if (T < 0 || check_format(tile, cap, F, (int)dtype) != TWELL_OK || check_d(d, (int)dtype) != TWELL_OK ||
+      check_weight_bytes(F, d, (int)dtype) != TWELL_OK)
+    return 0;
   return ffn_ws_layout(T, F, tile, cap, dtype).total;
 }
 
@@ -218,6 +227,7 @@ twell_status twell_sparse_ffn(const twell_matrix *packed, const void *x, const v
   twell_status st = check_matrix(packed, true);
   if (st != TWELL_OK) return st;
   if ((st = check_d(d, (int)packed->dtype)) != TWELL_OK) return st;
+  if ((st = check_weight_bytes(packed->cols, d, (int)packed->dtype)) != TWELL_OK) return st;
   if (packed->rows == 0) return hip_check(zero_int(packed->n_ovf, static_cast<hipStream_t>(stream)), "zero n_ovf");
   if ((st = check_ffn_ptrs(x, w_gate, w_up, w_down, gate_bias, y)) != TWELL_OK) return st;
   const size_t need = ffn_ws_layout(packed->rows, packed->cols, packed->tile, packed->cap, packed->dtype).total;
@@ -236,6 +246,7 @@ twell_status twell_ffn_forward(const void *x, const void *w_gate, const void *w_
   twell_status st = check_matrix(packed, true);
   if (st != TWELL_OK) return st;
   if ((st = check_d(d, (int)packed->dtype)) != TWELL_OK) return st;
+  if ((st = check_weight_bytes(packed->cols, d, (int)packed->dtype)) != TWELL_OK) return st;
   if (packed->rows == 0) return hip_check(zero_int(packed->n_ovf, static_cast<hipStream_t>(stream)), "zero n_ovf");
   if ((st = check_ffn_ptrs(x, w_gate, w_up, w_down, gate_bias, y)) != TWELL_OK) return st;
   const size_t need = ffn_ws_layout(packed->rows, packed->cols, packed->tile, packed->cap, packed->dtype).total;
@@ -267,6 +278,7 @@ twell_status dense_ffn_forward(const void *x, const void *w_gate, const void *w_
   if (F % 128 != 0 || F > (1 << 24)) return fail(TWELL_ERR_UNSUPPORTED, "F %d not built (multiple of 128)", F);
   twell_status st = check_d(d, (int)dtype);
   if (st != TWELL_OK) return st;
+  if ((st = check_weight_bytes(F, d, (int)dtype)) != TWELL_OK) return st;
   if (T == 0) return TWELL_OK;
   if ((st = check_ffn_ptrs(x, w_gate, w_up, w_down, gate_bias, y)) != TWELL_OK) return st;
   const size_t need = dense_ffn_workspace_size(T, d, F, dtype);

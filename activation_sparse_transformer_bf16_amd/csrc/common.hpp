@@ -84,6 +84,23 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Sum over the 64 lanes of a wave with DPP lane moves (no LDS traffic); the
+// total lands in lane 63.  Steps: pairs and quads (quad_perm), 8 and 16 lanes
+// (row_ror 4, 8), then rows 0+1 and 2+3 (row_bcast15 into rows 1 and 3) and
+// all four rows (row_bcast31 into rows 2 and 3).
+__device__ __forceinline__ float wave_sum_to_lane63(float v) {
+#define TWELL_DPP_ADD(CTRL, ROWS) \
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xF, false))
+  TWELL_DPP_ADD(0xB1, 0xF);   // quad_perm 1,0,3,2
+  TWELL_DPP_ADD(0x4E, 0xF);   // quad_perm 2,3,0,1
+  TWELL_DPP_ADD(0x124, 0xF);  // row_ror 4
+  TWELL_DPP_ADD(0x128, 0xF);  // row_ror 8
+  TWELL_DPP_ADD(0x142, 0xA);  // row_bcast15 into rows 1, 3
+  TWELL_DPP_ADD(0x143, 0xC);  // row_bcast31 into rows 2, 3
+#undef TWELL_DPP_ADD
+  return v;
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave (integers).
 __device__ __forceinline__ int wave_incl_scan(int v) {
   const int l = lane_id();

@@ -14,6 +14,8 @@
 // Rows flagged by the overflow scan are left to the dense fallback.
 #include "launch.hpp"
 
+#include <type_traits>
+
 namespace twell {
 
 // ---------------------------------------------------------------------------
@@ -90,7 +92,8 @@ hipError_t zero_int(int *p, hipStream_t s) {
 
 constexpr int SP_THREADS = 256;
 constexpr int SP_WAVES = SP_THREADS / 64;
-constexpr int LIST_MAX = 1024;  // entries per wave list
+constexpr int UP_LIST = 256;    // entries per wave list (tiles per group * cap)
+constexpr int DOWN_LIST = 512;  // entries per wave list (tiles per fill * cap)
 
 // Block -> (group, token block) so that group g runs on XCD g % 8 when the
 // group count is a multiple of 8 (groups beyond 8 run in successive phases).
@@ -136,9 +139,10 @@ __device__ __forceinline__ float dot16(const u32x4_t &a, const u32x4_t &b, float
 }
 
 // ---------------------------------------------------------------------------
-// Sparse up projection.  NC = 16-byte chunks per lane covering d.
+// Sparse up projection.  NC = 16-byte chunks per lane covering d; U = entries
+// in flight per wave (U * NC 16-byte loads per lane outstanding).
 
-template <Dt D, int NC>
+template <Dt D, int NC, int U>
 __global__ __launch_bounds__(SP_THREADS) void k_sparse_up(
     const typename DtT<D>::T *__restrict__ x, const typename DtT<D>::T *__restrict__ wu,
     const uint16_t *__restrict__ cnt, const typename DtT<D>::T *__restrict__ val,
@@ -146,13 +150,15 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_up(
     int d, int nt, int tile, int cap, int tpg, int n_groups, int tok_per_wg, int n_tb) {
   using TT = typename DtT<D>::T;
   constexpr int EPC = 16 / sizeof(TT);  // elements per 16-byte chunk
-  __shared__ Entry list[SP_WAVES][LIST_MAX];
+  __shared__ Entry list[SP_WAVES][UP_LIST];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   int g, tb;
   group_coords(blockIdx.x, n_groups, n_tb, g, tb);
   const int k0 = g * tpg;
   const int kn = min(tpg, nt - k0);
   Entry *L = list[wave];
+  const char *wub = reinterpret_cast<const char *>(wu);
+  const uint32_t row_bytes = (uint32_t)d * sizeof(TT);
 
   for (int it = wave; it < tok_per_wg; it += SP_WAVES) {
     const int t = tb * tok_per_wg + it;
@@ -175,30 +181,32 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_up(
     }
     wave_sync_lds();
 
-    for (int e = 0; e < E; e += 2) {
-      const Entry e0 = L[e];
-      const bool two = e + 1 < E;
-      const Entry e1 = two ? L[e + 1] : e0;
-      const int j0 = e0.j & 0x3FFFFFF, j1 = e1.j & 0x3FFFFFF;
-      const TT *r0 = wu + (size_t)j0 * d, *r1 = wu + (size_t)j1 * d;
-      u32x4_t w0[NC], w1[NC];
+    for (int e = 0; e < E; e += U) {
+      Entry en[U];
+      u32x4_t w[U][NC];
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        w0[c] = *reinterpret_cast<const u32x4_t *>(r0 + (c * 64 + lane) * EPC);
-        w1[c] = *reinterpret_cast<const u32x4_t *>(r1 + (c * 64 + lane) * EPC);
-      }
-      float p0 = 0.f, p1 = 0.f;
+      for (int u = 0; u < U; ++u) {
+        en[u] = L[min(e + u, E - 1)];
+        const char *r = wub + (size_t)((uint32_t)(en[u].j & 0x3FFFFFF) * row_bytes) + lane * 16;
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        p0 = dot16(xr[c], w0[c], p0, TT());
-        p1 = dot16(xr[c], w1[c], p1, TT());
+        for (int c = 0; c < NC; ++c) w[u][c] = *reinterpret_cast<const u32x4_t *>(r + c * 1024);
       }
-      p0 = wave_sum(p0);
-      p1 = wave_sum(p1);
-      if (lane == 0) {
-        const int s0 = (unsigned)e0.j >> 26, s1 = (unsigned)e1.j >> 26;
-        vbuf[((size_t)t * nt + j0 / tile) * cap + s0] = e0.w * p0;
-        if (two) vbuf[((size_t)t * nt + j1 / tile) * cap + s1] = e1.w * p1;
+      float p[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        p[u] = 0.f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) p[u] = dot16(xr[c], w[u][c], p[u], TT());
+        p[u] = wave_sum_to_lane63(p[u]);
+      }
+      if (lane == 63) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          if (e + u < E) {
+            const int j = en[u].j & 0x3FFFFFF, s = (unsigned)en[u].j >> 26;
+            vbuf[((size_t)t * nt + j / tile) * cap + s] = en[u].w * p[u];
+          }
+        }
       }
     }
     wave_sync_lds();
@@ -206,9 +214,10 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_up(
 }
 
 // ---------------------------------------------------------------------------
-// Sparse down projection.  VPL = output columns per lane (slice = 64 * VPL).
+// Sparse down projection.  VPL = output columns per lane (slice = 64 * VPL);
+// U = W_d row segments in flight per wave.
 
-template <Dt D, int VPL>
+template <Dt D, int VPL, int U>
 __global__ __launch_bounds__(SP_THREADS) void k_sparse_down(
     const float *__restrict__ vbuf, const uint16_t *__restrict__ cnt, const uint8_t *__restrict__ idx,
     const uint8_t *__restrict__ row_flag, const typename DtT<D>::T *__restrict__ wd,
@@ -216,14 +225,19 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_down(
     int n_tb) {
   using TT = typename DtT<D>::T;
   constexpr int VB = VPL * sizeof(TT);  // bytes per lane per row
-  static_assert(VB == 8 || VB == 16, "lane vector must be 8 or 16 bytes");
-  __shared__ Entry list[SP_WAVES][LIST_MAX];
+  static_assert(VB == 4 || VB == 8 || VB == 16, "lane vector must be 4, 8 or 16 bytes");
+  using V = typename std::conditional<VB == 16, u32x4_t,
+                                      typename std::conditional<VB == 8, u32x2_t, uint32_t>::type>::type;
+  __shared__ Entry list[SP_WAVES][DOWN_LIST];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   int sl, tb;
   group_coords(blockIdx.x, n_slices, n_tb, sl, tb);
   const int c0 = sl * 64 * VPL + lane * VPL;
+  // lane's column segment of every W_d row: base + row_offset(j) (32-bit)
+  const char *wdb = reinterpret_cast<const char *>(wd + c0);
+  const uint32_t row_bytes = (uint32_t)d * sizeof(TT);
   Entry *L = list[wave];
-  const int tiles_per_fill = min(64, LIST_MAX / cap);
+  const int tiles_per_fill = min(64, DOWN_LIST / cap);
 
   for (int it = wave; it < tok_per_wg; it += SP_WAVES) {
     const int t = tb * tok_per_wg + it;
@@ -240,64 +254,48 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_down(
       const int E = __shfl(incl, 63, 64);
       const size_t slot0 = ((size_t)t * nt + k) * cap;
       for (int s = 0, o = incl - n; s < n; ++s, ++o) {
-        L[o].j = k * tile + idx[slot0 + s];
+        L[o].j = (int)((uint32_t)(k * tile + idx[slot0 + s]) * row_bytes);  // byte offset of the row
         L[o].w = vbuf[slot0 + s];
       }
       wave_sync_lds();
-      int e = 0;
-      for (; e + 4 <= E; e += 4) {
-        Entry en[4];
-        u32x4_t w[4];
+      for (int e = 0; e < E; e += U) {
+        Entry en[U];
+        V w[U];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          en[u] = L[e + u];
-          const char *p = reinterpret_cast<const char *>(wd + (size_t)en[u].j * d + c0);
-          if constexpr (VB == 16) {
-            w[u] = *reinterpret_cast<const u32x4_t *>(p);
-          } else {
-            u32x2_t q = *reinterpret_cast<const u32x2_t *>(p);
-            w[u] = u32x4_t{q.x, q.y, 0u, 0u};
-          }
+        for (int u = 0; u < U; ++u) {
+          en[u] = L[min(e + u, E - 1)];
+          if (e + u >= E) en[u].w = 0.f;  // tail: duplicate row, zero weight
+          w[u] = *reinterpret_cast<const V *>(wdb + (uint32_t)en[u].j);
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < U; ++u) {
+          const uint32_t *wv = reinterpret_cast<const uint32_t *>(&w[u]);
           if constexpr (D == Dt::BF16) {
 #pragma unroll
             for (int v = 0; v < VPL / 2; ++v) {
-              acc[2 * v] = fmaf(en[u].w, bf16lo(w[u][v]), acc[2 * v]);
-              acc[2 * v + 1] = fmaf(en[u].w, bf16hi(w[u][v]), acc[2 * v + 1]);
+              acc[2 * v] = fmaf(en[u].w, bf16lo(wv[v]), acc[2 * v]);
+              acc[2 * v + 1] = fmaf(en[u].w, bf16hi(wv[v]), acc[2 * v + 1]);
             }
           } else {
 #pragma unroll
-            for (int v = 0; v < VPL; ++v) acc[v] = fmaf(en[u].w, __uint_as_float(w[u][v]), acc[v]);
+            for (int v = 0; v < VPL; ++v) acc[v] = fmaf(en[u].w, __uint_as_float(wv[v]), acc[v]);
           }
         }
-      }
-      for (; e < E; ++e) {
-        const Entry en = L[e];
-        const TT *p = wd + (size_t)en.j * d + c0;
-#pragma unroll
-        for (int v = 0; v < VPL; ++v) acc[v] = fmaf(en.w, to_f32(p[v]), acc[v]);
       }
       wave_sync_lds();
     }
 
-    TT *yo = y + (size_t)t * d + c0;
+    V out;
+    uint32_t *ov = reinterpret_cast<uint32_t *>(&out);
     if constexpr (D == Dt::BF16) {
-      uint32_t packed[VPL / 2];
 #pragma unroll
       for (int v = 0; v < VPL / 2; ++v)
-        packed[v] = (uint32_t)bf16_rne(acc[2 * v]) | ((uint32_t)bf16_rne(acc[2 * v + 1]) << 16);
-      if constexpr (VB == 16)
-        *reinterpret_cast<u32x4_t *>(yo) = u32x4_t{packed[0], packed[1], packed[2], packed[3]};
-      else
-        *reinterpret_cast<u32x2_t *>(yo) = u32x2_t{packed[0], packed[1]};
+        ov[v] = (uint32_t)bf16_rne(acc[2 * v]) | ((uint32_t)bf16_rne(acc[2 * v + 1]) << 16);
     } else {
-      if constexpr (VB == 16)
-        *reinterpret_cast<f32x4_t *>(yo) = f32x4_t{acc[0], acc[1], acc[2], acc[3]};
-      else
-        *reinterpret_cast<f32x2_t *>(yo) = f32x2_t{acc[0], acc[1]};
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) ov[v] = __float_as_uint(acc[v]);
     }
+    *reinterpret_cast<V *>(y + (size_t)t * d + c0) = out;
   }
 }
 
@@ -308,15 +306,19 @@ template <Dt D, int NC>
 static hipError_t launch_up(const SparseArgs &a, hipStream_t s) {
   using TT = typename DtT<D>::T;
   const int nt = a.F / a.tile;
-  // Tiles per group: one group per XCD when the tile count allows it, so that
-  // each XCD's L2 holds one slice of W_u^T rows.
-  int tpg = std::max(1, nt / 8);
-  tpg = std::min(tpg, std::min(64, LIST_MAX / a.cap));
+  // Tiles per group: about 4 MB of W_u^T rows per group (one XCD's L2); at
+  // the 1.5B-class and larger layer shapes this was the fastest setting of a
+  // sweep over 1..8 tiles per group.
+  const size_t group_target = (size_t)4 << 20;
+  const size_t tile_bytes = (size_t)a.tile * a.d * sizeof(TT);
+  int tpg = (int)std::max<size_t>(1, group_target / tile_bytes);
+  tpg = std::min(tpg, std::min(std::min(64, nt), UP_LIST / a.cap));
   while (nt % tpg != 0) --tpg;
   const int n_groups = nt / tpg;
-  const int tok = 32;
+  const int tok = 16;
   const int n_tb = (a.T + tok - 1) / tok;
-  hipLaunchKernelGGL((k_sparse_up<D, NC>), dim3(n_groups * n_tb), dim3(SP_THREADS), 0, s, (const TT *)a.x,
+  constexpr int U = NC >= 8 ? 2 : 4;
+  hipLaunchKernelGGL((k_sparse_up<D, NC, U>), dim3(n_groups * n_tb), dim3(SP_THREADS), 0, s, (const TT *)a.x,
                      (const TT *)a.wu, a.cnt, (const TT *)a.val, a.idx, a.row_flag, a.vbuf, a.T, a.d, nt, a.tile,
                      a.cap, tpg, n_groups, tok, n_tb);
   return hipGetLastError();
@@ -349,9 +351,9 @@ static hipError_t launch_down(const SparseArgs &a, hipStream_t s) {
   using TT = typename DtT<D>::T;
   const int nt = a.F / a.tile;
   const int n_slices = a.d / (64 * VPL);
-  const int tok = 32;
+  const int tok = 16;
   const int n_tb = (a.T + tok - 1) / tok;
-  hipLaunchKernelGGL((k_sparse_down<D, VPL>), dim3(n_slices * n_tb), dim3(SP_THREADS), 0, s, a.vbuf, a.cnt,
+  hipLaunchKernelGGL((k_sparse_down<D, VPL, 8>), dim3(n_slices * n_tb), dim3(SP_THREADS), 0, s, a.vbuf, a.cnt,
                      a.idx, a.row_flag, (const TT *)a.wd, (TT *)a.y, a.T, a.d, nt, a.tile, a.cap, n_slices, tok,
                      n_tb);
   return hipGetLastError();
