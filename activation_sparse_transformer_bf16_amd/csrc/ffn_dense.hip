@@ -3,9 +3,10 @@
 // Lighter Transformer Language Models", Resumen Técnico §2.A, and the
 // q2bstudio post on TwELL, third paragraph) and the dense baseline layer.
 //
-//   k_gate_up: one matmul over [W_g rows | W_u rows] of the same 128 hidden
-//              units; epilogue a = ReLU(round(pre)) * u, rounded to the
-//              storage dtype (and optionally h = ReLU(round(pre)) stored).
+//   k_gate_up: one matmul over W_g and W_u rows of the same 128 hidden units,
+//              interleaved by 32 so that each lane holds the gate and the up
+//              value of a unit; epilogue a = ReLU(round(pre)) * u, rounded to
+//              the storage dtype (and optionally h = ReLU(round(pre)) stored).
 //   k_down:    y = a W_d with W_d [F][d] read n-contiguous and transposed into
 //              the k-contiguous LDS layout of the mainloop.
 // Rows may be gathered through an index list whose length lives on the device;
@@ -16,21 +17,25 @@
 namespace twell {
 
 template <Dt D>
-__global__ __launch_bounds__(GEMM_THREADS) void k_gate_up(
+__global__ __launch_bounds__(DMA_THREADS) void k_gate_up(
     const typename DtT<D>::T *__restrict__ x, const typename DtT<D>::T *__restrict__ wg,
     const typename DtT<D>::T *__restrict__ wu, const float *__restrict__ beta, int M, int K, int F,
     const int *__restrict__ rows, const int *__restrict__ n_rows_dev, typename DtT<D>::T *__restrict__ a_ws,
     typename DtT<D>::T *__restrict__ h_out, int h_cap) {
   using T = typename DtT<D>::T;
-  constexpr int BN = 256, HALF = 128;
+  constexpr int BN = 256, UNITS = 128;  // B tile: 128 hidden units, each as a W_g row and a W_u row
+  using WT = WaveTile<BN>;
+  constexpr int NWM = WT::NWM;
+  static_assert(WT::NWN == 2, "a wave holds one gate block and one up block");
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  const int mt = (M + GEMM_BM - 1) / GEMM_BM, ntl = F / HALF;
+  const int mt = (M + GEMM_BM - 1) / GEMM_BM, ntl = F / UNITS;
   int tm, tn;
   tile_coords(blockIdx.x, mt, ntl, tm, tn);
-  const int m0 = tm * GEMM_BM, n0 = tn * HALF;
+  const int m0 = tm * GEMM_BM, n0 = tn * UNITS;
   const int n_eff = n_rows_dev ? min(*n_rows_dev, M) : M;
   if (m0 >= n_eff) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int row0 = WT::row0(wave), col0 = WT::col0(wave);
   const size_t ldk = (size_t)K * sizeof(T);
   auto phys = [&](int r) { return rows ? rows[r] : r; };
 
@@ -39,46 +44,44 @@ __global__ __launch_bounds__(GEMM_THREADS) void k_gate_up(
     const int row = lr < n_eff ? phys(lr) : phys(0);
     return reinterpret_cast<const char *>(x) + (size_t)row * ldk;
   };
+  // B row r: 64-row group g = r / 64 covers units n0 + 32g .. n0 + 32g + 31,
+  // first as W_g rows, then as W_u rows, so the wave that owns columns
+  // [64g, 64g + 64) holds the gate and the up value of the same unit in the
+  // same lane (accumulator blocks 0 and 1).
   auto rowB = [&](int r) {
-    const T *w = r < HALF ? wg : wu;
-    return reinterpret_cast<const char *>(w) + (size_t)(n0 + (r & (HALF - 1))) * ldk;
+    const T *w = (r & 32) ? wu : wg;
+    return reinterpret_cast<const char *>(w) + (size_t)(n0 + 32 * (r >> 6) + (r & 31)) * ldk;
   };
 
-  f32x16_t acc[2][8];
+  auto rowv = [&](int r) -> const float * {
+    return beta != nullptr ? beta + phys(min(m0 + r, n_eff - 1)) : nullptr;
+  };
+  auto init = [&](f32x16_t (&a)[NWM][2], const float *vals) {
 #pragma unroll
-  for (int bm = 0; bm < 2; ++bm) {
-    f32x16_t b0;
+    for (int bm = 0; bm < NWM; ++bm) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      int lr = m0 + acc_row(wave, bm, i, lane);
-      b0[i] = (beta != nullptr && lr < n_eff) ? beta[phys(lr)] : 0.0f;
+      for (int i = 0; i < 16; ++i) a[bm][0][i] = vals != nullptr ? vals[acc_row(row0, bm, i, lane)] : 0.0f;
+      a[bm][1] = f32x16_t{};
     }
-#pragma unroll
-    for (int bn = 0; bn < 4; ++bn) acc[bm][bn] = b0;
-#pragma unroll
-    for (int bn = 4; bn < 8; ++bn) acc[bm][bn] = f32x16_t{};
-  }
-
-  gemm_mainloop_dma<D, BN>(acc, rowA, rowB, (int)(ldk / SLAB), smem);
+  };
+  f32x16_t acc[NWM][2];
+  gemm_mainloop_dma<D, BN>(acc, rowA, rowB, rowv, init, (int)(ldk / SLAB), smem);
 
   const int col = lane & 31;
-  int row_base = m0 + 64 * wave + 4 * (lane >> 5);  // opaque: keep row math after the mainloop
+  int row_base = m0 + row0 + 4 * (lane >> 5);  // opaque: keep row math after the mainloop
   asm volatile("" : "+v"(row_base));
+  const size_t j = (size_t)n0 + col0 / 2 + col;
 #pragma unroll
-  for (int bm = 0; bm < 2; ++bm) {
+  for (int bm = 0; bm < NWM; ++bm) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int lr = row_base + 32 * bm + 8 * (i >> 2) + (i & 3);
       if (lr >= n_eff) continue;
-#pragma unroll
-      for (int bn = 0; bn < 4; ++bn) {
-        const T hb = from_f32<D>(acc[bm][bn][i]);
-        const bool act = active_bits(hb);
-        const float h = act ? to_f32(hb) : 0.0f;
-        const size_t j = (size_t)n0 + 32 * bn + col;
-        a_ws[(size_t)lr * F + j] = from_f32<D>(h * acc[bm][bn + 4][i]);
-        if (h_out != nullptr && lr < h_cap) h_out[(size_t)lr * F + j] = act ? hb : T(0);
-      }
+      const T hb = from_f32<D>(acc[bm][0][i]);
+      const bool act = active_bits(hb);
+      const float h = act ? to_f32(hb) : 0.0f;
+      a_ws[(size_t)lr * F + j] = from_f32<D>(h * acc[bm][1][i]);
+      if (h_out != nullptr && lr < h_cap) h_out[(size_t)lr * F + j] = act ? hb : T(0);
     }
   }
 }
@@ -140,7 +143,7 @@ static hipError_t launch_gate_up(const DenseArgs &a, hipStream_t s) {
   hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
   const int mt = (a.M + GEMM_BM - 1) / GEMM_BM, ntl = a.F / 128;
-  hipLaunchKernelGGL(kern, dim3(mt * ntl), dim3(GEMM_THREADS), lds, s, (const T *)a.x, (const T *)a.wg,
+  hipLaunchKernelGGL(kern, dim3(mt * ntl), dim3(DMA_THREADS), lds, s, (const T *)a.x, (const T *)a.wg,
                      (const T *)a.wu, a.beta, a.M, a.d, a.F, a.rows, a.n_rows_dev, (T *)a.a_ws,
                      (T *)a.h_out, a.h_cap);
   return hipGetLastError();

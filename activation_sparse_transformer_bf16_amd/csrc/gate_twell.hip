@@ -8,9 +8,8 @@
 // of gist.science "Sparser, Faster, Lighter Transformer Language Models",
 // Resumen Técnico §2.A, carried over to gfx950: the N tile of the matmul is
 // exactly one TwELL tile, so every (row, tile) pair is owned by one workgroup;
-// the rounded tile is staged in the LDS the mainloop no longer needs, and each
-// wave compacts whole rows with wave ballots (v_cmp masks) and mbcnt prefix
-// counts.
+// the activity masks and the rounded tile are staged in the LDS the mainloop
+// no longer needs, and one lane per row compacts it in ascending column order.
 #include "gemm.hpp"
 #include "launch.hpp"
 
@@ -67,13 +66,14 @@ __device__ __forceinline__ void copy_out(char *__restrict__ g, const char *l, in
 }
 
 template <Dt D, int BN, bool DUMP>
-__global__ __launch_bounds__(GEMM_THREADS) void k_gate_twell(
+__global__ __launch_bounds__(DMA_THREADS) void k_gate_twell(
     const typename DtT<D>::T *__restrict__ x, const typename DtT<D>::T *__restrict__ wg,
     const float *__restrict__ beta, int M, int K, int N, int cap, uint16_t *__restrict__ cnt,
     typename DtT<D>::T *__restrict__ val, uint8_t *__restrict__ idx,
     typename DtT<D>::T *__restrict__ pre_out) {
   using T = typename DtT<D>::T;
-  constexpr int NB = BN / 32;
+  using WT = WaveTile<BN>;
+  constexpr int NWM = WT::NWM, NWN = WT::NWN;
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int mt = (M + GEMM_BM - 1) / GEMM_BM, ntl = N / BN;
@@ -81,6 +81,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void k_gate_twell(
   tile_coords(blockIdx.x, mt, ntl, tm, tn);
   const int m0 = tm * GEMM_BM, n0 = tn * BN;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int row0 = WT::row0(wave), col0 = WT::col0(wave);
   const size_t ldk = (size_t)K * sizeof(T);
 
   auto rowA = [&](int r) {
@@ -90,25 +91,24 @@ __global__ __launch_bounds__(GEMM_THREADS) void k_gate_twell(
   auto rowB = [&](int r) { return reinterpret_cast<const char *>(wg) + (size_t)(n0 + r) * ldk; };
 
   // The accumulators start at beta so that the matmul adds the gate bias.
-  f32x16_t acc[2][NB];
+  auto rowv = [&](int r) -> const float * { return beta != nullptr ? beta + min(m0 + r, M - 1) : nullptr; };
+  auto init = [&](f32x16_t (&a)[NWM][NWN], const float *vals) {
 #pragma unroll
-  for (int bm = 0; bm < 2; ++bm) {
-    f32x16_t b0;
+    for (int bm = 0; bm < NWM; ++bm) {
+      f32x16_t b0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      int t = m0 + acc_row(wave, bm, i, lane);
-      b0[i] = (beta != nullptr && t < M) ? beta[t] : 0.0f;
+      for (int i = 0; i < 16; ++i) b0[i] = vals != nullptr ? vals[acc_row(row0, bm, i, lane)] : 0.0f;
+#pragma unroll
+      for (int bn = 0; bn < NWN; ++bn) a[bm][bn] = b0;
     }
-#pragma unroll
-    for (int bn = 0; bn < NB; ++bn) acc[bm][bn] = b0;
-  }
-
-  gemm_mainloop_dma<D, BN>(acc, rowA, rowB, (int)(ldk / SLAB), smem);
+  };
+  f32x16_t acc[NWM][NWN];
+  gemm_mainloop_dma<D, BN>(acc, rowA, rowB, rowv, init, (int)(ldk / SLAB), smem);
 
   // ---- TwELL epilogue ----
   // M  every wave compares its accumulators with the activity threshold of the
   //    rounded value (v_cmp, one 64-bit mask per register: 32 columns of two
-  //    rows) and files the masks in LDS as 256-bit row masks;
+  //    rows) and files the masks in LDS as BN-bit row masks;
   // then per pass of RPP rows:
   //  V  the waves that own those rows stage the rounded values in LDS;
   //  C  one lane per row walks the row's set bits in ascending order (ffbl),
@@ -126,23 +126,24 @@ __global__ __launch_bounds__(GEMM_THREADS) void k_gate_twell(
   const int vunit = (cap * S) % 16 == 0 ? 16 : ((cap * S) % 4 == 0 ? 4 : S);
   const int iunit = cap % 16 == 0 ? 16 : (cap % 4 == 0 ? 4 : 1);
   {
-    // lane k < 2*MW receives mask word k % MW of row R (k < MW) or R+4
-    const bool holder = lane < 2 * MW;
-    const int word = lane % MW;
-    const int roff = lane < MW ? 0 : 4;
-    uint32_t *dummy = reinterpret_cast<uint32_t *>(smem + L::dummy_off(cap)) + lane;
+    // lane k < 2*NWN receives mask word col0/32 + k % NWN of row R (k < NWN)
+    // or of row R+4
+    const bool holder = lane < 2 * NWN;
+    const int word = col0 / 32 + lane % NWN;
+    const int roff = lane < NWN ? 0 : 4;
+    uint32_t *dummy = reinterpret_cast<uint32_t *>(smem + L::dummy_off(cap)) + (tid & 63);
 #pragma unroll
-    for (int bm = 0; bm < 2; ++bm) {
+    for (int bm = 0; bm < NWM; ++bm) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         uint32_t w = 0;
 #pragma unroll
-        for (int bn = 0; bn < MW; ++bn) {
+        for (int bn = 0; bn < NWN; ++bn) {
           const uint64_t m = ballot(active_after_round<D>(acc[bm][bn][i]));
           w = (lane == bn) ? (uint32_t)m : w;
-          w = (lane == MW + bn) ? (uint32_t)(m >> 32) : w;
+          w = (lane == NWN + bn) ? (uint32_t)(m >> 32) : w;
         }
-        const int R = 64 * wave + 32 * bm + 8 * (i >> 2) + (i & 3);
+        const int R = row0 + 32 * bm + 8 * (i >> 2) + (i & 3);
         uint32_t *dst = holder ? masks + (R + roff) * MW + word : dummy;
         *dst = w;
       }
@@ -151,37 +152,39 @@ __global__ __launch_bounds__(GEMM_THREADS) void k_gate_twell(
   // The accumulators are read again by V: make them opaque here so that the
   // copies made for the masks are not kept live (which would spill).
 #pragma unroll
-  for (int bm = 0; bm < 2; ++bm)
+  for (int bm = 0; bm < NWM; ++bm)
 #pragma unroll
-    for (int bn = 0; bn < BN / 32; ++bn) asm volatile("" : "+a"(acc[bm][bn]));
+    for (int bn = 0; bn < NWN; ++bn) asm volatile("" : "+a"(acc[bm][bn]));
 #pragma unroll
   for (int p = 0; p < GEMM_BM / RPP; ++p) {
     // V: stage the rounded values of this pass and clear the slots
-    for (int o = tid * 16; o < RPP * (VS + IS); o += GEMM_THREADS * 16)
+    for (int o = tid * 16; o < RPP * (VS + IS); o += DMA_THREADS * 16)
       *reinterpret_cast<u32x4_t *>(vals + o) = u32x4_t{0u, 0u, 0u, 0u};
-    if ((64 * wave) / RPP == p) {
-      const int r0 = 64 * wave - p * RPP + 4 * (lane >> 5);
-      char *colp = tile + (lane & 31) * RS;
+    const int rl0 = row0 - p * RPP + 4 * (lane >> 5);  // lane's first row, relative to the pass
 #pragma unroll
-      for (int bm = 0; bm < 2; ++bm)
+    for (int bm = 0; bm < NWM; ++bm) {
+      if ((row0 + 32 * bm) / RPP != p) continue;  // wave-uniform
 #pragma unroll
-        for (int bn = 0; bn < BN / 32; ++bn)
+      for (int bn = 0; bn < NWN; ++bn) {
+        char *colp = tile + (col0 + 32 * bn + (lane & 31)) * RS;
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            put4(colp + bn * 32 * RS + (r0 + 32 * bm + 8 * g) * S, acc[bm][bn], 4 * g, T());
-            if constexpr (DUMP) {
-              const int t0 = m0 + p * RPP + r0 + 32 * bm + 8 * g;
+        for (int g = 0; g < 4; ++g) {
+          put4(colp + (rl0 + 32 * bm + 8 * g) * S, acc[bm][bn], 4 * g, T());
+          if constexpr (DUMP) {
+            const int t0 = m0 + p * RPP + rl0 + 32 * bm + 8 * g;
 #pragma unroll
-              for (int q = 0; q < 4; ++q)
-                if (t0 + q < M) pre_out[(size_t)(t0 + q) * N + n0 + bn * 32 + (lane & 31)] = from_f32<D>(acc[bm][bn][4 * g + q]);
-            }
+            for (int q = 0; q < 4; ++q)
+              if (t0 + q < M)
+                pre_out[(size_t)(t0 + q) * N + n0 + col0 + 32 * bn + (lane & 31)] = from_f32<D>(acc[bm][bn][4 * g + q]);
           }
+        }
+      }
     }
     __syncthreads();
     // C: one lane per row
-    if (lane < RPP / 4) {
-      const int rl = wave * (RPP / 4) + lane;  // row within the pass
-      const int rg = p * RPP + rl;             // row within the tile
+    if (lane < RPP / DMA_WAVES) {
+      const int rl = wave * (RPP / DMA_WAVES) + lane;  // row within the pass
+      const int rg = p * RPP + rl;                     // row within the tile
       const int t = m0 + rg;
       int n = 0, total = 0;
 #pragma unroll
@@ -215,7 +218,7 @@ static hipError_t launch_gate(const GateArgs &a, hipStream_t s) {
   hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
   const int mt = (a.M + GEMM_BM - 1) / GEMM_BM, ntl = a.N / BN;
-  hipLaunchKernelGGL(kern, dim3(mt * ntl), dim3(GEMM_THREADS), lds, s, (const T *)a.x,
+  hipLaunchKernelGGL(kern, dim3(mt * ntl), dim3(DMA_THREADS), lds, s, (const T *)a.x,
                      (const T *)a.wg, a.beta, a.M, a.K, a.N, a.cap, a.cnt, (T *)a.val, a.idx,
                      (T *)a.pre_out);
   return hipGetLastError();

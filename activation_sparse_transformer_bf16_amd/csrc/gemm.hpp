@@ -1,20 +1,23 @@
-// MFMA GEMM mainloop for gfx950 shared by the gate, gate+up and down kernels.
+// MFMA GEMM mainloops for gfx950 shared by the gate, gate+up and down kernels.
 //
 // C[m][n] = sum_k A[m][k] * B(k, n), accumulated in fp32 on the matrix cores:
 // bf16 operands use v_mfma_f32_32x32x16_bf16, fp32 operands v_mfma_f32_32x32x2_f32.
+// The workgroup tile is BM = 256 rows x BN (128 or 256) columns.
 //
-// Workgroup tile: BM = 256 rows x BN (128 or 256) columns, 4 waves.  Wave w
-// owns rows [64w, 64w + 64) and every column of the tile, i.e. 2 x BN/32
-// blocks of 32x32 accumulators (a whole TwELL tile row sits in one wave,
-// which lets the TwELL epilogue run without any cross-wave exchange).
-//
-// K is consumed 128 bytes at a time (64 bf16 / 32 fp32).  Each stage keeps
-// A [256][128 B] and B [BN][128 B] in LDS; every 128-byte row is 8 chunks of
-// 16 bytes, and chunk c of row r sits at physical chunk c ^ ((r >> 1) & 7),
-// which makes the 16-lane phases of ds_read_b128 conflict-free on the 64-bank
-// gfx950 LDS (two consecutive rows fill the 256-byte bank width).  Two stages
-// are double-buffered; the next stage's global loads are issued before the
-// current stage's MFMAs and written to LDS after them.
+// Two mainloops:
+//  * gemm_mainloop_dma (A and B both K-contiguous: the gate and gate+up
+//    matmuls): 8 waves, direct global -> LDS loads through a 4-stage ring,
+//    described below.
+//  * gemm_mainloop (B N-contiguous, W_d [F][d] in the down projection): 4
+//    waves, register-staged loads with an in-register 8x8 transpose of B.
+//    Wave w owns rows [64w, 64w + 64) and every column of the tile.  K is
+//    consumed 128 bytes at a time (64 bf16 / 32 fp32); each stage keeps
+//    A [256][128 B] and B [BN][128 B] in LDS, every 128-byte row is 8 chunks
+//    of 16 bytes, and chunk c of row r sits at physical chunk c ^ ((r >> 1) & 7),
+//    which makes the 16-lane phases of ds_read_b128 conflict-free on the
+//    64-bank gfx950 LDS.  Two stages are double-buffered; the next stage's
+//    global loads are issued before the current stage's MFMAs and written to
+//    LDS after them.
 #pragma once
 
 #include "common.hpp"
@@ -228,11 +231,20 @@ __device__ __forceinline__ void gemm_mainloop(f32x16_t (&acc)[2][BN / 32], LA &l
 // global_load_lds_dwordx4 moves 16 bytes per lane from global memory straight
 // into LDS (M0 + 16 * lane), with no VGPR staging, so several stages can be in
 // flight at once.  K is consumed in 64-byte slabs (32 bf16 / 16 fp32) through a
-// ring of DMA_STAGES LDS stages; the loads of stage kt+3 are issued while stage
-// kt is multiplied.  The loads are written as inline assembly and their
-// completion is tracked with explicit s_waitcnt vmcnt: the compiler otherwise
-// assumes every LDS read may alias an in-flight direct load and waits for all
-// of them, which would serialise the ring.
+// ring of DMA_STAGES LDS stages that all start filled.  The loads are written
+// as inline assembly and their completion is tracked with explicit s_waitcnt
+// vmcnt: the compiler otherwise assumes every LDS read may alias an in-flight
+// direct load and waits for all of them, which would serialise the ring.
+//
+// The workgroup has 8 waves (two per SIMD, so one wave's LDS reads overlap the
+// other's MFMAs).  For BN = 256 the waves form a 2 x 4 grid of 128 x 64 wave
+// tiles; for BN = 128 a 4 x 2 grid of 64 x 64.  A wave always spans 64 columns
+// (two 32-column accumulator blocks) and WaveTile<BN>::NWM blocks of 32 rows.
+// A wave's operand fragments are double-buffered in registers: the second
+// half of slab kt is read from LDS while the first half is multiplied, and the
+// first half of slab kt+1 while the second half of slab kt is multiplied.  One
+// barrier per slab, placed after the last read of slab kt, frees its LDS stage
+// for the loads of slab kt + DMA_STAGES.
 //
 // Each 64-byte LDS row holds 4 chunks of 16 bytes; chunk c of row r sits at
 // physical chunk c ^ ((r >> 2) & 3), so the 16 lanes of one ds_read_b128 phase
@@ -241,8 +253,22 @@ __device__ __forceinline__ void gemm_mainloop(f32x16_t (&acc)[2][BN / 32], LA &l
 
 constexpr int DMA_STAGES = 4;
 constexpr int SLAB = 64;  // K bytes per stage
+constexpr int DMA_WAVES = 8;
+constexpr int DMA_THREADS = 64 * DMA_WAVES;
 
-__host__ __device__ constexpr int gemm_dma_lds_bytes(int bn) { return DMA_STAGES * (GEMM_BM + bn) * SLAB; }
+// LDS: the ring, then one fp32 value per tile row (the gate bias, loaded with
+// the first stages so that no separate global round trip delays the tile).
+__host__ __device__ constexpr int gemm_dma_ring_bytes(int bn) { return DMA_STAGES * (GEMM_BM + bn) * SLAB; }
+__host__ __device__ constexpr int gemm_dma_lds_bytes(int bn) { return gemm_dma_ring_bytes(bn) + GEMM_BM * 4; }
+
+template <int BN>
+struct WaveTile {
+  static constexpr int WPR = BN / 64;                        // waves across the N tile
+  static constexpr int NWN = 2;                              // 32-column blocks per wave
+  static constexpr int NWM = GEMM_BM / 32 / (DMA_WAVES / WPR);  // 32-row blocks per wave
+  __device__ __forceinline__ static int row0(int wave) { return (wave / WPR) * 32 * NWM; }
+  __device__ __forceinline__ static int col0(int wave) { return (wave % WPR) * 64; }
+};
 
 __device__ __forceinline__ int lds_off64(int row, int chunk) {
   return row * SLAB + ((chunk ^ ((row >> 2) & 3)) << 4);
@@ -258,6 +284,10 @@ __device__ __forceinline__ uint32_t lds_address(const void *p) {
 __device__ __forceinline__ void dma16(const void *g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
 }
+// One wave-wide 4-byte-per-lane copy global -> LDS [lds, lds + 256).
+__device__ __forceinline__ void dma4(const void *g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 template <int N>
@@ -265,11 +295,25 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Wait until at most n (0..3, wave-uniform) stages of OPS loads each are still
+// in flight.
+template <int OPS>
+__device__ __forceinline__ void wait_stages(int n) {
+  if (n >= 3)
+    wait_vmcnt<3 * OPS>();
+  else if (n == 2)
+    wait_vmcnt<2 * OPS>();
+  else if (n == 1)
+    wait_vmcnt<OPS>();
+  else
+    wait_vmcnt<0>();
+}
+
 // Rows of one operand tile loaded by DMA.  NR rows x 4 chunks = NR*4 lane
-// slots = NR/16 wave instructions, spread over the 4 waves.
+// slots = NR/16 wave instructions, spread over the 8 waves.
 template <int NR>
 struct DmaRows {
-  static constexpr int PER_WAVE = NR / 64;  // instructions per wave per stage
+  static constexpr int PER_WAVE = NR / 16 / DMA_WAVES;  // instructions per wave per stage
   const char *ptr[PER_WAVE];
   uint32_t lds_off[PER_WAVE];  // byte offset of the wave's 1 KB block in the stage
 
@@ -290,74 +334,100 @@ struct DmaRows {
   }
 };
 
-template <Dt D, int BN>
-__device__ __forceinline__ void mfma_slab(f32x16_t (&acc)[2][BN / 32], const char *stage, int wave, int lane) {
+// Operand fragments of one 32-k half slab for a wave tile.
+template <int NWM, int NWN>
+struct Frag {
+  u32x4_t a[NWM], b[NWN];
+};
+
+template <int NWM, int NWN>
+__device__ __forceinline__ void read_frag(Frag<NWM, NWN> &f, const char *stage, int row0, int col0, int half,
+                                          int lane) {
   const char *As = stage;
   const char *Bs = stage + GEMM_BM * SLAB;
   const int r = lane & 31, h = lane >> 5;
 #pragma unroll
-  for (int g = 0; g < 2; ++g) {
-    u32x4_t a[2], b[BN / 32];
+  for (int i = 0; i < NWM; ++i)
+    f.a[i] = *reinterpret_cast<const u32x4_t *>(As + lds_off64(row0 + 32 * i + r, 2 * half + h));
 #pragma unroll
-    for (int bm = 0; bm < 2; ++bm)
-      a[bm] = *reinterpret_cast<const u32x4_t *>(As + lds_off64(64 * wave + 32 * bm + r, 2 * g + h));
+  for (int j = 0; j < NWN; ++j)
+    f.b[j] = *reinterpret_cast<const u32x4_t *>(Bs + lds_off64(col0 + 32 * j + r, 2 * half + h));
+}
+
+template <Dt D, int NWM, int NWN>
+__device__ __forceinline__ void mfma_frag(f32x16_t (&acc)[NWM][NWN], const Frag<NWM, NWN> &f) {
 #pragma unroll
-    for (int bn = 0; bn < BN / 32; ++bn)
-      b[bn] = *reinterpret_cast<const u32x4_t *>(Bs + lds_off64(32 * bn + r, 2 * g + h));
+  for (int i = 0; i < NWM; ++i)
 #pragma unroll
-    for (int bm = 0; bm < 2; ++bm)
-#pragma unroll
-      for (int bn = 0; bn < BN / 32; ++bn) Mfma<D>::step(acc[bm][bn], a[bm], b[bn]);
-  }
+    for (int j = 0; j < NWN; ++j) Mfma<D>::step(acc[i][j], f.a[i], f.b[j]);
 }
 
 // Mainloop over nk 64-byte K slabs; A rows from rowA(r), B rows from rowB(r).
-template <Dt D, int BN, class RA, class RB>
-__device__ __forceinline__ void gemm_mainloop_dma(f32x16_t (&acc)[2][BN / 32], RA rowA, RB rowB, int nk,
-                                                  char *smem) {
+// rowv(r) points at one fp32 value per tile row r (or is null for every r);
+// those values are copied to LDS with the first stages, and init(acc, vals)
+// sets the accumulators before the first MFMA, vals being the LDS copy
+// (GEMM_BM floats) or null.
+template <Dt D, int BN, class RA, class RB, class RV, class INIT>
+__device__ __forceinline__ void gemm_mainloop_dma(f32x16_t (&acc)[WaveTile<BN>::NWM][WaveTile<BN>::NWN], RA rowA,
+                                                  RB rowB, RV rowv, INIT init, int nk, char *smem) {
+  using WT = WaveTile<BN>;
+  constexpr int NWM = WT::NWM, NWN = WT::NWN;
   constexpr int STAGE = (GEMM_BM + BN) * SLAB;
   constexpr int OPS = DmaRows<GEMM_BM>::PER_WAVE + DmaRows<BN>::PER_WAVE;  // DMA ops per stage per lane
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int wave_u = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row0 = WT::row0(wave_u), col0 = WT::col0(wave_u);
   const uint32_t base = lds_address(smem);
+  const bool has_rowv = rowv(0) != nullptr;
   DmaRows<GEMM_BM> da;
   DmaRows<BN> db;
   da.init(wave_u, lane, 0, rowA);
   db.init(wave_u, lane, GEMM_BM * SLAB, rowB);
+  // waves 0-3 copy 64 row values each; issued before the stages, so the
+  // stage waits below cover them (loads complete in order)
+  if (has_rowv && wave_u < GEMM_BM / 64)
+    dma4(rowv(64 * wave_u + lane), base + gemm_dma_ring_bytes(BN) + 256 * wave_u);
 #pragma unroll
-  for (int s = 0; s < DMA_STAGES - 1; ++s) {
+  for (int s = 0; s < DMA_STAGES; ++s) {
     if (s < nk) {
       da.issue(s, base + s * STAGE);
       db.issue(s, base + s * STAGE);
     }
   }
+  wait_stages<OPS>(min(nk - 1, DMA_STAGES - 1));
+  __syncthreads();
+  init(acc, has_rowv ? reinterpret_cast<const float *>(smem + gemm_dma_ring_bytes(BN)) : nullptr);
+  Frag<NWM, NWN> f0, f1;
+  read_frag(f0, smem, row0, col0, 0, lane);
   for (int kt = 0; kt < nk; ++kt) {
-    // stage kt landed once at most the younger stages' loads are outstanding
-    if (kt + 2 < nk)
-      wait_vmcnt<2 * OPS>();
-    else if (kt + 1 < nk)
-      wait_vmcnt<OPS>();
-    else
-      wait_vmcnt<0>();
-    __syncthreads();
-    const int nxt = kt + DMA_STAGES - 1;
-    if (nxt < nk) {
-      const uint32_t sb = base + (nxt % DMA_STAGES) * STAGE;
-      da.issue(nxt, sb);
-      db.issue(nxt, sb);
+    const int slot = kt % DMA_STAGES;
+    read_frag(f1, smem + slot * STAGE, row0, col0, 1, lane);
+    mfma_frag<D>(acc, f0);
+    if (kt + 1 < nk) {
+      // every wave has read all of slab kt (the barrier waits for its LDS
+      // reads) and slab kt+1 has landed for every wave
+      wait_stages<OPS>(min(nk - 2 - kt, DMA_STAGES - 2));
+      __syncthreads();
+      if (kt + DMA_STAGES < nk) {
+        const uint32_t sb = base + slot * STAGE;
+        da.issue(kt + DMA_STAGES, sb);
+        db.issue(kt + DMA_STAGES, sb);
+      }
+      read_frag(f0, smem + ((kt + 1) % DMA_STAGES) * STAGE, row0, col0, 0, lane);
     }
-    mfma_slab<D, BN>(acc, smem + (kt % DMA_STAGES) * STAGE, wave, lane);
+    mfma_frag<D>(acc, f1);
   }
-  // no DMA is left in flight; make the last stage's LDS reads complete before
+  // no DMA is left in flight; make every wave's last LDS reads complete before
   // the caller reuses LDS
   __syncthreads();
 }
 
 // Accumulator element (bm, bn, i) of lane l sits at tile row
-//   64*wave + 32*bm + 8*(i/4) + 4*(l/32) + (i%4)   and tile column 32*bn + (l%32).
-__device__ __forceinline__ int acc_row(int wave, int bm, int i, int lane) {
-  return 64 * wave + 32 * bm + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+//   row0 + 32*bm + 8*(i/4) + 4*(l/32) + (i%4)   and tile column col0 + 32*bn + (l%32),
+// with (row0, col0) the origin of the wave's tile (64 * wave, 0 in the 4-wave
+// register-staged mainloop).
+__device__ __forceinline__ int acc_row(int row0, int bm, int i, int lane) {
+  return row0 + 32 * bm + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
 }
 
 // Grouped, XCD-aware order of (m-tile, n-tile) pairs: the tiles that run at the
