@@ -68,8 +68,10 @@ twell_status check_format(int tile, int cap, int F, int dtype) {
 
 twell_status check_d(int d, int dtype) {
   if (d <= 0) return fail(TWELL_ERR_INVALID_ARG, "d must be positive");
+  // one row of x is held in registers as at most 16 16-byte chunks per lane
   const int q = dtype == TWELL_BF16 ? 512 : 256;
-  if (d % q != 0 || d > 8192) return fail(TWELL_ERR_UNSUPPORTED, "d %d not built (multiple of %d, <= 8192)", d, q);
+  if (d % q != 0 || d > 16 * q)
+    return fail(TWELL_ERR_UNSUPPORTED, "d %d not built (multiple of %d, <= %d)", d, q, 16 * q);
   return TWELL_OK;
 }
 
@@ -98,16 +100,21 @@ twell_status check_matrix(const twell_matrix *m, bool need_ovf_all) {
   return TWELL_OK;
 }
 
+// Workspace of the sparse forward: row flags | compact entry lists (8 bytes per
+// entry) | entry counts | dense fallback activations.
 struct FfnWs {
-  size_t flag, v, a, total;
+  size_t flag, list, list_n, a, total;
+  int stride;
 };
 
 FfnWs ffn_ws_layout(int T, int F, int tile, int cap, twell_dtype dt) {
   FfnWs w;
   const size_t nt = (size_t)F / tile;
+  w.stride = (int)((nt * cap + 7) / 8 * 8);
   w.flag = 0;
-  w.v = align_up((size_t)T, ALIGN_WS);
-  w.a = align_up(w.v + (size_t)T * nt * cap * 4, ALIGN_WS);
+  w.list = align_up((size_t)T, ALIGN_WS);
+  w.list_n = align_up(w.list + (size_t)T * w.stride * 8, ALIGN_WS);
+  w.a = align_up(w.list_n + (size_t)T * 4, ALIGN_WS);
   w.total = std::max(align_up(w.a + (size_t)T * F * dt_size(dt), ALIGN_WS), ALIGN_WS);
   return w;
 }
@@ -127,14 +134,15 @@ twell_status run_sparse(const twell_matrix *m, const void *x, const void *wg, co
   const FfnWs L = ffn_ws_layout(T, F, m->tile, m->cap, m->dtype);
   char *base = static_cast<char *>(ws);
   uint8_t *row_flag = reinterpret_cast<uint8_t *>(base + L.flag);
-  float *vbuf = reinterpret_cast<float *>(base + L.v);
+  void *list = base + L.list;
+  int *list_n = reinterpret_cast<int *>(base + L.list_n);
   void *a_ws = base + L.a;
   const Dt D = to_dt(m->dtype);
 
   ScanArgs sc{m->cnt, T, F / m->tile, m->cap, row_flag, m->ovf_rows, m->ovf_cap, m->n_ovf};
   TW_TRY(overflow_scan(sc, s), "overflow scan");
 
-  SparseArgs sa{D, T, d, F, m->tile, m->cap, m->cnt, m->val, m->idx, row_flag, x, wu, wd, vbuf, y};
+  SparseArgs sa{D, T, d, F, m->tile, m->cap, m->cnt, m->val, m->idx, row_flag, x, wu, wd, list, list_n, L.stride, y};
   TW_TRY(sparse_up(sa, s), "sparse up projection");
   TW_TRY(sparse_down(sa, s), "sparse down projection");
 

@@ -45,7 +45,9 @@ struct SparseArgs {
   const void *x;            // [T][d]
   const void *wu;           // [F][d]
   const void *wd;           // [F][d]
-  float *vbuf;              // [T][nt][cap] fp32: h * u per TwELL slot
+  void *list;               // [T][stride] entries (uint32 row byte offset, fp32 v = h * u)
+  int *list_n;              // [T] entries per row
+  int stride;               // list entries per row: nt * cap rounded up to a multiple of 8
   void *y;                  // [T][d]
 };
 hipError_t sparse_up(const SparseArgs &a, hipStream_t s);

@@ -7,10 +7,12 @@
 // weights resident in one XCD's 4 MB L2:
 //   up:   hidden units are split into groups of TwELL tiles and group g runs on
 //         XCD g % 8; per active entry (t, j) one wave dots x_t (held in
-//         registers) with the W_u^T row j, and stores v = h * u in fp32.
+//         registers) with the W_u^T row j, and writes (row offset of j,
+//         v = h * u in fp32) to row t's compact entry list.
 //   down: the d output columns are split into slices and slice s runs on
-//         XCD s % 8; per token one wave accumulates v * W_d[j][slice] over all
-//         the token's entries in fp32 registers and rounds y once.
+//         XCD s % 8; per token one wave walks the token's entry list with
+//         scalar loads, accumulates v * W_d[j][slice] in fp32 registers and
+//         rounds y once.
 // Rows flagged by the overflow scan are left to the dense fallback.
 #include "launch.hpp"
 
@@ -92,8 +94,7 @@ hipError_t zero_int(int *p, hipStream_t s) {
 
 constexpr int SP_THREADS = 256;
 constexpr int SP_WAVES = SP_THREADS / 64;
-constexpr int UP_LIST = 256;    // entries per wave list (tiles per group * cap)
-constexpr int DOWN_LIST = 512;  // entries per wave list (tiles per fill * cap)
+constexpr int UP_LIST = 256;  // entries per wave list (tiles per group * cap)
 
 // Block -> (group, token block) so that group g runs on XCD g % 8 when the
 // group count is a multiple of 8 (groups beyond 8 run in successive phases).
@@ -114,10 +115,31 @@ __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-struct Entry {
-  int j;      // hidden unit (global column); bits 26.. hold the slot s for the up kernel
-  float w;    // h (up) or v = h*u (down)
-};
+__device__ __forceinline__ uint32_t read_lane(uint32_t v, int q) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, q);
+}
+
+// Raw buffer over [p, p + 2 GiB): a load takes a per-lane VGPR offset and a
+// wave-uniform SGPR offset, so a gathered weight row costs no per-lane address
+// arithmetic.  Every offset used here is below 2 GiB (weights are limited to
+// that size).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *p) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, 0x7FFFFFFF, 0x00020000);
+}
+template <class V>
+__device__ __forceinline__ V buffer_load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff);
+template <>
+__device__ __forceinline__ uint32_t buffer_load<uint32_t>(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+template <>
+__device__ __forceinline__ u32x2_t buffer_load<u32x2_t>(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+}
+template <>
+__device__ __forceinline__ u32x4_t buffer_load<u32x4_t>(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
 
 // Dot product of one 16-byte chunk pair, fp32 accumulation.
 __device__ __forceinline__ float dot16(const u32x4_t &a, const u32x4_t &b, float acc, uint16_t) {
@@ -138,27 +160,94 @@ __device__ __forceinline__ float dot16(const u32x4_t &a, const u32x4_t &b, float
   return acc;
 }
 
+#define TWELL_ROW_SUM_DPP(v)                                                                                   \
+  do {                                                                                                         \
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));  /* quad_perm 1,0,3,2 */ \
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));  /* quad_perm 2,3,0,1 */ \
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false)); /* row_ror 4 */        \
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false)); /* row_ror 8 */        \
+  } while (0)
+
+// Joint wave reduction of U partial-sum registers (one entry each, 64 lanes).
+// v_permlane32_swap / v_permlane16_swap fold the halves and quarters of the
+// wave of two registers into one, then DPP sums each 16-lane row; every lane
+// of row r ends up with the total of entry Reduce<U>::entry(r).
+template <int U> struct Reduce;
+template <>
+struct Reduce<4> {
+  __device__ __forceinline__ static int entry(int row) { return ((row & 1) << 1) | (row >> 1); }
+  __device__ __forceinline__ static float run(const float (&p)[4]) {
+    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[0]), __float_as_uint(p[1]), false, false);
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[2]), __float_as_uint(p[3]), false, false);
+    const float s01 = __uint_as_float(a[0]) + __uint_as_float(a[1]);  // lanes 0-31: entry 0, 32-63: entry 1
+    const float s23 = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+    auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(s01), __float_as_uint(s23), false, false);
+    float v = __uint_as_float(c[0]) + __uint_as_float(c[1]);  // rows: entries 0, 2, 1, 3
+    TWELL_ROW_SUM_DPP(v);
+    return v;
+  }
+};
+template <>
+struct Reduce<2> {
+  __device__ __forceinline__ static int entry(int row) { return row >> 1; }
+  __device__ __forceinline__ static float run(const float (&p)[2]) {
+    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[0]), __float_as_uint(p[1]), false, false);
+    const float s = __uint_as_float(a[0]) + __uint_as_float(a[1]);  // lanes 0-31: entry 0, 32-63: entry 1
+    auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+    float v = __uint_as_float(c[0]) + __uint_as_float(c[1]);  // rows: entries 0, 0, 1, 1
+    TWELL_ROW_SUM_DPP(v);
+    return v;
+  }
+};
+
+// Number of TwELL entries of a row in tiles [0, k_end), wave-uniform.
+__device__ __forceinline__ int entries_before(const uint16_t *__restrict__ crow, int k_end, int cap, int lane) {
+  int n = 0;
+  for (int kb = 0; kb < k_end; kb += 64) {
+    const int k = kb + lane;
+    n += k < k_end ? min((int)crow[k], cap) : 0;
+  }
+  return __builtin_amdgcn_readlane(wave_incl_scan(n), 63);
+}
+
 // ---------------------------------------------------------------------------
 // Sparse up projection.  NC = 16-byte chunks per lane covering d; U = entries
 // in flight per wave (U * NC 16-byte loads per lane outstanding).
+//
+// Writes, per non-overflow row t, the compact entry list of the row:
+//   list[t * stride + e] = (byte offset of hidden unit j's weight row, v = h * u)
+// for e < list_n[t], in ascending (tile, slot) order, i.e. ascending j, and
+// zero entries up to the next multiple of 8.
+
+struct UpEntry {
+  uint32_t off;   // byte offset of the unit's row in W_u^T (and in W_d)
+  uint32_t dst;   // index of the entry in the compact list
+  float h;        // the gate activation
+  uint32_t pad;
+};
 
 template <Dt D, int NC, int U>
 __global__ __launch_bounds__(SP_THREADS) void k_sparse_up(
     const typename DtT<D>::T *__restrict__ x, const typename DtT<D>::T *__restrict__ wu,
     const uint16_t *__restrict__ cnt, const typename DtT<D>::T *__restrict__ val,
-    const uint8_t *__restrict__ idx, const uint8_t *__restrict__ row_flag, float *__restrict__ vbuf, int T,
-    int d, int nt, int tile, int cap, int tpg, int n_groups, int tok_per_wg, int n_tb) {
+    const uint8_t *__restrict__ idx, const uint8_t *__restrict__ row_flag, u32x2_t *__restrict__ list,
+    int *__restrict__ list_n, int stride, int T, int d, int nt, int tile, int cap, int tpg, int n_groups,
+    int tok_per_wg, int n_tb) {
   using TT = typename DtT<D>::T;
   constexpr int EPC = 16 / sizeof(TT);  // elements per 16-byte chunk
-  __shared__ Entry list[SP_WAVES][UP_LIST];
+  __shared__ UpEntry lists[SP_WAVES][UP_LIST];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   int g, tb;
   group_coords(blockIdx.x, n_groups, n_tb, g, tb);
   const int k0 = g * tpg;
   const int kn = min(tpg, nt - k0);
-  Entry *L = list[wave];
-  const char *wub = reinterpret_cast<const char *>(wu);
+  UpEntry *L = lists[wave];
+  const __amdgpu_buffer_rsrc_t wur = buffer_rsrc(wu);
+  const uint32_t lane_off = lane * 16;
   const uint32_t row_bytes = (uint32_t)d * sizeof(TT);
+  // lanes 16 r (r = 0..3) store the entry whose total their row holds
+  const int my_u = Reduce<U>::entry(lane >> 4);
+  const bool storer = (lane & 15) == 0 && (U == 4 || (lane & 31) == 0);
 
   for (int it = wave; it < tok_per_wg; it += SP_WAVES) {
     const int t = tb * tok_per_wg + it;
@@ -169,44 +258,51 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_up(
 #pragma unroll
     for (int c = 0; c < NC; ++c) xr[c] = *reinterpret_cast<const u32x4_t *>(xt + (c * 64 + lane) * EPC);
 
-    // Gather the entries of the group's tiles into the wave list (tpg <= 64).
+    const uint16_t *crow = cnt + (size_t)t * nt;
+    const size_t lbase = (size_t)t * stride;
+    const int before = entries_before(crow, k0, cap, lane);
+    if (g == 0) {  // the row's entry count, and zero entries up to a multiple of 8
+      const int total = entries_before(crow, nt, cap, lane);
+      if (lane == 0) list_n[t] = total;
+      if (lane < ((total + 7) & ~7) - total) list[lbase + total + lane] = u32x2_t{0u, 0u};
+    }
+    // The group's entries into the wave list (tpg <= 64 tiles, one per lane).
     const int k = k0 + lane;
-    const int n = lane < kn ? min((int)cnt[(size_t)t * nt + k], cap) : 0;
+    const int n = lane < kn ? min((int)crow[k], cap) : 0;
     const int incl = wave_incl_scan(n);
-    const int E = __shfl(incl, 63, 64);
+    const int E = __builtin_amdgcn_readlane(incl, 63);
     const size_t slot0 = ((size_t)t * nt + k) * cap;
     for (int s = 0, o = incl - n; s < n; ++s, ++o) {
-      L[o].j = (k * tile + idx[slot0 + s]) | (s << 26);
-      L[o].w = to_f32(val[slot0 + s]);
+      UpEntry en;
+      en.off = (uint32_t)(k * tile + idx[slot0 + s]) * row_bytes;
+      en.dst = (uint32_t)(before + o);
+      en.h = to_f32(val[slot0 + s]);
+      en.pad = 0;
+      L[o] = en;
     }
     wave_sync_lds();
 
-    for (int e = 0; e < E; e += U) {
-      Entry en[U];
-      u32x4_t w[U][NC];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        en[u] = L[min(e + u, E - 1)];
-        const char *r = wub + (size_t)((uint32_t)(en[u].j & 0x3FFFFFF) * row_bytes) + lane * 16;
-#pragma unroll
-        for (int c = 0; c < NC; ++c) w[u][c] = *reinterpret_cast<const u32x4_t *>(r + c * 1024);
-      }
-      float p[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        p[u] = 0.f;
-#pragma unroll
-        for (int c = 0; c < NC; ++c) p[u] = dot16(xr[c], w[u][c], p[u], TT());
-        p[u] = wave_sum_to_lane63(p[u]);
-      }
-      if (lane == 63) {
+    for (int e0 = 0; e0 < E; e0 += 64) {
+      const int ne = min(64, E - e0);
+      const uint32_t moff = L[min(e0 + lane, E - 1)].off;
+      for (int u0 = 0; u0 < ne; u0 += U) {
+        u32x4_t w[U][NC];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          if (e + u < E) {
-            const int j = en[u].j & 0x3FFFFFF, s = (unsigned)en[u].j >> 26;
-            vbuf[((size_t)t * nt + j / tile) * cap + s] = en[u].w * p[u];
-          }
+          const uint32_t off = read_lane(moff, min(u0 + u, ne - 1));
+#pragma unroll
+          for (int c = 0; c < NC; ++c) w[u][c] = buffer_load<u32x4_t>(wur, lane_off + c * 1024, off);
         }
+        const UpEntry mine = L[e0 + min(u0 + my_u, ne - 1)];
+        float p[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          p[u] = 0.f;
+#pragma unroll
+          for (int c = 0; c < NC; ++c) p[u] = dot16(xr[c], w[u][c], p[u], TT());
+        }
+        const float tot = Reduce<U>::run(p);
+        if (storer && u0 + my_u < ne) list[lbase + mine.dst] = u32x2_t{mine.off, __float_as_uint(mine.h * tot)};
       }
     }
     wave_sync_lds();
@@ -214,77 +310,60 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_up(
 }
 
 // ---------------------------------------------------------------------------
-// Sparse down projection.  VPL = output columns per lane (slice = 64 * VPL);
-// U = W_d row segments in flight per wave.
+// Sparse down projection over the compact lists.  VPL = output columns per
+// lane (slice = 64 * VPL); U = W_d row segments in flight per wave.  List
+// entries are wave-uniform and read with scalar loads; the weight v is a
+// scalar operand of the FMAs.
 
 template <Dt D, int VPL, int U>
 __global__ __launch_bounds__(SP_THREADS) void k_sparse_down(
-    const float *__restrict__ vbuf, const uint16_t *__restrict__ cnt, const uint8_t *__restrict__ idx,
+    const u32x2_t *__restrict__ list, const int *__restrict__ list_n, int stride,
     const uint8_t *__restrict__ row_flag, const typename DtT<D>::T *__restrict__ wd,
-    typename DtT<D>::T *__restrict__ y, int T, int d, int nt, int tile, int cap, int n_slices, int tok_per_wg,
-    int n_tb) {
+    typename DtT<D>::T *__restrict__ y, int T, int d, int n_slices, int tok_per_wg, int n_tb) {
   using TT = typename DtT<D>::T;
   constexpr int VB = VPL * sizeof(TT);  // bytes per lane per row
   static_assert(VB == 4 || VB == 8 || VB == 16, "lane vector must be 4, 8 or 16 bytes");
+  static_assert(U <= 8, "lists are zero-padded to a multiple of 8 entries");
   using V = typename std::conditional<VB == 16, u32x4_t,
                                       typename std::conditional<VB == 8, u32x2_t, uint32_t>::type>::type;
-  __shared__ Entry list[SP_WAVES][DOWN_LIST];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   int sl, tb;
   group_coords(blockIdx.x, n_slices, n_tb, sl, tb);
-  const int c0 = sl * 64 * VPL + lane * VPL;
-  // lane's column segment of every W_d row: base + row_offset(j) (32-bit)
-  const char *wdb = reinterpret_cast<const char *>(wd + c0);
-  const uint32_t row_bytes = (uint32_t)d * sizeof(TT);
-  Entry *L = list[wave];
-  const int tiles_per_fill = min(64, DOWN_LIST / cap);
-
+  const __amdgpu_buffer_rsrc_t wdr = buffer_rsrc(wd + sl * 64 * VPL);  // the slice's columns of row 0
+  const uint32_t lane_off = lane * VB;
   for (int it = wave; it < tok_per_wg; it += SP_WAVES) {
-    const int t = tb * tok_per_wg + it;
+    const int t = __builtin_amdgcn_readfirstlane(tb * tok_per_wg + it);
     if (t >= T) break;
     if (row_flag[t]) continue;
+    const int n = list_n[t];
+    const u32x2_t *lt = list + (size_t)t * stride;
     float acc[VPL];
 #pragma unroll
     for (int v = 0; v < VPL; ++v) acc[v] = 0.f;
-
-    for (int kb = 0; kb < nt; kb += tiles_per_fill) {
-      const int k = kb + lane;
-      const int n = (lane < tiles_per_fill && k < nt) ? min((int)cnt[(size_t)t * nt + k], cap) : 0;
-      const int incl = wave_incl_scan(n);
-      const int E = __shfl(incl, 63, 64);
-      const size_t slot0 = ((size_t)t * nt + k) * cap;
-      for (int s = 0, o = incl - n; s < n; ++s, ++o) {
-        L[o].j = (int)((uint32_t)(k * tile + idx[slot0 + s]) * row_bytes);  // byte offset of the row
-        L[o].w = vbuf[slot0 + s];
+    for (int e = 0; e < n; e += U) {
+      V w[U];
+      float sw[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const u32x2_t en = lt[e + u];
+        sw[u] = __uint_as_float(en[1]);
+        w[u] = buffer_load<V>(wdr, lane_off, en[0]);
       }
-      wave_sync_lds();
-      for (int e = 0; e < E; e += U) {
-        Entry en[U];
-        V w[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          en[u] = L[min(e + u, E - 1)];
-          if (e + u >= E) en[u].w = 0.f;  // tail: duplicate row, zero weight
-          w[u] = *reinterpret_cast<const V *>(wdb + (uint32_t)en[u].j);
-        }
+      for (int u = 0; u < U; ++u) {
+        const uint32_t *wv = reinterpret_cast<const uint32_t *>(&w[u]);
+        if constexpr (D == Dt::BF16) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const uint32_t *wv = reinterpret_cast<const uint32_t *>(&w[u]);
-          if constexpr (D == Dt::BF16) {
-#pragma unroll
-            for (int v = 0; v < VPL / 2; ++v) {
-              acc[2 * v] = fmaf(en[u].w, bf16lo(wv[v]), acc[2 * v]);
-              acc[2 * v + 1] = fmaf(en[u].w, bf16hi(wv[v]), acc[2 * v + 1]);
-            }
-          } else {
-#pragma unroll
-            for (int v = 0; v < VPL; ++v) acc[v] = fmaf(en[u].w, __uint_as_float(wv[v]), acc[v]);
+          for (int v = 0; v < VPL / 2; ++v) {
+            acc[2 * v] = fmaf(sw[u], bf16lo(wv[v]), acc[2 * v]);
+            acc[2 * v + 1] = fmaf(sw[u], bf16hi(wv[v]), acc[2 * v + 1]);
           }
+        } else {
+#pragma unroll
+          for (int v = 0; v < VPL; ++v) acc[v] = fmaf(sw[u], __uint_as_float(wv[v]), acc[v]);
         }
       }
-      wave_sync_lds();
     }
-
     V out;
     uint32_t *ov = reinterpret_cast<uint32_t *>(&out);
     if constexpr (D == Dt::BF16) {
@@ -295,7 +374,7 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_down(
 #pragma unroll
       for (int v = 0; v < VPL; ++v) ov[v] = __float_as_uint(acc[v]);
     }
-    *reinterpret_cast<V *>(y + (size_t)t * d + c0) = out;
+    *reinterpret_cast<V *>(y + (size_t)t * d + sl * 64 * VPL + lane * VPL) = out;
   }
 }
 
@@ -317,10 +396,10 @@ static hipError_t launch_up(const SparseArgs &a, hipStream_t s) {
   const int n_groups = nt / tpg;
   const int tok = 16;
   const int n_tb = (a.T + tok - 1) / tok;
-  constexpr int U = NC >= 8 ? 2 : 4;
+  constexpr int U = NC <= 8 ? 4 : 2;
   hipLaunchKernelGGL((k_sparse_up<D, NC, U>), dim3(n_groups * n_tb), dim3(SP_THREADS), 0, s, (const TT *)a.x,
-                     (const TT *)a.wu, a.cnt, (const TT *)a.val, a.idx, a.row_flag, a.vbuf, a.T, a.d, nt, a.tile,
-                     a.cap, tpg, n_groups, tok, n_tb);
+                     (const TT *)a.wu, a.cnt, (const TT *)a.val, a.idx, a.row_flag, (u32x2_t *)a.list, a.list_n,
+                     a.stride, a.T, a.d, nt, a.tile, a.cap, tpg, n_groups, tok, n_tb);
   return hipGetLastError();
 }
 
@@ -349,13 +428,12 @@ hipError_t sparse_up(const SparseArgs &a, hipStream_t s) {
 template <Dt D, int VPL>
 static hipError_t launch_down(const SparseArgs &a, hipStream_t s) {
   using TT = typename DtT<D>::T;
-  const int nt = a.F / a.tile;
   const int n_slices = a.d / (64 * VPL);
   const int tok = 16;
   const int n_tb = (a.T + tok - 1) / tok;
-  hipLaunchKernelGGL((k_sparse_down<D, VPL, 8>), dim3(n_slices * n_tb), dim3(SP_THREADS), 0, s, a.vbuf, a.cnt,
-                     a.idx, a.row_flag, (const TT *)a.wd, (TT *)a.y, a.T, a.d, nt, a.tile, a.cap, n_slices, tok,
-                     n_tb);
+  hipLaunchKernelGGL((k_sparse_down<D, VPL, 8>), dim3(n_slices * n_tb), dim3(SP_THREADS), 0, s,
+                     (const u32x2_t *)a.list, a.list_n, a.stride, a.row_flag, (const TT *)a.wd, (TT *)a.y, a.T, a.d,
+                     n_slices, tok, n_tb);
   return hipGetLastError();
 }
 

@@ -34,9 +34,10 @@
  *   rounded to the storage dtype with round-to-nearest-even.
  * - Shapes: T tokens (T >= 0; T == 0 is a no-op apart from *n_ovf = 0, and
  *   x and y may then be NULL),
- *   d = d_model, F = d_ff.  d must be a multiple of 256 (fp32) or 512 (bf16)
- *   and at most 8192; F must be a multiple of the TwELL tile width, and one
- *   weight matrix (F*d elements) must stay below 2 GiB.
+ *   d = d_model, F = d_ff.  d must be a multiple of 256 and at most 4096
+ *   (fp32), or a multiple of 512 and at most 8192 (bf16); F must be a
+ *   multiple of the TwELL tile width, and one weight matrix (F*d elements)
+ *   must stay below 2 GiB.
  * - Weights are rows per hidden unit, row-major: w_gate [F][d] (= W_g^T, the
  *   nn.Linear weight layout), w_up [F][d] (= W_u^T), w_down [F][d] (= W_d,
  *   transposed once at load time so that every hidden unit's down row is

@@ -91,8 +91,9 @@ def test_ffn_forward_validation():
     assert _ffn(_matrix(), ws_bytes=16) == twell.TWELL_ERR_WORKSPACE
     assert _ffn(_matrix(), ws=None) == twell.TWELL_ERR_WORKSPACE
     assert _ffn(_matrix(), ws=FAKE + 16) == twell.TWELL_ERR_UNSUPPORTED
-    # fp32 accepts d % 256
+    # fp32 accepts d % 256 up to 4096
     assert _ffn(_matrix(dtype=twell.TWELL_F32), d=384) == twell.TWELL_ERR_UNSUPPORTED
+    assert _ffn(_matrix(dtype=twell.TWELL_F32), d=4352) == twell.TWELL_ERR_UNSUPPORTED
 
 
 def test_sparse_ffn_and_gate_pack_validation():

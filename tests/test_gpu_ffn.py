@@ -25,6 +25,10 @@ SMALL = [
     ("bf16", 1, 512, 512, 256, 16, -1.0),
     ("bf16", 64, 512, 512, 256, 16, 6.0),          # everything active: every row overflows
     ("bf16", 70, 512, 768, 256, 16, -1e30),        # nothing active: y == 0
+    ("bf16", 40, 5120, 512, 256, 16, -1.5),        # wide rows: 10 chunks per lane, 2 entries in flight
+    ("bf16", 20, 8192, 512, 128, 8, -1.0),         # widest bf16 rows
+    ("f32", 33, 2560, 512, 128, 8, -1.0),          # wide fp32 rows
+    ("f32", 17, 4096, 256, 256, 16, -0.5),         # widest fp32 rows
 ]
 
 
