@@ -139,12 +139,12 @@ twell_status run_sparse(const twell_matrix *m, const void *x, const void *wg, co
   void *a_ws = base + L.a;
   const Dt D = to_dt(m->dtype);
 
-  ScanArgs sc{m->cnt, T, F / m->tile, m->cap, row_flag, m->ovf_rows, m->ovf_cap, m->n_ovf};
-  TW_TRY(overflow_scan(sc, s), "overflow scan");
-
+  // The up kernel finds the overflow rows itself (row_flag); their list
+  // follows, for the dense fallback.
   SparseArgs sa{D, T, d, F, m->tile, m->cap, m->cnt, m->val, m->idx, row_flag, x, wu, wd, list, list_n, L.stride, y};
   TW_TRY(sparse_up(sa, s), "sparse up projection");
   TW_TRY(sparse_down(sa, s), "sparse down projection");
+  TW_TRY(compact_rows(row_flag, T, m->ovf_rows, m->ovf_cap, m->n_ovf, s), "overflow row list");
 
   DenseArgs da{D, x, wg, wu, wd, beta, y, T, d, F, m->ovf_rows, m->n_ovf, a_ws, m->dense, m->ovf_cap};
   TW_TRY(dense_gate_up(da, s), "fallback gate/up matmul");

@@ -14,11 +14,13 @@
 #include "gemm.hpp"
 #include "launch.hpp"
 
+#include <algorithm>
+
 namespace twell {
 
 template <Dt D>
-__global__ __launch_bounds__(DMA_THREADS) void k_gate_up(
-    const typename DtT<D>::T *__restrict__ x, const typename DtT<D>::T *__restrict__ wg,
+__device__ __forceinline__ void gate_up_tile(
+    int bid, const typename DtT<D>::T *__restrict__ x, const typename DtT<D>::T *__restrict__ wg,
     const typename DtT<D>::T *__restrict__ wu, const float *__restrict__ beta, int M, int K, int F,
     const int *__restrict__ rows, const int *__restrict__ n_rows_dev, typename DtT<D>::T *__restrict__ a_ws,
     typename DtT<D>::T *__restrict__ h_out, int h_cap) {
@@ -30,7 +32,7 @@ __global__ __launch_bounds__(DMA_THREADS) void k_gate_up(
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int mt = (M + GEMM_BM - 1) / GEMM_BM, ntl = F / UNITS;
   int tm, tn;
-  tile_coords(blockIdx.x, mt, ntl, tm, tn);
+  tile_coords(bid, mt, ntl, tm, tn);
   const int m0 = tm * GEMM_BM, n0 = tn * UNITS;
   const int n_eff = n_rows_dev ? min(*n_rows_dev, M) : M;
   if (m0 >= n_eff) return;
@@ -87,8 +89,8 @@ __global__ __launch_bounds__(DMA_THREADS) void k_gate_up(
 }
 
 template <Dt D>
-__global__ __launch_bounds__(GEMM_THREADS) void k_down(
-    const typename DtT<D>::T *__restrict__ a_ws, const typename DtT<D>::T *__restrict__ wd, int M, int K,
+__device__ __forceinline__ void down_tile(
+    int bid, const typename DtT<D>::T *__restrict__ a_ws, const typename DtT<D>::T *__restrict__ wd, int M, int K,
     int N, const int *__restrict__ rows, const int *__restrict__ n_rows_dev,
     typename DtT<D>::T *__restrict__ y) {
   using T = typename DtT<D>::T;
@@ -96,7 +98,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void k_down(
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int mt = (M + GEMM_BM - 1) / GEMM_BM, ntl = N / BN;
   int tm, tn;
-  tile_coords(blockIdx.x, mt, ntl, tm, tn);
+  tile_coords(bid, mt, ntl, tm, tn);
   const int m0 = tm * GEMM_BM, n0 = tn * BN;
   const int n_eff = n_rows_dev ? min(*n_rows_dev, M) : M;
   if (m0 >= n_eff) return;
@@ -135,6 +137,36 @@ __global__ __launch_bounds__(GEMM_THREADS) void k_down(
   }
 }
 
+// Each workgroup takes tiles bid, bid + gridDim.x, ...: the dense baseline
+// launches one workgroup per tile, the fallback (row count on the device) a
+// grid of at most FALLBACK_WGS, so that an empty fallback costs little.
+constexpr int FALLBACK_WGS = 256;
+
+template <Dt D>
+__global__ __launch_bounds__(DMA_THREADS) void k_gate_up(
+    const typename DtT<D>::T *__restrict__ x, const typename DtT<D>::T *__restrict__ wg,
+    const typename DtT<D>::T *__restrict__ wu, const float *__restrict__ beta, int M, int K, int F,
+    const int *__restrict__ rows, const int *__restrict__ n_rows_dev, typename DtT<D>::T *__restrict__ a_ws,
+    typename DtT<D>::T *__restrict__ h_out, int h_cap) {
+  const int tiles = (M + GEMM_BM - 1) / GEMM_BM * (F / 128);
+  for (int bid = blockIdx.x; bid < tiles; bid += gridDim.x)
+    gate_up_tile<D>(bid, x, wg, wu, beta, M, K, F, rows, n_rows_dev, a_ws, h_out, h_cap);
+}
+
+template <Dt D, bool LOOP>
+__global__ __launch_bounds__(GEMM_THREADS) void k_down(
+    const typename DtT<D>::T *__restrict__ a_ws, const typename DtT<D>::T *__restrict__ wd, int M, int K,
+    int N, const int *__restrict__ rows, const int *__restrict__ n_rows_dev,
+    typename DtT<D>::T *__restrict__ y) {
+  if constexpr (LOOP) {
+    const int tiles = (M + GEMM_BM - 1) / GEMM_BM * (N / 256);
+    for (int bid = blockIdx.x; bid < tiles; bid += gridDim.x)
+      down_tile<D>(bid, a_ws, wd, M, K, N, rows, n_rows_dev, y);
+  } else {
+    down_tile<D>(blockIdx.x, a_ws, wd, M, K, N, rows, n_rows_dev, y);
+  }
+}
+
 template <Dt D>
 static hipError_t launch_gate_up(const DenseArgs &a, hipStream_t s) {
   using T = typename DtT<D>::T;
@@ -143,7 +175,8 @@ static hipError_t launch_gate_up(const DenseArgs &a, hipStream_t s) {
   hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
   const int mt = (a.M + GEMM_BM - 1) / GEMM_BM, ntl = a.F / 128;
-  hipLaunchKernelGGL(kern, dim3(mt * ntl), dim3(DMA_THREADS), lds, s, (const T *)a.x, (const T *)a.wg,
+  const int grid = a.n_rows_dev ? std::min(mt * ntl, FALLBACK_WGS) : mt * ntl;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(DMA_THREADS), lds, s, (const T *)a.x, (const T *)a.wg,
                      (const T *)a.wu, a.beta, a.M, a.d, a.F, a.rows, a.n_rows_dev, (T *)a.a_ws,
                      (T *)a.h_out, a.h_cap);
   return hipGetLastError();
@@ -152,12 +185,13 @@ static hipError_t launch_gate_up(const DenseArgs &a, hipStream_t s) {
 template <Dt D>
 static hipError_t launch_down(const DenseArgs &a, hipStream_t s) {
   using T = typename DtT<D>::T;
-  auto kern = k_down<D>;
+  auto kern = a.n_rows_dev ? k_down<D, true> : k_down<D, false>;
   const int lds = gemm_lds_bytes(256);
   hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
   const int mt = (a.M + GEMM_BM - 1) / GEMM_BM, ntl = a.d / 256;
-  hipLaunchKernelGGL(kern, dim3(mt * ntl), dim3(GEMM_THREADS), lds, s, (const T *)a.a_ws, (const T *)a.wd,
+  const int grid = a.n_rows_dev ? std::min(mt * ntl, FALLBACK_WGS) : mt * ntl;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(GEMM_THREADS), lds, s, (const T *)a.a_ws, (const T *)a.wd,
                      a.M, a.F, a.d, a.rows, a.n_rows_dev, (T *)a.y);
   return hipGetLastError();
 }

@@ -34,6 +34,9 @@ struct ScanArgs {
 };
 hipError_t overflow_scan(const ScanArgs &a, hipStream_t s);
 
+// Ascending list of the rows with row_flag[t] != 0, and its true length.
+hipError_t compact_rows(const uint8_t *row_flag, int T, int *ovf_rows, int ovf_cap, int *n_ovf, hipStream_t s);
+
 // Sparse up / down projections over the TwELL entries of non-overflow rows.
 struct SparseArgs {
   Dt dtype;
@@ -41,7 +44,7 @@ struct SparseArgs {
   const uint16_t *cnt;
   const void *val;
   const uint8_t *idx;
-  const uint8_t *row_flag;  // [T], 1 = overflow row (handled by the dense fallback)
+  uint8_t *row_flag;        // [T], written by the up kernel: 1 = overflow row (dense fallback)
   const void *x;            // [T][d]
   const void *wu;           // [F][d]
   const void *wd;           // [F][d]

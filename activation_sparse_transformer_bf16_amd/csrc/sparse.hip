@@ -83,6 +83,41 @@ hipError_t overflow_scan(const ScanArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Ascending list of the rows whose flag is set (flags written by the up
+// kernel); one workgroup, T bytes read.
+constexpr int COMPACT_THREADS = 1024;
+__global__ __launch_bounds__(COMPACT_THREADS) void k_compact_rows(const uint8_t *__restrict__ row_flag, int T,
+                                                                   int *__restrict__ ovf_rows, int ovf_cap,
+                                                                   int *__restrict__ n_ovf) {
+  __shared__ int wcount[COMPACT_THREADS / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int carry = 0;
+  for (int base = 0; base < T; base += COMPACT_THREADS) {
+    const int t = base + tid;
+    const bool f = t < T && row_flag[t] != 0;
+    const uint64_t m = ballot(f);
+    if (lane == 0) wcount[wave] = popc64(m);
+    __syncthreads();
+    int before = carry, total = 0;
+    for (int w = 0; w < COMPACT_THREADS / 64; ++w) {
+      before += (w < wave) ? wcount[w] : 0;
+      total += wcount[w];
+    }
+    if (f) {
+      const int pos = before + mbcnt(m);
+      if (pos < ovf_cap) ovf_rows[pos] = t;
+    }
+    carry += total;
+    __syncthreads();
+  }
+  if (tid == 0) *n_ovf = carry;
+}
+
+hipError_t compact_rows(const uint8_t *row_flag, int T, int *ovf_rows, int ovf_cap, int *n_ovf, hipStream_t s) {
+  hipLaunchKernelGGL(k_compact_rows, dim3(1), dim3(COMPACT_THREADS), 0, s, row_flag, T, ovf_rows, ovf_cap, n_ovf);
+  return hipGetLastError();
+}
+
 __global__ void k_zero_int(int *p) { *p = 0; }
 hipError_t zero_int(int *p, hipStream_t s) {
   hipLaunchKernelGGL(k_zero_int, dim3(1), dim3(1), 0, s, p);
@@ -200,16 +235,6 @@ struct Reduce<2> {
   }
 };
 
-// Number of TwELL entries of a row in tiles [0, k_end), wave-uniform.
-__device__ __forceinline__ int entries_before(const uint16_t *__restrict__ crow, int k_end, int cap, int lane) {
-  int n = 0;
-  for (int kb = 0; kb < k_end; kb += 64) {
-    const int k = kb + lane;
-    n += k < k_end ? min((int)crow[k], cap) : 0;
-  }
-  return __builtin_amdgcn_readlane(wave_incl_scan(n), 63);
-}
-
 // ---------------------------------------------------------------------------
 // Sparse up projection.  NC = 16-byte chunks per lane covering d; U = entries
 // in flight per wave (U * NC 16-byte loads per lane outstanding).
@@ -217,7 +242,10 @@ __device__ __forceinline__ int entries_before(const uint16_t *__restrict__ crow,
 // Writes, per non-overflow row t, the compact entry list of the row:
 //   list[t * stride + e] = (byte offset of hidden unit j's weight row, v = h * u)
 // for e < list_n[t], in ascending (tile, slot) order, i.e. ascending j, and
-// zero entries up to the next multiple of 8.
+// zero entries up to the next multiple of 8.  A row overflows iff one of its
+// tiles counts more than cap entries; every wave decides that from the row's
+// counts, skips such rows, and the group-0 wave records row_flag[t] (1 for an
+// overflow row) and list_n[t] = -1 for them.
 
 struct UpEntry {
   uint32_t off;   // byte offset of the unit's row in W_u^T (and in W_d)
@@ -230,7 +258,7 @@ template <Dt D, int NC, int U>
 __global__ __launch_bounds__(SP_THREADS) void k_sparse_up(
     const typename DtT<D>::T *__restrict__ x, const typename DtT<D>::T *__restrict__ wu,
     const uint16_t *__restrict__ cnt, const typename DtT<D>::T *__restrict__ val,
-    const uint8_t *__restrict__ idx, const uint8_t *__restrict__ row_flag, u32x2_t *__restrict__ list,
+    const uint8_t *__restrict__ idx, uint8_t *__restrict__ row_flag, u32x2_t *__restrict__ list,
     int *__restrict__ list_n, int stride, int T, int d, int nt, int tile, int cap, int tpg, int n_groups,
     int tok_per_wg, int n_tb) {
   using TT = typename DtT<D>::T;
@@ -252,20 +280,36 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_up(
   for (int it = wave; it < tok_per_wg; it += SP_WAVES) {
     const int t = tb * tok_per_wg + it;
     if (t >= T) break;
-    if (row_flag[t]) continue;
     const TT *xt = x + (size_t)t * d;
     u32x4_t xr[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) xr[c] = *reinterpret_cast<const u32x4_t *>(xt + (c * 64 + lane) * EPC);
 
+    // Overflow test and entry counts from the row's tile counts: entries in
+    // tiles before the group (where its entries start in the list), and for
+    // group 0 the row total.
     const uint16_t *crow = cnt + (size_t)t * nt;
     const size_t lbase = (size_t)t * stride;
-    const int before = entries_before(crow, k0, cap, lane);
-    if (g == 0) {  // the row's entry count, and zero entries up to a multiple of 8
-      const int total = entries_before(crow, nt, cap, lane);
-      if (lane == 0) list_n[t] = total;
-      if (lane < ((total + 7) & ~7) - total) list[lbase + total + lane] = u32x2_t{0u, 0u};
+    const int k_end = g == 0 ? nt : k0;
+    int partial = 0;
+    bool over = false;
+    for (int kb = 0; kb < nt; kb += 64) {
+      const int kk = kb + lane;
+      const int c = kk < nt ? (int)crow[kk] : 0;
+      over |= c > cap;
+      partial += kk < k_end ? min(c, cap) : 0;
     }
+    const bool ovf = ballot(over) != 0;
+    const int sum = __builtin_amdgcn_readlane(wave_incl_scan(partial), 63);
+    if (g == 0) {
+      if (lane == 0) {
+        row_flag[t] = ovf ? 1 : 0;
+        list_n[t] = ovf ? -1 : sum;
+      }
+      if (!ovf && lane < ((sum + 7) & ~7) - sum) list[lbase + sum + lane] = u32x2_t{0u, 0u};
+    }
+    if (ovf) continue;
+    const int before = g == 0 ? 0 : sum;
     // The group's entries into the wave list (tpg <= 64 tiles, one per lane).
     const int k = k0 + lane;
     const int n = lane < kn ? min((int)crow[k], cap) : 0;
@@ -318,7 +362,7 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_up(
 template <Dt D, int VPL, int U>
 __global__ __launch_bounds__(SP_THREADS) void k_sparse_down(
     const u32x2_t *__restrict__ list, const int *__restrict__ list_n, int stride,
-    const uint8_t *__restrict__ row_flag, const typename DtT<D>::T *__restrict__ wd,
+    const typename DtT<D>::T *__restrict__ wd,
     typename DtT<D>::T *__restrict__ y, int T, int d, int n_slices, int tok_per_wg, int n_tb) {
   using TT = typename DtT<D>::T;
   constexpr int VB = VPL * sizeof(TT);  // bytes per lane per row
@@ -334,8 +378,8 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_down(
   for (int it = wave; it < tok_per_wg; it += SP_WAVES) {
     const int t = __builtin_amdgcn_readfirstlane(tb * tok_per_wg + it);
     if (t >= T) break;
-    if (row_flag[t]) continue;
     const int n = list_n[t];
+    if (n < 0) continue;  // overflow row: the dense fallback writes it
     const u32x2_t *lt = list + (size_t)t * stride;
     float acc[VPL];
 #pragma unroll
@@ -432,8 +476,8 @@ static hipError_t launch_down(const SparseArgs &a, hipStream_t s) {
   const int tok = 16;
   const int n_tb = (a.T + tok - 1) / tok;
   hipLaunchKernelGGL((k_sparse_down<D, VPL, 8>), dim3(n_slices * n_tb), dim3(SP_THREADS), 0, s,
-                     (const u32x2_t *)a.list, a.list_n, a.stride, a.row_flag, (const TT *)a.wd, (TT *)a.y, a.T, a.d,
-                     n_slices, tok, n_tb);
+                     (const u32x2_t *)a.list, a.list_n, a.stride, (const TT *)a.wd, (TT *)a.y, a.T, a.d, n_slices,
+                     tok, n_tb);
   return hipGetLastError();
 }
 
