@@ -310,19 +310,27 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_up(
     }
     if (ovf) continue;
     const int before = g == 0 ? 0 : sum;
-    // The group's entries into the wave list (tpg <= 64 tiles, one per lane).
-    const int k = k0 + lane;
-    const int n = lane < kn ? min((int)crow[k], cap) : 0;
+    // The group's entries into the wave list.  Tile k0 + q has n(q) entries
+    // (lane q, q < kn <= 64); its slots are contiguous after those of tile q-1,
+    // so the wave loads all kn * cap slots with one lane per slot and files
+    // the occupied ones at (entries of the tiles before q) + slot.
+    const int n = lane < kn ? min((int)crow[k0 + lane], cap) : 0;
     const int incl = wave_incl_scan(n);
     const int E = __builtin_amdgcn_readlane(incl, 63);
-    const size_t slot0 = ((size_t)t * nt + k) * cap;
-    for (int s = 0, o = incl - n; s < n; ++s, ++o) {
-      UpEntry en;
-      en.off = (uint32_t)(k * tile + idx[slot0 + s]) * row_bytes;
-      en.dst = (uint32_t)(before + o);
-      en.h = to_f32(val[slot0 + s]);
-      en.pad = 0;
-      L[o] = en;
+    const size_t gslot0 = ((size_t)t * nt + k0) * cap;  // first slot of the group
+    for (int q0 = 0; q0 < kn * cap; q0 += 64) {
+      const int q = q0 + lane;
+      const int kq = q / cap, sq = q - kq * cap;
+      const int nq = __shfl(n, kq & 63, 64);
+      const int oq = __shfl(incl - n, kq & 63, 64) + sq;
+      if (q < kn * cap && sq < nq) {
+        UpEntry en;
+        en.off = (uint32_t)((k0 + kq) * tile + idx[gslot0 + q]) * row_bytes;
+        en.dst = (uint32_t)(before + oq);
+        en.h = to_f32(val[gslot0 + q]);
+        en.pad = 0;
+        L[oq] = en;
+      }
     }
     wave_sync_lds();
 
@@ -354,71 +362,93 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_up(
 }
 
 // ---------------------------------------------------------------------------
-// Sparse down projection over the compact lists.  VPL = output columns per
-// lane (slice = 64 * VPL); U = W_d row segments in flight per wave.  List
-// entries are wave-uniform and read with scalar loads; the weight v is a
-// scalar operand of the FMAs.
+// Sparse down projection over the compact lists.  Every workgroup covers one
+// 256-column slice of y; each lane loads 16 bytes of a W_d row per
+// instruction (the vector memory pipeline's cost is per instruction, so wide
+// loads matter): for bf16 the two half-waves take two different entries
+// (8 columns per lane), for fp32 the whole wave takes one entry (4 columns
+// per lane).  List entries are wave-uniform and read with scalar loads.
+// U = load instructions in flight per wave.
 
-template <Dt D, int VPL, int U>
+template <Dt D, int U>
 __global__ __launch_bounds__(SP_THREADS) void k_sparse_down(
     const u32x2_t *__restrict__ list, const int *__restrict__ list_n, int stride,
-    const typename DtT<D>::T *__restrict__ wd,
-    typename DtT<D>::T *__restrict__ y, int T, int d, int n_slices, int tok_per_wg, int n_tb) {
+    const typename DtT<D>::T *__restrict__ wd, typename DtT<D>::T *__restrict__ y, int T, int d, int n_slices,
+    int tok_per_wg, int n_tb) {
   using TT = typename DtT<D>::T;
-  constexpr int VB = VPL * sizeof(TT);  // bytes per lane per row
-  static_assert(VB == 4 || VB == 8 || VB == 16, "lane vector must be 4, 8 or 16 bytes");
-  static_assert(U <= 8, "lists are zero-padded to a multiple of 8 entries");
-  using V = typename std::conditional<VB == 16, u32x4_t,
-                                      typename std::conditional<VB == 8, u32x2_t, uint32_t>::type>::type;
+  constexpr int CPL = 16 / sizeof(TT);      // columns per lane
+  constexpr int EPI = 64 * CPL / 256;       // entries per load instruction (2 bf16, 1 fp32)
+  constexpr int STEP = U * EPI;             // entries per iteration
+  static_assert(8 % STEP == 0 || STEP % 8 == 0, "lists are zero-padded to a multiple of 8 entries");
+  static_assert(STEP <= 8, "lists are zero-padded to a multiple of 8 entries");
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int half = EPI == 2 ? lane >> 5 : 0;
+  const int lcol = (EPI == 2 ? (lane & 31) : lane) * CPL;  // lane's first column in the slice
   int sl, tb;
   group_coords(blockIdx.x, n_slices, n_tb, sl, tb);
-  const __amdgpu_buffer_rsrc_t wdr = buffer_rsrc(wd + sl * 64 * VPL);  // the slice's columns of row 0
-  const uint32_t lane_off = lane * VB;
+  const __amdgpu_buffer_rsrc_t wdr = buffer_rsrc(wd + sl * 256);  // the slice's columns of row 0
+  const uint32_t lane_off = lcol * sizeof(TT);
   for (int it = wave; it < tok_per_wg; it += SP_WAVES) {
     const int t = __builtin_amdgcn_readfirstlane(tb * tok_per_wg + it);
     if (t >= T) break;
     const int n = list_n[t];
     if (n < 0) continue;  // overflow row: the dense fallback writes it
     const u32x2_t *lt = list + (size_t)t * stride;
-    float acc[VPL];
+    float acc[CPL];
 #pragma unroll
-    for (int v = 0; v < VPL; ++v) acc[v] = 0.f;
-    for (int e = 0; e < n; e += U) {
-      V w[U];
+    for (int v = 0; v < CPL; ++v) acc[v] = 0.f;
+    for (int e = 0; e < n; e += STEP) {
+      u32x4_t w[U];
       float sw[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const u32x2_t en = lt[e + u];
-        sw[u] = __uint_as_float(en[1]);
-        w[u] = buffer_load<V>(wdr, lane_off, en[0]);
+        const u32x2_t ea = lt[e + EPI * u];
+        if constexpr (EPI == 2) {
+          const u32x2_t eb = lt[e + EPI * u + 1];
+          sw[u] = __uint_as_float(half ? eb[1] : ea[1]);
+          w[u] = buffer_load<u32x4_t>(wdr, lane_off + (half ? eb[0] : ea[0]), 0u);
+        } else {
+          sw[u] = __uint_as_float(ea[1]);
+          w[u] = buffer_load<u32x4_t>(wdr, lane_off, ea[0]);
+        }
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const uint32_t *wv = reinterpret_cast<const uint32_t *>(&w[u]);
         if constexpr (D == Dt::BF16) {
 #pragma unroll
-          for (int v = 0; v < VPL / 2; ++v) {
-            acc[2 * v] = fmaf(sw[u], bf16lo(wv[v]), acc[2 * v]);
-            acc[2 * v + 1] = fmaf(sw[u], bf16hi(wv[v]), acc[2 * v + 1]);
+          for (int v = 0; v < 4; ++v) {
+            const uint32_t wv = w[u][v];
+            acc[2 * v] = fmaf(sw[u], bf16lo(wv), acc[2 * v]);
+            acc[2 * v + 1] = fmaf(sw[u], bf16hi(wv), acc[2 * v + 1]);
           }
         } else {
 #pragma unroll
-          for (int v = 0; v < VPL; ++v) acc[v] = fmaf(sw[u], __uint_as_float(wv[v]), acc[v]);
+          for (int v = 0; v < 4; ++v) {
+            const uint32_t wv = w[u][v];
+            acc[v] = fmaf(sw[u], __uint_as_float(wv), acc[v]);
+          }
         }
       }
     }
-    V out;
-    uint32_t *ov = reinterpret_cast<uint32_t *>(&out);
+    if constexpr (EPI == 2) {
+      // lanes l and l + 32 hold the same columns for the even and the odd
+      // entries: add the halves
+#pragma unroll
+      for (int v = 0; v < CPL; ++v) {
+        auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[v]), __float_as_uint(acc[v]), false, false);
+        acc[v] = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+      }
+    }
+    u32x4_t out;
     if constexpr (D == Dt::BF16) {
 #pragma unroll
-      for (int v = 0; v < VPL / 2; ++v)
-        ov[v] = (uint32_t)bf16_rne(acc[2 * v]) | ((uint32_t)bf16_rne(acc[2 * v + 1]) << 16);
+      for (int v = 0; v < 4; ++v)
+        out[v] = (uint32_t)bf16_rne(acc[2 * v]) | ((uint32_t)bf16_rne(acc[2 * v + 1]) << 16);
     } else {
 #pragma unroll
-      for (int v = 0; v < VPL; ++v) ov[v] = __float_as_uint(acc[v]);
+      for (int v = 0; v < 4; ++v) out[v] = __float_as_uint(acc[v]);
     }
-    *reinterpret_cast<V *>(y + (size_t)t * d + sl * 64 * VPL + lane * VPL) = out;
+    if (half == 0) *reinterpret_cast<u32x4_t *>(y + (size_t)t * d + sl * 256 + lcol) = out;
   }
 }
 
@@ -469,22 +499,21 @@ hipError_t sparse_up(const SparseArgs &a, hipStream_t s) {
   return a.dtype == Dt::BF16 ? up_dispatch<Dt::BF16>(a, s) : up_dispatch<Dt::F32>(a, s);
 }
 
-template <Dt D, int VPL>
+template <Dt D, int U>
 static hipError_t launch_down(const SparseArgs &a, hipStream_t s) {
   using TT = typename DtT<D>::T;
-  const int n_slices = a.d / (64 * VPL);
+  const int n_slices = a.d / 256;
   const int tok = 16;
   const int n_tb = (a.T + tok - 1) / tok;
-  hipLaunchKernelGGL((k_sparse_down<D, VPL, 8>), dim3(n_slices * n_tb), dim3(SP_THREADS), 0, s,
-                     (const u32x2_t *)a.list, a.list_n, a.stride, (const TT *)a.wd, (TT *)a.y, a.T, a.d, n_slices,
-                     tok, n_tb);
+  hipLaunchKernelGGL((k_sparse_down<D, U>), dim3(n_slices * n_tb), dim3(SP_THREADS), 0, s, (const u32x2_t *)a.list,
+                     a.list_n, a.stride, (const TT *)a.wd, (TT *)a.y, a.T, a.d, n_slices, tok, n_tb);
   return hipGetLastError();
 }
 
 hipError_t sparse_down(const SparseArgs &a, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
-  // 256-column slices: VPL 4 (8-byte bf16 / 16-byte fp32 lane vectors).
-  return a.dtype == Dt::BF16 ? launch_down<Dt::BF16, 4>(a, s) : launch_down<Dt::F32, 4>(a, s);
+  // 256-column slices; 8 list entries per iteration
+  return a.dtype == Dt::BF16 ? launch_down<Dt::BF16, 4>(a, s) : launch_down<Dt::F32, 8>(a, s);
 }
 
 }  // namespace twell
