@@ -367,7 +367,7 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_up(
 // instruction (the vector memory pipeline's cost is per instruction, so wide
 // loads matter): for bf16 the two half-waves take two different entries
 // (8 columns per lane), for fp32 the whole wave takes one entry (4 columns
-// per lane).  List entries are wave-uniform and read with scalar loads.
+// per lane).  The token's list goes through LDS, 64 entries per load.
 // U = load instructions in flight per wave.
 
 template <Dt D, int U>
@@ -379,8 +379,8 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_down(
   constexpr int CPL = 16 / sizeof(TT);      // columns per lane
   constexpr int EPI = 64 * CPL / 256;       // entries per load instruction (2 bf16, 1 fp32)
   constexpr int STEP = U * EPI;             // entries per iteration
-  static_assert(8 % STEP == 0 || STEP % 8 == 0, "lists are zero-padded to a multiple of 8 entries");
-  static_assert(STEP <= 8, "lists are zero-padded to a multiple of 8 entries");
+  static_assert(STEP <= 64 && 64 % STEP == 0, "a 64-entry chunk holds whole iterations");
+  __shared__ u32x2_t chunk[SP_WAVES][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int half = EPI == 2 ? lane >> 5 : 0;
   const int lcol = (EPI == 2 ? (lane & 31) : lane) * CPL;  // lane's first column in the slice
@@ -388,6 +388,7 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_down(
   group_coords(blockIdx.x, n_slices, n_tb, sl, tb);
   const __amdgpu_buffer_rsrc_t wdr = buffer_rsrc(wd + sl * 256);  // the slice's columns of row 0
   const uint32_t lane_off = lcol * sizeof(TT);
+  u32x2_t *C = chunk[wave];
   for (int it = wave; it < tok_per_wg; it += SP_WAVES) {
     const int t = __builtin_amdgcn_readfirstlane(tb * tok_per_wg + it);
     if (t >= T) break;
@@ -397,38 +398,43 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_down(
     float acc[CPL];
 #pragma unroll
     for (int v = 0; v < CPL; ++v) acc[v] = 0.f;
-    for (int e = 0; e < n; e += STEP) {
-      u32x4_t w[U];
-      float sw[U];
+    for (int e0 = 0; e0 < n; e0 += 64) {
+      // 64 entries of the list to LDS with one load; each lane then reads the
+      // entry it works on (lanes of a half-wave read the same one), so the
+      // row offset and the weight arrive per lane without any selects.  The
+      // list is zero-padded to a multiple of 8 entries; entries beyond that
+      // in the chunk are never read.
+      const int ne = min(64, (n - e0 + 7) & ~7);
+      if (lane < ne) C[lane] = lt[e0 + lane];
+      wave_sync_lds();
+      for (int e = 0; e < ne; e += STEP) {
+        u32x4_t w[U];
+        float sw[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const u32x2_t ea = lt[e + EPI * u];
-        if constexpr (EPI == 2) {
-          const u32x2_t eb = lt[e + EPI * u + 1];
-          sw[u] = __uint_as_float(half ? eb[1] : ea[1]);
-          w[u] = buffer_load<u32x4_t>(wdr, lane_off + (half ? eb[0] : ea[0]), 0u);
-        } else {
-          sw[u] = __uint_as_float(ea[1]);
-          w[u] = buffer_load<u32x4_t>(wdr, lane_off, ea[0]);
+        for (int u = 0; u < U; ++u) {
+          const u32x2_t en = C[e + EPI * u + half];
+          sw[u] = __uint_as_float(en[1]);
+          w[u] = buffer_load<u32x4_t>(wdr, lane_off + en[0], 0u);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          if constexpr (D == Dt::BF16) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const uint32_t wv = w[u][v];
+              acc[2 * v] = fmaf(sw[u], bf16lo(wv), acc[2 * v]);
+              acc[2 * v + 1] = fmaf(sw[u], bf16hi(wv), acc[2 * v + 1]);
+            }
+          } else {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const uint32_t wv = w[u][v];
+              acc[v] = fmaf(sw[u], __uint_as_float(wv), acc[v]);
+            }
+          }
         }
       }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if constexpr (D == Dt::BF16) {
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const uint32_t wv = w[u][v];
-            acc[2 * v] = fmaf(sw[u], bf16lo(wv), acc[2 * v]);
-            acc[2 * v + 1] = fmaf(sw[u], bf16hi(wv), acc[2 * v + 1]);
-          }
-        } else {
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const uint32_t wv = w[u][v];
-            acc[v] = fmaf(sw[u], __uint_as_float(wv), acc[v]);
-          }
-        }
-      }
+      wave_sync_lds();
     }
     if constexpr (EPI == 2) {
       // lanes l and l + 32 hold the same columns for the even and the odd
