@@ -140,12 +140,15 @@ size_t twell_ffn_workspace_size(int T, int d, int F, int tile, int cap, twell_dt
  *   y = (ReLU(x W_g^T + beta) * (x W_u^T)) W_d
  * computed as (1) the dense gate matmul on the matrix cores whose epilogue
  * adds beta, rounds to the storage dtype, applies ReLU and writes TwELL into
- * *packed directly (no dense pre-activation matrix is stored); (2) a scan that
- * lists the overflowing rows; (3) the up projection for the active entries of
- * non-overflowing rows only; (4) the down projection as a weighted sum of
- * w_down rows, fp32 accumulation, one rounding to the storage dtype; (5) the
- * dense fallback (gate, up and down matmuls) for the overflowing rows, which
- * also writes packed->dense when it is non-NULL.
+ * *packed directly (no dense pre-activation matrix is stored); (2) the
+ * overflow test of every row (some tile counts more than cap entries) and the
+ * ascending list of the overflowing rows; (3) the up projection for the
+ * active entries of non-overflowing rows only; (4) the down projection as a
+ * weighted sum of w_down rows, fp32 accumulation, one rounding to the storage
+ * dtype; (5) the dense fallback (gate, up and down matmuls) for the
+ * overflowing rows, which also writes packed->dense when it is non-NULL.
+ * Step (2) runs inside the up projection's kernel, which reads every row's
+ * counts anyway, plus a one-pass compaction of the row flags.
  * Sources: gist.science Resumen Técnico §2.A and §2.B.
  *
  * packed: caller-owned TwELL buffers with rows == T, cols == F; tile, cap and
@@ -154,7 +157,9 @@ size_t twell_ffn_workspace_size(int T, int d, int F, int tile, int cap, twell_dt
  * completes) *packed describes round(pre) exactly as twell_pack would.
  * y: [T][d] in the storage dtype, fully written.
  * workspace: device buffer of at least twell_ffn_workspace_size() bytes,
- * 256-byte aligned; its contents on entry do not matter.
+ * 256-byte aligned; its contents on entry do not matter.  It holds one flag
+ * byte per row, per row a list of up to F/tile*cap (weight-row offset, v)
+ * pairs of 8 bytes, and the fallback's [T][F] activations.
  * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP.
  */
 twell_status twell_ffn_forward(const void *x, const void *w_gate, const void *w_up,
