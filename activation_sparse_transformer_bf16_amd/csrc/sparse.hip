@@ -339,11 +339,25 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_up(
       const uint32_t moff = L[min(e0 + lane, E - 1)].off;
       for (int u0 = 0; u0 < ne; u0 += U) {
         u32x4_t w[U][NC];
+        if (u0 + U <= ne) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const uint32_t off = read_lane(moff, min(u0 + u, ne - 1));
+          for (int u = 0; u < U; ++u) {
+            const uint32_t off = read_lane(moff, u0 + u);
 #pragma unroll
-          for (int c = 0; c < NC; ++c) w[u][c] = buffer_load<u32x4_t>(wur, lane_off + c * 1024, off);
+            for (int c = 0; c < NC; ++c) w[u][c] = buffer_load<u32x4_t>(wur, lane_off + c * 1024, off);
+          }
+        } else {  // last batch: no loads for its missing entries
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            if (u0 + u < ne) {
+              const uint32_t off = read_lane(moff, u0 + u);
+#pragma unroll
+              for (int c = 0; c < NC; ++c) w[u][c] = buffer_load<u32x4_t>(wur, lane_off + c * 1024, off);
+            } else {
+#pragma unroll
+              for (int c = 0; c < NC; ++c) w[u][c] = u32x4_t{0u, 0u, 0u, 0u};
+            }
+          }
         }
         const UpEntry mine = L[e0 + min(u0 + my_u, ne - 1)];
         float p[U];
@@ -476,7 +490,7 @@ static hipError_t launch_up(const SparseArgs &a, hipStream_t s) {
   const int n_groups = nt / tpg;
   const int tok = 16;
   const int n_tb = (a.T + tok - 1) / tok;
-  constexpr int U = NC <= 8 ? 4 : 2;
+  constexpr int U = NC <= 4 ? 4 : 2;
   hipLaunchKernelGGL((k_sparse_up<D, NC, U>), dim3(n_groups * n_tb), dim3(SP_THREADS), 0, s, (const TT *)a.x,
                      (const TT *)a.wu, a.cnt, (const TT *)a.val, a.idx, a.row_flag, (u32x2_t *)a.list, a.list_n,
                      a.stride, a.T, a.d, nt, a.tile, a.cap, tpg, n_groups, tok, n_tb);
