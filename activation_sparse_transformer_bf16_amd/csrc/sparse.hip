@@ -131,10 +131,16 @@ constexpr int SP_THREADS = 256;
 constexpr int SP_WAVES = SP_THREADS / 64;
 constexpr int UP_LIST = 256;  // entries per wave list (tiles per group * cap)
 
-// Block -> (group, token block) so that group g runs on XCD g % 8 when the
-// group count is a multiple of 8 (groups beyond 8 run in successive phases).
+// Block -> (group, token block).  With 8 or more groups, group g runs on XCD
+// g % 8: groups are taken 8 at a time (a phase), the group count rounded up to
+// a multiple of 8 (blocks of a missing group return at once), so that each
+// XCD's L2 holds one group's weights per phase.  With fewer groups, group
+// bid % n_groups (XCD x serves group x % n_groups).
+__host__ __device__ constexpr int padded_groups(int n_groups) {
+  return n_groups >= 8 ? (n_groups + 7) / 8 * 8 : n_groups;
+}
 __device__ __forceinline__ void group_coords(int bid, int n_groups, int n_tb, int &g, int &tb) {
-  if (n_groups % 8 == 0) {
+  if (n_groups >= 8) {
     const int q = bid / 8;
     g = bid % 8 + 8 * (q / n_tb);
     tb = q % n_tb;
@@ -267,6 +273,7 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_up(
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   int g, tb;
   group_coords(blockIdx.x, n_groups, n_tb, g, tb);
+  if (g >= n_groups) return;
   const int k0 = g * tpg;
   const int kn = min(tpg, nt - k0);
   UpEntry *L = lists[wave];
@@ -400,6 +407,7 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_down(
   const int lcol = (EPI == 2 ? (lane & 31) : lane) * CPL;  // lane's first column in the slice
   int sl, tb;
   group_coords(blockIdx.x, n_slices, n_tb, sl, tb);
+  if (sl >= n_slices) return;
   const __amdgpu_buffer_rsrc_t wdr = buffer_rsrc(wd + sl * 256);  // the slice's columns of row 0
   const uint32_t lane_off = lcol * sizeof(TT);
   u32x2_t *C = chunk[wave];
@@ -491,7 +499,7 @@ static hipError_t launch_up(const SparseArgs &a, hipStream_t s) {
   const int tok = 16;
   const int n_tb = (a.T + tok - 1) / tok;
   constexpr int U = NC <= 4 ? 4 : 2;
-  hipLaunchKernelGGL((k_sparse_up<D, NC, U>), dim3(n_groups * n_tb), dim3(SP_THREADS), 0, s, (const TT *)a.x,
+  hipLaunchKernelGGL((k_sparse_up<D, NC, U>), dim3(padded_groups(n_groups) * n_tb), dim3(SP_THREADS), 0, s, (const TT *)a.x,
                      (const TT *)a.wu, a.cnt, (const TT *)a.val, a.idx, a.row_flag, (u32x2_t *)a.list, a.list_n,
                      a.stride, a.T, a.d, nt, a.tile, a.cap, tpg, n_groups, tok, n_tb);
   return hipGetLastError();
@@ -525,7 +533,7 @@ static hipError_t launch_down(const SparseArgs &a, hipStream_t s) {
   const int n_slices = a.d / 256;
   const int tok = 16;
   const int n_tb = (a.T + tok - 1) / tok;
-  hipLaunchKernelGGL((k_sparse_down<D, U>), dim3(n_slices * n_tb), dim3(SP_THREADS), 0, s, (const u32x2_t *)a.list,
+  hipLaunchKernelGGL((k_sparse_down<D, U>), dim3(padded_groups(n_slices) * n_tb), dim3(SP_THREADS), 0, s, (const u32x2_t *)a.list,
                      a.list_n, a.stride, (const TT *)a.wd, (TT *)a.y, a.T, a.d, n_slices, tok, n_tb);
   return hipGetLastError();
 }
