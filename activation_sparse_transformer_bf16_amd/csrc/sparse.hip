@@ -384,31 +384,33 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_up(
 
 // ---------------------------------------------------------------------------
 // Sparse down projection over the compact lists.  Every workgroup covers one
-// 256-column slice of y; each lane loads 16 bytes of a W_d row per
+// SLICE-column slice of y; each lane loads 16 bytes of a W_d row per
 // instruction (the vector memory pipeline's cost is per instruction, so wide
-// loads matter): for bf16 the two half-waves take two different entries
-// (8 columns per lane), for fp32 the whole wave takes one entry (4 columns
-// per lane).  The token's list goes through LDS, 64 entries per load.
+// loads matter), SLICE / (16 / s) lanes per entry: for bf16 and 256 columns
+// the two half-waves take two different entries, for fp32 the whole wave
+// takes one.  The token's list goes through LDS, 64 entries per load.
 // U = load instructions in flight per wave.
 
-template <Dt D, int U>
+template <Dt D, int SLICE, int U>
 __global__ __launch_bounds__(SP_THREADS) void k_sparse_down(
     const u32x2_t *__restrict__ list, const int *__restrict__ list_n, int stride,
     const typename DtT<D>::T *__restrict__ wd, typename DtT<D>::T *__restrict__ y, int T, int d, int n_slices,
     int tok_per_wg, int n_tb) {
   using TT = typename DtT<D>::T;
   constexpr int CPL = 16 / sizeof(TT);      // columns per lane
-  constexpr int EPI = 64 * CPL / 256;       // entries per load instruction (2 bf16, 1 fp32)
+  constexpr int LPE = SLICE / CPL;          // lanes per entry
+  constexpr int EPI = 64 / LPE;             // entries per load instruction
   constexpr int STEP = U * EPI;             // entries per iteration
+  static_assert(EPI == 1 || EPI == 2, "32 or 64 lanes per entry");
   static_assert(STEP <= 64 && 64 % STEP == 0, "a 64-entry chunk holds whole iterations");
   __shared__ u32x2_t chunk[SP_WAVES][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int half = EPI == 2 ? lane >> 5 : 0;
-  const int lcol = (EPI == 2 ? (lane & 31) : lane) * CPL;  // lane's first column in the slice
+  const int part = lane / LPE;                 // which of the EPI entries this lane works on
+  const int lcol = (lane % LPE) * CPL;         // lane's first column in the slice
   int sl, tb;
   group_coords(blockIdx.x, n_slices, n_tb, sl, tb);
   if (sl >= n_slices) return;
-  const __amdgpu_buffer_rsrc_t wdr = buffer_rsrc(wd + sl * 256);  // the slice's columns of row 0
+  const __amdgpu_buffer_rsrc_t wdr = buffer_rsrc(wd + sl * SLICE);  // the slice's columns of row 0
   const uint32_t lane_off = lcol * sizeof(TT);
   u32x2_t *C = chunk[wave];
   for (int it = wave; it < tok_per_wg; it += SP_WAVES) {
@@ -434,7 +436,7 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_down(
         float sw[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          const u32x2_t en = C[e + EPI * u + half];
+          const u32x2_t en = C[e + EPI * u + part];
           sw[u] = __uint_as_float(en[1]);
           w[u] = buffer_load<u32x4_t>(wdr, lane_off + en[0], 0u);
         }
@@ -458,9 +460,9 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_down(
       }
       wave_sync_lds();
     }
+    // lanes l and l + 32 hold the same columns for the even and the odd
+    // entries: add the halves
     if constexpr (EPI == 2) {
-      // lanes l and l + 32 hold the same columns for the even and the odd
-      // entries: add the halves
 #pragma unroll
       for (int v = 0; v < CPL; ++v) {
         auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[v]), __float_as_uint(acc[v]), false, false);
@@ -476,7 +478,7 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_down(
 #pragma unroll
       for (int v = 0; v < 4; ++v) out[v] = __float_as_uint(acc[v]);
     }
-    if (half == 0) *reinterpret_cast<u32x4_t *>(y + (size_t)t * d + sl * 256 + lcol) = out;
+    if (part == 0) *reinterpret_cast<u32x4_t *>(y + (size_t)t * d + sl * SLICE + lcol) = out;
   }
 }
 
@@ -527,21 +529,24 @@ hipError_t sparse_up(const SparseArgs &a, hipStream_t s) {
   return a.dtype == Dt::BF16 ? up_dispatch<Dt::BF16>(a, s) : up_dispatch<Dt::F32>(a, s);
 }
 
-template <Dt D, int U>
+template <Dt D, int SLICE, int U>
 static hipError_t launch_down(const SparseArgs &a, hipStream_t s) {
   using TT = typename DtT<D>::T;
-  const int n_slices = a.d / 256;
+  const int n_slices = a.d / SLICE;
   const int tok = 16;
   const int n_tb = (a.T + tok - 1) / tok;
-  hipLaunchKernelGGL((k_sparse_down<D, U>), dim3(padded_groups(n_slices) * n_tb), dim3(SP_THREADS), 0, s, (const u32x2_t *)a.list,
-                     a.list_n, a.stride, (const TT *)a.wd, (TT *)a.y, a.T, a.d, n_slices, tok, n_tb);
+  hipLaunchKernelGGL((k_sparse_down<D, SLICE, U>), dim3(padded_groups(n_slices) * n_tb), dim3(SP_THREADS), 0, s,
+                     (const u32x2_t *)a.list, a.list_n, a.stride, (const TT *)a.wd, (TT *)a.y, a.T, a.d, n_slices,
+                     tok, n_tb);
   return hipGetLastError();
 }
 
 hipError_t sparse_down(const SparseArgs &a, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
-  // 256-column slices; 8 list entries per iteration
-  return a.dtype == Dt::BF16 ? launch_down<Dt::BF16, 4>(a, s) : launch_down<Dt::F32, 8>(a, s);
+  // 256-column output slices, 8 list entries per iteration.  (128-column
+  // slices, which would keep F rows of a slice within one XCD's L2 for
+  // F > 8192, measured slower at F = 14336.)
+  return a.dtype == Dt::BF16 ? launch_down<Dt::BF16, 256, 4>(a, s) : launch_down<Dt::F32, 256, 8>(a, s);
 }
 
 }  // namespace twell

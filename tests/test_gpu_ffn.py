@@ -29,6 +29,8 @@ SMALL = [
     ("bf16", 20, 8192, 512, 128, 8, -1.0),         # widest bf16 rows
     ("f32", 33, 2560, 512, 128, 8, -1.0),          # wide fp32 rows
     ("f32", 17, 4096, 256, 256, 16, -0.5),         # widest fp32 rows
+    ("bf16", 24, 512, 8448, 256, 16, -2.0),        # many hidden units per output slice
+    ("f32", 20, 256, 4352, 128, 8, -1.5),          # fp32, many hidden units per output slice
 ]
 
 
