@@ -17,18 +17,19 @@
 
 namespace twell {
 
-// LDS layout of the TwELL epilogue:
+// LDS layout of the TwELL epilogue (RPP = rows per pass: 256, 128 or 64, the
+// largest whose layout fits the 160 KB of LDS for the given cap):
 //   masks  [256 rows][MW dwords]   activity bits of the whole tile (MW = BN/32)
 //   tile   [BN cols][RS bytes]     rounded values of RPP rows, column-major
 //   vals   [RPP][VS bytes]         slot values of each row of the pass
 //   idxs   [RPP][IS bytes]         slot column offsets
 //   dummy  [64][4 bytes]           where the lanes that hold no mask word write
-template <Dt D, int BN>
+template <Dt D, int BN, int RPP_>
 struct EpilogueLds {
   using T = typename DtT<D>::T;
   static constexpr int S = (int)sizeof(T);
   static constexpr int MW = BN / 32;
-  static constexpr int RPP = (BN * (128 * S + 8) <= 72 * 1024) ? 128 : 64;
+  static constexpr int RPP = RPP_;
   static constexpr int RS = RPP * S + 8;
   static constexpr int MASKS = GEMM_BM * MW * 4;
   static constexpr int TILE_OFF = MASKS;
@@ -40,6 +41,7 @@ struct EpilogueLds {
   __host__ __device__ static constexpr int dummy_off(int cap) { return idxs_off(cap) + RPP * is(cap); }
   __host__ __device__ static constexpr int bytes(int cap) { return dummy_off(cap) + 64 * 4; }
 };
+constexpr int LDS_MAX = 160 * 1024;
 
 // Four consecutive rows (accumulator registers i0..i0+3) of one column, rounded.
 __device__ __forceinline__ void put4(char *dst, const f32x16_t &a, int i0, uint16_t) {
@@ -52,20 +54,26 @@ __device__ __forceinline__ void put4(char *dst, const f32x16_t &a, int i0, float
   *reinterpret_cast<f32x2_t *>(dst + 8) = f32x2_t{a[i0 + 2], a[i0 + 3]};
 }
 
-// Copy `bytes` bytes LDS -> global in the widest unit both sides allow.
-__device__ __forceinline__ void copy_out(char *__restrict__ g, const char *l, int bytes, int unit) {
-  if (unit >= 16) {
-    for (int o = 0; o < bytes; o += 16) *reinterpret_cast<u32x4_t *>(g + o) = *reinterpret_cast<const u32x4_t *>(l + o);
-  } else if (unit >= 4) {
-    for (int o = 0; o < bytes; o += 4) *reinterpret_cast<uint32_t *>(g + o) = *reinterpret_cast<const uint32_t *>(l + o);
-  } else if (unit == 2) {
-    for (int o = 0; o < bytes; o += 2) *reinterpret_cast<uint16_t *>(g + o) = *reinterpret_cast<const uint16_t *>(l + o);
-  } else {
-    for (int o = 0; o < bytes; ++o) g[o] = l[o];
-  }
+// LDS writes of a wave visible to the whole wave.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <Dt D, int BN, bool DUMP>
+// Copy one chunk of `unit` (16, 4, 2 or 1) bytes LDS -> global.
+__device__ __forceinline__ void copy_chunk(char *__restrict__ g, const char *l, int unit) {
+  if (unit == 16)
+    *reinterpret_cast<u32x4_t *>(g) = *reinterpret_cast<const u32x4_t *>(l);
+  else if (unit == 4)
+    *reinterpret_cast<uint32_t *>(g) = *reinterpret_cast<const uint32_t *>(l);
+  else if (unit == 2)
+    *reinterpret_cast<uint16_t *>(g) = *reinterpret_cast<const uint16_t *>(l);
+  else
+    *g = *l;
+}
+
+template <Dt D, int BN, int RPP_, bool DUMP>
 __global__ __launch_bounds__(DMA_THREADS) void k_gate_twell(
     const typename DtT<D>::T *__restrict__ x, const typename DtT<D>::T *__restrict__ wg,
     const float *__restrict__ beta, int M, int K, int N, int cap, uint16_t *__restrict__ cnt,
@@ -109,13 +117,15 @@ __global__ __launch_bounds__(DMA_THREADS) void k_gate_twell(
   // M  every wave compares its accumulators with the activity threshold of the
   //    rounded value (v_cmp, one 64-bit mask per register: 32 columns of two
   //    rows) and files the masks in LDS as BN-bit row masks;
-  // then per pass of RPP rows:
+  // then per pass of RPP rows (one pass when all 256 rows fit):
   //  V  the waves that own those rows stage the rounded values in LDS;
-  //  C  one lane per row walks the row's set bits in ascending order (ffbl),
-  //     puts the first `cap` (value, column) pairs in the row's LDS slots and
-  //     writes count, slots and zero padding to global memory with vector
-  //     stores.
-  using L = EpilogueLds<D, BN>;
+  //  C  MW lanes per row, one per 32-column mask word: a segmented prefix
+  //     count over the row's words gives each word's first slot, each lane
+  //     walks its word's set bits in ascending order (ffbl) and puts the
+  //     (value, column) pairs that fall below `cap` in the row's LDS slots;
+  //     then the row's count, slots and zero padding go to global memory
+  //     with vector stores.
+  using L = EpilogueLds<D, BN, RPP_>;
   constexpr int MW = L::MW, RPP = L::RPP, RS = L::RS, S = L::S;
   const int ntiles = N / BN;
   const int VS = L::vs(cap), IS = L::is(cap);
@@ -181,40 +191,52 @@ __global__ __launch_bounds__(DMA_THREADS) void k_gate_twell(
       }
     }
     __syncthreads();
-    // C: one lane per row
-    if (lane < RPP / DMA_WAVES) {
-      const int rl = wave * (RPP / DMA_WAVES) + lane;  // row within the pass
-      const int rg = p * RPP + rl;                     // row within the tile
+    // C: MW lanes per row (wsub = mask word), RPS rows per wave step
+    constexpr int RPS = 64 / MW;
+    const int wsub = lane % MW;
+    const int nvc = (cap * S) / vunit, nic = cap / iunit;  // chunks of the slot values / indices
+    for (int rl = wave * RPS + lane / MW; rl - lane / MW < RPP; rl += DMA_WAVES * RPS) {
+      const int rg = p * RPP + rl;  // row within the tile
       const int t = m0 + rg;
-      int n = 0, total = 0;
+      uint32_t m = masks[rg * MW + wsub];
+      const int c = __popc(m);
+      int incl = c;
 #pragma unroll
-      for (int w = 0; w < MW; ++w) {
-        uint32_t m = masks[rg * MW + w];
-        total += __popc(m);
-        while (m != 0 && n < cap) {
-          const int c = 32 * w + __builtin_ctz(m);
-          m &= m - 1;
-          *reinterpret_cast<T *>(vals + rl * VS + n * S) = *reinterpret_cast<const T *>(tile + c * RS + rl * S);
-          idxs[rl * IS + n] = (char)c;
-          ++n;
-        }
+      for (int o = 1; o < MW; o <<= 1) {
+        const int u = __shfl_up(incl, o, MW);
+        if (wsub >= o) incl += u;
       }
+      const int total = __shfl(incl, MW - 1, MW);
+      int n = incl - c;
+      while (m != 0 && n < cap) {
+        const int col = 32 * wsub + __builtin_ctz(m);
+        m &= m - 1;
+        *reinterpret_cast<T *>(vals + rl * VS + n * S) = *reinterpret_cast<const T *>(tile + col * RS + rl * S);
+        idxs[rl * IS + n] = (char)col;
+        ++n;
+      }
+      wave_lds_sync();
       if (t < M) {
         const size_t slot0 = ((size_t)t * ntiles + tn) * cap;
-        cnt[(size_t)t * ntiles + tn] = (uint16_t)total;
-        copy_out(reinterpret_cast<char *>(val + slot0), vals + rl * VS, cap * S, vunit);
-        copy_out(reinterpret_cast<char *>(idx + slot0), idxs + rl * IS, cap, iunit);
+        if (wsub == 0) cnt[(size_t)t * ntiles + tn] = (uint16_t)total;
+        for (int q = wsub; q < nvc + nic; q += MW) {
+          if (q < nvc)
+            copy_chunk(reinterpret_cast<char *>(val + slot0) + q * vunit, vals + rl * VS + q * vunit, vunit);
+          else
+            copy_chunk(reinterpret_cast<char *>(idx + slot0) + (q - nvc) * iunit, idxs + rl * IS + (q - nvc) * iunit,
+                       iunit);
+        }
       }
     }
-    __syncthreads();
+    if (p + 1 < GEMM_BM / RPP) __syncthreads();
   }
 }
 
-template <Dt D, int BN, bool DUMP>
+template <Dt D, int BN, int RPP, bool DUMP>
 static hipError_t launch_gate(const GateArgs &a, hipStream_t s) {
   using T = typename DtT<D>::T;
-  auto kern = k_gate_twell<D, BN, DUMP>;
-  const int lds = std::max(gemm_dma_lds_bytes(BN), EpilogueLds<D, BN>::bytes(64));
+  auto kern = k_gate_twell<D, BN, RPP, DUMP>;
+  const int lds = std::max(gemm_dma_lds_bytes(BN), EpilogueLds<D, BN, RPP>::bytes(a.cap));
   hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
   const int mt = (a.M + GEMM_BM - 1) / GEMM_BM, ntl = a.N / BN;
@@ -224,9 +246,17 @@ static hipError_t launch_gate(const GateArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// The largest rows-per-pass whose epilogue layout fits the LDS for this cap.
+template <Dt D, int BN, bool DUMP>
+static hipError_t launch_gate_rpp(const GateArgs &a, hipStream_t s) {
+  if (EpilogueLds<D, BN, 256>::bytes(a.cap) <= LDS_MAX) return launch_gate<D, BN, 256, DUMP>(a, s);
+  if (EpilogueLds<D, BN, 128>::bytes(a.cap) <= LDS_MAX) return launch_gate<D, BN, 128, DUMP>(a, s);
+  return launch_gate<D, BN, 64, DUMP>(a, s);
+}
+
 template <Dt D, int BN>
 static hipError_t launch_gate(const GateArgs &a, hipStream_t s) {
-  return a.pre_out != nullptr ? launch_gate<D, BN, true>(a, s) : launch_gate<D, BN, false>(a, s);
+  return a.pre_out != nullptr ? launch_gate_rpp<D, BN, true>(a, s) : launch_gate_rpp<D, BN, false>(a, s);
 }
 
 hipError_t gate_twell(const GateArgs &a, hipStream_t s) {
