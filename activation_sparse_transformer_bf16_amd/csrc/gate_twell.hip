@@ -54,6 +54,16 @@ __device__ __forceinline__ void put4(char *dst, const f32x16_t &a, int i0, float
   *reinterpret_cast<f32x2_t *>(dst + 8) = f32x2_t{a[i0 + 2], a[i0 + 3]};
 }
 
+// v shifted by a DPP row shift (CTRL), or 0 where `take` is false.  The DPP
+// move runs with every lane active (a lane can only read an active lane), the
+// selection after it.
+template <int CTRL>
+__device__ __forceinline__ int seg_shift_add(int v, bool take) {
+  int sh = __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+  asm volatile("" : "+v"(sh));
+  return take ? sh : 0;
+}
+
 // LDS writes of a wave visible to the whole wave.
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -135,64 +145,84 @@ __global__ __launch_bounds__(DMA_THREADS) void k_gate_twell(
   uint32_t *masks = reinterpret_cast<uint32_t *>(smem);
   const int vunit = (cap * S) % 16 == 0 ? 16 : ((cap * S) % 4 == 0 ? 4 : S);
   const int iunit = cap % 16 == 0 ? 16 : (cap % 4 == 0 ? 4 : 1);
-  {
-    // lane k < 2*NWN receives mask word col0/32 + k % NWN of row R (k < NWN)
-    // or of row R+4
-    const bool holder = lane < 2 * NWN;
-    const int word = col0 / 32 + lane % NWN;
-    const int roff = lane < NWN ? 0 : 4;
-    uint32_t *dummy = reinterpret_cast<uint32_t *>(smem + L::dummy_off(cap)) + (tid & 63);
+  // lane k < 2*NWN receives mask word col0/32 + k % NWN of row R (k < NWN)
+  // or of row R+4
+  const bool holder = lane < 2 * NWN;
+  const int word = col0 / 32 + lane % NWN;
+  const int roff = lane < NWN ? 0 : 4;
+  uint32_t *dummy = reinterpret_cast<uint32_t *>(smem + L::dummy_off(cap)) + (tid & 63);
+  auto put_masks = [&](int bm, int i) {
+    uint32_t w = 0;
 #pragma unroll
-    for (int bm = 0; bm < NWM; ++bm) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        uint32_t w = 0;
-#pragma unroll
-        for (int bn = 0; bn < NWN; ++bn) {
-          const uint64_t m = ballot(active_after_round<D>(acc[bm][bn][i]));
-          w = (lane == bn) ? (uint32_t)m : w;
-          w = (lane == NWN + bn) ? (uint32_t)(m >> 32) : w;
-        }
-        const int R = row0 + 32 * bm + 8 * (i >> 2) + (i & 3);
-        uint32_t *dst = holder ? masks + (R + roff) * MW + word : dummy;
-        *dst = w;
-      }
+    for (int bn = 0; bn < NWN; ++bn) {
+      const uint64_t m = ballot(active_after_round<D>(acc[bm][bn][i]));
+      w = (lane == bn) ? (uint32_t)m : w;
+      w = (lane == NWN + bn) ? (uint32_t)(m >> 32) : w;
     }
-  }
-  // The accumulators are read again by V: make them opaque here so that the
-  // copies made for the masks are not kept live (which would spill).
-#pragma unroll
-  for (int bm = 0; bm < NWM; ++bm)
-#pragma unroll
-    for (int bn = 0; bn < NWN; ++bn) asm volatile("" : "+a"(acc[bm][bn]));
-#pragma unroll
-  for (int p = 0; p < GEMM_BM / RPP; ++p) {
-    // V: stage the rounded values of this pass and clear the slots
-    for (int o = tid * 16; o < RPP * (VS + IS); o += DMA_THREADS * 16)
-      *reinterpret_cast<u32x4_t *>(vals + o) = u32x4_t{0u, 0u, 0u, 0u};
+    const int R = row0 + 32 * bm + 8 * (i >> 2) + (i & 3);
+    uint32_t *dst = holder ? masks + (R + roff) * MW + word : dummy;
+    *dst = w;
+  };
+  // rounded values of rows 32 bm + 8 g + {0..3} (+4 for the upper half-wave)
+  // of the wave's blocks, into the column-major tile of pass p
+  auto put_values = [&](int p, int bm, int g) {
     const int rl0 = row0 - p * RPP + 4 * (lane >> 5);  // lane's first row, relative to the pass
 #pragma unroll
-    for (int bm = 0; bm < NWM; ++bm) {
-      if ((row0 + 32 * bm) / RPP != p) continue;  // wave-uniform
+    for (int bn = 0; bn < NWN; ++bn) {
+      char *colp = tile + (col0 + 32 * bn + (lane & 31)) * RS;
+      put4(colp + (rl0 + 32 * bm + 8 * g) * S, acc[bm][bn], 4 * g, T());
+      if constexpr (DUMP) {
+        const int t0 = m0 + p * RPP + rl0 + 32 * bm + 8 * g;
 #pragma unroll
-      for (int bn = 0; bn < NWN; ++bn) {
-        char *colp = tile + (col0 + 32 * bn + (lane & 31)) * RS;
+        for (int q = 0; q < 4; ++q)
+          if (t0 + q < M)
+            pre_out[(size_t)(t0 + q) * N + n0 + col0 + 32 * bn + (lane & 31)] = from_f32<D>(acc[bm][bn][4 * g + q]);
+      }
+    }
+  };
+  auto clear_slots = [&]() {
+    for (int o = tid * 16; o < RPP * (VS + IS); o += DMA_THREADS * 16)
+      *reinterpret_cast<u32x4_t *>(vals + o) = u32x4_t{0u, 0u, 0u, 0u};
+  };
+  if constexpr (RPP == GEMM_BM) {
+    // one pass: masks and values from the same register reads
+    clear_slots();
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          put4(colp + (rl0 + 32 * bm + 8 * g) * S, acc[bm][bn], 4 * g, T());
-          if constexpr (DUMP) {
-            const int t0 = m0 + p * RPP + rl0 + 32 * bm + 8 * g;
+    for (int bm = 0; bm < NWM; ++bm)
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-              if (t0 + q < M)
-                pre_out[(size_t)(t0 + q) * N + n0 + col0 + 32 * bn + (lane & 31)] = from_f32<D>(acc[bm][bn][4 * g + q]);
-          }
-        }
+      for (int g = 0; g < 4; ++g) {
+        put_values(0, bm, g);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) put_masks(bm, 4 * g + q);
+      }
+  } else {
+#pragma unroll
+    for (int bm = 0; bm < NWM; ++bm)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) put_masks(bm, i);
+    // The accumulators are read again by V: make them opaque here so that
+    // the copies made for the masks are not kept live (which would spill).
+#pragma unroll
+    for (int bm = 0; bm < NWM; ++bm)
+#pragma unroll
+      for (int bn = 0; bn < NWN; ++bn) asm volatile("" : "+a"(acc[bm][bn]));
+  }
+#pragma unroll
+  for (int p = 0; p < GEMM_BM / RPP; ++p) {
+    if constexpr (RPP != GEMM_BM) {
+      // V: stage the rounded values of this pass and clear the slots
+      clear_slots();
+#pragma unroll
+      for (int bm = 0; bm < NWM; ++bm) {
+        if ((row0 + 32 * bm) / RPP != p) continue;  // wave-uniform
+#pragma unroll
+        for (int g = 0; g < 4; ++g) put_values(p, bm, g);
       }
     }
     __syncthreads();
     // C: MW lanes per row (wsub = mask word), RPS rows per wave step
     constexpr int RPS = 64 / MW;
+    static_assert(MW == 4 || MW == 8, "tile of 128 or 256 columns");
     const int wsub = lane % MW;
     const int nvc = (cap * S) / vunit, nic = cap / iunit;  // chunks of the slot values / indices
     for (int rl = wave * RPS + lane / MW; rl - lane / MW < RPP; rl += DMA_WAVES * RPS) {
@@ -200,13 +230,13 @@ __global__ __launch_bounds__(DMA_THREADS) void k_gate_twell(
       const int t = m0 + rg;
       uint32_t m = masks[rg * MW + wsub];
       const int c = __popc(m);
+      // inclusive prefix count over the row's MW lanes (DPP row shifts; a
+      // row of 16 lanes holds 16 / MW segments, lanes below the shift in a
+      // segment add nothing); the last lane of the segment holds the total
       int incl = c;
-#pragma unroll
-      for (int o = 1; o < MW; o <<= 1) {
-        const int u = __shfl_up(incl, o, MW);
-        if (wsub >= o) incl += u;
-      }
-      const int total = __shfl(incl, MW - 1, MW);
+      incl += seg_shift_add<0x111>(incl, wsub >= 1);    // row_shr 1
+      incl += seg_shift_add<0x112>(incl, wsub >= 2);    // row_shr 2
+      if constexpr (MW == 8) incl += seg_shift_add<0x114>(incl, wsub >= 4);  // row_shr 4
       int n = incl - c;
       while (m != 0 && n < cap) {
         const int col = 32 * wsub + __builtin_ctz(m);
@@ -218,7 +248,7 @@ __global__ __launch_bounds__(DMA_THREADS) void k_gate_twell(
       wave_lds_sync();
       if (t < M) {
         const size_t slot0 = ((size_t)t * ntiles + tn) * cap;
-        if (wsub == 0) cnt[(size_t)t * ntiles + tn] = (uint16_t)total;
+        if (wsub == MW - 1) cnt[(size_t)t * ntiles + tn] = (uint16_t)incl;
         for (int q = wsub; q < nvc + nic; q += MW) {
           if (q < nvc)
             copy_chunk(reinterpret_cast<char *>(val + slot0) + q * vunit, vals + rl * VS + q * vunit, vunit);
