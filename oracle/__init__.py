@@ -23,6 +23,10 @@ What the oracle computes, and which passage each part follows:
   matrix) and the q2bstudio post (third paragraph: compact ELL plus dense
   backup for rows with many non-zeros).  The pages fix no field layout; the
   layout used here is the one declared in ``include/twell.h``.
+* ``hybrid``: the hybrid training format (compact ELL rows plus a dense
+  backup for rows with many non-zeros) and its conversion from TwELL:
+  Resumen Técnico §2.A (hybrid format for training) and §2.B (training
+  kernels: TwELL to hybrid conversion).
 * ``numerics``: exact decoding of the storage dtypes to float64 and
   round-to-nearest-even encoding to bf16.
 
