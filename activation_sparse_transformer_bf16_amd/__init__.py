@@ -32,6 +32,17 @@ class TwellMatrixC(ctypes.Structure):
     ]
 
 
+class TwellHybridC(ctypes.Structure):
+    """Mirror of ``twell_hybrid`` (include/twell.h)."""
+
+    _fields_ = [
+        ("rows", ctypes.c_int32), ("cols", ctypes.c_int32), ("width", ctypes.c_int32),
+        ("dtype", ctypes.c_int), ("cnt", ctypes.c_void_p), ("val", ctypes.c_void_p),
+        ("col", ctypes.c_void_p), ("dense_rows", ctypes.c_void_p), ("n_dense", ctypes.c_void_p),
+        ("dense", ctypes.c_void_p), ("dense_cap", ctypes.c_int32),
+    ]
+
+
 class TwellError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"{message} (status {status})")
@@ -60,6 +71,7 @@ def _load():
         "twell_sparse_ffn": (I, [M, P, P, P, P, P, P, I, P, Z, P]),
         "dense_ffn_workspace_size": (Z, [I, I, I, I]),
         "dense_ffn_forward": (I, [P, P, P, P, P, P, I, I, I, I, P, Z, P]),
+        "twell_to_hybrid": (I, [M, ctypes.POINTER(TwellHybridC), P]),
     }
     # Private function objects: changing argtypes on the public handle (lib())
     # cannot make this binding pass truncated pointers.
@@ -84,7 +96,7 @@ _lib = _Fns(_private)
 EXPORTS = ("twell_abi_version", "twell_status_str", "twell_last_error", "twell_pack",
            "twell_ffn_workspace_size", "twell_ffn_forward", "twell_gate_pack", "twell_overflow_scan",
            "twell_sparse_ffn",
-           "dense_ffn_workspace_size", "dense_ffn_forward")
+           "dense_ffn_workspace_size", "dense_ffn_forward", "twell_to_hybrid")
 
 
 def lib():
@@ -187,6 +199,53 @@ class TwellMatrix:
     @property
     def device(self):
         return self.cnt.device
+
+
+@dataclass
+class TwellHybrid:
+    """Device buffers of one hybrid matrix (see ``twell_hybrid`` in include/twell.h)."""
+
+    rows: int
+    cols: int
+    width: int
+    dtype: object        # torch dtype of the values
+    cnt: object          # int32 [rows]
+    val: object          # dtype [rows, width]
+    col: object          # int32 [rows, width]
+    dense_rows: object   # int32 [dense_cap]
+    n_dense: object      # int32 [1]
+    dense: object        # dtype [dense_cap, cols] or None
+    dense_cap: int
+
+    @classmethod
+    def empty(cls, rows: int, cols: int, width: int, dtype, device, dense_cap: Optional[int] = None,
+              dense: bool = True) -> "TwellHybrid":
+        torch = _torch()
+        dense_cap = rows if dense_cap is None else dense_cap
+        return cls(rows, cols, width, dtype,
+                   torch.empty((rows,), dtype=torch.int32, device=device),
+                   torch.empty((rows, width), dtype=dtype, device=device),
+                   torch.empty((rows, width), dtype=torch.int32, device=device),
+                   torch.empty((max(dense_cap, 1),), dtype=torch.int32, device=device),
+                   torch.empty((1,), dtype=torch.int32, device=device),
+                   torch.empty((max(dense_cap, 1), cols), dtype=dtype, device=device) if dense else None,
+                   dense_cap)
+
+    def c_struct(self) -> TwellHybridC:
+        return TwellHybridC(self.rows, self.cols, self.width, _dtype_code(self.dtype), _ptr(self.cnt),
+                            _ptr(self.val), _ptr(self.col), _ptr(self.dense_rows), _ptr(self.n_dense),
+                            _ptr(self.dense), self.dense_cap)
+
+
+def twell_to_hybrid(packed: TwellMatrix, width: int, dense_cap: Optional[int] = None, dense: bool = True,
+                    out: Optional[TwellHybrid] = None) -> TwellHybrid:
+    """Convert a TwELL matrix (with its dense backup rows) to the hybrid format."""
+    if out is None:
+        out = TwellHybrid.empty(packed.rows, packed.cols, width, packed.dtype, packed.device, dense_cap, dense)
+    m = packed.c_struct()
+    h = out.c_struct()
+    _check(_lib.twell_to_hybrid(ctypes.byref(m), ctypes.byref(h), _stream(packed.device)))
+    return out
 
 
 def twell_pack(pre, tile: int, cap: int, ovf_cap: Optional[int] = None, dense: bool = True,

@@ -216,6 +216,35 @@ twell_status twell_gate_pack(const void *x, const void *w_gate, const float *gat
   return TWELL_OK;
 }
 
+twell_status twell_to_hybrid(const twell_matrix *packed, twell_hybrid *out, void *stream) {
+  g_err[0] = 0;
+  twell_status st = check_matrix(packed, true);
+  if (st != TWELL_OK) return st;
+  if (out == nullptr) return fail(TWELL_ERR_INVALID_ARG, "null twell_hybrid");
+  if (out->rows != packed->rows || out->cols != packed->cols || out->dtype != packed->dtype)
+    return fail(TWELL_ERR_INVALID_ARG, "hybrid rows/cols/dtype must equal the TwELL matrix's");
+  if (out->width < 1) return fail(TWELL_ERR_INVALID_ARG, "width must be >= 1");
+  if (out->dense_cap < 0) return fail(TWELL_ERR_INVALID_ARG, "dense_cap must be >= 0");
+  if (out->n_dense == nullptr) return fail(TWELL_ERR_INVALID_ARG, "null n_dense");
+  if (out->dense_cap > 0 && out->dense_rows == nullptr)
+    return fail(TWELL_ERR_INVALID_ARG, "null dense_rows with dense_cap > 0");
+  const int T = packed->rows;
+  if (T > 0 && (out->cnt == nullptr || out->val == nullptr || out->col == nullptr))
+    return fail(TWELL_ERR_INVALID_ARG, "null cnt/val/col");
+  if (T > 0 && packed->dense == nullptr)
+    return fail(TWELL_ERR_INVALID_ARG, "the TwELL matrix needs its dense backup rows (packed->dense)");
+  if (!aligned(out->cnt, 4) || !aligned(out->val, dt_size(out->dtype)) || !aligned(out->col, 4) ||
+      !aligned(out->dense_rows, 4) || !aligned(out->n_dense, 4) || !aligned(out->dense, dt_size(out->dtype)))
+    return fail(TWELL_ERR_UNSUPPORTED, "misaligned twell_hybrid buffer");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (T == 0) return hip_check(zero_int(out->n_dense, s), "zero n_dense");
+  HybridArgs ha{to_dt(packed->dtype), T, packed->cols, packed->tile, packed->cap, packed->cnt, packed->val,
+                packed->idx, packed->ovf_rows, packed->n_ovf, packed->ovf_cap, packed->dense, out->width,
+                out->cnt, out->val, out->col, out->dense_rows, out->n_dense, out->dense_cap, out->dense};
+  TW_TRY(twell_to_hybrid_launch(ha, s), "TwELL to hybrid");
+  return TWELL_OK;
+}
+
 twell_status twell_overflow_scan(twell_matrix *packed, void *stream) {
   g_err[0] = 0;
   twell_status st = check_matrix(packed, false);

@@ -1,0 +1,198 @@
+// TwELL -> hybrid conversion (the training format of gist.science "Sparser,
+// Faster, Lighter Transformer Language Models", Resumen Técnico §2.A: rows
+// with few non-zeros in a compact ELL matrix, the others in a dense backup;
+// the conversion kernel is one of the training kernels of §2.B).
+//
+//   k_hybrid_rows:  one wave per row.  The row's TwELL counts give its true
+//                   entry count and whether it overflowed TwELL.  A row with
+//                   at most `width` entries becomes an ELL row: from its
+//                   TwELL slots (one lane per slot, positions from a prefix
+//                   count over the tiles), or, when it overflowed TwELL, by a
+//                   ballot compaction of its dense backup row.  Other rows get
+//                   all-padding ELL slots.
+//   k_compact_gt:   ascending list of the rows with more than `width` entries.
+//   k_hybrid_dense: one workgroup per listed row: the dense backup row, copied
+//                   from TwELL's dense backup or scattered from the slots.
+#include "launch.hpp"
+
+#include <algorithm>
+
+namespace twell {
+
+constexpr int HY_WAVES = 4;
+
+// Position of row t in the ascending list rows[0..n), or -1.
+__device__ __forceinline__ int find_row(const int *__restrict__ rows, int n, int t) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (rows[mid] < t)
+      lo = mid + 1;
+    else
+      hi = mid;
+  }
+  return (lo < n && rows[lo] == t) ? lo : -1;
+}
+
+template <Dt D>
+__global__ __launch_bounds__(64 * HY_WAVES) void k_hybrid_rows(
+    const uint16_t *__restrict__ cnt, const typename DtT<D>::T *__restrict__ val, const uint8_t *__restrict__ idx,
+    const int *__restrict__ ovf_rows, const int *__restrict__ n_ovf, int ovf_cap,
+    const typename DtT<D>::T *__restrict__ tw_dense, int T, int F, int tile, int cap, int width,
+    int *__restrict__ out_cnt, typename DtT<D>::T *__restrict__ out_val, int *__restrict__ out_col) {
+  using TT = typename DtT<D>::T;
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * HY_WAVES + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int nt = F / tile;
+  const uint16_t *crow = cnt + (size_t)t * nt;
+  int total = 0;
+  bool over = false;
+  for (int kb = 0; kb < nt; kb += 64) {
+    const int k = kb + lane;
+    const int c = k < nt ? (int)crow[k] : 0;
+    total += c;
+    over |= c > cap;
+  }
+  total = __builtin_amdgcn_readlane(wave_incl_scan(total), 63);
+  const bool tw_ovf = ballot(over) != 0;
+  if (lane == 0) out_cnt[t] = total;
+  TT *vrow = out_val + (size_t)t * width;
+  int *crow_out = out_col + (size_t)t * width;
+  const int n_ell = total <= width ? total : 0;  // ELL entries written below
+  if (total <= width) {
+    if (!tw_ovf) {
+      // one lane per TwELL slot, tiles in chunks of 64 / cap
+      int before = 0;  // entries of the tiles before the chunk
+      const int tiles_per_chunk = max(1, 64 / cap);
+      for (int kb = 0; kb < nt; kb += tiles_per_chunk) {
+        const int kt = min(tiles_per_chunk, nt - kb);
+        // per-tile counts of the chunk, prefix over them (lane = tile)
+        const int n = lane < kt ? (int)crow[kb + lane] : 0;
+        const int incl = wave_incl_scan(n);
+        for (int q0 = 0; q0 < kt * cap; q0 += 64) {
+          const int q = q0 + lane;
+          const int kq = q / cap, sq = q - kq * cap;
+          const int nq = __shfl(n, kq & 63, 64);
+          const int pos = before + __shfl(incl - n, kq & 63, 64) + sq;
+          if (q < kt * cap && sq < nq && pos < width) {
+            const size_t slot = ((size_t)t * nt + kb + kq) * cap + sq;
+            vrow[pos] = val[slot];
+            crow_out[pos] = (kb + kq) * tile + idx[slot];
+          }
+        }
+        before += __builtin_amdgcn_readlane(incl, 63);
+      }
+    } else {
+      // the TwELL slots lost entries of this row: compact its dense backup row
+      const int r = find_row(ovf_rows, min(*n_ovf, ovf_cap), t);
+      const TT *drow = tw_dense + (size_t)max(r, 0) * F;
+      int before = 0;
+      for (int jb = 0; r >= 0 && jb < F; jb += 64) {
+        const int j = jb + lane;
+        const TT v = j < F ? drow[j] : TT(0);
+        const bool act = j < F && active_bits(v);
+        const uint64_t m = ballot(act);
+        const int pos = before + mbcnt(m);
+        if (act && pos < width) {
+          vrow[pos] = v;
+          crow_out[pos] = j;
+        }
+        before += popc64(m);
+      }
+    }
+  }
+  // padding: +0 values, column 0
+  for (int s = n_ell + lane; s < width; s += 64) {
+    vrow[s] = TT(0);
+    crow_out[s] = 0;
+  }
+}
+
+// Ascending list of the rows t with cnt[t] > width; one workgroup.
+constexpr int HY_COMPACT_THREADS = 1024;
+__global__ __launch_bounds__(HY_COMPACT_THREADS) void k_compact_gt(const int *__restrict__ cnt, int T, int width,
+                                                                    int *__restrict__ rows, int rows_cap,
+                                                                    int *__restrict__ n_rows) {
+  __shared__ int wcount[HY_COMPACT_THREADS / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int carry = 0;
+  for (int base = 0; base < T; base += HY_COMPACT_THREADS) {
+    const int t = base + tid;
+    const bool f = t < T && cnt[t] > width;
+    const uint64_t m = ballot(f);
+    if (lane == 0) wcount[wave] = popc64(m);
+    __syncthreads();
+    int before = carry, total = 0;
+    for (int w = 0; w < HY_COMPACT_THREADS / 64; ++w) {
+      before += (w < wave) ? wcount[w] : 0;
+      total += wcount[w];
+    }
+    if (f) {
+      const int pos = before + mbcnt(m);
+      if (pos < rows_cap) rows[pos] = t;
+    }
+    carry += total;
+    __syncthreads();
+  }
+  if (tid == 0) *n_rows = carry;
+}
+
+constexpr int HY_DENSE_THREADS = 256;
+
+template <Dt D>
+__global__ __launch_bounds__(HY_DENSE_THREADS) void k_hybrid_dense(
+    const uint16_t *__restrict__ cnt, const typename DtT<D>::T *__restrict__ val, const uint8_t *__restrict__ idx,
+    const int *__restrict__ ovf_rows, const int *__restrict__ n_ovf, int ovf_cap,
+    const typename DtT<D>::T *__restrict__ tw_dense, int F, int tile, int cap, const int *__restrict__ dense_rows,
+    const int *__restrict__ n_dense, int dense_cap, typename DtT<D>::T *__restrict__ out_dense) {
+  using TT = typename DtT<D>::T;
+  const int n = min(*n_dense, dense_cap);
+  const int nt = F / tile;
+  for (int r = blockIdx.x; r < n; r += gridDim.x) {
+    const int t = dense_rows[r];
+    TT *orow = out_dense + (size_t)r * F;
+    const int p = find_row(ovf_rows, min(*n_ovf, ovf_cap), t);
+    if (p >= 0) {
+      const TT *drow = tw_dense + (size_t)p * F;
+      for (int j = threadIdx.x; j < F; j += HY_DENSE_THREADS) orow[j] = drow[j];
+    } else {
+      for (int j = threadIdx.x; j < F; j += HY_DENSE_THREADS) orow[j] = TT(0);
+      __syncthreads();
+      // every entry of a row that did not overflow TwELL is in its slots
+      for (int q = threadIdx.x; q < nt * cap; q += HY_DENSE_THREADS) {
+        const int k = q / cap, s = q - k * cap;
+        const size_t slot = ((size_t)t * nt + k) * cap + s;
+        const int c = idx[slot];
+        if (s < (int)cnt[(size_t)t * nt + k] && c < tile) orow[k * tile + c] = val[slot];
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <Dt D>
+static hipError_t launch_hybrid(const HybridArgs &a, hipStream_t s) {
+  using TT = typename DtT<D>::T;
+  hipLaunchKernelGGL(k_hybrid_rows<D>, dim3((a.T + HY_WAVES - 1) / HY_WAVES), dim3(64 * HY_WAVES), 0, s, a.cnt,
+                     (const TT *)a.val, a.idx, a.ovf_rows, a.n_ovf, a.ovf_cap, (const TT *)a.tw_dense, a.T, a.F,
+                     a.tile, a.cap, a.width, a.out_cnt, (TT *)a.out_val, a.out_col);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_compact_gt, dim3(1), dim3(HY_COMPACT_THREADS), 0, s, a.out_cnt, a.T, a.width, a.dense_rows,
+                     a.dense_cap, a.n_dense);
+  e = hipGetLastError();
+  if (e != hipSuccess || a.out_dense == nullptr || a.dense_cap == 0) return e;
+  const int grid = std::min(a.T, 1024);
+  hipLaunchKernelGGL(k_hybrid_dense<D>, dim3(grid), dim3(HY_DENSE_THREADS), 0, s, a.cnt, (const TT *)a.val, a.idx,
+                     a.ovf_rows, a.n_ovf, a.ovf_cap, (const TT *)a.tw_dense, a.F, a.tile, a.cap, a.dense_rows,
+                     a.n_dense, a.dense_cap, (TT *)a.out_dense);
+  return hipGetLastError();
+}
+
+hipError_t twell_to_hybrid_launch(const HybridArgs &a, hipStream_t s) {
+  if (a.T <= 0) return hipSuccess;
+  return a.dtype == Dt::BF16 ? launch_hybrid<Dt::BF16>(a, s) : launch_hybrid<Dt::F32>(a, s);
+}
+
+}  // namespace twell

@@ -99,6 +99,28 @@ struct DenseRowsArgs {
 };
 hipError_t pack_dense_rows(const DenseRowsArgs &a, hipStream_t s);
 
+// TwELL -> hybrid (ELL rows of `width` slots + dense backup rows).
+struct HybridArgs {
+  Dt dtype;
+  int T, F, tile, cap;
+  const uint16_t *cnt;   // TwELL
+  const void *val;
+  const uint8_t *idx;
+  const int *ovf_rows;
+  const int *n_ovf;
+  int ovf_cap;
+  const void *tw_dense;  // [ovf_cap][F] ReLU'd TwELL overflow rows
+  int width;             // hybrid
+  int *out_cnt;          // [T]
+  void *out_val;         // [T][width]
+  int *out_col;          // [T][width]
+  int *dense_rows;       // [dense_cap]
+  int *n_dense;          // [1]
+  int dense_cap;
+  void *out_dense;       // [dense_cap][F] or null
+};
+hipError_t twell_to_hybrid_launch(const HybridArgs &a, hipStream_t s);
+
 // *p = 0 with a one-thread kernel (safe under stream capture).
 hipError_t zero_int(int *p, hipStream_t s);
 

@@ -213,6 +213,48 @@ twell_status dense_ffn_forward(const void *x, const void *w_gate, const void *w_
                                int d, int F, twell_dtype dtype, void *workspace,
                                size_t ws_bytes, void *stream);
 
+/*
+ * twell_hybrid -- the hybrid format for training activations: rows with few
+ * non-zeros as rows of a compact ELL matrix, rows with many in a dense backup
+ * matrix (gist.science "Sparser, Faster, Lighter Transformer Language Models",
+ * Resumen Técnico §2.A; q2bstudio post on TwELL, third paragraph).  The pages
+ * fix no width or layout; here, for a row t of the activation matrix:
+ *     cnt[t]             number of active entries (IEEE v > 0 on the bits).
+ *     ELL row            iff cnt[t] <= width: val[t][s], col[t][s] for
+ *                        s < cnt[t] hold the s-th active entry in ascending
+ *                        column order (value bits, column index); every other
+ *                        slot holds +0 and column 0.
+ *     dense row          iff cnt[t] > width: its ELL slots are all padding,
+ *                        t is listed in dense_rows (ascending; *n_dense is the
+ *                        true count, only the first dense_cap are listed) and
+ *                        dense[r][:] holds ReLU(row dense_rows[r]) when dense
+ *                        is non-NULL.
+ */
+typedef struct {
+  int32_t rows, cols;    /* T, F: as the TwELL matrix converted */
+  int32_t width;         /* ELL slots per row, >= 1 */
+  twell_dtype dtype;     /* value dtype */
+  int32_t *cnt;          /* [rows] */
+  void *val;             /* [rows][width], dtype */
+  int32_t *col;          /* [rows][width] */
+  int32_t *dense_rows;   /* [dense_cap] */
+  int32_t *n_dense;      /* [1] */
+  void *dense;           /* [dense_cap][cols], dtype; may be NULL (not written) */
+  int32_t dense_cap;     /* rows available in dense_rows (and dense) */
+} twell_hybrid;
+
+/*
+ * twell_to_hybrid -- convert a TwELL matrix to the hybrid format (the training
+ * conversion kernel of the same summary, §2.B).  The result is the hybrid of
+ * the activation matrix the TwELL matrix describes, whatever its tile and
+ * capacity: rows that overflowed TwELL are taken from packed->dense, so
+ * packed->dense must be non-NULL and packed->ovf_cap >= packed->rows (as
+ * written by twell_pack, or by twell_ffn_forward with a dense buffer).
+ * out: caller-owned buffers with rows, cols and dtype equal to packed's.
+ * Errors: INVALID_ARG, UNSUPPORTED (alignment), HIP.
+ */
+twell_status twell_to_hybrid(const twell_matrix *packed, twell_hybrid *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -141,3 +141,27 @@ def test_binding_keeps_its_own_argtypes():
         assert ctypes.c_void_p in twell._lib.twell_ffn_forward.argtypes
     finally:
         pub.argtypes = saved
+
+
+def _hybrid(rows=8, cols=512, width=16, dtype=twell.TWELL_BF16, dense_cap=8, **kw):
+    h = twell.TwellHybridC(rows, cols, width, dtype, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, dense_cap)
+    for k, v in kw.items():
+        setattr(h, k, v)
+    return h
+
+
+def test_to_hybrid_validation():
+    H = L.twell_to_hybrid
+    m = _matrix(dense=FAKE)
+    assert H(ctypes.byref(m), None, None) == twell.TWELL_ERR_INVALID_ARG
+    assert H(ctypes.byref(m), ctypes.byref(_hybrid(rows=7)), None) == twell.TWELL_ERR_INVALID_ARG
+    assert H(ctypes.byref(m), ctypes.byref(_hybrid(cols=256)), None) == twell.TWELL_ERR_INVALID_ARG
+    assert H(ctypes.byref(m), ctypes.byref(_hybrid(dtype=twell.TWELL_F32)), None) == twell.TWELL_ERR_INVALID_ARG
+    assert H(ctypes.byref(m), ctypes.byref(_hybrid(width=0)), None) == twell.TWELL_ERR_INVALID_ARG
+    assert H(ctypes.byref(m), ctypes.byref(_hybrid(n_dense=None)), None) == twell.TWELL_ERR_INVALID_ARG
+    assert H(ctypes.byref(m), ctypes.byref(_hybrid(val=FAKE + 1)), None) == twell.TWELL_ERR_UNSUPPORTED
+    # the TwELL matrix must carry its dense backup rows, for every row
+    m_nodense = _matrix()
+    assert H(ctypes.byref(m_nodense), ctypes.byref(_hybrid()), None) == twell.TWELL_ERR_INVALID_ARG
+    m_short = _matrix(dense=FAKE, ovf_cap=4)
+    assert H(ctypes.byref(m_short), ctypes.byref(_hybrid()), None) == twell.TWELL_ERR_INVALID_ARG
