@@ -27,6 +27,9 @@ What the oracle computes, and which passage each part follows:
   backup for rows with many non-zeros) and its conversion from TwELL:
   Resumen Técnico §2.A (hybrid format for training) and §2.B (training
   kernels: TwELL to hybrid conversion).
+* ``penalty``: the L1 activation penalty ||h||_1 and its gradient, from
+  TwELL: Resumen Técnico §2.B (training strategy: L1 regularisation of the ReLU activations)
+  and §4 (coefficient 2e-5).
 * ``numerics``: exact decoding of the storage dtypes to float64 and
   round-to-nearest-even encoding to bf16.
 
