@@ -72,6 +72,9 @@ def _load():
         "dense_ffn_workspace_size": (Z, [I, I, I, I]),
         "dense_ffn_forward": (I, [P, P, P, P, P, P, I, I, I, I, P, Z, P]),
         "twell_to_hybrid": (I, [M, ctypes.POINTER(TwellHybridC), P]),
+        "twell_l1_workspace_size": (Z, []),
+        "twell_l1_norm": (I, [M, P, P, Z, P]),
+        "twell_l1_grad": (I, [M, ctypes.c_float, P, P, P]),
     }
     # Private function objects: changing argtypes on the public handle (lib())
     # cannot make this binding pass truncated pointers.
@@ -96,7 +99,8 @@ _lib = _Fns(_private)
 EXPORTS = ("twell_abi_version", "twell_status_str", "twell_last_error", "twell_pack",
            "twell_ffn_workspace_size", "twell_ffn_forward", "twell_gate_pack", "twell_overflow_scan",
            "twell_sparse_ffn",
-           "dense_ffn_workspace_size", "dense_ffn_forward", "twell_to_hybrid")
+           "dense_ffn_workspace_size", "dense_ffn_forward", "twell_to_hybrid",
+           "twell_l1_workspace_size", "twell_l1_norm", "twell_l1_grad")
 
 
 def lib():
@@ -246,6 +250,36 @@ def twell_to_hybrid(packed: TwellMatrix, width: int, dense_cap: Optional[int] = 
     h = out.c_struct()
     _check(_lib.twell_to_hybrid(ctypes.byref(m), ctypes.byref(h), _stream(packed.device)))
     return out
+
+
+def twell_l1_workspace_size() -> int:
+    return int(_lib.twell_l1_workspace_size())
+
+
+def twell_l1_norm(packed: TwellMatrix, out=None, workspace=None):
+    """||h||_1 of the activations a TwELL matrix describes, as a float64 device tensor [1]."""
+    torch = _torch()
+    device = packed.device
+    if out is None:
+        out = torch.empty((1,), dtype=torch.float64, device=device)
+    ws = _workspace(twell_l1_workspace_size(), device, workspace)
+    m = packed.c_struct()
+    _check(_lib.twell_l1_norm(ctypes.byref(m), _ptr(out), _ptr(ws), ws.numel(), _stream(device)))
+    return out
+
+
+def twell_l1_grad(packed: TwellMatrix, lam: float, grad_val=None, grad_dense=None, dense: bool = True):
+    """d(lam ||h||_1)/dh in the TwELL pattern: (grad_val, grad_dense or None)."""
+    torch = _torch()
+    device = packed.device
+    if grad_val is None:
+        grad_val = torch.empty_like(packed.val)
+    if grad_dense is None and dense and packed.dense is not None:
+        grad_dense = torch.empty_like(packed.dense)
+    m = packed.c_struct()
+    _check(_lib.twell_l1_grad(ctypes.byref(m), ctypes.c_float(lam), _ptr(grad_val), _ptr(grad_dense),
+                              _stream(device)))
+    return grad_val, grad_dense
 
 
 def twell_pack(pre, tile: int, cap: int, ovf_cap: Optional[int] = None, dense: bool = True,

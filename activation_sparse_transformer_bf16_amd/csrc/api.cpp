@@ -245,6 +245,42 @@ twell_status twell_to_hybrid(const twell_matrix *packed, twell_hybrid *out, void
   return TWELL_OK;
 }
 
+size_t twell_l1_workspace_size(void) { return (size_t)L1_BLOCKS * sizeof(double); }
+
+twell_status twell_l1_norm(const twell_matrix *packed, double *out, void *workspace, size_t ws_bytes,
+                           void *stream) {
+  g_err[0] = 0;
+  twell_status st = check_matrix(packed, true);
+  if (st != TWELL_OK) return st;
+  if (out == nullptr) return fail(TWELL_ERR_INVALID_ARG, "null out");
+  if (packed->rows > 0 && packed->dense == nullptr)
+    return fail(TWELL_ERR_INVALID_ARG, "the TwELL matrix needs its dense backup rows (packed->dense)");
+  if (workspace == nullptr || ws_bytes < twell_l1_workspace_size())
+    return fail(TWELL_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", twell_l1_workspace_size(),
+                workspace ? ws_bytes : 0);
+  if (!aligned(out, 8) || !aligned(workspace, 8)) return fail(TWELL_ERR_UNSUPPORTED, "misaligned out/workspace");
+  L1Args la{to_dt(packed->dtype), packed->rows, packed->cols, packed->tile, packed->cap, packed->cnt, packed->val,
+            packed->n_ovf, packed->ovf_cap, packed->dense, static_cast<double *>(workspace), out, 0.0f, nullptr,
+            nullptr};
+  TW_TRY(l1_norm(la, static_cast<hipStream_t>(stream)), "L1 norm");
+  return TWELL_OK;
+}
+
+twell_status twell_l1_grad(const twell_matrix *packed, float lam, void *grad_val, void *grad_dense, void *stream) {
+  g_err[0] = 0;
+  twell_status st = check_matrix(packed, false);
+  if (st != TWELL_OK) return st;
+  if (packed->rows > 0 && grad_val == nullptr) return fail(TWELL_ERR_INVALID_ARG, "null grad_val");
+  if (grad_dense != nullptr && packed->dense == nullptr)
+    return fail(TWELL_ERR_INVALID_ARG, "grad_dense needs the TwELL matrix's dense backup rows");
+  if (!aligned(grad_val, dt_size(packed->dtype)) || !aligned(grad_dense, dt_size(packed->dtype)))
+    return fail(TWELL_ERR_UNSUPPORTED, "misaligned grad_val/grad_dense");
+  L1Args la{to_dt(packed->dtype), packed->rows, packed->cols, packed->tile, packed->cap, packed->cnt, packed->val,
+            packed->n_ovf, packed->ovf_cap, packed->dense, nullptr, nullptr, lam, grad_val, grad_dense};
+  TW_TRY(l1_grad(la, static_cast<hipStream_t>(stream)), "L1 gradient");
+  return TWELL_OK;
+}
+
 twell_status twell_overflow_scan(twell_matrix *packed, void *stream) {
   g_err[0] = 0;
   twell_status st = check_matrix(packed, false);

@@ -121,6 +121,26 @@ struct HybridArgs {
 };
 hipError_t twell_to_hybrid_launch(const HybridArgs &a, hipStream_t s);
 
+// L1 activation penalty from TwELL: ||h||_1 (float64, deterministic) and the
+// gradient lam * [h > 0] in the TwELL pattern.
+constexpr int L1_BLOCKS = 512;
+struct L1Args {
+  Dt dtype;
+  int T, F, tile, cap;
+  const uint16_t *cnt;
+  const void *val;
+  const int *n_ovf;
+  int ovf_cap;
+  const void *dense;   // [ovf_cap][F] ReLU'd overflow rows
+  double *partial;     // [L1_BLOCKS] workspace (norm)
+  double *out;         // [1] (norm)
+  float lam;           // (gradient)
+  void *grad_val;      // [T][F/tile][cap] (gradient)
+  void *grad_dense;    // [ovf_cap][F] or null (gradient)
+};
+hipError_t l1_norm(const L1Args &a, hipStream_t s);
+hipError_t l1_grad(const L1Args &a, hipStream_t s);
+
 // *p = 0 with a one-thread kernel (safe under stream capture).
 hipError_t zero_int(int *p, hipStream_t s);
 

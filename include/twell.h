@@ -255,6 +255,38 @@ typedef struct {
  */
 twell_status twell_to_hybrid(const twell_matrix *packed, twell_hybrid *out, void *stream);
 
+/*
+ * The L1 activation penalty of the training recipe (gist.science "Sparser,
+ * Faster, Lighter Transformer Language Models", Resumen Técnico §2.B,
+ * training-strategy paragraph; §4: coefficient 2e-5), from TwELL without
+ * expanding the activations.  The pages do not fix the normalisation: the
+ * penalty is lam * ||h||_1 over all entries of h = ReLU(pre), any per-token
+ * or per-unit scaling folded into lam by the caller.
+ *
+ * twell_l1_norm: *out (device double) = ||h||_1, float64 sums in a fixed
+ * order (deterministic).  Reads the used slots of rows that did not overflow
+ * and the dense backup rows of those that did, so packed->dense must be
+ * non-NULL and packed->ovf_cap >= packed->rows.  workspace: device buffer of
+ * at least twell_l1_workspace_size() bytes, 8-byte aligned.
+ * Errors: INVALID_ARG, UNSUPPORTED (alignment), WORKSPACE, HIP.
+ */
+size_t twell_l1_workspace_size(void);
+twell_status twell_l1_norm(const twell_matrix *packed, double *out, void *workspace, size_t ws_bytes,
+                           void *stream);
+
+/*
+ * twell_l1_grad: d(lam ||h||_1)/dh in the TwELL matrix's own pattern (the
+ * subgradient 0 taken at h = 0): grad_val [rows][cols/tile][cap] (dtype)
+ * receives lam rounded to the storage dtype in every used slot and +0 in the
+ * padding; grad_dense [ovf_cap][cols] (dtype), when non-NULL, receives lam at
+ * the active entries of the dense backup rows (r < min(n_ovf, ovf_cap)) and
+ * +0 elsewhere.  With cnt, idx, ovf_rows and n_ovf of packed these buffers
+ * form the gradient as a TwELL matrix.
+ * Errors: INVALID_ARG, UNSUPPORTED (alignment), HIP.
+ */
+twell_status twell_l1_grad(const twell_matrix *packed, float lam, void *grad_val, void *grad_dense,
+                           void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -165,3 +165,18 @@ def test_to_hybrid_validation():
     assert H(ctypes.byref(m_nodense), ctypes.byref(_hybrid()), None) == twell.TWELL_ERR_INVALID_ARG
     m_short = _matrix(dense=FAKE, ovf_cap=4)
     assert H(ctypes.byref(m_short), ctypes.byref(_hybrid()), None) == twell.TWELL_ERR_INVALID_ARG
+
+
+def test_l1_validation():
+    assert twell.twell_l1_workspace_size() >= 8
+    m = _matrix(dense=FAKE)
+    N = L.twell_l1_norm
+    assert N(ctypes.byref(m), None, FAKE, 1 << 20, None) == twell.TWELL_ERR_INVALID_ARG
+    assert N(ctypes.byref(m), FAKE, FAKE, 8, None) == twell.TWELL_ERR_WORKSPACE
+    assert N(ctypes.byref(m), FAKE, None, 1 << 20, None) == twell.TWELL_ERR_WORKSPACE
+    assert N(ctypes.byref(m), FAKE + 4, FAKE, 1 << 20, None) == twell.TWELL_ERR_UNSUPPORTED
+    assert N(ctypes.byref(_matrix()), FAKE, FAKE, 1 << 20, None) == twell.TWELL_ERR_INVALID_ARG  # no dense rows
+    G = L.twell_l1_grad
+    assert G(ctypes.byref(m), ctypes.c_float(1.0), None, None, None) == twell.TWELL_ERR_INVALID_ARG
+    assert G(ctypes.byref(_matrix()), ctypes.c_float(1.0), FAKE, FAKE, None) == twell.TWELL_ERR_INVALID_ARG
+    assert G(ctypes.byref(m), ctypes.c_float(1.0), FAKE + 1, None, None) == twell.TWELL_ERR_UNSUPPORTED
