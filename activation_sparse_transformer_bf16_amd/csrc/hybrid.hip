@@ -6,7 +6,7 @@
 //   k_hybrid_rows:  one wave per row.  The row's TwELL counts give its true
 //                   entry count and whether it overflowed TwELL.  A row with
 //                   at most `width` entries becomes an ELL row: from its
-//                   TwELL slots (one lane per slot, positions from a prefix
+//                   TwELL slots (one lane per tile, positions from a prefix
 //                   count over the tiles), or, when it overflowed TwELL, by a
 //                   ballot compaction of its dense backup row.  Other rows get
 //                   all-padding ELL slots.
@@ -62,23 +62,19 @@ __global__ __launch_bounds__(64 * HY_WAVES) void k_hybrid_rows(
   const int n_ell = total <= width ? total : 0;  // ELL entries written below
   if (total <= width) {
     if (!tw_ovf) {
-      // one lane per TwELL slot, tiles in chunks of 64 / cap
+      // lanes take tiles (64 at a time); a lane copies its tile's entries to
+      // the row position given by a prefix count over the tiles
       int before = 0;  // entries of the tiles before the chunk
-      const int tiles_per_chunk = max(1, 64 / cap);
-      for (int kb = 0; kb < nt; kb += tiles_per_chunk) {
-        const int kt = min(tiles_per_chunk, nt - kb);
-        // per-tile counts of the chunk, prefix over them (lane = tile)
-        const int n = lane < kt ? (int)crow[kb + lane] : 0;
+      for (int kb = 0; kb < nt; kb += 64) {
+        const int k = kb + lane;
+        const int n = k < nt ? (int)crow[k] : 0;
         const int incl = wave_incl_scan(n);
-        for (int q0 = 0; q0 < kt * cap; q0 += 64) {
-          const int q = q0 + lane;
-          const int kq = q / cap, sq = q - kq * cap;
-          const int nq = __shfl(n, kq & 63, 64);
-          const int pos = before + __shfl(incl - n, kq & 63, 64) + sq;
-          if (q < kt * cap && sq < nq && pos < width) {
-            const size_t slot = ((size_t)t * nt + kb + kq) * cap + sq;
-            vrow[pos] = val[slot];
-            crow_out[pos] = (kb + kq) * tile + idx[slot];
+        const int pos0 = before + incl - n;
+        const size_t slot0 = ((size_t)t * nt + k) * cap;
+        for (int s = 0; s < n; ++s) {
+          if (pos0 + s < width) {
+            vrow[pos0 + s] = val[slot0 + s];
+            crow_out[pos0 + s] = k * tile + idx[slot0 + s];
           }
         }
         before += __builtin_amdgcn_readlane(incl, 63);
@@ -183,7 +179,7 @@ static hipError_t launch_hybrid(const HybridArgs &a, hipStream_t s) {
                      a.dense_cap, a.n_dense);
   e = hipGetLastError();
   if (e != hipSuccess || a.out_dense == nullptr || a.dense_cap == 0) return e;
-  const int grid = std::min(a.T, 1024);
+  const int grid = std::min(a.T, 256);
   hipLaunchKernelGGL(k_hybrid_dense<D>, dim3(grid), dim3(HY_DENSE_THREADS), 0, s, a.cnt, (const TT *)a.val, a.idx,
                      a.ovf_rows, a.n_ovf, a.ovf_cap, (const TT *)a.tw_dense, a.F, a.tile, a.cap, a.dense_rows,
                      a.n_dense, a.dense_cap, (TT *)a.out_dense);

@@ -5,9 +5,9 @@
 //
 //   k_l1_partial: ||h||_1 = sum of the used TwELL slots of rows that did not
 //                 overflow plus the dense backup rows of those that did; one
-//                 wave per row (lanes over slots), float64 sums, one partial
+//                 wave per row (lanes over tiles), float64 sums, one partial
 //                 per workgroup in a fixed order.
-//   k_l1_final:   the partials summed in index order (deterministic).
+//   k_l1_final:   the partials summed in a fixed order (deterministic).
 //   k_l1_grad:    d(lam ||h||_1)/dh in the TwELL matrix's own pattern: lam
 //                 (rounded to the storage dtype) in every used slot, 0 in the
 //                 padding, lam at the active entries of the dense backup rows.
@@ -24,6 +24,11 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
   return v;
 }
 
+// Rows of one wave: lanes take tiles (a chunk of 64 tiles at a time); a lane
+// adds the used slots of its tile.  Rows that overflowed are skipped here and
+// summed from the dense backup below.  Every sum runs in a fixed order: per
+// lane in slot order, across lanes in a fixed butterfly, across waves and
+// workgroups in index order.
 template <Dt D>
 __global__ __launch_bounds__(L1_THREADS) void k_l1_partial(const uint16_t *__restrict__ cnt,
                                                           const typename DtT<D>::T *__restrict__ val,
@@ -34,16 +39,18 @@ __global__ __launch_bounds__(L1_THREADS) void k_l1_partial(const uint16_t *__res
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nt = F / tile;
   double acc = 0.0;
-  // TwELL slots of the rows that did not overflow
   for (int t = blockIdx.x * L1_WAVES + wave; t < T; t += gridDim.x * L1_WAVES) {
     const uint16_t *crow = cnt + (size_t)t * nt;
     bool over = false;
-    for (int kb = 0; kb < nt; kb += 64) over |= (kb + lane < nt) && (int)crow[kb + lane] > cap;
-    if (ballot(over) != 0) continue;
-    for (int q = lane; q < nt * cap; q += 64) {
-      const int k = q / cap, s = q - k * cap;
-      if (s < (int)crow[k]) acc += (double)to_f32(val[(size_t)t * nt * cap + q]);
+    double row = 0.0;
+    for (int kb = 0; kb < nt; kb += 64) {
+      const int k = kb + lane;
+      const int c = k < nt ? (int)crow[k] : 0;
+      over |= c > cap;
+      const typename DtT<D>::T *v = val + ((size_t)t * nt + k) * cap;
+      for (int s = 0; s < min(c, cap); ++s) row += (double)to_f32(v[s]);
     }
+    if (ballot(over) == 0) acc += row;
   }
   // dense backup rows (ReLU'd, so every entry is >= 0)
   const int nd = min(*n_ovf, ovf_cap);
@@ -59,14 +66,17 @@ __global__ __launch_bounds__(L1_THREADS) void k_l1_partial(const uint16_t *__res
   }
 }
 
+// One wave: lane l adds partials l, l + 64, ... in order, then a fixed
+// butterfly across the lanes.
 __global__ void k_l1_final(const double *__restrict__ partial, int n, double *__restrict__ out) {
-  if (threadIdx.x == 0) {
-    double s = 0.0;
-    for (int i = 0; i < n; ++i) s += partial[i];
-    *out = s;
-  }
+  const int lane = threadIdx.x & 63;
+  double s = 0.0;
+  for (int i = lane; i < n; i += 64) s += partial[i];
+  s = wave_sum_f64(s);
+  if (lane == 0) *out = s;
 }
 
+// One thread per (row, tile): its cap slots get lam or +0.
 template <Dt D>
 __global__ __launch_bounds__(L1_THREADS) void k_l1_grad(const uint16_t *__restrict__ cnt,
                                                        const int *__restrict__ n_ovf, int ovf_cap,
@@ -77,12 +87,12 @@ __global__ __launch_bounds__(L1_THREADS) void k_l1_grad(const uint16_t *__restri
   using TT = typename DtT<D>::T;
   const TT g = from_f32<D>(lam);
   const int nt = F / tile;
-  const size_t n_slots = (size_t)T * nt * cap;
+  const size_t n_tiles = (size_t)T * nt;
   const size_t stride = (size_t)gridDim.x * L1_THREADS;
-  for (size_t q = (size_t)blockIdx.x * L1_THREADS + threadIdx.x; q < n_slots; q += stride) {
-    const size_t tk = q / cap;
-    const int s = (int)(q - tk * cap);
-    grad_val[q] = s < (int)cnt[tk] ? g : TT(0);
+  for (size_t tk = (size_t)blockIdx.x * L1_THREADS + threadIdx.x; tk < n_tiles; tk += stride) {
+    const int c = min((int)cnt[tk], cap);
+    TT *gv = grad_val + tk * cap;
+    for (int s = 0; s < cap; ++s) gv[s] = s < c ? g : TT(0);
   }
   if (grad_dense != nullptr) {
     const size_t n_dense = (size_t)min(*n_ovf, ovf_cap) * F;

@@ -36,6 +36,7 @@ METRIC = "sparse-FFN tokens/s at 99% sparsity; achieved HBM GB/s vs peak; speedu
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 MFMA_F32_PEAK_TFLOPS = 157.3
+HYBRID_WIDTH = 256           # ELL slots per row for the TwELL -> hybrid timing
 
 
 def log(*a):
@@ -190,6 +191,35 @@ def measure(w, steps, warmup, want_torch=True, want_cold=True, settle_ms=50.0):
         cold = {"sparse_ms": cold_time(sparse, 7, flush), "dense_ms": cold_time(dense, 7, flush)}
         del flush
 
+    # Training-format kernels on this batch's TwELL matrix (with its dense
+    # backup rows): TwELL -> hybrid at an ELL width of 256, the L1 norm and the
+    # L1 gradient.
+    packed_tr = tw.TwellMatrix.empty(T, F, w.tile, w.cap, x.dtype, dev, T, dense=True)
+    tw.twell_ffn_forward(x, wg, wu, wd, b, packed=packed_tr, y=y, workspace=ws)
+    hy = tw.TwellHybrid.empty(T, F, HYBRID_WIDTH, x.dtype, dev)
+    l1_out = torch.empty((1,), dtype=torch.float64, device=dev)
+    l1_ws = torch.empty((tw.twell_l1_workspace_size(),), dtype=torch.uint8, device=dev)
+    gval, gdense = torch.empty_like(packed_tr.val), torch.empty_like(packed_tr.dense)
+    ms_hybrid, _ = event_time(lambda: tw.twell_to_hybrid(packed_tr, HYBRID_WIDTH, out=hy), steps, warmup)
+    ms_l1, _ = event_time(lambda: tw.twell_l1_norm(packed_tr, out=l1_out, workspace=l1_ws), steps, warmup)
+    ms_l1g, _ = event_time(lambda: tw.twell_l1_grad(packed_tr, 2e-5, gval, gdense), steps, warmup)
+    torch.cuda.synchronize()
+    n_dense = int(hy.n_dense.item())
+    nnz_all = int(packed_tr.cnt.cpu().numpy().view(np.uint16).astype(np.int64).sum())
+    nt = F // w.tile
+    # bytes the conversion must move: counts and used slots read, ELL rows
+    # (values + int32 columns) and counts written, dense rows copied
+    hybrid_bytes = (T * nt * 2 + nnz_all * (s + 1) + T * 4 + T * HYBRID_WIDTH * (s + 4)
+                    + n_dense * F * s * 2)
+    training = {"hybrid_width": HYBRID_WIDTH, "n_dense": n_dense,
+                "to_hybrid_us": ms_hybrid * 1e3, "to_hybrid_GBps": hybrid_bytes / (ms_hybrid * 1e-3) / 1e9,
+                "l1_norm_us": ms_l1 * 1e3, "l1_grad_us": ms_l1g * 1e3,
+                "note": "TwELL -> hybrid conversion, ||h||_1 and its gradient on this batch; GBps over the "
+                        "bytes the conversion must move"}
+    log(f"[bench] training formats: to_hybrid {ms_hybrid * 1e3:.1f} us, l1 norm {ms_l1 * 1e3:.1f} us, "
+        f"l1 grad {ms_l1g * 1e3:.1f} us")
+    del packed_tr, hy, l1_out, l1_ws, gval, gdense
+
     # A plain device copy of known size (256 MiB read + 256 MiB written).  It
     # is not part of any measurement here; in rocprofv3 counter runs its
     # FETCH_SIZE / WRITE_SIZE readings calibrate the byte counters.
@@ -217,6 +247,7 @@ def measure(w, steps, warmup, want_torch=True, want_cold=True, settle_ms=50.0):
         "gate_tflops": flops_gate / (ms_gate * 1e-3) / 1e12, "peak": peak,
         "dense_tflops": 3 * flops_gate / (ms_dense * 1e-3) / 1e12,
         "gather_gbs": B_alg / (ms_rest * 1e-3) / 1e9,
+        "training": training,
     }
     del x, wg, wu, wd, b, packed, y, ws, yd, wsd
     torch.cuda.empty_cache()
@@ -357,6 +388,7 @@ def main():
                    "note": "up+down+fallback time within the forward sequence; bytes per active entry "
                            "= one W_u^T row + one W_d row"},
         "dense_mfma_tflops": r["dense_tflops"],
+        "training_formats": r["training"],
         "density": r["density"],
         "n_ovf": r["n_ovf"],
     }
