@@ -124,6 +124,11 @@ def cold_time(fn, reps, flush_buf):
     return times[len(times) // 2]
 
 
+def n_dense_rows_bytes(packed, F, s):
+    """Bytes of the dense backup rows a TwELL matrix holds."""
+    return min(int(packed.n_ovf.item()), packed.ovf_cap) * F * s
+
+
 def gather_bytes(T, d, F, tile, cap, s, nnz_kept, rows_sparse):
     """Algorithmic bytes of the up + down stages: one W_u^T row and one W_d row per
     active entry of the non-overflow rows, the x row read and y row written per
@@ -215,10 +220,24 @@ def measure(w, steps, warmup, want_torch=True, want_cold=True, settle_ms=50.0):
                 "to_hybrid_us": ms_hybrid * 1e3, "to_hybrid_GBps": hybrid_bytes / (ms_hybrid * 1e-3) / 1e9,
                 "l1_norm_us": ms_l1 * 1e3, "l1_grad_us": ms_l1g * 1e3,
                 "note": "TwELL -> hybrid conversion, ||h||_1 and its gradient on this batch; GBps over the "
-                        "bytes the conversion must move"}
+                        "bytes the conversion must move; twell_pack of the batch's rounded gate "
+                        "pre-activations (read T*F values, write the TwELL matrix)"}
     log(f"[bench] training formats: to_hybrid {ms_hybrid * 1e3:.1f} us, l1 norm {ms_l1 * 1e3:.1f} us, "
         f"l1 grad {ms_l1g * 1e3:.1f} us")
     del packed_tr, hy, l1_out, l1_ws, gval, gdense
+
+    # Standalone twell_pack of this batch's rounded gate pre-activations
+    # (dumped once by the gate kernel): HBM-bound, T*F*s bytes read plus the
+    # TwELL matrix written.
+    packed_p = tw.TwellMatrix.empty(T, F, w.tile, w.cap, x.dtype, dev, T, dense=True)
+    _, pre = tw.twell_gate_pack(x, wg, b, packed=packed_p, pre_out=True, scan=False)
+    ms_pack, _ = event_time(lambda: tw.twell_pack(pre, w.tile, w.cap, out=packed_p), steps, warmup)
+    pack_bytes = T * F * s + T * nt * (2 + w.cap * (s + 1)) + n_dense_rows_bytes(packed_p, F, s)
+    training["twell_pack_us"] = ms_pack * 1e3
+    training["twell_pack_GBps"] = pack_bytes / (ms_pack * 1e-3) / 1e9
+    training["twell_pack_frac_of_hbm_peak"] = pack_bytes / (ms_pack * 1e-3) / 1e9 / HBM_PEAK_GBS
+    log(f"[bench] twell_pack {ms_pack * 1e3:.1f} us ({training['twell_pack_GBps']:.0f} GB/s)")
+    del pre, packed_p
 
     # A plain device copy of known size (256 MiB read + 256 MiB written).  It
     # is not part of any measurement here; in rocprofv3 counter runs its
