@@ -30,11 +30,16 @@ What the oracle computes, and which passage each part follows:
 * ``penalty``: the L1 activation penalty ||h||_1 and its gradient, from
   TwELL: Resumen Técnico §2.B (training strategy: L1 regularisation of the ReLU activations)
   and §4 (coefficient 2e-5).
+* ``backward``: the gradients of the layer (dx, dW_g, dW_u, dW_d) with the
+  L1 penalty, from the stored activations in hybrid form: Resumen Técnico
+  §2.A (hybrid activations kept for back-propagation) and §2.B (training
+  kernels: hybrid-dense and dense-hybrid products, sparse transpose).
 * ``numerics``: exact decoding of the storage dtypes to float64 and
   round-to-nearest-even encoding to bf16.
 
 Every function here is pinned by ``-m "not gpu"`` tests against exact
-rational arithmetic, hand-worked examples, closed forms and invariants.
+rational arithmetic, hand-worked examples, closed forms, invariants, and for
+the backward pass automatic differentiation and finite differences.
 """
 
 from .numerics import decode, round_to_bf16, round_to_storage, storage_zero  # noqa: F401

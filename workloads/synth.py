@@ -146,3 +146,15 @@ def pre_activations(T: int, F: int, dtype: str, seed: int = 0, density: float = 
                               0xFF800000, 0x7FC00000, 0xFFC00001], dtype=np.uint32)
             bits[pos] = table[kind]
     return s
+
+
+def grad_output(T: int, d: int, dtype: str, seed: int = 0) -> np.ndarray:
+    """A seeded upstream gradient dy [T, d] (standard normals) in the storage dtype.
+
+    Drawn from its own stream (seed sequence [seed, 2]) so that it never
+    repeats the draws of ``ffn_inputs`` for the same seed.
+    """
+    if dtype not in DTYPES:
+        raise ValueError(f"unknown dtype {dtype!r}")
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 2])))
+    return to_storage(rng.standard_normal((T, d)), dtype)
