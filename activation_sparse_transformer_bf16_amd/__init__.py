@@ -75,6 +75,9 @@ def _load():
         "twell_l1_workspace_size": (Z, []),
         "twell_l1_norm": (I, [M, P, P, Z, P]),
         "twell_l1_grad": (I, [M, ctypes.c_float, P, P, P]),
+        "twell_ffn_backward_workspace_size": (Z, [I, I, I, I, I, I]),
+        "twell_ffn_backward": (I, [ctypes.POINTER(TwellHybridC), P, P, P, P, P, ctypes.c_float, I, P, P, P, P,
+                                   P, Z, P]),
     }
     # Private function objects: changing argtypes on the public handle (lib())
     # cannot make this binding pass truncated pointers.
@@ -100,7 +103,8 @@ EXPORTS = ("twell_abi_version", "twell_status_str", "twell_last_error", "twell_p
            "twell_ffn_workspace_size", "twell_ffn_forward", "twell_gate_pack", "twell_overflow_scan",
            "twell_sparse_ffn",
            "dense_ffn_workspace_size", "dense_ffn_forward", "twell_to_hybrid",
-           "twell_l1_workspace_size", "twell_l1_norm", "twell_l1_grad")
+           "twell_l1_workspace_size", "twell_l1_norm", "twell_l1_grad",
+           "twell_ffn_backward_workspace_size", "twell_ffn_backward")
 
 
 def lib():
@@ -280,6 +284,40 @@ def twell_l1_grad(packed: TwellMatrix, lam: float, grad_val=None, grad_dense=Non
     _check(_lib.twell_l1_grad(ctypes.byref(m), ctypes.c_float(lam), _ptr(grad_val), _ptr(grad_dense),
                               _stream(device)))
     return grad_val, grad_dense
+
+
+def twell_ffn_backward_workspace_size(T: int, d: int, F: int, width: int, dense_cap: int, dtype) -> int:
+    return int(_lib.twell_ffn_backward_workspace_size(T, d, F, width, dense_cap, _dtype_code(dtype)))
+
+
+def twell_ffn_backward(hy: TwellHybrid, x, w_gate, w_up, w_down, dy, lam: float = 0.0, dx=None, dw_gate=None,
+                       dw_up=None, dw_down=None, workspace=None):
+    """Gradients of the FFN layer from its hybrid activations: (dx, dw_gate, dw_up, dw_down);
+    dx in the activation dtype, the weight gradients fp32 [F, d]."""
+    torch = _torch()
+    device = x.device
+    T, d = x.shape
+    F = hy.cols
+    _need(x, "x", device, hy.dtype, (hy.rows, d))
+    _need(dy, "dy", device, hy.dtype, (T, d))
+    for w, name in ((w_gate, "w_gate"), (w_up, "w_up"), (w_down, "w_down")):
+        _need(w, name, device, hy.dtype, (F, d))
+    if dx is None:
+        dx = torch.empty((T, d), dtype=hy.dtype, device=device)
+    outs = []
+    for g, name in ((dw_gate, "dw_gate"), (dw_up, "dw_up"), (dw_down, "dw_down")):
+        if g is None:
+            g = torch.empty((F, d), dtype=torch.float32, device=device)
+        _need(g, name, device, torch.float32, (F, d))
+        outs.append(g)
+    _need(dx, "dx", device, hy.dtype, (T, d))
+    ws = _workspace(twell_ffn_backward_workspace_size(T, d, F, hy.width, hy.dense_cap, hy.dtype), device,
+                    workspace)
+    h = hy.c_struct()
+    _check(_lib.twell_ffn_backward(ctypes.byref(h), _ptr(x), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(dy),
+                                   ctypes.c_float(lam), d, _ptr(dx), _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]),
+                                   _ptr(ws), ws.numel(), _stream(device)))
+    return dx, outs[0], outs[1], outs[2]
 
 
 def twell_pack(pre, tile: int, cap: int, ovf_cap: Optional[int] = None, dense: bool = True,

@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cstring>
 
 #include "launch.hpp"
 #include "twell.h"
@@ -333,6 +334,107 @@ twell_status twell_ffn_forward(const void *x, const void *w_gate, const void *w_
               packed->cnt, packed->val, packed->idx, nullptr};
   TW_TRY(gate_twell(ga, s), "gate matmul");
   return run_sparse(packed, x, w_gate, w_up, w_down, gate_bias, y, d, workspace, s);
+}
+
+}  // extern "C"
+
+namespace {
+
+// The backward's gather kernels hold x_t and dy_t in registers (at most 8
+// 16-byte chunks per lane each) and cut d into 128-column slices; its
+// transpose keeps a 64-bit mask per hidden unit in LDS.
+constexpr int BW_MAX_F = 16384;
+
+twell_status check_backward_shape(int T, int d, int F, int width, int dense_cap, int dtype) {
+  if (!valid_dtype(dtype)) return fail(TWELL_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (T < 0 || F <= 0 || width < 1 || dense_cap < 0)
+    return fail(TWELL_ERR_INVALID_ARG, "need rows >= 0, cols > 0, width >= 1, dense_cap >= 0");
+  if (d <= 0) return fail(TWELL_ERR_INVALID_ARG, "d must be positive");
+  const int q = dtype == TWELL_BF16 ? 512 : 256;
+  if (d % q != 0 || d > 8 * q)
+    return fail(TWELL_ERR_UNSUPPORTED, "backward: d %d not built (multiple of %d, <= %d)", d, q, 8 * q);
+  if (F > BW_MAX_F) return fail(TWELL_ERR_UNSUPPORTED, "backward: cols %d not built (<= %d)", F, BW_MAX_F);
+  twell_status st = check_weight_bytes(F, d, dtype);
+  if (st != TWELL_OK) return st;
+  if ((size_t)T * d * dt_size((twell_dtype)dtype) >= ((size_t)1 << 31))
+    return fail(TWELL_ERR_UNSUPPORTED, "backward: x / dy of T*d = %zu elements are too large", (size_t)T * d);
+  if ((size_t)T * width + (size_t)dense_cap * F >= ((size_t)1 << 31))
+    return fail(TWELL_ERR_UNSUPPORTED, "backward: rows*width + dense_cap*cols must stay below 2^31 entries");
+  return TWELL_OK;
+}
+
+// Workspace of the backward: compacted dense rows | per-entry (du, dpre) |
+// per-entry column-major position | column-major records | per-block column
+// counts | their running offsets | column totals | column starts.
+struct BwWs {
+  size_t dcol, dn, ent, pos, csc, blk, boff, tot, colptr, total;
+};
+
+BwWs bw_ws_layout(int T, int F, int width, int dense_cap) {
+  BwWs w;
+  const size_t NE = (size_t)T * width + (size_t)dense_cap * F;
+  const size_t NB = ((size_t)T + 63) / 64;
+  w.dcol = 0;
+  w.dn = align_up(w.dcol + (size_t)dense_cap * F * 4, ALIGN_WS);
+  w.ent = align_up(w.dn + (size_t)dense_cap * 4, ALIGN_WS);
+  w.pos = align_up(w.ent + NE * 8, ALIGN_WS);
+  w.csc = align_up(w.pos + NE * 4, ALIGN_WS);
+  w.blk = align_up(w.csc + NE * 16, ALIGN_WS);
+  w.boff = align_up(w.blk + NB * F, ALIGN_WS);
+  w.tot = align_up(w.boff + NB * F * 4, ALIGN_WS);
+  w.colptr = align_up(w.tot + (size_t)F * 4, ALIGN_WS);
+  w.total = align_up(w.colptr + ((size_t)F + 1) * 4, ALIGN_WS);
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t twell_ffn_backward_workspace_size(int T, int d, int F, int width, int dense_cap, twell_dtype dtype) {
+  char saved[sizeof(g_err)];
+  memcpy(saved, g_err, sizeof(g_err));
+  const twell_status st = check_backward_shape(T, d, F, width, dense_cap, (int)dtype);
+  memcpy(g_err, saved, sizeof(g_err));
+  if (st != TWELL_OK) return 0;
+  return bw_ws_layout(T, F, width, dense_cap).total;
+}
+
+twell_status twell_ffn_backward(const twell_hybrid *h, const void *x, const void *w_gate, const void *w_up,
+                                const void *w_down, const void *dy, float lam, int d, void *dx, float *dw_gate,
+                                float *dw_up, float *dw_down, void *workspace, size_t ws_bytes, void *stream) {
+  g_err[0] = 0;
+  if (h == nullptr) return fail(TWELL_ERR_INVALID_ARG, "null twell_hybrid");
+  twell_status st = check_backward_shape(h->rows, d, h->cols, h->width, h->dense_cap, (int)h->dtype);
+  if (st != TWELL_OK) return st;
+  const int T = h->rows, F = h->cols;
+  if (h->n_dense == nullptr) return fail(TWELL_ERR_INVALID_ARG, "null n_dense");
+  if (T > 0 && (h->cnt == nullptr || h->val == nullptr || h->col == nullptr))
+    return fail(TWELL_ERR_INVALID_ARG, "null cnt/val/col");
+  if (h->dense_cap > 0 && (h->dense_rows == nullptr || h->dense == nullptr))
+    return fail(TWELL_ERR_INVALID_ARG, "dense_cap > 0 needs dense_rows and the dense backup rows");
+  if (!aligned(h->cnt, 4) || !aligned(h->val, dt_size(h->dtype)) || !aligned(h->col, 4) ||
+      !aligned(h->dense_rows, 4) || !aligned(h->n_dense, 4) || !aligned(h->dense, dt_size(h->dtype)))
+    return fail(TWELL_ERR_UNSUPPORTED, "misaligned twell_hybrid buffer");
+  if (!w_gate || !w_up || !w_down || !dw_gate || !dw_up || !dw_down)
+    return fail(TWELL_ERR_INVALID_ARG, "null weight or weight-gradient pointer");
+  if (T > 0 && (!x || !dy || !dx)) return fail(TWELL_ERR_INVALID_ARG, "null x/dy/dx");
+  if (!aligned(x, 16) || !aligned(dy, 16) || !aligned(dx, 16) || !aligned(w_gate, 16) || !aligned(w_up, 16) ||
+      !aligned(w_down, 16) || !aligned(dw_gate, 16) || !aligned(dw_up, 16) || !aligned(dw_down, 16))
+    return fail(TWELL_ERR_UNSUPPORTED, "x, dy, dx, weights and weight gradients must be 16-byte aligned");
+  const BwWs L = bw_ws_layout(T, F, h->width, h->dense_cap);
+  if (workspace == nullptr || ws_bytes < L.total)
+    return fail(TWELL_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total, workspace ? ws_bytes : 0);
+  if (!aligned(workspace, ALIGN_WS)) return fail(TWELL_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+  char *base = static_cast<char *>(workspace);
+  BackwardArgs ba{to_dt(h->dtype), T, d, F, h->width, h->cnt, h->val, h->col, h->dense_rows, h->n_dense,
+                  h->dense_cap, h->dense, x, dy, w_gate, w_up, w_down, lam, dx, dw_gate, dw_up, dw_down,
+                  reinterpret_cast<int *>(base + L.dcol), reinterpret_cast<int *>(base + L.dn), base + L.ent,
+                  reinterpret_cast<int *>(base + L.pos), base + L.csc, reinterpret_cast<uint8_t *>(base + L.blk),
+                  reinterpret_cast<int *>(base + L.boff), reinterpret_cast<int *>(base + L.tot),
+                  reinterpret_cast<int *>(base + L.colptr)};
+  TW_TRY(ffn_backward(ba, static_cast<hipStream_t>(stream)), "FFN backward");
+  return TWELL_OK;
 }
 
 size_t dense_ffn_workspace_size(int T, int d, int F, twell_dtype dtype) {

@@ -21,19 +21,6 @@ namespace twell {
 
 constexpr int HY_WAVES = 4;
 
-// Position of row t in the ascending list rows[0..n), or -1.
-__device__ __forceinline__ int find_row(const int *__restrict__ rows, int n, int t) {
-  int lo = 0, hi = n;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (rows[mid] < t)
-      lo = mid + 1;
-    else
-      hi = mid;
-  }
-  return (lo < n && rows[lo] == t) ? lo : -1;
-}
-
 template <Dt D>
 __global__ __launch_bounds__(64 * HY_WAVES) void k_hybrid_rows(
     const uint16_t *__restrict__ cnt, const typename DtT<D>::T *__restrict__ val, const uint8_t *__restrict__ idx,

@@ -141,6 +141,34 @@ struct L1Args {
 hipError_t l1_norm(const L1Args &a, hipStream_t s);
 hipError_t l1_grad(const L1Args &a, hipStream_t s);
 
+// FFN backward from hybrid activations: dx (activation dtype) and dW_g,
+// dW_u, dW_d (fp32, [F][d]).  Workspace pieces: dcol/dn (compacted dense
+// rows), ent (du, dpre per entry slot), pos (column-major place of each
+// entry), csc (column-major records t, a, du, dpre), blk/boff/tot/colptr
+// (the transpose's counts and offsets).
+struct BackwardArgs {
+  Dt dtype;
+  int T, d, F, width;
+  const int *cnt;
+  const void *val;
+  const int *col;
+  const int *dense_rows;
+  const int *n_dense;
+  int dense_cap;
+  const void *dense;
+  const void *x, *dy, *wg, *wu, *wd;
+  float lam;
+  void *dx;
+  float *dwg, *dwu, *dwd;
+  int *dcol, *dn;
+  void *ent;
+  int *pos;
+  void *csc;
+  uint8_t *blk;
+  int *boff, *tot, *colptr;
+};
+hipError_t ffn_backward(const BackwardArgs &a, hipStream_t s);
+
 // *p = 0 with a one-thread kernel (safe under stream capture).
 hipError_t zero_int(int *p, hipStream_t s);
 

@@ -287,6 +287,42 @@ twell_status twell_l1_norm(const twell_matrix *packed, double *out, void *worksp
 twell_status twell_l1_grad(const twell_matrix *packed, float lam, void *grad_val, void *grad_dense,
                            void *stream);
 
+/*
+ * twell_ffn_backward -- gradients of the ReLU-gated FFN layer from its
+ * activations in the hybrid format (gist.science "Sparser, Faster, Lighter
+ * Transformer Language Models", Resumen Técnico §2.A: the hybrid format keeps
+ * the activations needed for back-propagation; §2.B: training kernels for
+ * hybrid-times-dense and dense-times-hybrid products and the sparse
+ * transpose).  With the forward y = (h * (x W_u^T)) W_d, h = ReLU(x W_g^T +
+ * beta) as stored in `h`, the caller's upstream gradient dy and the L1 term
+ * lam * ||h||_1, for every active entry (t, j) of h (u = x_t . W_u[j]):
+ *     da = dy_t . W_d[j],   du = da * h,   dpre = da * u + lam
+ *     dx_t    = sum_j du W_u[j] + dpre W_g[j]
+ *     dW_u[j] = sum_t du x_t,  dW_g[j] = sum_t dpre x_t,  dW_d[j] = sum_t h u dy_t
+ * The stored h is used as it is (the forward's rounding passed through as the
+ * identity); ReLU's derivative is 1 on active entries and 0 elsewhere.  No
+ * gradient is formed for the gate bias.
+ *
+ * h:      the activations (rows T, cols F, width, dtype); every dense row must
+ *         be listed and stored: dense_cap >= *n_dense and dense non-NULL when
+ *         dense_cap > 0 (a dense row that is not stored contributes nothing).
+ * x, dy:  [T][d] dtype;  w_gate, w_up, w_down: [F][d] dtype (as the forward).
+ * dx:     [T][d] dtype, overwritten (one rounding of fp32 sums).
+ * dw_gate, dw_up, dw_down: [F][d] fp32, overwritten.
+ * workspace: >= twell_ffn_backward_workspace_size(T, d, F, width, dense_cap,
+ *         dtype) bytes, 256-byte aligned; about 28 bytes per entry slot, and
+ *         there are T*width + dense_cap*F entry slots.
+ * Sums run in a fixed order (deterministic); fp32 accumulation.
+ * Supported: bf16 d a multiple of 512 up to 4096, fp32 d a multiple of 256 up
+ * to 2048; F <= 16384; T*d and F*d elements below 2 GiB of storage;
+ * T*width + dense_cap*F < 2^31.
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP.
+ */
+size_t twell_ffn_backward_workspace_size(int T, int d, int F, int width, int dense_cap, twell_dtype dtype);
+twell_status twell_ffn_backward(const twell_hybrid *h, const void *x, const void *w_gate, const void *w_up,
+                                const void *w_down, const void *dy, float lam, int d, void *dx, float *dw_gate,
+                                float *dw_up, float *dw_down, void *workspace, size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

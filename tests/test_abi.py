@@ -180,3 +180,36 @@ def test_l1_validation():
     assert G(ctypes.byref(m), ctypes.c_float(1.0), None, None, None) == twell.TWELL_ERR_INVALID_ARG
     assert G(ctypes.byref(_matrix()), ctypes.c_float(1.0), FAKE, FAKE, None) == twell.TWELL_ERR_INVALID_ARG
     assert G(ctypes.byref(m), ctypes.c_float(1.0), FAKE + 1, None, None) == twell.TWELL_ERR_UNSUPPORTED
+
+
+def test_backward_validation_and_workspace():
+    import torch
+    ws = twell.twell_ffn_backward_workspace_size
+    n = ws(8192, 2048, 8192, 256, 8192, torch.bfloat16)
+    # per entry slot: (du, dpre) 8 B + position 4 B + column-major record 16 B
+    slots = 8192 * 256 + 8192 * 8192
+    assert n >= slots * 28 and n % 256 == 0
+    assert ws(8, 8192, 512, 16, 8, torch.bfloat16) == 0      # d above the backward's limit
+    assert ws(8, 4096, 512, 16, 8, torch.float32) == 0       # fp32 d above 2048
+    assert ws(8, 2048, 32768, 16, 8, torch.bfloat16) == 0    # F above 16384
+    assert ws(8, 2048, 512, 0, 8, torch.bfloat16) == 0       # width 0
+    assert ws(0, 512, 512, 16, 0, torch.bfloat16) > 0
+    B = L.twell_ffn_backward
+    h = _hybrid()
+
+    def call(hy, d=512, x=FAKE, dy=FAKE, dx=FAKE, dwg=FAKE, wsb=1 << 40):
+        return B(ctypes.byref(hy) if hy is not None else None, x, FAKE, FAKE, FAKE, dy, ctypes.c_float(0.0), d,
+                 dx, dwg, FAKE, FAKE, FAKE, wsb, None)
+
+    assert call(None) == twell.TWELL_ERR_INVALID_ARG
+    assert call(h, d=300) == twell.TWELL_ERR_UNSUPPORTED
+    assert call(h, d=8192) == twell.TWELL_ERR_UNSUPPORTED
+    assert call(_hybrid(width=0)) == twell.TWELL_ERR_INVALID_ARG
+    assert call(_hybrid(cols=20000)) == twell.TWELL_ERR_UNSUPPORTED
+    assert call(_hybrid(n_dense=None)) == twell.TWELL_ERR_INVALID_ARG
+    assert call(_hybrid(dense=None)) == twell.TWELL_ERR_INVALID_ARG        # dense_cap > 0 needs the rows
+    assert call(_hybrid(col=FAKE + 2)) == twell.TWELL_ERR_UNSUPPORTED
+    assert call(h, x=None) == twell.TWELL_ERR_INVALID_ARG
+    assert call(h, dwg=None) == twell.TWELL_ERR_INVALID_ARG
+    assert call(h, dx=FAKE + 8) == twell.TWELL_ERR_UNSUPPORTED
+    assert call(h, wsb=100) == twell.TWELL_ERR_WORKSPACE
