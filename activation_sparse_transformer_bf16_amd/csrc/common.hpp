@@ -112,19 +112,6 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
-// Position of row t in the ascending list rows[0..n), or -1.
-__device__ __forceinline__ int find_row(const int *__restrict__ rows, int n, int t) {
-  int lo = 0, hi = n;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (rows[mid] < t)
-      lo = mid + 1;
-    else
-      hi = mid;
-  }
-  return (lo < n && rows[lo] == t) ? lo : -1;
-}
-
 // Workgroups are dispatched round-robin over the 8 XCDs of an MI355X
 // (blockIdx.x % 8 is the XCD).  Remap a linear block id so that consecutive
 // remapped ids land on the same XCD, sharing its L2.  Identity when the grid

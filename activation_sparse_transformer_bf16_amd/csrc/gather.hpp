@@ -1,4 +1,5 @@
-// Pieces shared by the gather kernels (sparse forward and backward): XCD
+// Pieces shared by the gather kernels (sparse forward and backward) and the
+// format conversions: row lookup in an ascending list, XCD
 // placement of weight groups / column slices, raw buffer loads with a
 // wave-uniform row offset, 16-byte dot products and joint wave reductions.
 #pragma once
@@ -6,6 +7,19 @@
 #include "common.hpp"
 
 namespace twell {
+
+// Position of row t in the ascending list rows[0..n), or -1.
+__device__ __forceinline__ int find_row(const int *__restrict__ rows, int n, int t) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (rows[mid] < t)
+      lo = mid + 1;
+    else
+      hi = mid;
+  }
+  return (lo < n && rows[lo] == t) ? lo : -1;
+}
 
 constexpr int SP_THREADS = 256;
 constexpr int SP_WAVES = SP_THREADS / 64;

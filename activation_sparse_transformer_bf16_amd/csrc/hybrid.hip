@@ -13,6 +13,7 @@
 //   k_compact_gt:   ascending list of the rows with more than `width` entries.
 //   k_hybrid_dense: one workgroup per listed row: the dense backup row, copied
 //                   from TwELL's dense backup or scattered from the slots.
+#include "gather.hpp"
 #include "launch.hpp"
 
 #include <algorithm>

@@ -15,6 +15,9 @@ line on stdout:
   cpu_baseline the float64 CPU oracle timed on a bounded sample of the batch
   speedups     against the library's dense matrix-core FFN and against a
                torch (hipBLASLt) dense FFN on the same inputs
+  training_formats / backward
+               TwELL -> hybrid, the L1 penalty, a standalone pack, and the
+               backward pass from the hybrid activations, on the same batch
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload NAME]
                        [--no-cpu-baseline] [--sweep] [--sweep-out FILE]
@@ -37,6 +40,7 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 MFMA_F32_PEAK_TFLOPS = 157.3
 HYBRID_WIDTH = 256           # ELL slots per row for the TwELL -> hybrid timing
+L1_LAMBDA = 2e-5             # L1 coefficient of the training recipe
 
 
 def log(*a):
@@ -207,7 +211,7 @@ def measure(w, steps, warmup, want_torch=True, want_cold=True, settle_ms=50.0):
     gval, gdense = torch.empty_like(packed_tr.val), torch.empty_like(packed_tr.dense)
     ms_hybrid, _ = event_time(lambda: tw.twell_to_hybrid(packed_tr, HYBRID_WIDTH, out=hy), steps, warmup)
     ms_l1, _ = event_time(lambda: tw.twell_l1_norm(packed_tr, out=l1_out, workspace=l1_ws), steps, warmup)
-    ms_l1g, _ = event_time(lambda: tw.twell_l1_grad(packed_tr, 2e-5, gval, gdense), steps, warmup)
+    ms_l1g, _ = event_time(lambda: tw.twell_l1_grad(packed_tr, L1_LAMBDA, gval, gdense), steps, warmup)
     torch.cuda.synchronize()
     n_dense = int(hy.n_dense.item())
     nnz_all = int(packed_tr.cnt.cpu().numpy().view(np.uint16).astype(np.int64).sum())
@@ -224,7 +228,46 @@ def measure(w, steps, warmup, want_torch=True, want_cold=True, settle_ms=50.0):
                         "pre-activations (read T*F values, write the TwELL matrix)"}
     log(f"[bench] training formats: to_hybrid {ms_hybrid * 1e3:.1f} us, l1 norm {ms_l1 * 1e3:.1f} us, "
         f"l1 grad {ms_l1g * 1e3:.1f} us")
-    del packed_tr, hy, l1_out, l1_ws, gval, gdense
+    del l1_out, l1_ws, gval, gdense
+
+    # Backward from these hybrid activations (every dense row kept): dx and
+    # the three weight gradients with the L1 term, for a seeded dy.
+    from workloads.synth import grad_output
+    dy = to_dev(grad_output(T, d, w.dtype, seed=0), w.dtype, dev)
+    bw_ws = torch.empty((tw.twell_ffn_backward_workspace_size(T, d, F, HYBRID_WIDTH, hy.dense_cap, x.dtype),),
+                        dtype=torch.uint8, device=dev)
+    dxb = torch.empty_like(x)
+    dwb = [torch.empty((F, d), dtype=torch.float32, device=dev) for _ in range(3)]
+    bw = lambda: tw.twell_ffn_backward(hy, x, wg, wu, wd, dy, L1_LAMBDA, dxb, *dwb, workspace=bw_ws)
+    ms_bw, _ = event_time(bw, steps, warmup)
+    # gathered per active entry: W_u and W_d rows (entry gradients), W_u and
+    # W_g rows (dx), x and dy rows (weight gradients); plus the weight
+    # gradients written once and the x / dy / dx rows
+    bw_bytes = nnz_all * 6 * d * s + 3 * F * d * 4 + 3 * T * d * s
+    backward = {"us": ms_bw * 1e3, "tokens_per_s": T / (ms_bw * 1e-3), "hybrid_width": HYBRID_WIDTH,
+                "n_dense": n_dense, "entries": nnz_all, "bytes_alg": bw_bytes,
+                "achieved_GBps": bw_bytes / (ms_bw * 1e-3) / 1e9,
+                "frac_of_hbm_peak": bw_bytes / (ms_bw * 1e-3) / 1e9 / HBM_PEAK_GBS, "lam": L1_LAMBDA,
+                "note": "twell_ffn_backward: dx (activation dtype) and fp32 dW_g, dW_u, dW_d from the hybrid "
+                        "activations; bytes_alg = 6 rows of d per active entry + weight gradients + x, dy, dx"}
+    log(f"[bench] backward {ms_bw * 1e3:.1f} us ({backward['achieved_GBps']:.0f} GB/s algorithmic)")
+    if want_torch:
+        import torch.nn.functional as Fn
+        hd = torch.relu(torch.addmm(b[:, None].to(x.dtype), x, wg.t()))
+        ud = Fn.linear(x, wu)
+
+        def torch_backward():  # dense, with h and u saved by the forward (bf16 outputs)
+            da = dy @ wd.t()
+            du = da * hd
+            dp = (da * ud + L1_LAMBDA) * (hd > 0)
+            return du @ wu + dp @ wg, du.t() @ x, dp.t() @ x, (hd * ud).t() @ dy
+
+        ms_tbw, _ = event_time(torch_backward, steps, warmup)
+        backward["torch_dense_backward_us"] = ms_tbw * 1e3
+        backward["speedup_vs_torch_dense_backward"] = ms_tbw / ms_bw
+        log(f"[bench] torch (hipBLASLt) dense backward {ms_tbw * 1e3:.1f} us")
+        del hd, ud
+    del packed_tr, hy, dy, bw_ws, dxb, dwb
 
     # Standalone twell_pack of this batch's rounded gate pre-activations
     # (dumped once by the gate kernel): HBM-bound, T*F*s bytes read plus the
@@ -266,7 +309,7 @@ def measure(w, steps, warmup, want_torch=True, want_cold=True, settle_ms=50.0):
         "gate_tflops": flops_gate / (ms_gate * 1e-3) / 1e12, "peak": peak,
         "dense_tflops": 3 * flops_gate / (ms_dense * 1e-3) / 1e12,
         "gather_gbs": B_alg / (ms_rest * 1e-3) / 1e9,
-        "training": training,
+        "training": training, "backward": backward,
     }
     del x, wg, wu, wd, b, packed, y, ws, yd, wsd
     torch.cuda.empty_cache()
@@ -408,6 +451,7 @@ def main():
                            "= one W_u^T row + one W_d row"},
         "dense_mfma_tflops": r["dense_tflops"],
         "training_formats": r["training"],
+        "backward": r["backward"],
         "density": r["density"],
         "n_ovf": r["n_ovf"],
     }
