@@ -37,7 +37,8 @@ namespace twell {
 constexpr int BW_THREADS = 256;
 constexpr int BW_WAVES = BW_THREADS / 64;
 constexpr int BW_RB = 64;     // rows per block of the transpose (one bit each)
-constexpr int BW_SLICE = 128; // columns of d per dx / dW slice
+constexpr int DX_SLICE = 128; // columns of d per dx slice
+constexpr int DW_SLICE = 128; // columns of d per dW slice
 
 template <class TT>
 struct RowSrc {
@@ -321,20 +322,24 @@ __global__ __launch_bounds__(SP_THREADS) void k_bw_entries(RowSrc<typename DtT<D
 }
 
 // ---------------------------------------------------------------------------
-// dx and dW: one wave per (row or unit, BW_SLICE-column slice of d), slice s
+// dx and dW: one wave per (row or unit, column slice of d), slice s
 // on XCD s % 8.  Each lane loads 16 bytes per instruction, LPE lanes per
 // entry, EPI entries per instruction; the list goes through LDS 64 entries at
 // a time; the EPI partial sums are added at the end with lane swaps.
 
 template <int EPI>
 __device__ __forceinline__ float add_parts(float v) {
-  if constexpr (EPI >= 2) {
+  static_assert(EPI == 1 || EPI == 2 || EPI == 4 || EPI == 8, "1, 2, 4 or 8 entries per instruction");
+  if constexpr (EPI >= 2) {  // lanes l and l ^ 32
     auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
     v = __uint_as_float(p[0]) + __uint_as_float(p[1]);
   }
-  if constexpr (EPI == 4) {
+  if constexpr (EPI >= 4) {  // lanes l and l ^ 16
     auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
     v = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  }
+  if constexpr (EPI == 8) {  // lanes l and l ^ 8 (row_ror 8 inside a 16-lane row)
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
   }
   return v;
 }
@@ -365,7 +370,7 @@ __global__ __launch_bounds__(SP_THREADS) void k_bw_dx(RowSrc<typename DtT<D>::T>
                                                      int tok_per_wg, int n_tb) {
   using TT = typename DtT<D>::T;
   constexpr int CPL = 16 / sizeof(TT);
-  constexpr int LPE = BW_SLICE / CPL;
+  constexpr int LPE = DX_SLICE / CPL;
   constexpr int EPI = 64 / LPE;
   constexpr int STEP = U * EPI;
   static_assert(STEP <= 64 && 64 % STEP == 0, "a 64-entry chunk holds whole iterations");
@@ -375,7 +380,7 @@ __global__ __launch_bounds__(SP_THREADS) void k_bw_dx(RowSrc<typename DtT<D>::T>
   int sl, tb;
   group_coords(blockIdx.x, n_slices, n_tb, sl, tb);
   if (sl >= n_slices) return;
-  const __amdgpu_buffer_rsrc_t wur = buffer_rsrc(wu + sl * BW_SLICE), wgr = buffer_rsrc(wg + sl * BW_SLICE);
+  const __amdgpu_buffer_rsrc_t wur = buffer_rsrc(wu + sl * DX_SLICE), wgr = buffer_rsrc(wg + sl * DX_SLICE);
   const uint32_t lane_off = lcol * sizeof(TT);
   const uint32_t row_bytes = (uint32_t)d * sizeof(TT);
   u32x4_t *C = chunk[wave];
@@ -426,7 +431,7 @@ __global__ __launch_bounds__(SP_THREADS) void k_bw_dx(RowSrc<typename DtT<D>::T>
 #pragma unroll
       for (int v = 0; v < 4; ++v) out[v] = __float_as_uint(acc[v]);
     }
-    if (part == 0) *reinterpret_cast<u32x4_t *>(dx + (size_t)t * d + sl * BW_SLICE + lcol) = out;
+    if (part == 0) *reinterpret_cast<u32x4_t *>(dx + (size_t)t * d + sl * DX_SLICE + lcol) = out;
   }
 }
 
@@ -446,7 +451,7 @@ __global__ __launch_bounds__(SP_THREADS) void k_bw_dw(const int *__restrict__ co
                                                      int units_per_wg, int n_ub) {
   using TT = typename DtT<D>::T;
   constexpr int CPL = 16 / sizeof(TT);
-  constexpr int LPE = BW_SLICE / CPL;
+  constexpr int LPE = DW_SLICE / CPL;
   constexpr int EPI = 64 / LPE;
   constexpr int STEP = U * EPI;
   static_assert(STEP <= 64 && 64 % STEP == 0, "a 64-entry chunk holds whole iterations");
@@ -456,7 +461,7 @@ __global__ __launch_bounds__(SP_THREADS) void k_bw_dw(const int *__restrict__ co
   int sl, ub;
   group_coords(blockIdx.x, n_slices, n_ub, sl, ub);
   if (sl >= n_slices) return;
-  const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(x + sl * BW_SLICE), gr = buffer_rsrc(dy + sl * BW_SLICE);
+  const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(x + sl * DW_SLICE), gr = buffer_rsrc(dy + sl * DW_SLICE);
   const uint32_t lane_off = lcol * sizeof(TT);
   const uint32_t row_bytes = (uint32_t)d * sizeof(TT);
   u32x4_t *C = chunk[wave];
@@ -505,7 +510,7 @@ __global__ __launch_bounds__(SP_THREADS) void k_bw_dw(const int *__restrict__ co
       ad[v] = add_parts<EPI>(ad[v]);
     }
     if (part == 0) {
-      const size_t o = (size_t)j * d + sl * BW_SLICE + lcol;
+      const size_t o = (size_t)j * d + sl * DW_SLICE + lcol;
       store_f32<CPL>(dwg + o, ag);
       store_f32<CPL>(dwu + o, au);
       store_f32<CPL>(dwd + o, ad);
@@ -561,7 +566,7 @@ static hipError_t launch_backward(const BackwardArgs &a, hipStream_t st) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(k_bw_colptr, dim3(1), dim3(COLPTR_THREADS), 0, st, a.tot, a.F, a.colptr);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int n_slices = a.d / BW_SLICE;
+  const int n_slices = a.d / DX_SLICE, n_wslices = a.d / DW_SLICE;
   if (a.T > 0) {
     if ((e = hipFuncSetAttribute((const void *)k_bw_pos<TT>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                  mask_lds)) != hipSuccess)
@@ -587,11 +592,11 @@ static hipError_t launch_backward(const BackwardArgs &a, hipStream_t st) {
                        n_tb);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  const int upw = 16;
+  const int upw = 8;  // units per workgroup; 8 loads in flight per lane (fastest in a sweep)
   const int n_ub = (a.F + upw - 1) / upw;
-  hipLaunchKernelGGL((k_bw_dw<D, 4>), dim3(padded_groups(n_slices) * n_ub), dim3(SP_THREADS), 0, st, a.colptr,
+  hipLaunchKernelGGL((k_bw_dw<D, 8>), dim3(padded_groups(n_wslices) * n_ub), dim3(SP_THREADS), 0, st, a.colptr,
                      (const u32x4_t *)a.csc, (const TT *)a.x, (const TT *)a.dy, a.dwg, a.dwu, a.dwd, a.T, a.F, a.d,
-                     n_slices, upw, n_ub);
+                     n_wslices, upw, n_ub);
   return hipGetLastError();
 }
 
