@@ -69,6 +69,7 @@ def _load():
         "twell_gate_pack": (I, [P, P, P, I, M, P, P]),
         "twell_overflow_scan": (I, [M, P]),
         "twell_sparse_ffn": (I, [M, P, P, P, P, P, P, I, P, Z, P]),
+        "twell_sparse_ffn_fused": (I, [M, P, P, P, P, P, P, I, P, Z, P]),
         "dense_ffn_workspace_size": (Z, [I, I, I, I]),
         "dense_ffn_forward": (I, [P, P, P, P, P, P, I, I, I, I, P, Z, P]),
         "twell_to_hybrid": (I, [M, ctypes.POINTER(TwellHybridC), P]),
@@ -104,7 +105,7 @@ EXPORTS = ("twell_abi_version", "twell_status_str", "twell_last_error", "twell_p
            "twell_sparse_ffn",
            "dense_ffn_workspace_size", "dense_ffn_forward", "twell_to_hybrid",
            "twell_l1_workspace_size", "twell_l1_norm", "twell_l1_grad",
-           "twell_ffn_backward_workspace_size", "twell_ffn_backward")
+           "twell_ffn_backward_workspace_size", "twell_ffn_backward", "twell_sparse_ffn_fused")
 
 
 def lib():
@@ -421,6 +422,20 @@ def twell_sparse_ffn(packed: TwellMatrix, x, w_gate, w_up, w_down, gate_bias=Non
     _check(_lib.twell_sparse_ffn(ctypes.byref(m), _ptr(x), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
                                  _ptr(gate_bias), _ptr(y), d, _ptr(ws), ws.numel(),
                                  _stream(device)))
+    return y
+
+
+def twell_sparse_ffn_fused(packed: TwellMatrix, x, w_gate, w_up, w_down, gate_bias=None, y=None,
+                           workspace=None):
+    """twell_sparse_ffn with the up and down projections in one kernel; returns y."""
+    torch = _torch()
+    device, T, d, F = _ffn_checks(x, w_gate, w_up, w_down, gate_bias)
+    if y is None:
+        y = torch.empty((T, d), dtype=x.dtype, device=device)
+    ws = _workspace(twell_ffn_workspace_size(T, d, F, packed.tile, packed.cap, x.dtype), device, workspace)
+    m = packed.c_struct()
+    _check(_lib.twell_sparse_ffn_fused(ctypes.byref(m), _ptr(x), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+                                       _ptr(gate_bias), _ptr(y), d, _ptr(ws), ws.numel(), _stream(device)))
     return y
 
 

@@ -153,6 +153,25 @@ twell_status run_sparse(const twell_matrix *m, const void *x, const void *wg, co
   return TWELL_OK;
 }
 
+// The same sequence with the fused up+down kernel in place of the two gather
+// kernels (the compact lists are not used).
+twell_status run_sparse_fused(const twell_matrix *m, const void *x, const void *wg, const void *wu, const void *wd,
+                              const float *beta, void *y, int d, void *ws, hipStream_t s) {
+  const int T = m->rows, F = m->cols;
+  const FfnWs L = ffn_ws_layout(T, F, m->tile, m->cap, m->dtype);
+  char *base = static_cast<char *>(ws);
+  uint8_t *row_flag = reinterpret_cast<uint8_t *>(base + L.flag);
+  void *a_ws = base + L.a;
+  const Dt D = to_dt(m->dtype);
+  SparseArgs sa{D, T, d, F, m->tile, m->cap, m->cnt, m->val, m->idx, row_flag, x, wu, wd, nullptr, nullptr, 0, y};
+  TW_TRY(sparse_fused(sa, s), "fused sparse up/down projection");
+  TW_TRY(compact_rows(row_flag, T, m->ovf_rows, m->ovf_cap, m->n_ovf, s), "overflow row list");
+  DenseArgs da{D, x, wg, wu, wd, beta, y, T, d, F, m->ovf_rows, m->n_ovf, a_ws, m->dense, m->ovf_cap};
+  TW_TRY(dense_gate_up(da, s), "fallback gate/up matmul");
+  TW_TRY(dense_down(da, s), "fallback down matmul");
+  return TWELL_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -311,6 +330,26 @@ twell_status twell_sparse_ffn(const twell_matrix *packed, const void *x, const v
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (packed->rows == 0) return hip_check(zero_int(packed->n_ovf, s), "zero n_ovf");
   return run_sparse(packed, x, w_gate, w_up, w_down, gate_bias, y, d, workspace, s);
+}
+
+twell_status twell_sparse_ffn_fused(const twell_matrix *packed, const void *x, const void *w_gate, const void *w_up,
+                                    const void *w_down, const float *gate_bias, void *y, int d, void *workspace,
+                                    size_t ws_bytes, void *stream) {
+  g_err[0] = 0;
+  twell_status st = check_matrix(packed, true);
+  if (st != TWELL_OK) return st;
+  if ((st = check_d(d, (int)packed->dtype)) != TWELL_OK) return st;
+  const int q = packed->dtype == TWELL_BF16 ? 512 : 256;
+  if (d > 8 * q) return fail(TWELL_ERR_UNSUPPORTED, "fused kernel: d %d not built (<= %d)", d, 8 * q);
+  if ((st = check_weight_bytes(packed->cols, d, (int)packed->dtype)) != TWELL_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (packed->rows == 0) return hip_check(zero_int(packed->n_ovf, s), "zero n_ovf");
+  if ((st = check_ffn_ptrs(x, w_gate, w_up, w_down, gate_bias, y)) != TWELL_OK) return st;
+  const size_t need = ffn_ws_layout(packed->rows, packed->cols, packed->tile, packed->cap, packed->dtype).total;
+  if (workspace == nullptr || ws_bytes < need)
+    return fail(TWELL_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : 0);
+  if (!aligned(workspace, ALIGN_WS)) return fail(TWELL_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+  return run_sparse_fused(packed, x, w_gate, w_up, w_down, gate_bias, y, d, workspace, s);
 }
 
 twell_status twell_ffn_forward(const void *x, const void *w_gate, const void *w_up, const void *w_down,

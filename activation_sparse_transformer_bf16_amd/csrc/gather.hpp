@@ -122,6 +122,18 @@ struct Reduce<4> {
   }
 };
 template <>
+struct Reduce<1> {
+  __device__ __forceinline__ static int entry(int) { return 0; }
+  __device__ __forceinline__ static float run(const float (&p)[1]) {
+    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[0]), __float_as_uint(p[0]), false, false);
+    const float s = __uint_as_float(a[0]) + __uint_as_float(a[1]);  // halves added
+    auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+    float v = __uint_as_float(c[0]) + __uint_as_float(c[1]);  // every row: the whole wave
+    TWELL_ROW_SUM_DPP(v);
+    return v;
+  }
+};
+template <>
 struct Reduce<2> {
   __device__ __forceinline__ static int entry(int row) { return row >> 1; }
   __device__ __forceinline__ static float run(const float (&p)[2]) {

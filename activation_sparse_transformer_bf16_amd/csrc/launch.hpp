@@ -55,6 +55,9 @@ struct SparseArgs {
 };
 hipError_t sparse_up(const SparseArgs &a, hipStream_t s);
 hipError_t sparse_down(const SparseArgs &a, hipStream_t s);
+// Up and down in one kernel (one wave per token); writes row_flag and the y
+// rows of non-overflow tokens; list / list_n / stride are not used.
+hipError_t sparse_fused(const SparseArgs &a, hipStream_t s);
 
 // Dense ReGLU FFN on the matrix cores over a (possibly gathered) set of rows:
 // logical row r < n_rows reads x[rows ? rows[r] : r] and writes y at the same

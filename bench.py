@@ -182,6 +182,13 @@ def measure(w, steps, warmup, want_torch=True, want_cold=True, settle_ms=50.0):
     ms_sparse, wall = event_time(sparse, steps, warmup)
     log(f"[bench] sparse forward: {ms_sparse * 1e3:.1f} us/step ({wall:.2f}s wall for {steps} steps)")
 
+    # The fused up+down kernel (one wave per token, both gathers in one flow)
+    # in place of the two XCD-placed gather kernels, same gate and fallback.
+    fused_rest = lambda: tw.twell_sparse_ffn_fused(packed, x, wg, wu, wd, b, y=y, workspace=ws)
+    _, ms_fused_rest = split_time(gate, fused_rest, steps, warmup)
+    ms_fused, _ = event_time(lambda: (gate(), fused_rest()), steps, warmup)
+    log(f"[bench] fused up+down: {ms_fused_rest * 1e3:.1f} us in sequence, forward {ms_fused * 1e3:.1f} us")
+
     ms_torch = None
     if want_torch:
         import torch.nn.functional as Fn
@@ -310,6 +317,10 @@ def measure(w, steps, warmup, want_torch=True, want_cold=True, settle_ms=50.0):
         "dense_tflops": 3 * flops_gate / (ms_dense * 1e-3) / 1e12,
         "gather_gbs": B_alg / (ms_rest * 1e-3) / 1e9,
         "training": training, "backward": backward,
+        "fused": {"forward_us": ms_fused * 1e3, "up_down_fallback_us": ms_fused_rest * 1e3,
+                  "two_kernel_up_down_fallback_us": ms_rest * 1e3,
+                  "note": "gate then twell_sparse_ffn_fused (up and down in one kernel, one wave per token); "
+                          "the headline uses the two XCD-placed gather kernels"},
     }
     del x, wg, wu, wd, b, packed, y, ws, yd, wsd
     torch.cuda.empty_cache()
@@ -452,6 +463,7 @@ def main():
         "dense_mfma_tflops": r["dense_tflops"],
         "training_formats": r["training"],
         "backward": r["backward"],
+        "fused_up_down": r["fused"],
         "density": r["density"],
         "n_ovf": r["n_ovf"],
     }

@@ -288,6 +288,22 @@ twell_status twell_l1_grad(const twell_matrix *packed, float lam, void *grad_val
                            void *stream);
 
 /*
+ * twell_sparse_ffn_fused -- twell_sparse_ffn with the up and down projections
+ * in ONE kernel: the single fused inference kernel of gist.science "Sparser,
+ * Faster, Lighter Transformer Language Models", Resumen Técnico §2.B (up and
+ * down from the TwELL gate activations in one flow, intermediates in
+ * registers).  One wave per token computes v = h * (x_t . W_u^T[j]) for each
+ * of its entries and adds v * W_d[j] to y_t in registers; overflow rows take
+ * the dense fallback as in twell_sparse_ffn.  Same arguments, workspace
+ * (twell_ffn_workspace_size) and results (within the same tolerance; the sum
+ * order differs) as twell_sparse_ffn; d limited to 4096 (bf16) / 2048 (fp32).
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP.
+ */
+twell_status twell_sparse_ffn_fused(const twell_matrix *packed, const void *x, const void *w_gate, const void *w_up,
+                                    const void *w_down, const float *gate_bias, void *y, int d, void *workspace,
+                                    size_t ws_bytes, void *stream);
+
+/*
  * twell_ffn_backward -- gradients of the ReLU-gated FFN layer from its
  * activations in the hybrid format (gist.science "Sparser, Faster, Lighter
  * Transformer Language Models", Resumen Técnico §2.A: the hybrid format keeps

@@ -119,3 +119,36 @@ def test_zero_tokens():
     y, p = tw.twell_ffn_forward(x, w, w, w, None)
     assert y.shape == (0, 512) and int(p.n_ovf.item()) == 0
     assert tw.dense_ffn_forward(x, w, w, w, None).shape == (0, 512)
+
+
+FUSED_SMALL = [c for c in SMALL if c[2] <= (4096 if c[0] == "bf16" else 2048)]
+
+
+@pytest.mark.parametrize("dtype,T,d,F,tile,cap,bias", FUSED_SMALL)
+def test_fused_up_down(dtype, T, d, F, tile, cap, bias):
+    """twell_sparse_ffn_fused (up and down in one kernel) after the gate: y
+    against the oracle, every row, and the overflow rows listed as by the
+    two-kernel route."""
+    print(f"fused {dtype} T={T} d={d} F={F} tile={tile} cap={cap} bias={bias if np.isscalar(bias) else 'hot'}",
+          flush=True)
+    inp = ffn_inputs(T, d, F, dtype, seed=T + 1, gate_bias=_bias(bias, T))
+    x, wg, wu, wd, b = dev_inputs(inp)
+    p, _ = tw.twell_gate_pack(x, wg, b, tile=tile, cap=cap, scan=False)
+    y = tw.twell_sparse_ffn_fused(p, x, wg, wu, wd, b)
+    yh = from_dev(y, dtype)
+    check_y(yh, inp, dtype)
+    n_fused = int(p.n_ovf.item())
+    rows_fused = p.ovf_rows[:n_fused].cpu().numpy().copy()
+    tw.twell_sparse_ffn(p, x, wg, wu, wd, b)
+    assert int(p.n_ovf.item()) == n_fused
+    assert np.array_equal(p.ovf_rows[:n_fused].cpu().numpy(), rows_fused)
+
+
+def test_fused_rejects_wide_rows():
+    import torch
+    inp = ffn_inputs(4, 8192, 512, "bf16", seed=1, gate_bias=-1.0)
+    x, wg, wu, wd, b = dev_inputs(inp)
+    p, _ = tw.twell_gate_pack(x, wg, b, tile=256, cap=16, scan=False)
+    with pytest.raises(tw.TwellError):
+        tw.twell_sparse_ffn_fused(p, x, wg, wu, wd, b)
+    torch.cuda.synchronize()

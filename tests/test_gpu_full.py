@@ -53,3 +53,18 @@ def test_density_sweep_points(rho):
     x, wg, wu, wd, b = dev_inputs(inp)
     y, packed = tw.twell_ffn_forward(x, wg, wu, wd, b, tile=w.tile, cap=w.cap)
     check_y(from_dev(y, w.dtype), inp, w.dtype, rows=_rows(w.T))
+
+
+@pytest.mark.parametrize("name", ["layer_1p5b_bf16", "skewed_bf16", "large_bf16"])
+def test_full_size_fused_up_down(name):
+    """The fused up+down kernel at full size, as the benchmark times it (gate,
+    then twell_sparse_ffn_fused): y on sampled rows, dense-fallback rows of the
+    skewed workload included."""
+    w = CONFIGS[name]
+    print(f"full fused {name}", flush=True)
+    inp = w.inputs()
+    x, wg, wu, wd, b = dev_inputs(inp)
+    p, _ = tw.twell_gate_pack(x, wg, b, tile=w.tile, cap=w.cap, scan=False)
+    y = tw.twell_sparse_ffn_fused(p, x, wg, wu, wd, b)
+    hot = [t for t in range(w.T) if t % SEQ < 3]
+    check_y(from_dev(y, w.dtype), inp, w.dtype, rows=_rows(w.T, hot))
