@@ -166,18 +166,25 @@ __global__ __launch_bounds__(COLPTR_THREADS) void k_bw_colptr(const int *__restr
                                                              int *__restrict__ colptr) {
   __shared__ int wsum[COLPTR_THREADS / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int PER_MAX = 16;  // F <= 16384
   const int per = (F + COLPTR_THREADS - 1) / COLPTR_THREADS;
   const int j0 = min(F, tid * per), j1 = min(F, j0 + per);
+  int v[PER_MAX];
   int mine = 0;
-  for (int j = j0; j < j1; ++j) mine += tot[j];
+#pragma unroll
+  for (int q = 0; q < PER_MAX; ++q) {
+    v[q] = j0 + q < j1 ? tot[j0 + q] : 0;
+    mine += v[q];
+  }
   const int incl = wave_incl_scan(mine);
   if (lane == 63) wsum[wave] = incl;
   __syncthreads();
   int before = incl - mine;
   for (int w = 0; w < wave; ++w) before += wsum[w];
-  for (int j = j0; j < j1; ++j) {
-    colptr[j] = before;
-    before += tot[j];
+#pragma unroll
+  for (int q = 0; q < PER_MAX; ++q) {
+    if (j0 + q < j1) colptr[j0 + q] = before;
+    before += v[q];
   }
   if (tid == COLPTR_THREADS - 1) colptr[F] = before;
 }

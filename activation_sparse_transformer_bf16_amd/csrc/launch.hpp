@@ -126,7 +126,7 @@ hipError_t twell_to_hybrid_launch(const HybridArgs &a, hipStream_t s);
 
 // L1 activation penalty from TwELL: ||h||_1 (float64, deterministic) and the
 // gradient lam * [h > 0] in the TwELL pattern.
-constexpr int L1_BLOCKS = 2048;
+constexpr int L1_BLOCKS = 1024;
 struct L1Args {
   Dt dtype;
   int T, F, tile, cap;

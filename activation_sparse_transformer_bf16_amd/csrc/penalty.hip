@@ -66,12 +66,22 @@ __global__ __launch_bounds__(L1_THREADS) void k_l1_partial(const uint16_t *__res
   }
 }
 
-// One wave: lane l adds partials l, l + 64, ... in order, then a fixed
-// butterfly across the lanes.
+// One wave: lane l adds partials l, l + 64, ... in order (loaded 8 at a time,
+// so the loads do not wait for each other), then a fixed butterfly across
+// the lanes.
 __global__ void k_l1_final(const double *__restrict__ partial, int n, double *__restrict__ out) {
   const int lane = threadIdx.x & 63;
   double s = 0.0;
-  for (int i = lane; i < n; i += 64) s += partial[i];
+  for (int i0 = 0; i0 < n; i0 += 8 * 64) {
+    double v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int i = i0 + q * 64 + lane;
+      v[q] = i < n ? partial[i] : 0.0;
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) s += v[q];
+  }
   s = wave_sum_f64(s);
   if (lane == 0) *out = s;
 }

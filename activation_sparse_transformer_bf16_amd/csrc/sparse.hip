@@ -44,6 +44,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_overflow_scan(const uint16_t *
       if (t < T) {
         const uint16_t *c = cnt + (size_t)t * nt;
         if (vec) {
+#pragma unroll 4
           for (int k = 0; k < nt; k += 8) {
             u32x4_t w = *reinterpret_cast<const u32x4_t *>(c + k);
 #pragma unroll
@@ -85,28 +86,44 @@ hipError_t overflow_scan(const ScanArgs &a, hipStream_t s) {
 }
 
 // Ascending list of the rows whose flag is set (flags written by the up
-// kernel); one workgroup, T bytes read.
+// kernel); one workgroup, T bytes read, 8 consecutive flags per thread per
+// round (thread order = row order).
 constexpr int COMPACT_THREADS = 1024;
+constexpr int COMPACT_PER = 8;
 __global__ __launch_bounds__(COMPACT_THREADS) void k_compact_rows(const uint8_t *__restrict__ row_flag, int T,
                                                                    int *__restrict__ ovf_rows, int ovf_cap,
                                                                    int *__restrict__ n_ovf) {
   __shared__ int wcount[COMPACT_THREADS / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int carry = 0;
-  for (int base = 0; base < T; base += COMPACT_THREADS) {
-    const int t = base + tid;
-    const bool f = t < T && row_flag[t] != 0;
-    const uint64_t m = ballot(f);
-    if (lane == 0) wcount[wave] = popc64(m);
+  for (int base = 0; base < T; base += COMPACT_THREADS * COMPACT_PER) {
+    const int t0 = base + tid * COMPACT_PER;
+    uint32_t f[COMPACT_PER];
+    if (t0 + COMPACT_PER <= T && (reinterpret_cast<uintptr_t>(row_flag + t0) & 7) == 0) {
+      const u32x2_t w = *reinterpret_cast<const u32x2_t *>(row_flag + t0);
+#pragma unroll
+      for (int q = 0; q < COMPACT_PER; ++q) f[q] = (w[q / 4] >> (8 * (q % 4))) & 0xFFu;
+    } else {
+#pragma unroll
+      for (int q = 0; q < COMPACT_PER; ++q) f[q] = t0 + q < T ? row_flag[t0 + q] : 0u;
+    }
+    int c = 0;
+#pragma unroll
+    for (int q = 0; q < COMPACT_PER; ++q) c += f[q] != 0;
+    const int incl = wave_incl_scan(c);
+    if (lane == 63) wcount[wave] = incl;
     __syncthreads();
-    int before = carry, total = 0;
+    int pos = carry + incl - c, total = 0;
     for (int w = 0; w < COMPACT_THREADS / 64; ++w) {
-      before += (w < wave) ? wcount[w] : 0;
+      pos += (w < wave) ? wcount[w] : 0;
       total += wcount[w];
     }
-    if (f) {
-      const int pos = before + mbcnt(m);
-      if (pos < ovf_cap) ovf_rows[pos] = t;
+#pragma unroll
+    for (int q = 0; q < COMPACT_PER; ++q) {
+      if (f[q] != 0) {
+        if (pos < ovf_cap) ovf_rows[pos] = t0 + q;
+        ++pos;
+      }
     }
     carry += total;
     __syncthreads();
