@@ -102,9 +102,10 @@ twell_status check_matrix(const twell_matrix *m, bool need_ovf_all) {
 }
 
 // Workspace of the sparse forward: row flags | compact entry lists (8 bytes per
-// entry) | entry counts | dense fallback activations.
+// entry) | entry counts | dense fallback activations | the fallback's split-K
+// partial tiles (64 MB).
 struct FfnWs {
-  size_t flag, list, list_n, a, total;
+  size_t flag, list, list_n, a, partial, total;
   int stride;
 };
 
@@ -116,7 +117,8 @@ FfnWs ffn_ws_layout(int T, int F, int tile, int cap, twell_dtype dt) {
   w.list = align_up((size_t)T, ALIGN_WS);
   w.list_n = align_up(w.list + (size_t)T * w.stride * 8, ALIGN_WS);
   w.a = align_up(w.list_n + (size_t)T * 4, ALIGN_WS);
-  w.total = std::max(align_up(w.a + (size_t)T * F * dt_size(dt), ALIGN_WS), ALIGN_WS);
+  w.partial = align_up(w.a + (size_t)T * F * dt_size(dt), ALIGN_WS);
+  w.total = std::max(align_up(w.partial + (T > 0 ? FALLBACK_PARTIAL_FLOATS * 4 : 0), ALIGN_WS), ALIGN_WS);
   return w;
 }
 
@@ -147,7 +149,8 @@ twell_status run_sparse(const twell_matrix *m, const void *x, const void *wg, co
   TW_TRY(sparse_down(sa, s), "sparse down projection");
   TW_TRY(compact_rows(row_flag, T, m->ovf_rows, m->ovf_cap, m->n_ovf, s), "overflow row list");
 
-  DenseArgs da{D, x, wg, wu, wd, beta, y, T, d, F, m->ovf_rows, m->n_ovf, a_ws, m->dense, m->ovf_cap};
+  DenseArgs da{D, x, wg, wu, wd, beta, y, T, d, F, m->ovf_rows, m->n_ovf, a_ws, m->dense, m->ovf_cap,
+               reinterpret_cast<float *>(base + L.partial)};
   TW_TRY(dense_gate_up(da, s), "fallback gate/up matmul");
   TW_TRY(dense_down(da, s), "fallback down matmul");
   return TWELL_OK;
@@ -166,7 +169,8 @@ twell_status run_sparse_fused(const twell_matrix *m, const void *x, const void *
   SparseArgs sa{D, T, d, F, m->tile, m->cap, m->cnt, m->val, m->idx, row_flag, x, wu, wd, nullptr, nullptr, 0, y};
   TW_TRY(sparse_fused(sa, s), "fused sparse up/down projection");
   TW_TRY(compact_rows(row_flag, T, m->ovf_rows, m->ovf_cap, m->n_ovf, s), "overflow row list");
-  DenseArgs da{D, x, wg, wu, wd, beta, y, T, d, F, m->ovf_rows, m->n_ovf, a_ws, m->dense, m->ovf_cap};
+  DenseArgs da{D, x, wg, wu, wd, beta, y, T, d, F, m->ovf_rows, m->n_ovf, a_ws, m->dense, m->ovf_cap,
+               reinterpret_cast<float *>(base + L.partial)};
   TW_TRY(dense_gate_up(da, s), "fallback gate/up matmul");
   TW_TRY(dense_down(da, s), "fallback down matmul");
   return TWELL_OK;

@@ -10,7 +10,11 @@
 //   k_down:    y = a W_d with W_d [F][d] read n-contiguous and transposed into
 //              the k-contiguous LDS layout of the mainloop.
 // Rows may be gathered through an index list whose length lives on the device;
-// workgroups past that length return before loading anything.
+// workgroups past that length return before loading anything.  For that
+// fallback, when the rows fill fewer output tiles than the grid has
+// workgroups, K is split into S ranges so that tiles * S work items keep the
+// grid busy: each item writes an fp32 partial tile, and a reduction kernel
+// adds the S partials in K order and applies the epilogue.
 #include "gemm.hpp"
 #include "launch.hpp"
 
@@ -18,33 +22,62 @@
 
 namespace twell {
 
+constexpr int FALLBACK_WGS = 256;       // grid of the fallback kernels
+constexpr int SPLIT_TILE = GEMM_BM * 256;  // floats of one partial tile (256 x 256)
+
+// K ranges per output tile for the fallback: enough to give every workgroup
+// of the grid a work item, at most smax and at most nk (K slabs).
+__device__ __forceinline__ int fallback_split(int tiles, int nk, int smax) {
+  const int s = min(min(FALLBACK_WGS / max(tiles, 1), smax), nk);
+  return max(s, 1);
+}
+constexpr int GATE_UP_SPLIT_MAX = 16;
+constexpr int DOWN_SPLIT_MAX = 32;
+
+// Partial tiles are stored in the accumulators' own order: register i of
+// block (bm, bn) of wave w is 64 consecutive floats, one per lane, so every
+// store is one contiguous 256-byte write.  These map a tile element
+// (row, col) to that position.
+// gate / up tiles (8 waves, 128 x 64 wave tiles, NWM = 4, NWN = 2):
+__device__ __forceinline__ int gate_up_part_index(int row, int col) {
+  const int w = (row >> 7) * 4 + (col >> 6), bm = (row & 127) >> 5, bn = (col & 63) >> 5;
+  const int rr = row & 31, i = 4 * (rr >> 3) + (rr & 3), lane = ((rr & 7) >> 2) * 32 + (col & 31);
+  return (((w * 4 + bm) * 2 + bn) * 16 + i) * 64 + lane;
+}
+// down tiles (4 waves of 64 rows, 2 x 8 blocks):
+__device__ __forceinline__ int down_part_index(int row, int col) {
+  const int w = row >> 6, bm = (row & 63) >> 5, bn = col >> 5;
+  const int rr = row & 31, i = 4 * (rr >> 3) + (rr & 3), lane = ((rr & 7) >> 2) * 32 + (col & 31);
+  return (((w * 2 + bm) * 8 + bn) * 16 + i) * 64 + lane;
+}
+
+// One 256-row x 128-unit tile (tm, tn) of the gate / up matmul over K slabs
+// [k0, k0 + nk).  part == null: the epilogue writes a (and h); otherwise the
+// raw fp32 accumulators go to the partial tile part[row][col] (no bias).
 template <Dt D>
 __device__ __forceinline__ void gate_up_tile(
-    int bid, const typename DtT<D>::T *__restrict__ x, const typename DtT<D>::T *__restrict__ wg,
-    const typename DtT<D>::T *__restrict__ wu, const float *__restrict__ beta, int M, int K, int F,
-    const int *__restrict__ rows, const int *__restrict__ n_rows_dev, typename DtT<D>::T *__restrict__ a_ws,
-    typename DtT<D>::T *__restrict__ h_out, int h_cap) {
+    int tm, int tn, int k0, int nk, float *__restrict__ part, const typename DtT<D>::T *__restrict__ x,
+    const typename DtT<D>::T *__restrict__ wg, const typename DtT<D>::T *__restrict__ wu,
+    const float *__restrict__ beta, int M, int K, int F, const int *__restrict__ rows, int n_eff,
+    typename DtT<D>::T *__restrict__ a_ws, typename DtT<D>::T *__restrict__ h_out, int h_cap) {
   using T = typename DtT<D>::T;
   constexpr int BN = 256, UNITS = 128;  // B tile: 128 hidden units, each as a W_g row and a W_u row
   using WT = WaveTile<BN>;
   constexpr int NWM = WT::NWM;
   static_assert(WT::NWN == 2, "a wave holds one gate block and one up block");
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  const int mt = (M + GEMM_BM - 1) / GEMM_BM, ntl = F / UNITS;
-  int tm, tn;
-  tile_coords(bid, mt, ntl, tm, tn);
   const int m0 = tm * GEMM_BM, n0 = tn * UNITS;
-  const int n_eff = n_rows_dev ? min(*n_rows_dev, M) : M;
   if (m0 >= n_eff) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int row0 = WT::row0(wave), col0 = WT::col0(wave);
   const size_t ldk = (size_t)K * sizeof(T);
   auto phys = [&](int r) { return rows ? rows[r] : r; };
 
+  const size_t koff = (size_t)k0 * SLAB;
   auto rowA = [&](int r) {
     const int lr = m0 + r;
     const int row = lr < n_eff ? phys(lr) : phys(0);
-    return reinterpret_cast<const char *>(x) + (size_t)row * ldk;
+    return reinterpret_cast<const char *>(x) + (size_t)row * ldk + koff;
   };
   // B row r: 64-row group g = r / 64 covers units n0 + 32g .. n0 + 32g + 31,
   // first as W_g rows, then as W_u rows, so the wave that owns columns
@@ -52,11 +85,11 @@ __device__ __forceinline__ void gate_up_tile(
   // same lane (accumulator blocks 0 and 1).
   auto rowB = [&](int r) {
     const T *w = (r & 32) ? wu : wg;
-    return reinterpret_cast<const char *>(w) + (size_t)(n0 + 32 * (r >> 6) + (r & 31)) * ldk;
+    return reinterpret_cast<const char *>(w) + (size_t)(n0 + 32 * (r >> 6) + (r & 31)) * ldk + koff;
   };
 
   auto rowv = [&](int r) -> const float * {
-    return beta != nullptr ? beta + phys(min(m0 + r, n_eff - 1)) : nullptr;
+    return beta != nullptr && part == nullptr ? beta + phys(min(m0 + r, n_eff - 1)) : nullptr;
   };
   auto init = [&](f32x16_t (&a)[NWM][2], const float *vals) {
 #pragma unroll
@@ -67,9 +100,19 @@ __device__ __forceinline__ void gate_up_tile(
     }
   };
   f32x16_t acc[NWM][2];
-  gemm_mainloop_dma<D, BN>(acc, rowA, rowB, rowv, init, (int)(ldk / SLAB), smem);
+  gemm_mainloop_dma<D, BN>(acc, rowA, rowB, rowv, init, nk, smem);
 
   const int col = lane & 31;
+  if (part != nullptr) {
+    float *q = part + (size_t)wave * (NWM * 2 * 16 * 64) + lane;
+#pragma unroll
+    for (int bm = 0; bm < NWM; ++bm)
+#pragma unroll
+      for (int bn = 0; bn < 2; ++bn)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) q[((bm * 2 + bn) * 16 + i) * 64] = acc[bm][bn][i];
+    return;
+  }
   int row_base = m0 + row0 + 4 * (lane >> 5);  // opaque: keep row math after the mainloop
   asm volatile("" : "+v"(row_base));
   const size_t j = (size_t)n0 + col0 / 2 + col;
@@ -88,19 +131,17 @@ __device__ __forceinline__ void gate_up_tile(
   }
 }
 
+// One 256 x 256 tile (tm, tn) of y = a W_d over K chunks [k0, k0 + nk) of
+// 128 bytes; part == null: y is written, otherwise the fp32 partial tile.
 template <Dt D>
 __device__ __forceinline__ void down_tile(
-    int bid, const typename DtT<D>::T *__restrict__ a_ws, const typename DtT<D>::T *__restrict__ wd, int M, int K,
-    int N, const int *__restrict__ rows, const int *__restrict__ n_rows_dev,
+    int tm, int tn, int k0, int nk, float *__restrict__ part, const typename DtT<D>::T *__restrict__ a_ws,
+    const typename DtT<D>::T *__restrict__ wd, int M, int K, int N, const int *__restrict__ rows, int n_eff,
     typename DtT<D>::T *__restrict__ y) {
   using T = typename DtT<D>::T;
   constexpr int BN = 256;
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  const int mt = (M + GEMM_BM - 1) / GEMM_BM, ntl = N / BN;
-  int tm, tn;
-  tile_coords(bid, mt, ntl, tm, tn);
   const int m0 = tm * GEMM_BM, n0 = tn * BN;
-  const int n_eff = n_rows_dev ? min(*n_rows_dev, M) : M;
   if (m0 >= n_eff) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const size_t ldk = (size_t)K * sizeof(T);
@@ -108,10 +149,12 @@ __device__ __forceinline__ void down_tile(
   KRowLoader<GEMM_BM> la;
   la.init(tid, [&](int r) {
     int lr = min(m0 + r, n_eff - 1);
-    return reinterpret_cast<const char *>(a_ws) + (size_t)lr * ldk;
+    return reinterpret_cast<const char *>(a_ws) + (size_t)lr * ldk + (size_t)k0 * KCHUNK_BYTES;
   });
   NColLoader<D, BN> lb;
-  lb.init(tid, wd, (size_t)N * sizeof(T), n0);
+  // chunk kt covers k rows [kt * KCHUNK_BYTES / s, ...) of W_d: start at chunk k0
+  lb.init(tid, reinterpret_cast<const char *>(wd) + (size_t)k0 * (KCHUNK_BYTES / sizeof(T)) * N * sizeof(T),
+          (size_t)N * sizeof(T), n0);
 
   f32x16_t acc[2][8];
 #pragma unroll
@@ -119,9 +162,19 @@ __device__ __forceinline__ void down_tile(
 #pragma unroll
     for (int bn = 0; bn < 8; ++bn) acc[bm][bn] = f32x16_t{};
 
-  gemm_mainloop<D, BN>(acc, la, lb, K / (KCHUNK_BYTES / (int)sizeof(T)), smem);
+  gemm_mainloop<D, BN>(acc, la, lb, nk, smem);
 
   const int col = lane & 31;
+  if (part != nullptr) {
+    float *q = part + (size_t)wave * (2 * 8 * 16 * 64) + lane;
+#pragma unroll
+    for (int bm = 0; bm < 2; ++bm)
+#pragma unroll
+      for (int bn = 0; bn < 8; ++bn)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) q[((bm * 8 + bn) * 16 + i) * 64] = acc[bm][bn][i];
+    return;
+  }
   int row_base = m0 + 64 * wave + 4 * (lane >> 5);  // opaque: keep row math after the mainloop
   asm volatile("" : "+v"(row_base));
 #pragma unroll
@@ -137,33 +190,127 @@ __device__ __forceinline__ void down_tile(
   }
 }
 
-// Each workgroup takes tiles bid, bid + gridDim.x, ...: the dense baseline
-// launches one workgroup per tile, the fallback (row count on the device) a
-// grid of at most FALLBACK_WGS, so that an empty fallback costs little.
-constexpr int FALLBACK_WGS = 256;
-
+// The dense baseline launches one workgroup per tile.  The fallback (row count
+// on the device) runs FALLBACK_WGS workgroups over the work items: every tile
+// whole when the rows fill the grid, else tiles x S K ranges into partials.
 template <Dt D>
 __global__ __launch_bounds__(DMA_THREADS) void k_gate_up(
     const typename DtT<D>::T *__restrict__ x, const typename DtT<D>::T *__restrict__ wg,
     const typename DtT<D>::T *__restrict__ wu, const float *__restrict__ beta, int M, int K, int F,
     const int *__restrict__ rows, const int *__restrict__ n_rows_dev, typename DtT<D>::T *__restrict__ a_ws,
-    typename DtT<D>::T *__restrict__ h_out, int h_cap) {
-  const int tiles = (M + GEMM_BM - 1) / GEMM_BM * (F / 128);
-  for (int bid = blockIdx.x; bid < tiles; bid += gridDim.x)
-    gate_up_tile<D>(bid, x, wg, wu, beta, M, K, F, rows, n_rows_dev, a_ws, h_out, h_cap);
+    typename DtT<D>::T *__restrict__ h_out, int h_cap, float *__restrict__ partial) {
+  using T = typename DtT<D>::T;
+  const int nk = (int)((size_t)K * sizeof(T) / SLAB);
+  const int mt = (M + GEMM_BM - 1) / GEMM_BM, ntl = F / 128;
+  if (n_rows_dev == nullptr) {
+    int tm, tn;
+    tile_coords(blockIdx.x, mt, ntl, tm, tn);
+    gate_up_tile<D>(tm, tn, 0, nk, nullptr, x, wg, wu, beta, M, K, F, rows, M, a_ws, h_out, h_cap);
+    return;
+  }
+  const int n_eff = min(*n_rows_dev, M);
+  const int tiles = (n_eff + GEMM_BM - 1) / GEMM_BM * ntl;
+  const int S = fallback_split(tiles, nk, GATE_UP_SPLIT_MAX);
+  for (int w = blockIdx.x; w < tiles * S; w += gridDim.x) {
+    const int tile = w / S, kc = w - tile * S;
+    const int k0 = kc * nk / S, k1 = (kc + 1) * nk / S;
+    gate_up_tile<D>(tile / ntl, tile % ntl, k0, k1 - k0, S > 1 ? partial + (size_t)w * SPLIT_TILE : nullptr, x,
+                    wg, wu, beta, M, K, F, rows, n_eff, a_ws, h_out, h_cap);
+  }
+}
+
+// The fallback's gate / up epilogue after a split: pre = (sum of the S
+// partials in K order) + beta, h = ReLU(round(pre)), a = round(h * u).
+template <Dt D>
+__global__ __launch_bounds__(256) void k_gate_up_reduce(const float *__restrict__ partial,
+                                                        const float *__restrict__ beta, int M, int K, int F,
+                                                        const int *__restrict__ rows,
+                                                        const int *__restrict__ n_rows_dev,
+                                                        typename DtT<D>::T *__restrict__ a_ws,
+                                                        typename DtT<D>::T *__restrict__ h_out, int h_cap) {
+  using T = typename DtT<D>::T;
+  const int nk = (int)((size_t)K * sizeof(T) / SLAB);
+  const int ntl = F / 128;
+  const int n_eff = min(*n_rows_dev, M);
+  const int tiles = (n_eff + GEMM_BM - 1) / GEMM_BM * ntl;
+  const int S = fallback_split(tiles, nk, GATE_UP_SPLIT_MAX);
+  if (S == 1) return;
+  const size_t total = (size_t)tiles * GEMM_BM * 128;
+  for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (size_t)gridDim.x * 256) {
+    const int tile = (int)(e / (GEMM_BM * 128));
+    const int rem = (int)(e - (size_t)tile * GEMM_BM * 128);
+    const int r = rem / 128, u = rem % 128;  // tile row, unit within the tile
+    const int lr = (tile / ntl) * GEMM_BM + r;
+    if (lr >= n_eff) continue;
+    const int gcol = 64 * (u >> 5) + (u & 31);  // gate column; the up column is gcol + 32
+    const float *p = partial + (size_t)tile * S * SPLIT_TILE;
+    const int ig = gate_up_part_index(r, gcol), iu = gate_up_part_index(r, gcol + 32);
+    float pre = 0.f, up = 0.f;
+    for (int kc = 0; kc < S; ++kc) {
+      pre += p[(size_t)kc * SPLIT_TILE + ig];
+      up += p[(size_t)kc * SPLIT_TILE + iu];
+    }
+    const int prow = rows ? rows[lr] : lr;
+    if (beta != nullptr) pre += beta[prow];
+    const T hb = from_f32<D>(pre);
+    const bool act = active_bits(hb);
+    const float h = act ? to_f32(hb) : 0.0f;
+    const size_t j = (size_t)(tile % ntl) * 128 + u;
+    a_ws[(size_t)lr * F + j] = from_f32<D>(h * up);
+    if (h_out != nullptr && lr < h_cap) h_out[(size_t)lr * F + j] = act ? hb : T(0);
+  }
 }
 
 template <Dt D, bool LOOP>
 __global__ __launch_bounds__(GEMM_THREADS) void k_down(
     const typename DtT<D>::T *__restrict__ a_ws, const typename DtT<D>::T *__restrict__ wd, int M, int K,
     int N, const int *__restrict__ rows, const int *__restrict__ n_rows_dev,
-    typename DtT<D>::T *__restrict__ y) {
+    typename DtT<D>::T *__restrict__ y, float *__restrict__ partial) {
+  using T = typename DtT<D>::T;
+  const int nk = K / (KCHUNK_BYTES / (int)sizeof(T));
+  const int mt = (M + GEMM_BM - 1) / GEMM_BM, ntl = N / 256;
   if constexpr (LOOP) {
-    const int tiles = (M + GEMM_BM - 1) / GEMM_BM * (N / 256);
-    for (int bid = blockIdx.x; bid < tiles; bid += gridDim.x)
-      down_tile<D>(bid, a_ws, wd, M, K, N, rows, n_rows_dev, y);
+    const int n_eff = min(*n_rows_dev, M);
+    const int tiles = (n_eff + GEMM_BM - 1) / GEMM_BM * ntl;
+    const int S = fallback_split(tiles, nk, DOWN_SPLIT_MAX);
+    for (int w = blockIdx.x; w < tiles * S; w += gridDim.x) {
+      const int tile = w / S, kc = w - tile * S;
+      const int k0 = kc * nk / S, k1 = (kc + 1) * nk / S;
+      down_tile<D>(tile / ntl, tile % ntl, k0, k1 - k0, S > 1 ? partial + (size_t)w * SPLIT_TILE : nullptr,
+                   a_ws, wd, M, K, N, rows, n_eff, y);
+    }
   } else {
-    down_tile<D>(blockIdx.x, a_ws, wd, M, K, N, rows, n_rows_dev, y);
+    int tm, tn;
+    tile_coords(blockIdx.x, mt, ntl, tm, tn);
+    down_tile<D>(tm, tn, 0, nk, nullptr, a_ws, wd, M, K, N, rows, M, y);
+  }
+}
+
+// y rows of the fallback after a split: the S partials added in K order.
+template <Dt D>
+__global__ __launch_bounds__(256) void k_down_reduce(const float *__restrict__ partial, int M, int K, int N,
+                                                     const int *__restrict__ rows,
+                                                     const int *__restrict__ n_rows_dev,
+                                                     typename DtT<D>::T *__restrict__ y) {
+  using T = typename DtT<D>::T;
+  const int nk = K / (KCHUNK_BYTES / (int)sizeof(T));
+  const int ntl = N / 256;
+  const int n_eff = min(*n_rows_dev, M);
+  const int tiles = (n_eff + GEMM_BM - 1) / GEMM_BM * ntl;
+  const int S = fallback_split(tiles, nk, DOWN_SPLIT_MAX);
+  if (S == 1) return;
+  const size_t total = (size_t)tiles * SPLIT_TILE;
+  for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (size_t)gridDim.x * 256) {
+    const int tile = (int)(e / SPLIT_TILE);
+    const int rem = (int)(e - (size_t)tile * SPLIT_TILE);
+    const int r = rem / 256, c = rem % 256;
+    const int lr = (tile / ntl) * GEMM_BM + r;
+    if (lr >= n_eff) continue;
+    const float *p = partial + (size_t)tile * S * SPLIT_TILE + down_part_index(r, c);
+    float v = 0.f;
+    for (int kc = 0; kc < S; ++kc) v += p[(size_t)kc * SPLIT_TILE];
+    const size_t prow = rows ? (size_t)rows[lr] : (size_t)lr;
+    y[prow * N + (size_t)(tile % ntl) * 256 + c] = from_f32<D>(v);
   }
 }
 
@@ -175,10 +322,14 @@ static hipError_t launch_gate_up(const DenseArgs &a, hipStream_t s) {
   hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
   const int mt = (a.M + GEMM_BM - 1) / GEMM_BM, ntl = a.F / 128;
-  const int grid = a.n_rows_dev ? std::min(mt * ntl, FALLBACK_WGS) : mt * ntl;
+  const int grid = a.n_rows_dev ? FALLBACK_WGS : mt * ntl;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(DMA_THREADS), lds, s, (const T *)a.x, (const T *)a.wg,
                      (const T *)a.wu, a.beta, a.M, a.d, a.F, a.rows, a.n_rows_dev, (T *)a.a_ws,
-                     (T *)a.h_out, a.h_cap);
+                     (T *)a.h_out, a.h_cap, a.partial);
+  e = hipGetLastError();
+  if (e != hipSuccess || a.n_rows_dev == nullptr) return e;
+  hipLaunchKernelGGL(k_gate_up_reduce<D>, dim3(1024), dim3(256), 0, s, (const float *)a.partial, a.beta, a.M, a.d,
+                     a.F, a.rows, a.n_rows_dev, (T *)a.a_ws, (T *)a.h_out, a.h_cap);
   return hipGetLastError();
 }
 
@@ -190,9 +341,13 @@ static hipError_t launch_down(const DenseArgs &a, hipStream_t s) {
   hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
   const int mt = (a.M + GEMM_BM - 1) / GEMM_BM, ntl = a.d / 256;
-  const int grid = a.n_rows_dev ? std::min(mt * ntl, FALLBACK_WGS) : mt * ntl;
+  const int grid = a.n_rows_dev ? FALLBACK_WGS : mt * ntl;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(GEMM_THREADS), lds, s, (const T *)a.a_ws, (const T *)a.wd,
-                     a.M, a.F, a.d, a.rows, a.n_rows_dev, (T *)a.y);
+                     a.M, a.F, a.d, a.rows, a.n_rows_dev, (T *)a.y, a.partial);
+  e = hipGetLastError();
+  if (e != hipSuccess || a.n_rows_dev == nullptr) return e;
+  hipLaunchKernelGGL(k_down_reduce<D>, dim3(1024), dim3(256), 0, s, (const float *)a.partial, a.M, a.F, a.d,
+                     a.rows, a.n_rows_dev, (T *)a.y);
   return hipGetLastError();
 }
 

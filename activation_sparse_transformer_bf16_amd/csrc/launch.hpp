@@ -74,7 +74,11 @@ struct DenseArgs {
   void *a_ws;          // [M][F] storage dtype, logical rows
   void *h_out;         // [h_cap][F] storage dtype (ReLU'd gate rows) or null
   int h_cap;
+  float *partial;      // fallback only: FALLBACK_PARTIAL_FLOATS fp32 of split-K partial tiles
 };
+// Partial tiles of the fallback's split-K: at most one 256 x 256 fp32 tile per
+// workgroup of its grid (256).
+constexpr size_t FALLBACK_PARTIAL_FLOATS = (size_t)256 * 256 * 256;
 hipError_t dense_gate_up(const DenseArgs &a, hipStream_t s);
 hipError_t dense_down(const DenseArgs &a, hipStream_t s);
 
