@@ -159,7 +159,10 @@ size_t twell_ffn_workspace_size(int T, int d, int F, int tile, int cap, twell_dt
  * workspace: device buffer of at least twell_ffn_workspace_size() bytes,
  * 256-byte aligned; its contents on entry do not matter.  It holds one flag
  * byte per row, per row a list of up to F/tile*cap (weight-row offset, v)
- * pairs of 8 bytes, and the fallback's [T][F] activations.
+ * pairs of 8 bytes, the fallback's [T][F] activations, and 64 MB of fp32
+ * partial tiles for the fallback's split-K (used when the overflowing rows
+ * are too few to fill the GPU; their sums are taken in a fixed order, so y
+ * stays deterministic).
  * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP.
  */
 twell_status twell_ffn_forward(const void *x, const void *w_gate, const void *w_up,
