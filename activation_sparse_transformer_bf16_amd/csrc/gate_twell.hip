@@ -9,7 +9,8 @@
 // Resumen Técnico §2.A, carried over to gfx950: the N tile of the matmul is
 // exactly one TwELL tile, so every (row, tile) pair is owned by one workgroup;
 // the activity masks and the rounded tile are staged in the LDS the mainloop
-// no longer needs, and one lane per row compacts it in ascending column order.
+// no longer needs, and one lane per 32-column mask word of a row compacts it
+// in ascending column order.
 #include "gemm.hpp"
 #include "launch.hpp"
 

@@ -10,10 +10,12 @@
 //         registers) with the W_u^T row j, and writes (row offset of j,
 //         v = h * u in fp32) to row t's compact entry list.
 //   down: the d output columns are split into slices and slice s runs on
-//         XCD s % 8; per token one wave walks the token's entry list with
-//         scalar loads, accumulates v * W_d[j][slice] in fp32 registers and
-//         rounds y once.
-// Rows flagged by the overflow scan are left to the dense fallback.
+//         XCD s % 8; per token one wave copies the token's entry list to LDS
+//         64 entries at a time, accumulates v * W_d[j][slice] in fp32
+//         registers (two entries per load instruction for bf16) and rounds y
+//         once.
+// The up kernel also decides which rows overflow (a tile with more than cap
+// entries); those rows are left to the dense fallback.
 #include "gather.hpp"
 #include "launch.hpp"
 

@@ -332,11 +332,17 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_gate_twell.layer_1p5b_bf16.coun
 
 
 def gate_source_hash():
+    """Hash of the gate kernel's sources with comments and blank space removed
+    (a comment edit does not change the kernel the counters were taken on)."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in GATE_SOURCES:
-        with open(os.path.join(ROOT, "activation_sparse_transformer_bf16_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "activation_sparse_transformer_bf16_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
