@@ -328,16 +328,17 @@ def measure(w, steps, warmup, want_torch=True, want_cold=True, settle_ms=50.0):
 
 
 GATE_SOURCES = ("gate_twell.hip", "gemm.hpp", "common.hpp")
+SPARSE_SOURCES = ("sparse.hip", "gather.hpp", "common.hpp")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_gate_twell.layer_1p5b_bf16.counters.txt")
 
 
-def gate_source_hash():
-    """Hash of the gate kernel's sources with comments and blank space removed
-    (a comment edit does not change the kernel the counters were taken on)."""
+def gate_source_hash(files=GATE_SOURCES):
+    """Hash of a kernel's sources with comments and blank space removed (a
+    comment edit does not change the kernel the counters were taken on)."""
     import hashlib
     import re
     h = hashlib.sha256()
-    for f in GATE_SOURCES:
+    for f in files:
         with open(os.path.join(ROOT, "activation_sparse_transformer_bf16_amd", "csrc", f)) as fh:
             text = fh.read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -346,23 +347,40 @@ def gate_source_hash():
     return h.hexdigest()[:16]
 
 
-def counted_traffic(workload_name):
-    """HBM bytes per gate-kernel launch from the committed rocprofv3 counter
-    summary (FETCH_SIZE + WRITE_SIZE, each scaled by the reading of a plain
-    copy of known size); None when there is none for this workload or the
-    kernel sources changed since the counters were taken."""
+def _counter_summary(workload_name):
     if workload_name != "layer_1p5b_bf16" or not os.path.exists(TRAFFIC_FILE):
-        return None
+        return {}
     kv = {}
     with open(TRAFFIC_FILE) as f:
         for line in f:
             if "=" in line and not line.startswith("#"):
                 k, v = line.split("=", 1)
                 kv[k.strip()] = v.strip()
+    return kv
+
+
+def counted_traffic(workload_name):
+    """HBM bytes per gate-kernel launch from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, each scaled by the reading of a plain
+    copy of known size); None when there is none for this workload or the
+    kernel sources changed since the counters were taken."""
+    kv = _counter_summary(workload_name)
     if kv.get("source_hash") != gate_source_hash():
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def counted_gather_traffic(workload_name):
+    """The same counters for one sparse up + one sparse down launch (bytes
+    between L2 and the memory fabric; Infinity Cache hits included), or None."""
+    kv = _counter_summary(workload_name)
+    if kv.get("sparse_source_hash") != gate_source_hash(SPARSE_SOURCES):
+        return None
+    try:
+        return float(kv["sparse_hbm_bytes_per_call"])
     except (KeyError, ValueError):
         return None
 
@@ -418,6 +436,28 @@ def sweep(args):
             json.dump(out, f, indent=1)
 
 
+def gather_record(w, r):
+    """Byte rates of the two gather stages (up, down; fallback included in the time)."""
+    t = r["ms_rest"] * 1e-3
+    s = 2 if w.dtype == "bf16" else 4
+    # compulsory: every weight row of W_u and W_d once, x read, y written, TwELL read
+    compulsory = 2 * w.F * w.d * s + 2 * w.T * w.d * s + w.T * w.n_tiles * (2 + w.cap * (s + 1))
+    rec = {"bytes_alg": r["gather_bytes"], "achieved_GBps": r["gather_gbs"],
+           "frac_of_hbm_peak": r["gather_gbs"] / HBM_PEAK_GBS,
+           "compulsory_bytes": compulsory, "compulsory_frac_of_hbm_peak": compulsory / t / 1e9 / HBM_PEAK_GBS}
+    counted = counted_gather_traffic(w.name)
+    rec["counted_fabric_bytes"] = counted
+    if counted:
+        rec["counted_GBps"] = counted / t / 1e9
+        rec["counted_frac_of_hbm_peak"] = counted / t / 1e9 / HBM_PEAK_GBS
+        rec["reuse_factor"] = r["gather_bytes"] / counted
+    rec["note"] = ("up+down+fallback time within the forward sequence; bytes_alg per active entry = one W_u^T row "
+                   "+ one W_d row; compulsory = each weight row once + x, y and TwELL; counted = rocprofv3 "
+                   "FETCH_SIZE + WRITE_SIZE of one up and one down launch (L2 <-> fabric, Infinity Cache hits "
+                   "included), scaled by a plain copy")
+    return rec
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -462,10 +502,7 @@ def main():
                       "forward": r["ms_sparse"] * 1e3, "dense_ffn": r["ms_dense"] * 1e3,
                       "torch_dense_ffn": r["ms_torch"] * 1e3 if r["ms_torch"] else None},
         "cold_us": {k: v * 1e3 for k, v in r["cold"].items()},
-        "gather": {"bytes_alg": r["gather_bytes"], "achieved_GBps": r["gather_gbs"],
-                   "frac_of_hbm_peak": r["gather_gbs"] / HBM_PEAK_GBS,
-                   "note": "up+down+fallback time within the forward sequence; bytes per active entry "
-                           "= one W_u^T row + one W_d row"},
+        "gather": gather_record(w, r),
         "dense_mfma_tflops": r["dense_tflops"],
         "training_formats": r["training"],
         "backward": r["backward"],
