@@ -408,9 +408,9 @@ twell_status check_backward_shape(int T, int d, int F, int width, int dense_cap,
 
 // Workspace of the backward: compacted dense rows | per-entry (du, dpre) |
 // per-entry column-major position | column-major records | per-block column
-// counts | their running offsets | column totals | column starts.
+// counts | their running offsets | column totals | column starts | row order.
 struct BwWs {
-  size_t dcol, dn, ent, pos, csc, blk, boff, tot, colptr, total;
+  size_t dcol, dn, ent, pos, csc, blk, boff, tot, colptr, order, total;
 };
 
 BwWs bw_ws_layout(int T, int F, int width, int dense_cap) {
@@ -426,7 +426,8 @@ BwWs bw_ws_layout(int T, int F, int width, int dense_cap) {
   w.boff = align_up(w.blk + NB * F, ALIGN_WS);
   w.tot = align_up(w.boff + NB * F * 4, ALIGN_WS);
   w.colptr = align_up(w.tot + (size_t)F * 4, ALIGN_WS);
-  w.total = align_up(w.colptr + ((size_t)F + 1) * 4, ALIGN_WS);
+  w.order = align_up(w.colptr + ((size_t)F + 1) * 4, ALIGN_WS);
+  w.total = align_up(w.order + (size_t)T * 4, ALIGN_WS);
   return w;
 }
 
@@ -475,7 +476,7 @@ twell_status twell_ffn_backward(const twell_hybrid *h, const void *x, const void
                   reinterpret_cast<int *>(base + L.dcol), reinterpret_cast<int *>(base + L.dn), base + L.ent,
                   reinterpret_cast<int *>(base + L.pos), base + L.csc, reinterpret_cast<uint8_t *>(base + L.blk),
                   reinterpret_cast<int *>(base + L.boff), reinterpret_cast<int *>(base + L.tot),
-                  reinterpret_cast<int *>(base + L.colptr)};
+                  reinterpret_cast<int *>(base + L.colptr), reinterpret_cast<int *>(base + L.order)};
   TW_TRY(ffn_backward(ba, static_cast<hipStream_t>(stream)), "FFN backward");
   return TWELL_OK;
 }

@@ -15,7 +15,9 @@
 //   k_bw_count        per block of 64 rows, a 64-bit row mask per column in
 //                     LDS; writes the per-column entry counts of the block
 //   k_bw_colscan      per column, the running count over the blocks
-//   k_bw_colptr       column starts of the transposed (column-major) lists
+//   k_bw_colptr       column starts of the transposed (column-major) lists,
+//                     and the order in which the per-row kernels take the
+//                     rows: the long dense rows first
 //   k_bw_pos          each entry's place in its column's list: rows in
 //                     ascending order, from the same LDS row masks
 //   k_bw_entries      per (row, group of hidden units): u and da by gathering
@@ -162,8 +164,14 @@ __global__ __launch_bounds__(BW_THREADS) void k_bw_colscan(const uint8_t *__rest
 // colptr[j] = sum of tot[0..j), colptr[F] = the total; one workgroup, each
 // thread a contiguous run of columns.
 constexpr int COLPTR_THREADS = 1024;
+template <class TT>
+__device__ __forceinline__ void row_order(const RowSrc<TT> &s, int *__restrict__ order, int *wcount);
+
+// Also writes the row order of the per-row kernels (row_order, below).
+template <class TT>
 __global__ __launch_bounds__(COLPTR_THREADS) void k_bw_colptr(const int *__restrict__ tot, int F,
-                                                             int *__restrict__ colptr) {
+                                                             int *__restrict__ colptr, RowSrc<TT> s,
+                                                             int *__restrict__ order) {
   __shared__ int wsum[COLPTR_THREADS / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   constexpr int PER_MAX = 16;  // F <= 16384
@@ -187,6 +195,55 @@ __global__ __launch_bounds__(COLPTR_THREADS) void k_bw_colptr(const int *__restr
     before += v[q];
   }
   if (tid == COLPTR_THREADS - 1) colptr[F] = before;
+  if (order != nullptr) {
+    __syncthreads();
+    row_order(s, order, wsum);
+  }
+}
+
+// The order in which the per-row kernels take the rows: the stored dense rows
+// first (their lists are ~F * density long, the others ~width or less), then
+// every other row in ascending order, so that the long rows start early
+// instead of finishing last.  One workgroup; order[0..T) is a permutation.
+// (Runs in the column-starts kernel: one workgroup of COLPTR_THREADS.)
+template <class TT>
+__device__ __forceinline__ void row_order(const RowSrc<TT> &s, int *__restrict__ order, int *wcount) {
+  constexpr int ORDER_THREADS = COLPTR_THREADS;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nd = max(min(*s.n_dense, s.dense_cap), 0);
+  for (int i = tid; i < min(nd, s.T); i += ORDER_THREADS) order[i] = s.dense_rows[i];
+  constexpr int PER = 8;  // consecutive rows per thread per round
+  int carry = nd;
+  for (int base = 0; base < s.T; base += ORDER_THREADS * PER) {
+    const int t0 = base + tid * PER;
+    int c[PER];
+#pragma unroll
+    for (int q = 0; q < PER; ++q) c[q] = t0 + q < s.T ? s.cnt[t0 + q] : 0;
+    bool rest[PER];
+    int n = 0;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      rest[q] = t0 + q < s.T && (c[q] <= s.width || find_row(s.dense_rows, nd, t0 + q) < 0);
+      n += rest[q];
+    }
+    const int incl = wave_incl_scan(n);
+    if (lane == 63) wcount[wave] = incl;
+    __syncthreads();
+    int pos = carry + incl - n, total = 0;
+    for (int w = 0; w < ORDER_THREADS / 64; ++w) {
+      pos += (w < wave) ? wcount[w] : 0;
+      total += wcount[w];
+    }
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      if (rest[q]) {
+        if (pos < s.T) order[pos] = t0 + q;
+        ++pos;
+      }
+    }
+    carry += total;
+    __syncthreads();
+  }
 }
 
 // pos[slot] = colptr[j] + boff[b][j] + (rows of the block before t with an
@@ -245,7 +302,8 @@ __global__ __launch_bounds__(SP_THREADS) void k_bw_entries(RowSrc<typename DtT<D
                                                           const typename DtT<D>::T *__restrict__ wd, float lam,
                                                           int d, int upg, int n_groups, int tok_per_wg, int n_tb,
                                                           const int *__restrict__ pos, f32x2_t *__restrict__ ent,
-                                                          u32x4_t *__restrict__ csc) {
+                                                          u32x4_t *__restrict__ csc,
+                                                          const int *__restrict__ order) {
   using TT = typename DtT<D>::T;
   static_assert(U == 1 || U == 2, "one or two entries in flight");
   constexpr int EPC = 16 / sizeof(TT);
@@ -261,9 +319,12 @@ __global__ __launch_bounds__(SP_THREADS) void k_bw_entries(RowSrc<typename DtT<D
   const bool storer = U == 2 ? (lane & 31) == 0 : lane == 0;
   const int partner = U == 2 ? 16 : 32;
 
+  // the workgroup's rows, one per lane (tok_per_wg <= 64), read once
+  const int my_row = order[min(tb * tok_per_wg + min(lane, tok_per_wg - 1), s.T - 1)];
   for (int it = wave; it < tok_per_wg; it += SP_WAVES) {
-    const int t = tb * tok_per_wg + it;
-    if (t >= s.T) break;
+    const int ti = tb * tok_per_wg + it;
+    if (ti >= s.T) break;
+    const int t = min(max(__builtin_amdgcn_readlane(my_row, it), 0), s.T - 1);  // a valid hybrid gives a permutation
     const RowList L = row_list(s, t);
     if (L.n == 0) continue;
     const int eb = wave_lower_bound(L.col, L.n, j0);
@@ -374,7 +435,7 @@ __global__ __launch_bounds__(SP_THREADS) void k_bw_dx(RowSrc<typename DtT<D>::T>
                                                      const typename DtT<D>::T *__restrict__ wu,
                                                      const typename DtT<D>::T *__restrict__ wg,
                                                      typename DtT<D>::T *__restrict__ dx, int d, int n_slices,
-                                                     int tok_per_wg, int n_tb) {
+                                                     int tok_per_wg, int n_tb, const int *__restrict__ order) {
   using TT = typename DtT<D>::T;
   constexpr int CPL = 16 / sizeof(TT);
   constexpr int LPE = DX_SLICE / CPL;
@@ -391,9 +452,12 @@ __global__ __launch_bounds__(SP_THREADS) void k_bw_dx(RowSrc<typename DtT<D>::T>
   const uint32_t lane_off = lcol * sizeof(TT);
   const uint32_t row_bytes = (uint32_t)d * sizeof(TT);
   u32x4_t *C = chunk[wave];
+  // the workgroup's rows, one per lane (tok_per_wg <= 64), read once
+  const int my_row = order[min(tb * tok_per_wg + min(lane, tok_per_wg - 1), s.T - 1)];
   for (int it = wave; it < tok_per_wg; it += SP_WAVES) {
-    const int t = tb * tok_per_wg + it;
-    if (t >= s.T) break;
+    const int ti = tb * tok_per_wg + it;
+    if (ti >= s.T) break;
+    const int t = min(max(__builtin_amdgcn_readlane(my_row, it), 0), s.T - 1);  // a valid hybrid gives a permutation
     const RowList L = row_list(s, t);
     float acc[CPL];
 #pragma unroll
@@ -543,7 +607,7 @@ static hipError_t launch_entries(const BackwardArgs &a, const RowSrc<typename Dt
   const int n_tb = (a.T + tok - 1) / tok;
   hipLaunchKernelGGL((k_bw_entries<D, NC, U>), dim3(padded_groups(n_groups) * n_tb), dim3(SP_THREADS), 0, st, s,
                      (const TT *)a.x, (const TT *)a.dy, (const TT *)a.wu, (const TT *)a.wd, a.lam, a.d, upg,
-                     n_groups, tok, n_tb, a.pos, (f32x2_t *)a.ent, (u32x4_t *)a.csc);
+                     n_groups, tok, n_tb, a.pos, (f32x2_t *)a.ent, (u32x4_t *)a.csc, a.order);
   return hipGetLastError();
 }
 
@@ -571,7 +635,8 @@ static hipError_t launch_backward(const BackwardArgs &a, hipStream_t st) {
   hipLaunchKernelGGL(k_bw_colscan, dim3((a.F + BW_THREADS - 1) / BW_THREADS), dim3(BW_THREADS), 0, st, a.blk, NB,
                      a.F, a.boff, a.tot);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(k_bw_colptr, dim3(1), dim3(COLPTR_THREADS), 0, st, a.tot, a.F, a.colptr);
+  hipLaunchKernelGGL(k_bw_colptr<TT>, dim3(1), dim3(COLPTR_THREADS), 0, st, a.tot, a.F, a.colptr, s,
+                     a.T > 0 ? a.order : nullptr);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int n_slices = a.d / DX_SLICE, n_wslices = a.d / DW_SLICE;
   if (a.T > 0) {
@@ -596,7 +661,7 @@ static hipError_t launch_backward(const BackwardArgs &a, hipStream_t st) {
     const int n_tb = (a.T + tok - 1) / tok;
     hipLaunchKernelGGL((k_bw_dx<D, 4>), dim3(padded_groups(n_slices) * n_tb), dim3(SP_THREADS), 0, st, s,
                        (const f32x2_t *)a.ent, (const TT *)a.wu, (const TT *)a.wg, (TT *)a.dx, a.d, n_slices, tok,
-                       n_tb);
+                       n_tb, a.order);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   const int upw = 8;  // units per workgroup; 8 loads in flight per lane (fastest in a sweep)

@@ -173,6 +173,7 @@ struct BackwardArgs {
   void *csc;
   uint8_t *blk;
   int *boff, *tot, *colptr;
+  int *order;  // [T] row order of the per-row kernels
 };
 hipError_t ffn_backward(const BackwardArgs &a, hipStream_t s);
 
