@@ -227,7 +227,18 @@ def measure(w, steps, warmup, want_torch=True, want_cold=True, settle_ms=50.0):
     # (values + int32 columns) and counts written, dense rows copied
     hybrid_bytes = (T * nt * 2 + nnz_all * (s + 1) + T * 4 + T * HYBRID_WIDTH * (s + 4)
                     + n_dense * F * s * 2)
-    training = {"hybrid_width": HYBRID_WIDTH, "n_dense": n_dense,
+    # Activation memory kept for back-propagation: the dense h, the TwELL
+    # matrix (cnt, val, idx and its dense backup rows), and the hybrid
+    # format (cnt, ELL values and int32 columns, the dense row list and rows).
+    n_ovf_tr = int(packed_tr.n_ovf.item())
+    mem = {"dense_h_bytes": T * F * s,
+           "twell_bytes": T * nt * (2 + w.cap * (s + 1)) + n_ovf_tr * (4 + F * s),
+           "hybrid_bytes": T * 4 + T * HYBRID_WIDTH * (s + 4) + n_dense * (4 + F * s)}
+    mem["twell_over_dense"] = mem["twell_bytes"] / mem["dense_h_bytes"]
+    mem["hybrid_over_dense"] = mem["hybrid_bytes"] / mem["dense_h_bytes"]
+    log(f"[bench] activation memory: dense {mem['dense_h_bytes'] / 2**20:.0f} MiB, TwELL "
+        f"{mem['twell_bytes'] / 2**20:.1f} MiB, hybrid {mem['hybrid_bytes'] / 2**20:.1f} MiB")
+    training = {"hybrid_width": HYBRID_WIDTH, "n_dense": n_dense, "activation_memory": mem,
                 "to_hybrid_us": ms_hybrid * 1e3, "to_hybrid_GBps": hybrid_bytes / (ms_hybrid * 1e-3) / 1e9,
                 "l1_norm_us": ms_l1 * 1e3, "l1_grad_us": ms_l1g * 1e3,
                 "note": "TwELL -> hybrid conversion, ||h||_1 and its gradient on this batch; GBps over the "
