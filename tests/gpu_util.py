@@ -5,7 +5,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from oracle.ffn import ffn, gate_pre, rel_l2, row_rel_l2
+from oracle.ffn import ffn, gate_pre, rel_l2
 from oracle.numerics import decode, round_to_storage
 from oracle.twell import active, pack
 
@@ -169,11 +169,17 @@ def check_y(y_dev_np: np.ndarray, inp, dtype: str, rows=None, per_row=True):
     err = rel_l2(yg, y64)
     assert err <= tol, f"relative L2 error {err:.3e} > {tol:g}"
     if per_row:
-        r = row_rel_l2(yg, y64)
-        zero_rows = np.linalg.norm(y64, axis=1) == 0
+        # Each row's error relative to the larger of its own norm and the RMS
+        # row norm: a row that nearly cancels (few entries whose u or v is
+        # near zero) carries fp32 rounding the size of a typical row's, not
+        # of its own.
+        norms = np.linalg.norm(y64, axis=1)
+        zero_rows = norms == 0
         assert np.all(yg[zero_rows] == 0), "rows with no active unit must be exactly zero"
-        worst = float(np.max(r[~zero_rows])) if (~zero_rows).any() else 0.0
-        assert worst <= 4 * tol, f"worst row relative L2 error {worst:.3e}"
+        if (~zero_rows).any():
+            scale = np.maximum(norms, np.sqrt(np.mean(norms[~zero_rows] ** 2)))
+            worst = float(np.max((np.linalg.norm(yg - y64, axis=1) / scale)[~zero_rows]))
+            assert worst <= 4 * tol, f"worst row error {worst:.3e} (relative to max(row, RMS row) norm)"
     return err
 
 
