@@ -403,6 +403,14 @@ __device__ __forceinline__ void gemm_mainloop_dma(f32x16_t (&acc)[WaveTile<BN>::
     const int slot = kt % DMA_STAGES;
     read_frag(f1, smem + slot * STAGE, row0, col0, 1, lane);
     mfma_frag<D>(acc, f0);
+    // Scheduling hint: alternate the MFMAs of the first half with the LDS
+    // reads of the second, one each, instead of issuing the reads in a block
+    // (about 2% faster on the 1.5B-class gate).
+#pragma unroll
+    for (int q = 0; q < NWM + NWN; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+    }
     if (kt + 1 < nk) {
       // every wave has read all of slab kt (the barrier waits for its LDS
       // reads) and slab kt+1 has landed for every wave
