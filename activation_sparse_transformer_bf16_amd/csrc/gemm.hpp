@@ -22,6 +22,8 @@
 
 #include "common.hpp"
 
+#include <type_traits>
+
 namespace twell {
 
 constexpr int GEMM_BM = 256;
@@ -399,32 +401,60 @@ __device__ __forceinline__ void gemm_mainloop_dma(f32x16_t (&acc)[WaveTile<BN>::
   init(acc, has_rowv ? reinterpret_cast<const float *>(smem + gemm_dma_ring_bytes(BN)) : nullptr);
   Frag<NWM, NWN> f0, f1;
   read_frag(f0, smem, row0, col0, 0, lane);
-  for (int kt = 0; kt < nk; ++kt) {
+  // One slab kt < nk - 1 with WAIT stages (of OPS loads) left in flight at its
+  // barrier, issuing the loads of slab kt + DMA_STAGES if ISSUE.  The loop is
+  // peeled by these constants (no runtime selection of the wait) and the last
+  // slab has a block of its own: a path that joins the steady state with the
+  // last slab's makes the compiler wait for the next slab's first-half reads
+  // before the second-half MFMAs.
+  auto slab = [&](auto wait_c, auto issue_c, int kt) {
+    constexpr int WAIT = decltype(wait_c)::value;
+    constexpr bool ISSUE = decltype(issue_c)::value;
     const int slot = kt % DMA_STAGES;
     read_frag(f1, smem + slot * STAGE, row0, col0, 1, lane);
     mfma_frag<D>(acc, f0);
     // Scheduling hint: alternate the MFMAs of the first half with the LDS
-    // reads of the second, one each, instead of issuing the reads in a block
-    // (about 2% faster on the 1.5B-class gate).
+    // reads of the second, one each, instead of issuing the reads in a block.
 #pragma unroll
     for (int q = 0; q < NWM + NWN; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
     }
-    if (kt + 1 < nk) {
-      // every wave has read all of slab kt (the barrier waits for its LDS
-      // reads) and slab kt+1 has landed for every wave
-      wait_stages<OPS>(min(nk - 2 - kt, DMA_STAGES - 2));
-      __syncthreads();
-      if (kt + DMA_STAGES < nk) {
-        const uint32_t sb = base + slot * STAGE;
-        da.issue(kt + DMA_STAGES, sb);
-        db.issue(kt + DMA_STAGES, sb);
-      }
-      read_frag(f0, smem + ((kt + 1) % DMA_STAGES) * STAGE, row0, col0, 0, lane);
+    // every wave has read all of slab kt (the barrier waits for its LDS
+    // reads) and slab kt+1 has landed for every wave
+    wait_vmcnt<WAIT * OPS>();
+    __syncthreads();
+    if constexpr (ISSUE) {
+      const uint32_t sb = base + slot * STAGE;
+      da.issue(kt + DMA_STAGES, sb);
+      db.issue(kt + DMA_STAGES, sb);
     }
+    read_frag(f0, smem + ((kt + 1) % DMA_STAGES) * STAGE, row0, col0, 0, lane);
     mfma_frag<D>(acc, f1);
-  }
+    // the same alternation for the next slab's first-half reads
+#pragma unroll
+    for (int q = 0; q < NWM + NWN; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    }
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using BT = std::integral_constant<bool, true>;
+  using BF = std::integral_constant<bool, false>;
+  static_assert(DMA_STAGES == 4, "the peeled tail below assumes a 4-stage ring");
+  // slab kt waits for slab kt + 1: min(nk - 2 - kt, 2) stages stay in flight;
+  // slab kt + 4 is loaded while kt + 4 < nk
+  int kt = 0;
+  for (; kt + DMA_STAGES < nk; ++kt) slab(I2(), BT(), kt);
+  if (kt == nk - 4) slab(I2(), BF(), kt++);
+  if (kt == nk - 3) slab(I1(), BF(), kt++);
+  if (kt == nk - 2) slab(I0(), BF(), kt++);
+  // the last slab: both halves, no loads left
+  read_frag(f1, smem + (kt % DMA_STAGES) * STAGE, row0, col0, 1, lane);
+  mfma_frag<D>(acc, f0);
+  mfma_frag<D>(acc, f1);
   // no DMA is left in flight; make every wave's last LDS reads complete before
   // the caller reuses LDS
   __syncthreads();
