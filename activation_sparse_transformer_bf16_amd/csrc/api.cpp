@@ -205,10 +205,19 @@ twell_status twell_pack(const void *pre, twell_matrix *out, void *stream) {
   const int T = out->rows;
   if (T == 0) return hip_check(zero_int(out->n_ovf, s), "zero n_ovf");
   const Dt D = to_dt(out->dtype);
-  PackArgs pa{D, out->tile, out->cap, pre, T, out->cols, out->cnt, out->val, out->idx};
+  // With room for every row, the pack kernel writes each row's overflow flag
+  // into ovf_rows and one workgroup turns the flags into the list in place;
+  // otherwise a scan over the counts builds the (truncated) list.
+  const bool flags_in_list = out->ovf_cap >= T;
+  PackArgs pa{D, out->tile, out->cap, pre, T, out->cols, out->cnt, out->val, out->idx,
+              flags_in_list ? out->ovf_rows : nullptr};
   TW_TRY(pack_tiles(pa, s), "pack");
-  ScanArgs sc{out->cnt, T, out->cols / out->tile, out->cap, nullptr, out->ovf_rows, out->ovf_cap, out->n_ovf};
-  TW_TRY(overflow_scan(sc, s), "overflow scan");
+  if (flags_in_list) {
+    TW_TRY(compact_rows_in_place(out->ovf_rows, T, out->n_ovf, s), "overflow row list");
+  } else {
+    ScanArgs sc{out->cnt, T, out->cols / out->tile, out->cap, nullptr, out->ovf_rows, out->ovf_cap, out->n_ovf};
+    TW_TRY(overflow_scan(sc, s), "overflow scan");
+  }
   DenseRowsArgs dr{D, pre, T, out->cols, out->ovf_rows, out->n_ovf, out->ovf_cap, out->dense};
   TW_TRY(pack_dense_rows(dr, s), "dense rows");
   return TWELL_OK;

@@ -36,6 +36,8 @@ hipError_t overflow_scan(const ScanArgs &a, hipStream_t s);
 
 // Ascending list of the rows with row_flag[t] != 0, and its true length.
 hipError_t compact_rows(const uint8_t *row_flag, int T, int *ovf_rows, int ovf_cap, int *n_ovf, hipStream_t s);
+// The same from int32 flags [T], listing the rows over the flag array itself.
+hipError_t compact_rows_in_place(int *flags_then_rows, int T, int *n_ovf, hipStream_t s);
 
 // Sparse up / down projections over the TwELL entries of non-overflow rows.
 struct SparseArgs {
@@ -91,6 +93,7 @@ struct PackArgs {
   uint16_t *cnt;
   void *val;
   uint8_t *idx;
+  int *row_flag;  // [T] int32: 1 for an overflowing row, else 0; or null
 };
 hipError_t pack_tiles(const PackArgs &a, hipStream_t s);
 

@@ -24,58 +24,87 @@
 namespace twell {
 
 // ---------------------------------------------------------------------------
-// Overflow scan: row t overflows iff max_k cnt[t][k] > cap.  One workgroup;
-// rows are visited in ascending order so the list is deterministic.
+// Overflow scan: row t overflows iff max_k cnt[t][k] > cap.  One workgroup.
+// Rows are taken SCAN_CHUNK at a time: the chunk's counts are read as one flat
+// stream of 16-byte loads (consecutive threads, consecutive bytes), a count
+// above cap sets its row's flag byte in LDS, and the flags are then compacted
+// in ascending row order, so the list is deterministic.
 constexpr int SCAN_THREADS = 1024;
-constexpr int SCAN_ROWS = 4;  // rows in flight per thread
+constexpr int SCAN_PER = 8;                         // flag bytes per thread in the compaction
+constexpr int SCAN_CHUNK = SCAN_PER * SCAN_THREADS;  // rows per round
+constexpr int SCAN_LOADS = 16;                       // 16-byte loads per thread in flight
 
 __global__ __launch_bounds__(SCAN_THREADS) void k_overflow_scan(const uint16_t *__restrict__ cnt, int T, int nt,
                                                                int cap, uint8_t *__restrict__ row_flag,
                                                                int *__restrict__ ovf_rows, int ovf_cap,
                                                                int *__restrict__ n_ovf) {
-  __shared__ int wcount[SCAN_ROWS][SCAN_THREADS / 64];
+  __shared__ __align__(16) uint32_t flag4[SCAN_CHUNK / 4];
+  __shared__ int wcount[SCAN_THREADS / 64];
+  uint8_t *flag = reinterpret_cast<uint8_t *>(flag4);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const bool vec = (nt % 8) == 0;
   int carry = 0;
-  for (int base = 0; base < T; base += SCAN_THREADS * SCAN_ROWS) {
-    bool f[SCAN_ROWS];
+  for (int r0 = 0; r0 < T; r0 += SCAN_CHUNK) {
+    const int nr = min(SCAN_CHUNK, T - r0);
+    for (int i = tid; i < SCAN_CHUNK / 4; i += SCAN_THREADS) flag4[i] = 0u;
+    __syncthreads();
+    // counts of rows [r0, r0 + nr): elements [e_begin, e_end) of the flat array
+    const size_t e_begin = (size_t)r0 * nt, e_end = (size_t)(r0 + nr) * nt;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(cnt + e_begin);
+    const size_t head = min((size_t)(((16u - (a0 & 15u)) & 15u) / 2u), e_end - e_begin);
+    const size_t v0 = e_begin + head;
+    const size_t nv = (e_end - v0) / 8;  // whole 16-byte chunks
+    const size_t v_end = v0 + nv * 8;
+    for (size_t e = e_begin + tid; e < v0; e += SCAN_THREADS)
+      if (cnt[e] > cap) flag[e / nt - r0] = 1;
+    for (size_t e = v_end + tid; e < e_end; e += SCAN_THREADS)
+      if (cnt[e] > cap) flag[e / nt - r0] = 1;
+    for (size_t c0 = tid; c0 < nv; c0 += (size_t)SCAN_THREADS * SCAN_LOADS) {
+      u32x4_t w[SCAN_LOADS];
 #pragma unroll
-    for (int q = 0; q < SCAN_ROWS; ++q) {
-      const int t = base + q * SCAN_THREADS + tid;
-      int mx = 0;
-      if (t < T) {
-        const uint16_t *c = cnt + (size_t)t * nt;
-        if (vec) {
-#pragma unroll 4
-          for (int k = 0; k < nt; k += 8) {
-            u32x4_t w = *reinterpret_cast<const u32x4_t *>(c + k);
+      for (int q = 0; q < SCAN_LOADS; ++q) {
+        const size_t c = c0 + (size_t)q * SCAN_THREADS;
+        w[q] = c < nv ? *reinterpret_cast<const u32x4_t *>(cnt + v0 + c * 8) : u32x4_t{0u, 0u, 0u, 0u};
+      }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) mx = max(mx, (int)max(w[e] & 0xFFFFu, w[e] >> 16));
-          }
-        } else {
-          for (int k = 0; k < nt; ++k) mx = max(mx, (int)c[k]);
+      for (int q = 0; q < SCAN_LOADS; ++q) {
+        uint32_t mx = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mx = max(mx, max(w[q][j] & 0xFFFFu, w[q][j] >> 16));
+        if (mx > (uint32_t)cap) {
+          const size_t e0 = v0 + (c0 + (size_t)q * SCAN_THREADS) * 8;
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if (((w[q][j / 2] >> (16 * (j & 1))) & 0xFFFFu) > (uint32_t)cap) flag[(e0 + j) / nt - r0] = 1;
         }
       }
-      f[q] = t < T && mx > cap;
-      if (t < T && row_flag != nullptr) row_flag[t] = f[q] ? 1 : 0;
-    }
-    uint64_t m[SCAN_ROWS];
-#pragma unroll
-    for (int q = 0; q < SCAN_ROWS; ++q) {
-      m[q] = ballot(f[q]);
-      if (lane == 0) wcount[q][wave] = popc64(m[q]);
     }
     __syncthreads();
+    // compaction: thread tid owns the flags of rows r0 + 8 tid .. r0 + 8 tid + 7
+    const u32x2_t fw = reinterpret_cast<const u32x2_t *>(flag4)[tid];
+    int c = 0;
 #pragma unroll
-    for (int q = 0; q < SCAN_ROWS; ++q) {
-      int before = carry;
-      for (int w = 0; w < SCAN_THREADS / 64; ++w) before += (w < wave) ? wcount[q][w] : 0;
-      if (f[q]) {
-        const int pos = before + mbcnt(m[q]);
-        if (pos < ovf_cap) ovf_rows[pos] = base + q * SCAN_THREADS + tid;
-      }
-      for (int w = 0; w < SCAN_THREADS / 64; ++w) carry += wcount[q][w];
+    for (int j = 0; j < SCAN_PER; ++j) c += ((fw[j / 4] >> (8 * (j % 4))) & 0xFFu) != 0;
+    const int incl = wave_incl_scan(c);
+    if (lane == 63) wcount[wave] = incl;
+    __syncthreads();
+    int pos = carry + incl - c, total = 0;
+    for (int w = 0; w < SCAN_THREADS / 64; ++w) {
+      pos += (w < wave) ? wcount[w] : 0;
+      total += wcount[w];
     }
+#pragma unroll
+    for (int j = 0; j < SCAN_PER; ++j) {
+      const int rr = SCAN_PER * tid + j;
+      if (rr < nr) {
+        const bool f = ((fw[j / 4] >> (8 * (j % 4))) & 0xFFu) != 0;
+        if (row_flag != nullptr) row_flag[r0 + rr] = f ? 1 : 0;
+        if (f) {
+          if (pos < ovf_cap) ovf_rows[pos] = r0 + rr;
+          ++pos;
+        }
+      }
+    }
+    carry += total;
     __syncthreads();
   }
   if (tid == 0) *n_ovf = carry;
@@ -87,28 +116,55 @@ hipError_t overflow_scan(const ScanArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Ascending list of the rows whose flag is set (flags written by the up
-// kernel); one workgroup, T bytes read, 8 consecutive flags per thread per
-// round (thread order = row order).
+// Ascending list of the rows whose flag is set; one workgroup, 8 consecutive
+// flags per thread per round (thread order = row order).  Flags are bytes
+// (written by the up kernel into the workspace) or int32 words.  With int32
+// flags the list may overwrite the flag array itself: the list position of a
+// row never exceeds the row's index, and every thread reads the round's flags
+// before the barrier that precedes the round's writes.
 constexpr int COMPACT_THREADS = 1024;
 constexpr int COMPACT_PER = 8;
-__global__ __launch_bounds__(COMPACT_THREADS) void k_compact_rows(const uint8_t *__restrict__ row_flag, int T,
-                                                                   int *__restrict__ ovf_rows, int ovf_cap,
-                                                                   int *__restrict__ n_ovf) {
+
+template <class FlagT>
+__device__ __forceinline__ void load_flags(const FlagT *row_flag, int t0, int T, uint32_t (&f)[COMPACT_PER]);
+template <>
+__device__ __forceinline__ void load_flags<uint8_t>(const uint8_t *row_flag, int t0, int T,
+                                                   uint32_t (&f)[COMPACT_PER]) {
+  if (t0 + COMPACT_PER <= T && (reinterpret_cast<uintptr_t>(row_flag + t0) & 7) == 0) {
+    const u32x2_t w = *reinterpret_cast<const u32x2_t *>(row_flag + t0);
+#pragma unroll
+    for (int q = 0; q < COMPACT_PER; ++q) f[q] = (w[q / 4] >> (8 * (q % 4))) & 0xFFu;
+  } else {
+#pragma unroll
+    for (int q = 0; q < COMPACT_PER; ++q) f[q] = t0 + q < T ? row_flag[t0 + q] : 0u;
+  }
+}
+template <>
+__device__ __forceinline__ void load_flags<int>(const int *row_flag, int t0, int T, uint32_t (&f)[COMPACT_PER]) {
+  if (t0 + COMPACT_PER <= T && (reinterpret_cast<uintptr_t>(row_flag + t0) & 15) == 0) {
+    const u32x4_t a = *reinterpret_cast<const u32x4_t *>(row_flag + t0);
+    const u32x4_t b = *reinterpret_cast<const u32x4_t *>(row_flag + t0 + 4);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      f[q] = a[q];
+      f[q + 4] = b[q];
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < COMPACT_PER; ++q) f[q] = t0 + q < T ? (uint32_t)row_flag[t0 + q] : 0u;
+  }
+}
+
+template <class FlagT>
+__global__ __launch_bounds__(COMPACT_THREADS) void k_compact_rows(const FlagT *row_flag, int T, int *ovf_rows,
+                                                                  int ovf_cap, int *__restrict__ n_ovf) {
   __shared__ int wcount[COMPACT_THREADS / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int carry = 0;
   for (int base = 0; base < T; base += COMPACT_THREADS * COMPACT_PER) {
     const int t0 = base + tid * COMPACT_PER;
     uint32_t f[COMPACT_PER];
-    if (t0 + COMPACT_PER <= T && (reinterpret_cast<uintptr_t>(row_flag + t0) & 7) == 0) {
-      const u32x2_t w = *reinterpret_cast<const u32x2_t *>(row_flag + t0);
-#pragma unroll
-      for (int q = 0; q < COMPACT_PER; ++q) f[q] = (w[q / 4] >> (8 * (q % 4))) & 0xFFu;
-    } else {
-#pragma unroll
-      for (int q = 0; q < COMPACT_PER; ++q) f[q] = t0 + q < T ? row_flag[t0 + q] : 0u;
-    }
+    load_flags<FlagT>(row_flag, t0, T, f);
     int c = 0;
 #pragma unroll
     for (int q = 0; q < COMPACT_PER; ++q) c += f[q] != 0;
@@ -134,7 +190,14 @@ __global__ __launch_bounds__(COMPACT_THREADS) void k_compact_rows(const uint8_t 
 }
 
 hipError_t compact_rows(const uint8_t *row_flag, int T, int *ovf_rows, int ovf_cap, int *n_ovf, hipStream_t s) {
-  hipLaunchKernelGGL(k_compact_rows, dim3(1), dim3(COMPACT_THREADS), 0, s, row_flag, T, ovf_rows, ovf_cap, n_ovf);
+  hipLaunchKernelGGL(k_compact_rows<uint8_t>, dim3(1), dim3(COMPACT_THREADS), 0, s, row_flag, T, ovf_rows, ovf_cap,
+                     n_ovf);
+  return hipGetLastError();
+}
+
+hipError_t compact_rows_in_place(int *flags_then_rows, int T, int *n_ovf, hipStream_t s) {
+  hipLaunchKernelGGL(k_compact_rows<int>, dim3(1), dim3(COMPACT_THREADS), 0, s, flags_then_rows, T, flags_then_rows,
+                     T, n_ovf);
   return hipGetLastError();
 }
 

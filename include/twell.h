@@ -120,7 +120,9 @@ const char *twell_last_error(void);
  *
  * pre: [out->rows][out->cols] device buffer in out->dtype.  Fills every field
  * of *out as defined above: cnt, val, idx, ovf_rows (first ovf_cap),
- * *n_ovf, and dense (when non-NULL).  This is the format of gist.science
+ * *n_ovf, and dense (when non-NULL).  Entries of ovf_rows at and past
+ * min(n_ovf, ovf_cap) are unspecified on return: when ovf_cap >= rows the
+ * call keeps one overflow flag per row there before listing the rows.  This is the format of gist.science
  * Resumen Técnico §2.A applied to an explicit matrix; twell_ffn_forward
  * produces the same TwELL matrix inside the gate matmul.
  * Errors: INVALID_ARG (NULL pre/out/cnt/val/idx/n_ovf, ovf_rows NULL with
