@@ -26,13 +26,17 @@ constexpr int FALLBACK_WGS = 256;       // grid of the fallback kernels
 constexpr int SPLIT_TILE = GEMM_BM * 256;  // floats of one partial tile (256 x 256)
 
 // K ranges per output tile for the fallback: enough to give every workgroup
-// of the grid a work item, at most smax and at most nk (K slabs).
+// of the grid a work item, at most smax and at most nk (K slabs).  The limits
+// are measured: each K range adds a 256 KB fp32 partial tile written and read
+// back, and past 2 ranges (gate+up, K = d) or 16 (down, K = d_ff) that traffic
+// costs more than the idle workgroups it would fill.
 __device__ __forceinline__ int fallback_split(int tiles, int nk, int smax) {
   const int s = min(min(FALLBACK_WGS / max(tiles, 1), smax), nk);
   return max(s, 1);
 }
-constexpr int GATE_UP_SPLIT_MAX = 16;
-constexpr int DOWN_SPLIT_MAX = 32;
+constexpr int GATE_UP_SPLIT_MAX = 2;
+constexpr int DOWN_SPLIT_MAX = 16;
+constexpr int REDUCE_BATCH = 8;  // partials loaded together by the reduction kernels (added in K order)
 
 // Partial tiles are stored in the accumulators' own order: register i of
 // block (bm, bn) of wave w is 64 consecutive floats, one per lane, so every
@@ -246,7 +250,21 @@ __global__ __launch_bounds__(256) void k_gate_up_reduce(const float *__restrict_
     const float *p = partial + (size_t)tile * S * SPLIT_TILE;
     const int ig = gate_up_part_index(r, gcol), iu = gate_up_part_index(r, gcol + 32);
     float pre = 0.f, up = 0.f;
-    for (int kc = 0; kc < S; ++kc) {
+    int kc = 0;
+    for (; kc + REDUCE_BATCH <= S; kc += REDUCE_BATCH) {  // loads of a batch in flight together
+      float qg[REDUCE_BATCH], qu[REDUCE_BATCH];
+#pragma unroll
+      for (int i = 0; i < REDUCE_BATCH; ++i) {
+        qg[i] = p[(size_t)(kc + i) * SPLIT_TILE + ig];
+        qu[i] = p[(size_t)(kc + i) * SPLIT_TILE + iu];
+      }
+#pragma unroll
+      for (int i = 0; i < REDUCE_BATCH; ++i) {
+        pre += qg[i];
+        up += qu[i];
+      }
+    }
+    for (; kc < S; ++kc) {
       pre += p[(size_t)kc * SPLIT_TILE + ig];
       up += p[(size_t)kc * SPLIT_TILE + iu];
     }
@@ -308,7 +326,15 @@ __global__ __launch_bounds__(256) void k_down_reduce(const float *__restrict__ p
     if (lr >= n_eff) continue;
     const float *p = partial + (size_t)tile * S * SPLIT_TILE + down_part_index(r, c);
     float v = 0.f;
-    for (int kc = 0; kc < S; ++kc) v += p[(size_t)kc * SPLIT_TILE];
+    int kc = 0;
+    for (; kc + REDUCE_BATCH <= S; kc += REDUCE_BATCH) {  // loads of a batch in flight together
+      float q[REDUCE_BATCH];
+#pragma unroll
+      for (int i = 0; i < REDUCE_BATCH; ++i) q[i] = p[(size_t)(kc + i) * SPLIT_TILE];
+#pragma unroll
+      for (int i = 0; i < REDUCE_BATCH; ++i) v += q[i];
+    }
+    for (; kc < S; ++kc) v += p[(size_t)kc * SPLIT_TILE];
     const size_t prow = rows ? (size_t)rows[lr] : (size_t)lr;
     y[prow * N + (size_t)(tile % ntl) * 256 + c] = from_f32<D>(v);
   }

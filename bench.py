@@ -300,12 +300,15 @@ def measure(w, steps, warmup, want_torch=True, want_cold=True, settle_ms=50.0):
     log(f"[bench] twell_pack {ms_pack * 1e3:.1f} us ({training['twell_pack_GBps']:.0f} GB/s)")
     del pre, packed_p
 
-    # A plain device copy of known size (256 MiB read + 256 MiB written).  It
-    # is not part of any measurement here; in rocprofv3 counter runs its
-    # FETCH_SIZE / WRITE_SIZE readings calibrate the byte counters.
+    # A plain device copy of known size (256 MiB read + 256 MiB written): the
+    # measured HBM copy bandwidth beside the 8 TB/s spec; in rocprofv3 counter
+    # runs its FETCH_SIZE / WRITE_SIZE readings also calibrate the byte counters.
     src = torch.empty((1 << 26,), dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
-    dst.copy_(src)
+    ms_copy, _ = event_time(lambda: dst.copy_(src), steps, warmup)
+    copy_gbs = 2 * src.numel() * 4 / (ms_copy * 1e-3) / 1e9
+    log(f"[bench] device copy of 256 MiB: {copy_gbs:.0f} GB/s")
+    training["twell_pack_frac_of_measured_copy"] = training["twell_pack_GBps"] / copy_gbs
     del src, dst
 
     # one more forward to read the statistics of this batch
@@ -327,7 +330,7 @@ def measure(w, steps, warmup, want_torch=True, want_cold=True, settle_ms=50.0):
         "gate_tflops": flops_gate / (ms_gate * 1e-3) / 1e12, "peak": peak,
         "dense_tflops": 3 * flops_gate / (ms_dense * 1e-3) / 1e12,
         "gather_gbs": B_alg / (ms_rest * 1e-3) / 1e9,
-        "training": training, "backward": backward,
+        "training": training, "backward": backward, "copy_gbs": copy_gbs,
         "fused": {"forward_us": ms_fused * 1e3, "up_down_fallback_us": ms_fused_rest * 1e3,
                   "two_kernel_up_down_fallback_us": ms_rest * 1e3,
                   "note": "gate then twell_sparse_ffn_fused (up and down in one kernel, one wave per token); "
@@ -456,6 +459,7 @@ def gather_record(w, r):
     rec = {"bytes_alg": r["gather_bytes"], "achieved_GBps": r["gather_gbs"],
            "frac_of_hbm_peak": r["gather_gbs"] / HBM_PEAK_GBS,
            "compulsory_bytes": compulsory, "compulsory_frac_of_hbm_peak": compulsory / t / 1e9 / HBM_PEAK_GBS}
+    rec["compulsory_frac_of_measured_copy"] = compulsory / t / 1e9 / r["copy_gbs"]
     counted = counted_gather_traffic(w.name)
     rec["counted_fabric_bytes"] = counted
     if counted:
@@ -515,6 +519,7 @@ def main():
         "cold_us": {k: v * 1e3 for k, v in r["cold"].items()},
         "gather": gather_record(w, r),
         "dense_mfma_tflops": r["dense_tflops"],
+        "hbm_copy_GBps": r["copy_gbs"],
         "training_formats": r["training"],
         "backward": r["backward"],
         "fused_up_down": r["fused"],

@@ -78,3 +78,22 @@ def test_pack_full_size(dtype, T, F, tile, cap, hot):
     pre = pre_activations(T, F, dtype, seed=1, density=0.01, hot_rows=hot, hot_density=0.2)
     host = _run(pre, dtype, tile, cap)
     assert_packed_equal(host, pack(pre, dtype, tile, cap))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("ovf_cap_delta", [0, -1])
+def test_pack_list_spans_several_rounds(dtype, ovf_cap_delta):
+    """More rows than one round of the overflow-list kernels (8192 rows): with
+    room for every row the rows are listed over the flags in ovf_rows itself
+    (several rounds of that in-place compaction); with one slot less the
+    count scan builds the truncated list."""
+    T, F = 2 * 8192 + 515, 256
+    hot = tuple(range(3, T, 7))
+    print(f"pack rounds {dtype} T={T} ovf_cap=T{ovf_cap_delta:+d}", flush=True)
+    pre = pre_activations(T, F, dtype, seed=11, density=0.01, hot_rows=hot, hot_density=0.2)
+    ref = pack(pre, dtype, 128, 2)
+    assert ref.n_ovf > 2000
+    ovf_cap = T + ovf_cap_delta
+    host = _run(pre, dtype, 128, 2, ovf_cap=ovf_cap)
+    assert host["ovf_rows"].shape[0] == min(ref.n_ovf, ovf_cap)
+    assert_packed_equal(host, ref)
