@@ -181,26 +181,44 @@ hipError_t pack_tiles(const PackArgs &a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-// dense[r][:] = ReLU(pre[ovf_rows[r]][:]) for r < min(*n_ovf, ovf_cap).
+// dense[r][:] = ReLU(pre[ovf_rows[r]][:]) for r < min(*n_ovf, ovf_cap), 16
+// bytes per lane (rows are F * s bytes, a multiple of 256; both matrices are
+// 16-byte aligned).  One workgroup per row at a time.
+template <class TT>
+__device__ __forceinline__ uint32_t relu_word(uint32_t w);
+template <>
+__device__ __forceinline__ uint32_t relu_word<uint16_t>(uint32_t w) {
+  const uint32_t lo = active_bits((uint16_t)(w & 0xFFFFu)) ? (w & 0xFFFFu) : 0u;
+  const uint32_t hi = active_bits((uint16_t)(w >> 16)) ? (w & 0xFFFF0000u) : 0u;
+  return lo | hi;
+}
+template <>
+__device__ __forceinline__ uint32_t relu_word<float>(uint32_t w) {
+  return active_bits(__uint_as_float(w)) ? w : 0u;
+}
+
+constexpr int DENSE_ROWS_WGS = 512;
+
 template <Dt D>
 __global__ __launch_bounds__(256) void k_dense_rows(const typename DtT<D>::T *__restrict__ pre, int F,
                                                    const int *__restrict__ ovf_rows, const int *__restrict__ n_ovf,
                                                    int ovf_cap, typename DtT<D>::T *__restrict__ dense) {
   using TT = typename DtT<D>::T;
   const int n = min(*n_ovf, ovf_cap);
+  const int chunks = F * (int)sizeof(TT) / 16;
   for (int r = blockIdx.x; r < n; r += gridDim.x) {
-    const TT *src = pre + (size_t)ovf_rows[r] * F;
-    TT *dst = dense + (size_t)r * F;
-    for (int j = threadIdx.x; j < F; j += blockDim.x) {
-      const TT v = src[j];
-      dst[j] = active_bits(v) ? v : TT(0);
+    const u32x4_t *src = reinterpret_cast<const u32x4_t *>(pre + (size_t)ovf_rows[r] * F);
+    u32x4_t *dst = reinterpret_cast<u32x4_t *>(dense + (size_t)r * F);
+    for (int c = threadIdx.x; c < chunks; c += blockDim.x) {
+      const u32x4_t v = src[c];
+      dst[c] = u32x4_t{relu_word<TT>(v[0]), relu_word<TT>(v[1]), relu_word<TT>(v[2]), relu_word<TT>(v[3])};
     }
   }
 }
 
 hipError_t pack_dense_rows(const DenseRowsArgs &a, hipStream_t s) {
   if (a.dense == nullptr || a.ovf_cap <= 0 || a.T <= 0) return hipSuccess;
-  const int blocks = std::min(std::min(a.ovf_cap, a.T), 2048);
+  const int blocks = std::min(std::min(a.ovf_cap, a.T), DENSE_ROWS_WGS);
   if (a.dtype == Dt::BF16)
     hipLaunchKernelGGL(k_dense_rows<Dt::BF16>, dim3(blocks), dim3(256), 0, s, (const uint16_t *)a.pre, a.F,
                        a.ovf_rows, a.n_ovf, a.ovf_cap, (uint16_t *)a.dense);
