@@ -432,7 +432,14 @@ def cpu_baseline(w, inp, budget_s):
         n = w.T if t_cal * w.T / n0 <= 3 * budget_s else \
             int(max(n0, n0 * budget_s / max(t_cal, 1e-6)) // 256 * 256)
         t = run(n)
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:
+        pass
     return {"value": n / t, "unit": "tokens/s", "cores": int(used), "kind": "oracle",
+            "cpu_model": cpu_model,
             "sample": f"first {n} of {w.T} tokens of the same batch, one float64 pass "
                       f"(gate, TwELL pack, dense FFN) in {t:.1f}s; cpu threads available {cores}"}
 
