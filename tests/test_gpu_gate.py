@@ -41,6 +41,9 @@ def test_gate_pack_exact_inputs_bitwise(dtype, T, d, F, tile, cap, rho):
     assert_bitwise(from_dev(pre, dtype), want_pre, "pre_out")
     ref = pack(want_pre, dtype, tile, cap)
     assert_packed_equal(packed_to_host(p, dtype), ref, check_dense=False)
+    # the launch without the dump (the kernel the forward runs) gives the same matrix
+    p2, _ = tw.twell_gate_pack(x, wg, b, tile=tile, cap=cap)
+    assert_packed_equal(packed_to_host(p2, dtype), ref, check_dense=False)
 
 
 @pytest.mark.parametrize("dtype,T,d,F,tile,cap,bias", [
@@ -57,6 +60,10 @@ def test_gate_pack_gaussian_inputs(dtype, T, d, F, tile, cap, bias):
     pre64, bound = gate_bound(inp)
     host = packed_to_host(p, dtype)
     check_fused_pack(host, pre64, bound, dtype, tile, cap)
+    # the launch without the dump accumulates in the same order: the same matrix
+    host2 = packed_to_host(tw.twell_gate_pack(x, wg, b, tile=tile, cap=cap)[0], dtype)
+    for f in ("cnt", "val", "idx"):
+        assert_bitwise(host2[f], host[f], f)
     # the debugging dump agrees with the float64 gate within the bound plus one rounding
     g = decode(from_dev(pre, dtype), dtype)
     rel = 2.0 ** -8 if dtype == "bf16" else 0.0
