@@ -77,6 +77,7 @@ def _load():
         "twell_l1_norm": (I, [M, P, P, Z, P]),
         "twell_l1_grad": (I, [M, ctypes.c_float, P, P, P]),
         "twell_ffn_backward_workspace_size": (Z, [I, I, I, I, I, I]),
+        "twell_stream_probe": (I, [P, P, Z, I, P]),
         "twell_ffn_backward": (I, [ctypes.POINTER(TwellHybridC), P, P, P, P, P, ctypes.c_float, I, P, P, P, P,
                                    P, Z, P]),
     }
@@ -105,7 +106,8 @@ EXPORTS = ("twell_abi_version", "twell_status_str", "twell_last_error", "twell_p
            "twell_sparse_ffn",
            "dense_ffn_workspace_size", "dense_ffn_forward", "twell_to_hybrid",
            "twell_l1_workspace_size", "twell_l1_norm", "twell_l1_grad",
-           "twell_ffn_backward_workspace_size", "twell_ffn_backward", "twell_sparse_ffn_fused")
+           "twell_ffn_backward_workspace_size", "twell_ffn_backward", "twell_sparse_ffn_fused",
+           "twell_stream_probe")
 
 
 def lib():
@@ -450,3 +452,17 @@ def dense_ffn_forward(x, w_gate, w_up, w_down, gate_bias=None, y=None, workspace
                                   _ptr(y), T, d, F, _dtype_code(x.dtype), _ptr(ws), ws.numel(),
                                   _stream(device)))
     return y
+
+
+def twell_stream_probe(src, dst, mode: int) -> None:
+    """Streaming HBM probe on the current stream: mode 0 reads src (dst is a
+    device sink of at least 4 bytes), mode 1 copies src into dst."""
+    device = src.device
+    _need(src, "src", device)
+    _need(dst, "dst", device)
+    nbytes = src.numel() * src.element_size()
+    if mode == 1 and dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("dst is smaller than src")
+    if mode == 0 and dst.numel() * dst.element_size() < 4:
+        raise ValueError("the sink needs 4 bytes")
+    _check(_lib.twell_stream_probe(_ptr(src), _ptr(dst), nbytes, mode, _stream(device)))

@@ -195,6 +195,17 @@ const char *twell_status_str(twell_status s) {
 
 const char *twell_last_error(void) { return g_err; }
 
+twell_status twell_stream_probe(const void *src, void *dst, size_t bytes, int mode, void *stream) {
+  g_err[0] = 0;
+  if (mode != 0 && mode != 1) return fail(TWELL_ERR_INVALID_ARG, "mode must be 0 (read) or 1 (copy)");
+  if (bytes == 0) return TWELL_OK;
+  if (src == nullptr || dst == nullptr) return fail(TWELL_ERR_INVALID_ARG, "null src or dst");
+  if (bytes % 16 != 0) return fail(TWELL_ERR_UNSUPPORTED, "bytes must be a multiple of 16");
+  if (!aligned(src, 16) || !aligned(dst, mode == 0 ? 4 : 16))
+    return fail(TWELL_ERR_UNSUPPORTED, "misaligned probe buffer");
+  return hip_check(stream_probe(src, dst, bytes, mode, static_cast<hipStream_t>(stream)), "stream probe");
+}
+
 twell_status twell_pack(const void *pre, twell_matrix *out, void *stream) {
   g_err[0] = 0;
   twell_status st = check_matrix(out, false);

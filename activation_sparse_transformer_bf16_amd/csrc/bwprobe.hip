@@ -1,0 +1,66 @@
+// Streaming HBM probes: the measured read and copy bandwidth of the device,
+// the denominators that HBM-bound kernels are compared with beside the
+// 8 TB/s specification.  Every lane moves one 16-byte chunk and the grid has
+// a thread per chunk (up to 2^28 threads, then grid-stride): measured on
+// MI355X this beats grid-stride loops with 2-8 loads in flight per lane on
+// 2048-16384 workgroups (read 6.7 against 5.0-5.7 TB/s, copy 6.2 against
+// 4.3-4.9 TB/s).
+#include "launch.hpp"
+
+namespace twell {
+
+constexpr int PROBE_THREADS = 256;
+constexpr int PROBE_UNROLL = 1;
+
+// Reads n16 16-byte chunks; the XOR of everything read is stored only when it
+// equals a value no real buffer is expected to give, so the loads stay live
+// and the probe writes (almost) nothing.
+__global__ __launch_bounds__(PROBE_THREADS) void k_stream_read(const u32x4_t *__restrict__ src, size_t n16,
+                                                              uint32_t *__restrict__ sink) {
+  const size_t stride = (size_t)gridDim.x * PROBE_THREADS;
+  uint32_t acc = 0;
+  size_t i = (size_t)blockIdx.x * PROBE_THREADS + threadIdx.x;
+  for (; i + (PROBE_UNROLL - 1) * stride < n16; i += PROBE_UNROLL * stride) {
+    u32x4_t v[PROBE_UNROLL];
+#pragma unroll
+    for (int u = 0; u < PROBE_UNROLL; ++u) v[u] = src[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < PROBE_UNROLL; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+  }
+  for (; i < n16; i += stride) {
+    const u32x4_t v = src[i];
+    acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+  }
+  if (acc == 0x9E3779B9u) sink[0] = acc;
+}
+
+// dst = src, n16 16-byte chunks.
+__global__ __launch_bounds__(PROBE_THREADS) void k_stream_copy(const u32x4_t *__restrict__ src, size_t n16,
+                                                              u32x4_t *__restrict__ dst) {
+  const size_t stride = (size_t)gridDim.x * PROBE_THREADS;
+  size_t i = (size_t)blockIdx.x * PROBE_THREADS + threadIdx.x;
+  for (; i + (PROBE_UNROLL - 1) * stride < n16; i += PROBE_UNROLL * stride) {
+    u32x4_t v[PROBE_UNROLL];
+#pragma unroll
+    for (int u = 0; u < PROBE_UNROLL; ++u) v[u] = src[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < PROBE_UNROLL; ++u) dst[i + u * stride] = v[u];
+  }
+  for (; i < n16; i += stride) dst[i] = src[i];
+}
+
+hipError_t stream_probe(const void *src, void *dst, size_t bytes, int mode, hipStream_t s) {
+  const size_t n16 = bytes / 16;
+  if (n16 == 0) return hipSuccess;
+  const size_t want = (n16 + PROBE_THREADS * PROBE_UNROLL - 1) / (PROBE_THREADS * PROBE_UNROLL);
+  const int blocks = (int)std::min<size_t>(want, (size_t)1 << 20);
+  if (mode == 0)
+    hipLaunchKernelGGL(k_stream_read, dim3(blocks), dim3(PROBE_THREADS), 0, s, (const u32x4_t *)src, n16,
+                       (uint32_t *)dst);
+  else
+    hipLaunchKernelGGL(k_stream_copy, dim3(blocks), dim3(PROBE_THREADS), 0, s, (const u32x4_t *)src, n16,
+                       (u32x4_t *)dst);
+  return hipGetLastError();
+}
+
+}  // namespace twell

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "common.hpp"
 
 namespace twell {
@@ -182,5 +184,9 @@ hipError_t ffn_backward(const BackwardArgs &a, hipStream_t s);
 
 // *p = 0 with a one-thread kernel (safe under stream capture).
 hipError_t zero_int(int *p, hipStream_t s);
+
+// Streaming HBM probe: mode 0 reads `bytes` from src (dst: a 4-byte sink),
+// mode 1 copies them to dst.
+hipError_t stream_probe(const void *src, void *dst, size_t bytes, int mode, hipStream_t s);
 
 }  // namespace twell

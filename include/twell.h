@@ -344,6 +344,24 @@ twell_status twell_ffn_backward(const twell_hybrid *h, const void *x, const void
                                 const void *w_down, const void *dy, float lam, int d, void *dx, float *dw_gate,
                                 float *dw_up, float *dw_down, void *workspace, size_t ws_bytes, void *stream);
 
+/*
+ * twell_stream_probe -- streaming HBM probe (a measurement aid, not part of
+ * the layer's computation; the pages define no such operation).
+ *
+ * mode 0: reads `bytes` from src, one 16-byte load per lane (a thread per
+ *         chunk, grid-stride past 2^28 chunks); dst points at a 4-byte device sink that
+ *         is written only if the XOR of everything read equals 0x9E3779B9.
+ * mode 1: copies `bytes` from src to dst (the buffers must not overlap).
+ * bytes / (time of the call) is the device's measured read (mode 0) or
+ * copy (mode 1, count read + written bytes) bandwidth, the measured
+ * denominator beside the 8 TB/s specification for HBM-bound kernels.
+ * bytes == 0 launches nothing.
+ * Errors: INVALID_ARG (NULL src/dst with bytes > 0, mode not 0 or 1),
+ * UNSUPPORTED (bytes not a multiple of 16, src or dst not 16-byte aligned
+ * (the sink: 4-byte aligned)), HIP.
+ */
+twell_status twell_stream_probe(const void *src, void *dst, size_t bytes, int mode, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -213,3 +213,14 @@ def test_backward_validation_and_workspace():
     assert call(h, dwg=None) == twell.TWELL_ERR_INVALID_ARG
     assert call(h, dx=FAKE + 8) == twell.TWELL_ERR_UNSUPPORTED
     assert call(h, wsb=100) == twell.TWELL_ERR_WORKSPACE
+
+
+def test_stream_probe_validation():
+    assert L.twell_stream_probe(FAKE, FAKE, 1024, 2, None) == twell.TWELL_ERR_INVALID_ARG   # mode
+    assert L.twell_stream_probe(None, FAKE, 1024, 0, None) == twell.TWELL_ERR_INVALID_ARG
+    assert L.twell_stream_probe(FAKE, None, 1024, 1, None) == twell.TWELL_ERR_INVALID_ARG
+    assert L.twell_stream_probe(FAKE, FAKE, 1000, 1, None) == twell.TWELL_ERR_UNSUPPORTED  # bytes % 16
+    assert L.twell_stream_probe(FAKE + 8, FAKE, 1024, 0, None) == twell.TWELL_ERR_UNSUPPORTED
+    assert L.twell_stream_probe(FAKE, FAKE + 8, 1024, 1, None) == twell.TWELL_ERR_UNSUPPORTED
+    assert L.twell_stream_probe(FAKE, FAKE + 2, 1024, 0, None) == twell.TWELL_ERR_UNSUPPORTED  # sink
+    assert L.twell_stream_probe(None, None, 0, 0, None) == twell.TWELL_OK                    # nothing to do
