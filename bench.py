@@ -328,7 +328,7 @@ def measure(w, steps, warmup, want_torch=True, want_cold=True, settle_ms=50.0):
              "copy_GBps": 2 * half / (ms_pcopy * 1e-3) / 1e9}
     probe["read_frac_of_spec"] = probe["read_GBps"] / HBM_PEAK_GBS
     probe["copy_frac_of_spec"] = probe["copy_GBps"] / HBM_PEAK_GBS
-    probe["note"] = ("twell_stream_probe: 16-byte loads per lane, grid-stride; read 1 GiB, copy 512 MiB -> 512 MiB "
+    probe["note"] = ("twell_stream_probe: one 16-byte chunk per thread; read 1 GiB, copy 512 MiB -> 512 MiB "
                      "(bytes read + written); the measured denominators beside the 8 TB/s spec")
     training["twell_pack_frac_of_measured_read"] = training["twell_pack_GBps"] / probe["read_GBps"]
     log(f"[bench] stream probe: read {probe['read_GBps']:.0f} GB/s, copy {probe['copy_GBps']:.0f} GB/s")
