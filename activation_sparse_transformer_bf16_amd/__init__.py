@@ -78,6 +78,7 @@ def _load():
         "twell_l1_grad": (I, [M, ctypes.c_float, P, P, P]),
         "twell_ffn_backward_workspace_size": (Z, [I, I, I, I, I, I]),
         "twell_stream_probe": (I, [P, P, Z, I, P]),
+        "twell_mfma_probe": (I, [P, I, I, P]),
         "twell_ffn_backward": (I, [ctypes.POINTER(TwellHybridC), P, P, P, P, P, ctypes.c_float, I, P, P, P, P,
                                    P, Z, P]),
     }
@@ -107,7 +108,7 @@ EXPORTS = ("twell_abi_version", "twell_status_str", "twell_last_error", "twell_p
            "dense_ffn_workspace_size", "dense_ffn_forward", "twell_to_hybrid",
            "twell_l1_workspace_size", "twell_l1_norm", "twell_l1_grad",
            "twell_ffn_backward_workspace_size", "twell_ffn_backward", "twell_sparse_ffn_fused",
-           "twell_stream_probe")
+           "twell_stream_probe", "twell_mfma_probe")
 
 
 def lib():
@@ -466,3 +467,13 @@ def twell_stream_probe(src, dst, mode: int) -> None:
     if mode == 0 and dst.numel() * dst.element_size() < 4:
         raise ValueError("the sink needs 4 bytes")
     _check(_lib.twell_stream_probe(_ptr(src), _ptr(dst), nbytes, mode, _stream(device)))
+
+
+def twell_mfma_probe(sink, iters: int, blocks: int) -> float:
+    """Matrix-core probe on the current stream; returns the flops it performs
+    (sink: a device tensor of at least 4 bytes)."""
+    _need(sink, "sink", sink.device)
+    if sink.numel() * sink.element_size() < 4:
+        raise ValueError("the sink needs 4 bytes")
+    _check(_lib.twell_mfma_probe(_ptr(sink), iters, blocks, _stream(sink.device)))
+    return 2.0 * 32 * 32 * 16 * 8 * iters * 8 * blocks

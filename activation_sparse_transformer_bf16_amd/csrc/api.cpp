@@ -206,6 +206,13 @@ twell_status twell_stream_probe(const void *src, void *dst, size_t bytes, int mo
   return hip_check(stream_probe(src, dst, bytes, mode, static_cast<hipStream_t>(stream)), "stream probe");
 }
 
+twell_status twell_mfma_probe(float *sink, int iters, int blocks, void *stream) {
+  g_err[0] = 0;
+  if (sink == nullptr || iters < 1 || blocks < 1) return fail(TWELL_ERR_INVALID_ARG, "null sink, iters < 1 or blocks < 1");
+  if (!aligned(sink, 4)) return fail(TWELL_ERR_UNSUPPORTED, "misaligned sink");
+  return hip_check(mfma_probe(sink, iters, blocks, static_cast<hipStream_t>(stream)), "mfma probe");
+}
+
 twell_status twell_pack(const void *pre, twell_matrix *out, void *stream) {
   g_err[0] = 0;
   twell_status st = check_matrix(out, false);

@@ -64,3 +64,44 @@ hipError_t stream_probe(const void *src, void *dst, size_t bytes, int mode, hipS
 }
 
 }  // namespace twell
+
+namespace twell {
+
+// Matrix-core issue-rate probe: every wave runs `iters` rounds of 8
+// independent v_mfma_f32_32x32x16_bf16 on register operands (no memory
+// traffic in the loop), 8 waves per workgroup (two per SIMD).  The sum of the
+// accumulators is stored only when it equals a value the operands cannot
+// give, so the MFMAs stay live and the probe writes nothing.
+constexpr int MFMA_PROBE_THREADS = 512;
+constexpr int MFMA_PROBE_ACC = 8;
+
+__global__ __launch_bounds__(MFMA_PROBE_THREADS) void k_mfma_probe(float *__restrict__ sink, int iters) {
+  f32x16_t acc[MFMA_PROBE_ACC];
+#pragma unroll
+  for (int i = 0; i < MFMA_PROBE_ACC; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
+  bf16x8_t a, b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a[e] = (__bf16)(1e-3f * (float)(threadIdx.x + e));
+    b[e] = (__bf16)(1e-3f * (float)((int)threadIdx.x - e));
+  }
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < MFMA_PROBE_ACC; ++i) acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[i], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < MFMA_PROBE_ACC; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s += acc[i][e];
+  if (s == 1234567.0f) sink[0] = s;
+}
+
+hipError_t mfma_probe(float *sink, int iters, int blocks, hipStream_t s) {
+  hipLaunchKernelGGL(k_mfma_probe, dim3(blocks), dim3(MFMA_PROBE_THREADS), 0, s, sink, iters);
+  return hipGetLastError();
+}
+
+}  // namespace twell

@@ -189,4 +189,8 @@ hipError_t zero_int(int *p, hipStream_t s);
 // mode 1 copies them to dst.
 hipError_t stream_probe(const void *src, void *dst, size_t bytes, int mode, hipStream_t s);
 
+// Matrix-core probe: `blocks` workgroups of 8 waves, each wave `iters` rounds
+// of 8 independent 32x32x16 bf16 MFMAs on registers.
+hipError_t mfma_probe(float *sink, int iters, int blocks, hipStream_t s);
+
 }  // namespace twell

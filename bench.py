@@ -329,10 +329,21 @@ def measure(w, steps, warmup, want_torch=True, want_cold=True, settle_ms=50.0):
     probe["read_frac_of_spec"] = probe["read_GBps"] / HBM_PEAK_GBS
     probe["copy_frac_of_spec"] = probe["copy_GBps"] / HBM_PEAK_GBS
     probe["note"] = ("twell_stream_probe: one 16-byte chunk per thread; read 1 GiB, copy 512 MiB -> 512 MiB "
-                     "(bytes read + written); the measured denominators beside the 8 TB/s spec")
+                     "(bytes read + written); twell_mfma_probe: 32x32x16 bf16 MFMAs on registers; the measured "
+                     "denominators beside the 8 TB/s and 2.5 PFLOP/s specs")
     training["twell_pack_frac_of_measured_read"] = training["twell_pack_GBps"] / probe["read_GBps"]
+    # The library's matrix-core probe: the sustained bf16 MFMA rate of this
+    # device (1024 workgroups of 8 waves, 8 independent MFMAs per round).
+    mfma_flops = [0.0]
+
+    def mfma_run():
+        mfma_flops[0] = tw.twell_mfma_probe(sink, 2000, 1024)
+    ms_mfma, _ = event_time(mfma_run, steps, warmup)
+    probe["mfma_bf16_TFLOPs"] = mfma_flops[0] / (ms_mfma * 1e-3) / 1e12
+    probe["mfma_frac_of_spec"] = probe["mfma_bf16_TFLOPs"] / MFMA_BF16_PEAK_TFLOPS
+    log(f"[bench] mfma probe: {probe['mfma_bf16_TFLOPs']:.0f} TFLOP/s bf16")
     log(f"[bench] stream probe: read {probe['read_GBps']:.0f} GB/s, copy {probe['copy_GBps']:.0f} GB/s")
-    del big, sink, lo, hi
+    del big, lo, hi, sink
 
     # one more forward to read the statistics of this batch
     sparse()
@@ -538,6 +549,8 @@ def main():
         "config": {**w.summary(), "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": ach, "peak": r["peak"], "unit": "TFLOP/s",
                      "frac": ach / r["peak"], "traffic": counted_traffic(w.name),
+                     "measured_peak": r["probe"]["mfma_bf16_TFLOPs"] if w.dtype == "bf16" else None,
+                     "frac_of_measured_peak": ach / r["probe"]["mfma_bf16_TFLOPs"] if w.dtype == "bf16" else None,
                      "kernel": "k_gate_twell (gate matmul + TwELL epilogue)",
                      "duration_us": r["ms_gate_b2b"] * 1e3,
                      "timing": "HIP events around back-to-back launches on the launch stream"},

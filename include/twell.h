@@ -362,6 +362,22 @@ twell_status twell_ffn_backward(const twell_hybrid *h, const void *x, const void
  */
 twell_status twell_stream_probe(const void *src, void *dst, size_t bytes, int mode, void *stream);
 
+/*
+ * twell_mfma_probe -- matrix-core issue-rate probe (a measurement aid, not
+ * part of the layer's computation).
+ *
+ * Launches `blocks` workgroups of 512 threads (8 waves, two per SIMD); every
+ * wave runs `iters` rounds of 8 independent v_mfma_f32_32x32x16_bf16 on
+ * register operands, with no memory traffic in the loop.  The call performs
+ * 2*32*32*16 * 8 * iters * 8 * blocks flops; that ÷ the call's time is the
+ * device's sustained bf16 matrix-core rate, the measured denominator beside
+ * the 2.5 PFLOP/s specification for MFMA-bound kernels.  sink is a 4-byte
+ * device buffer, written only if the accumulators sum to 1234567.
+ * Errors: INVALID_ARG (NULL sink, iters < 1, blocks < 1), UNSUPPORTED (sink
+ * not 4-byte aligned), HIP.
+ */
+twell_status twell_mfma_probe(float *sink, int iters, int blocks, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -224,3 +224,10 @@ def test_stream_probe_validation():
     assert L.twell_stream_probe(FAKE, FAKE + 8, 1024, 1, None) == twell.TWELL_ERR_UNSUPPORTED
     assert L.twell_stream_probe(FAKE, FAKE + 2, 1024, 0, None) == twell.TWELL_ERR_UNSUPPORTED  # sink
     assert L.twell_stream_probe(None, None, 0, 0, None) == twell.TWELL_OK                    # nothing to do
+
+
+def test_mfma_probe_validation():
+    assert L.twell_mfma_probe(None, 10, 4, None) == twell.TWELL_ERR_INVALID_ARG
+    assert L.twell_mfma_probe(FAKE, 0, 4, None) == twell.TWELL_ERR_INVALID_ARG
+    assert L.twell_mfma_probe(FAKE, 10, 0, None) == twell.TWELL_ERR_INVALID_ARG
+    assert L.twell_mfma_probe(FAKE + 2, 10, 4, None) == twell.TWELL_ERR_UNSUPPORTED

@@ -22,3 +22,12 @@ def test_stream_probe_copy_and_read(nbytes):
     torch.cuda.synchronize()
     # the XOR of random bytes equals the sentinel with probability 2^-32
     assert int(sink.item()) in (7, 0x9E3779B9 - (1 << 32))
+
+
+def test_mfma_probe_runs_and_writes_nothing():
+    import torch
+    sink = torch.full((1,), 5.0, dtype=torch.float32, device="cuda:0")
+    flops = tw.twell_mfma_probe(sink, 10, 8)
+    torch.cuda.synchronize()
+    assert flops == 2.0 * 32 * 32 * 16 * 8 * 10 * 8 * 8
+    assert float(sink.item()) == 5.0
