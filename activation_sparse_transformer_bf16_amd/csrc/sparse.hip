@@ -371,6 +371,11 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_down(
   constexpr int STEP = U * EPI;             // entries per iteration
   static_assert(EPI == 1 || EPI == 2, "32 or 64 lanes per entry");
   static_assert(STEP <= 64 && 64 % STEP == 0, "a 64-entry chunk holds whole iterations");
+  // One iteration consumes STEP list entries and a chunk holds the list's
+  // entries rounded up to a multiple of 8 (the zero padding the up kernel
+  // writes); a larger STEP would read entries past them and load weight rows
+  // at stale offsets.
+  static_assert(8 % STEP == 0, "STEP must divide the list padding of 8 entries");
   __shared__ u32x2_t chunk[SP_WAVES][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int part = lane / LPE;                 // which of the EPI entries this lane works on
