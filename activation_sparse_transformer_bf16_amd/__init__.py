@@ -203,6 +203,28 @@ class TwellMatrix:
                    torch.empty((max(ovf_cap, 1), cols), dtype=dtype, device=device) if dense else None,
                    ovf_cap)
 
+    def validate(self, device=None) -> None:
+        """Check every buffer against the matrix's own fields (device, dtype,
+        shape, contiguity) before its pointers reach the library."""
+        torch = _torch()
+        device = self.cnt.device if device is None else device
+        _dtype_code(self.dtype)
+        if self.rows < 0 or self.cols <= 0 or self.tile <= 0 or self.cap <= 0 or self.cols % self.tile:
+            raise ValueError(f"bad TwELL shape rows={self.rows} cols={self.cols} tile={self.tile} cap={self.cap}")
+        nt = self.cols // self.tile
+        _need(self.cnt, "cnt", device, torch.int16, (self.rows, nt))
+        _need(self.val, "val", device, self.dtype, (self.rows, nt, self.cap))
+        _need(self.idx, "idx", device, torch.uint8, (self.rows, nt, self.cap))
+        _need(self.ovf_rows, "ovf_rows", device, torch.int32)
+        if self.ovf_rows.numel() < max(self.ovf_cap, 1):
+            raise ValueError(f"ovf_rows holds {self.ovf_rows.numel()} entries, ovf_cap is {self.ovf_cap}")
+        _need(self.n_ovf, "n_ovf", device, torch.int32, (1,))
+        if self.dense is not None:
+            _need(self.dense, "dense", device, self.dtype)
+            if self.dense.dim() != 2 or self.dense.shape[1] != self.cols or self.dense.shape[0] < self.ovf_cap:
+                raise ValueError(f"dense must have shape (>= {self.ovf_cap}, {self.cols}), "
+                                 f"got {tuple(self.dense.shape)}")
+
     def c_struct(self) -> TwellMatrixC:
         return TwellMatrixC(self.rows, self.cols, self.tile, self.cap, _dtype_code(self.dtype),
                             _ptr(self.cnt), _ptr(self.val), _ptr(self.idx), _ptr(self.ovf_rows),
@@ -243,6 +265,26 @@ class TwellHybrid:
                    torch.empty((max(dense_cap, 1), cols), dtype=dtype, device=device) if dense else None,
                    dense_cap)
 
+    def validate(self, device=None) -> None:
+        """Check every buffer against the hybrid matrix's own fields."""
+        torch = _torch()
+        device = self.cnt.device if device is None else device
+        _dtype_code(self.dtype)
+        if self.rows < 0 or self.cols <= 0 or self.width < 1 or self.dense_cap < 0:
+            raise ValueError(f"bad hybrid shape rows={self.rows} cols={self.cols} width={self.width}")
+        _need(self.cnt, "cnt", device, torch.int32, (self.rows,))
+        _need(self.val, "val", device, self.dtype, (self.rows, self.width))
+        _need(self.col, "col", device, torch.int32, (self.rows, self.width))
+        _need(self.dense_rows, "dense_rows", device, torch.int32)
+        if self.dense_rows.numel() < max(self.dense_cap, 1):
+            raise ValueError(f"dense_rows holds {self.dense_rows.numel()} entries, dense_cap is {self.dense_cap}")
+        _need(self.n_dense, "n_dense", device, torch.int32, (1,))
+        if self.dense is not None:
+            _need(self.dense, "dense", device, self.dtype)
+            if self.dense.dim() != 2 or self.dense.shape[1] != self.cols or self.dense.shape[0] < self.dense_cap:
+                raise ValueError(f"dense must have shape (>= {self.dense_cap}, {self.cols}), "
+                                 f"got {tuple(self.dense.shape)}")
+
     def c_struct(self) -> TwellHybridC:
         return TwellHybridC(self.rows, self.cols, self.width, _dtype_code(self.dtype), _ptr(self.cnt),
                             _ptr(self.val), _ptr(self.col), _ptr(self.dense_rows), _ptr(self.n_dense),
@@ -252,8 +294,12 @@ class TwellHybrid:
 def twell_to_hybrid(packed: TwellMatrix, width: int, dense_cap: Optional[int] = None, dense: bool = True,
                     out: Optional[TwellHybrid] = None) -> TwellHybrid:
     """Convert a TwELL matrix (with its dense backup rows) to the hybrid format."""
+    packed.validate()
     if out is None:
         out = TwellHybrid.empty(packed.rows, packed.cols, width, packed.dtype, packed.device, dense_cap, dense)
+    out.validate(packed.device)
+    if (out.rows, out.cols, out.width, out.dtype) != (packed.rows, packed.cols, width, packed.dtype):
+        raise ValueError("out must be a hybrid matrix of the TwELL matrix's rows, cols and dtype at this width")
     m = packed.c_struct()
     h = out.c_struct()
     _check(_lib.twell_to_hybrid(ctypes.byref(m), ctypes.byref(h), _stream(packed.device)))
@@ -268,8 +314,10 @@ def twell_l1_norm(packed: TwellMatrix, out=None, workspace=None):
     """||h||_1 of the activations a TwELL matrix describes, as a float64 device tensor [1]."""
     torch = _torch()
     device = packed.device
+    packed.validate()
     if out is None:
         out = torch.empty((1,), dtype=torch.float64, device=device)
+    _need(out, "out", device, torch.float64, (1,))
     ws = _workspace(twell_l1_workspace_size(), device, workspace)
     m = packed.c_struct()
     _check(_lib.twell_l1_norm(ctypes.byref(m), _ptr(out), _ptr(ws), ws.numel(), _stream(device)))
@@ -280,10 +328,16 @@ def twell_l1_grad(packed: TwellMatrix, lam: float, grad_val=None, grad_dense=Non
     """d(lam ||h||_1)/dh in the TwELL pattern: (grad_val, grad_dense or None)."""
     torch = _torch()
     device = packed.device
+    packed.validate()
     if grad_val is None:
         grad_val = torch.empty_like(packed.val)
     if grad_dense is None and dense and packed.dense is not None:
         grad_dense = torch.empty_like(packed.dense)
+    _need(grad_val, "grad_val", device, packed.dtype, tuple(packed.val.shape))
+    if grad_dense is not None:
+        if packed.dense is None:
+            raise ValueError("grad_dense needs the TwELL matrix's dense backup rows")
+        _need(grad_dense, "grad_dense", device, packed.dtype, tuple(packed.dense.shape))
     m = packed.c_struct()
     _check(_lib.twell_l1_grad(ctypes.byref(m), ctypes.c_float(lam), _ptr(grad_val), _ptr(grad_dense),
                               _stream(device)))
@@ -302,6 +356,7 @@ def twell_ffn_backward(hy: TwellHybrid, x, w_gate, w_up, w_down, dy, lam: float 
     device = x.device
     T, d = x.shape
     F = hy.cols
+    hy.validate(device)
     _need(x, "x", device, hy.dtype, (hy.rows, d))
     _need(dy, "dy", device, hy.dtype, (T, d))
     for w, name in ((w_gate, "w_gate"), (w_up, "w_up"), (w_down, "w_down")):
@@ -329,9 +384,16 @@ def twell_pack(pre, tile: int, cap: int, ovf_cap: Optional[int] = None, dense: b
     """Pack a pre-activation matrix [T, F] (fp32 or bf16, on the GPU) into TwELL."""
     device = pre.device
     _need(pre, "pre", device)
+    _dtype_code(pre.dtype)
+    if pre.dim() != 2:
+        raise ValueError(f"pre must be 2-D [T, F], got shape {tuple(pre.shape)}")
     T, F = pre.shape
     if out is None:
         out = TwellMatrix.empty(T, F, tile, cap, pre.dtype, device, ovf_cap, dense)
+    out.validate(device)
+    if (out.rows, out.cols, out.tile, out.cap, out.dtype) != (T, F, tile, cap, pre.dtype):
+        raise ValueError(f"out ({out.rows}x{out.cols}, tile {out.tile}, cap {out.cap}, {out.dtype}) does not "
+                         f"match pre ({T}x{F}, {pre.dtype}) at tile {tile}, cap {cap}")
     m = out.c_struct()
     _check(_lib.twell_pack(_ptr(pre), ctypes.byref(m), _stream(device)))
     return out
@@ -348,9 +410,12 @@ def dense_ffn_workspace_size(T: int, d: int, F: int, dtype) -> int:
 def _ffn_checks(x, w_gate, w_up, w_down, gate_bias):
     torch = _torch()
     device = x.device
+    if x.dim() != 2 or w_gate.dim() != 2:
+        raise ValueError("x and the weights must be 2-D")
     T, d = x.shape
     F = w_gate.shape[0]
     _need(x, "x", device)
+    _dtype_code(x.dtype)
     for name, w in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
         _need(w, name, device, x.dtype, (F, d))
     if gate_bias is not None:
@@ -360,9 +425,19 @@ def _ffn_checks(x, w_gate, w_up, w_down, gate_bias):
 
 def _workspace(nbytes: int, device, workspace=None):
     torch = _torch()
-    if workspace is not None and workspace.numel() * workspace.element_size() >= nbytes:
-        return workspace
+    if workspace is not None:
+        _need(workspace, "workspace", device, torch.uint8)
+        if workspace.numel() >= nbytes:
+            return workspace
     return torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=device)
+
+
+def _packed_for(packed: TwellMatrix, device, T: int, F: int, dtype) -> None:
+    """A caller's TwELL matrix must describe exactly the activations of x."""
+    packed.validate(device)
+    if (packed.rows, packed.cols, packed.dtype) != (T, F, dtype):
+        raise ValueError(f"packed ({packed.rows}x{packed.cols}, {packed.dtype}) does not match the layer "
+                         f"({T} tokens x {F} units, {dtype})")
 
 
 def twell_ffn_forward(x, w_gate, w_up, w_down, gate_bias=None, tile: int = 256, cap: int = 16,
@@ -373,8 +448,10 @@ def twell_ffn_forward(x, w_gate, w_up, w_down, gate_bias=None, tile: int = 256, 
     device, T, d, F = _ffn_checks(x, w_gate, w_up, w_down, gate_bias)
     if packed is None:
         packed = TwellMatrix.empty(T, F, tile, cap, x.dtype, device, T, dense=False)
+    _packed_for(packed, device, T, F, x.dtype)
     if y is None:
         y = torch.empty((T, d), dtype=x.dtype, device=device)
+    _need(y, "y", device, x.dtype, (T, d))
     ws = _workspace(twell_ffn_workspace_size(T, d, F, packed.tile, packed.cap, x.dtype), device, workspace)
     m = packed.c_struct()
     _check(_lib.twell_ffn_forward(_ptr(x), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(gate_bias),
@@ -389,14 +466,18 @@ def twell_gate_pack(x, w_gate, gate_bias=None, tile: int = 256, cap: int = 16,
     scan; returns (packed, pre or None)."""
     torch = _torch()
     device = x.device
+    if x.dim() != 2 or w_gate.dim() != 2:
+        raise ValueError("x and w_gate must be 2-D")
     T, d = x.shape
     F = w_gate.shape[0]
     _need(x, "x", device)
+    _dtype_code(x.dtype)
     _need(w_gate, "w_gate", device, x.dtype, (F, d))
     if gate_bias is not None:
         _need(gate_bias, "gate_bias", device, torch.float32, (T,))
     if packed is None:
         packed = TwellMatrix.empty(T, F, tile, cap, x.dtype, device, T, dense=False)
+    _packed_for(packed, device, T, F, x.dtype)
     pre = torch.empty((T, F), dtype=x.dtype, device=device) if pre_out else None
     m = packed.c_struct()
     _check(_lib.twell_gate_pack(_ptr(x), _ptr(w_gate), _ptr(gate_bias), d, ctypes.byref(m),
@@ -408,6 +489,7 @@ def twell_gate_pack(x, w_gate, gate_bias=None, tile: int = 256, cap: int = 16,
 
 def twell_overflow_scan(packed: TwellMatrix) -> TwellMatrix:
     """List the overflowing rows of a packed matrix (fills ovf_rows and n_ovf)."""
+    packed.validate()
     m = packed.c_struct()
     _check(_lib.twell_overflow_scan(ctypes.byref(m), _stream(packed.device)))
     return packed
@@ -418,8 +500,10 @@ def twell_sparse_ffn(packed: TwellMatrix, x, w_gate, w_up, w_down, gate_bias=Non
     """Up / down projections over TwELL plus the dense fallback; returns y."""
     torch = _torch()
     device, T, d, F = _ffn_checks(x, w_gate, w_up, w_down, gate_bias)
+    _packed_for(packed, device, T, F, x.dtype)
     if y is None:
         y = torch.empty((T, d), dtype=x.dtype, device=device)
+    _need(y, "y", device, x.dtype, (T, d))
     ws = _workspace(twell_ffn_workspace_size(T, d, F, packed.tile, packed.cap, x.dtype), device, workspace)
     m = packed.c_struct()
     _check(_lib.twell_sparse_ffn(ctypes.byref(m), _ptr(x), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
@@ -433,8 +517,10 @@ def twell_sparse_ffn_fused(packed: TwellMatrix, x, w_gate, w_up, w_down, gate_bi
     """twell_sparse_ffn with the up and down projections in one kernel; returns y."""
     torch = _torch()
     device, T, d, F = _ffn_checks(x, w_gate, w_up, w_down, gate_bias)
+    _packed_for(packed, device, T, F, x.dtype)
     if y is None:
         y = torch.empty((T, d), dtype=x.dtype, device=device)
+    _need(y, "y", device, x.dtype, (T, d))
     ws = _workspace(twell_ffn_workspace_size(T, d, F, packed.tile, packed.cap, x.dtype), device, workspace)
     m = packed.c_struct()
     _check(_lib.twell_sparse_ffn_fused(ctypes.byref(m), _ptr(x), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
@@ -448,6 +534,7 @@ def dense_ffn_forward(x, w_gate, w_up, w_down, gate_bias=None, y=None, workspace
     device, T, d, F = _ffn_checks(x, w_gate, w_up, w_down, gate_bias)
     if y is None:
         y = torch.empty((T, d), dtype=x.dtype, device=device)
+    _need(y, "y", device, x.dtype, (T, d))
     ws = _workspace(dense_ffn_workspace_size(T, d, F, x.dtype), device, workspace)
     _check(_lib.dense_ffn_forward(_ptr(x), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(gate_bias),
                                   _ptr(y), T, d, F, _dtype_code(x.dtype), _ptr(ws), ws.numel(),

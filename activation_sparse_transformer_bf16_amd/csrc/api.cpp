@@ -45,6 +45,7 @@ twell_status hip_check(hipError_t e, const char *what) {
   } while (0)
 
 constexpr size_t ALIGN_WS = 256;
+constexpr int GEMM_ROWS = 256;  // rows of one fallback matmul tile
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -101,25 +102,64 @@ twell_status check_matrix(const twell_matrix *m, bool need_ovf_all) {
   return TWELL_OK;
 }
 
-// Workspace of the sparse forward: row flags | compact entry lists (8 bytes per
-// entry) | entry counts | dense fallback activations | the fallback's split-K
-// partial tiles (64 MB).
+// Workspace of the sparse forward:
+//   row flags [T] u8 | entry counts [T] i32 |
+//   region A: the compact entry lists [T][stride] x 8 bytes, and afterwards
+//             (the lists are consumed by the down projection before the
+//             fallback starts, in stream order) the fallback's activations
+//             [R][F] in the storage dtype for one chunk of R overflow rows |
+//   the fallback's split-K partial tiles (only as many as a split can use).
+// The fallback takes the overflow rows R at a time, so the workspace stays
+// below the dense [T][F] activation matrix it replaces.
 struct FfnWs {
-  size_t flag, list, list_n, a, partial, total;
-  int stride;
+  size_t flag, list_n, list, a, partial, total;
+  int stride, chunk_rows, partial_tiles;
 };
 
-FfnWs ffn_ws_layout(int T, int F, int tile, int cap, twell_dtype dt) {
+// Rows per fallback chunk: half the batch (rounded up to 256 rows), all of
+// it for T <= 512; so the common case (few or no overflow rows) is one chunk
+// and the worst case (every row overflows) two.
+int default_chunk_rows(int T) {
+  const int half = (T + 1) / 2;
+  return std::max(1, std::min(T, (half + 255) / 256 * 256));
+}
+
+// The largest number of partial tiles the fallback's split-K can use with
+// chunks of R rows (the device picks S with the same fallback_split).
+int fallback_partial_tiles(int R, int d, int F, twell_dtype dt) {
+  const int s = dt_size(dt);
+  const int row_tiles = (R + GEMM_ROWS - 1) / GEMM_ROWS;
+  const int nk_gu = d * s / 64, ntl_gu = F / 128;   // gate+up: 64-byte K slabs, 128-unit tiles
+  const int nk_dn = F * s / 128, ntl_dn = d / 256;  // down: 128-byte K chunks, 256-column tiles
+  int best = 0;
+  for (int rt = 1; rt <= row_tiles; ++rt) {
+    const int tg = rt * ntl_gu, td = rt * ntl_dn;
+    const int sg = fallback_split(tg, nk_gu, GATE_UP_SPLIT_MAX, FALLBACK_PARTIAL_TILES_MAX);
+    const int sd = fallback_split(td, nk_dn, DOWN_SPLIT_MAX, FALLBACK_PARTIAL_TILES_MAX);
+    if (sg > 1) best = std::max(best, sg * tg);
+    if (sd > 1) best = std::max(best, sd * td);
+  }
+  return best;
+}
+
+FfnWs ffn_ws_layout(int T, int d, int F, int tile, int cap, twell_dtype dt, int chunk_rows) {
   FfnWs w;
   const size_t nt = (size_t)F / tile;
   w.stride = (int)((nt * cap + 7) / 8 * 8);
+  w.chunk_rows = chunk_rows;
+  w.partial_tiles = T > 0 ? fallback_partial_tiles(chunk_rows, d, F, dt) : 0;
   w.flag = 0;
-  w.list = align_up((size_t)T, ALIGN_WS);
-  w.list_n = align_up(w.list + (size_t)T * w.stride * 8, ALIGN_WS);
-  w.a = align_up(w.list_n + (size_t)T * 4, ALIGN_WS);
-  w.partial = align_up(w.a + (size_t)T * F * dt_size(dt), ALIGN_WS);
-  w.total = std::max(align_up(w.partial + (T > 0 ? FALLBACK_PARTIAL_FLOATS * 4 : 0), ALIGN_WS), ALIGN_WS);
+  w.list_n = align_up((size_t)T, ALIGN_WS);
+  w.list = align_up(w.list_n + (size_t)T * 4, ALIGN_WS);
+  w.a = w.list;  // aliases the lists (see above)
+  const size_t region = std::max((size_t)T * w.stride * 8, (size_t)chunk_rows * F * dt_size(dt));
+  w.partial = align_up(w.list + region, ALIGN_WS);
+  w.total = std::max(align_up(w.partial + (size_t)w.partial_tiles * FALLBACK_SPLIT_TILE * 4, ALIGN_WS), ALIGN_WS);
   return w;
+}
+
+FfnWs ffn_ws_layout(int T, int d, int F, int tile, int cap, twell_dtype dt) {
+  return ffn_ws_layout(T, d, F, tile, cap, dt, default_chunk_rows(T));
 }
 
 twell_status check_ffn_ptrs(const void *x, const void *wg, const void *wu, const void *wd, const float *beta,
@@ -131,15 +171,39 @@ twell_status check_ffn_ptrs(const void *x, const void *wg, const void *wu, const
   return TWELL_OK;
 }
 
+// The overflow-row list, then the dense fallback over it, chunk by chunk.
+// Chunk c takes list positions [c R, c R + R); its kernels read *n_ovf on the
+// device and exit at once when the list is shorter.  Only the first chunk
+// may split K (a later chunk runs only when more than R rows overflow, which
+// fills the grid).
+twell_status run_fallback(const twell_matrix *m, const void *x, const void *wg, const void *wu, const void *wd,
+                          const float *beta, void *y, int d, const FfnWs &L, char *base, const uint8_t *row_flag,
+                          hipStream_t s) {
+  const int T = m->rows, F = m->cols, R = L.chunk_rows;
+  const Dt D = to_dt(m->dtype);
+  TW_TRY(compact_rows(row_flag, T, m->ovf_rows, m->ovf_cap, m->n_ovf, s), "overflow row list");
+  for (int c0 = 0; c0 < T; c0 += R) {
+    const int rows = std::min(R, T - c0);
+    const bool first = c0 == 0;
+    const int h_cap = std::max(0, std::min(m->ovf_cap - c0, rows));
+    void *h_out = (m->dense != nullptr && h_cap > 0)
+                      ? static_cast<char *>(m->dense) + (size_t)c0 * F * dt_size(m->dtype)
+                      : nullptr;
+    DenseArgs da{D, x, wg, wu, wd, beta, y, rows, d, F, m->ovf_rows + c0, m->n_ovf, c0, base + L.a, h_out, h_cap,
+                 first ? reinterpret_cast<float *>(base + L.partial) : nullptr, first ? L.partial_tiles : 0};
+    TW_TRY(dense_gate_up(da, s), "fallback gate/up matmul");
+    TW_TRY(dense_down(da, s), "fallback down matmul");
+  }
+  return TWELL_OK;
+}
+
 twell_status run_sparse(const twell_matrix *m, const void *x, const void *wg, const void *wu, const void *wd,
-                        const float *beta, void *y, int d, void *ws, hipStream_t s) {
+                        const float *beta, void *y, int d, void *ws, const FfnWs &L, hipStream_t s) {
   const int T = m->rows, F = m->cols;
-  const FfnWs L = ffn_ws_layout(T, F, m->tile, m->cap, m->dtype);
   char *base = static_cast<char *>(ws);
   uint8_t *row_flag = reinterpret_cast<uint8_t *>(base + L.flag);
   void *list = base + L.list;
   int *list_n = reinterpret_cast<int *>(base + L.list_n);
-  void *a_ws = base + L.a;
   const Dt D = to_dt(m->dtype);
 
   // The up kernel finds the overflow rows itself (row_flag); their list
@@ -147,33 +211,20 @@ twell_status run_sparse(const twell_matrix *m, const void *x, const void *wg, co
   SparseArgs sa{D, T, d, F, m->tile, m->cap, m->cnt, m->val, m->idx, row_flag, x, wu, wd, list, list_n, L.stride, y};
   TW_TRY(sparse_up(sa, s), "sparse up projection");
   TW_TRY(sparse_down(sa, s), "sparse down projection");
-  TW_TRY(compact_rows(row_flag, T, m->ovf_rows, m->ovf_cap, m->n_ovf, s), "overflow row list");
-
-  DenseArgs da{D, x, wg, wu, wd, beta, y, T, d, F, m->ovf_rows, m->n_ovf, a_ws, m->dense, m->ovf_cap,
-               reinterpret_cast<float *>(base + L.partial)};
-  TW_TRY(dense_gate_up(da, s), "fallback gate/up matmul");
-  TW_TRY(dense_down(da, s), "fallback down matmul");
-  return TWELL_OK;
+  return run_fallback(m, x, wg, wu, wd, beta, y, d, L, base, row_flag, s);
 }
 
 // The same sequence with the fused up+down kernel in place of the two gather
 // kernels (the compact lists are not used).
 twell_status run_sparse_fused(const twell_matrix *m, const void *x, const void *wg, const void *wu, const void *wd,
-                              const float *beta, void *y, int d, void *ws, hipStream_t s) {
+                              const float *beta, void *y, int d, void *ws, const FfnWs &L, hipStream_t s) {
   const int T = m->rows, F = m->cols;
-  const FfnWs L = ffn_ws_layout(T, F, m->tile, m->cap, m->dtype);
   char *base = static_cast<char *>(ws);
   uint8_t *row_flag = reinterpret_cast<uint8_t *>(base + L.flag);
-  void *a_ws = base + L.a;
   const Dt D = to_dt(m->dtype);
   SparseArgs sa{D, T, d, F, m->tile, m->cap, m->cnt, m->val, m->idx, row_flag, x, wu, wd, nullptr, nullptr, 0, y};
   TW_TRY(sparse_fused(sa, s), "fused sparse up/down projection");
-  TW_TRY(compact_rows(row_flag, T, m->ovf_rows, m->ovf_cap, m->n_ovf, s), "overflow row list");
-  DenseArgs da{D, x, wg, wu, wd, beta, y, T, d, F, m->ovf_rows, m->n_ovf, a_ws, m->dense, m->ovf_cap,
-               reinterpret_cast<float *>(base + L.partial)};
-  TW_TRY(dense_gate_up(da, s), "fallback gate/up matmul");
-  TW_TRY(dense_down(da, s), "fallback down matmul");
-  return TWELL_OK;
+  return run_fallback(m, x, wg, wu, wd, beta, y, d, L, base, row_flag, s);
 }
 
 }  // namespace
@@ -245,7 +296,7 @@ size_t twell_ffn_workspace_size(int T, int d, int F, int tile, int cap, twell_dt
   if (T < 0 || check_format(tile, cap, F, (int)dtype) != TWELL_OK || check_d(d, (int)dtype) != TWELL_OK ||
       check_weight_bytes(F, d, (int)dtype) != TWELL_OK)
     return 0;
-  return ffn_ws_layout(T, F, tile, cap, dtype).total;
+  return ffn_ws_layout(T, d, F, tile, cap, dtype).total;
 }
 
 twell_status twell_gate_pack(const void *x, const void *w_gate, const float *gate_bias, int d, twell_matrix *packed,
@@ -354,13 +405,14 @@ twell_status twell_sparse_ffn(const twell_matrix *packed, const void *x, const v
   if ((st = check_weight_bytes(packed->cols, d, (int)packed->dtype)) != TWELL_OK) return st;
   if (packed->rows == 0) return hip_check(zero_int(packed->n_ovf, static_cast<hipStream_t>(stream)), "zero n_ovf");
   if ((st = check_ffn_ptrs(x, w_gate, w_up, w_down, gate_bias, y)) != TWELL_OK) return st;
-  const size_t need = ffn_ws_layout(packed->rows, packed->cols, packed->tile, packed->cap, packed->dtype).total;
+  const FfnWs L = ffn_ws_layout(packed->rows, d, packed->cols, packed->tile, packed->cap, packed->dtype);
+  const size_t need = L.total;
   if (workspace == nullptr || ws_bytes < need)
     return fail(TWELL_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : 0);
   if (!aligned(workspace, ALIGN_WS)) return fail(TWELL_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (packed->rows == 0) return hip_check(zero_int(packed->n_ovf, s), "zero n_ovf");
-  return run_sparse(packed, x, w_gate, w_up, w_down, gate_bias, y, d, workspace, s);
+  return run_sparse(packed, x, w_gate, w_up, w_down, gate_bias, y, d, workspace, L, s);
 }
 
 twell_status twell_sparse_ffn_fused(const twell_matrix *packed, const void *x, const void *w_gate, const void *w_up,
@@ -376,11 +428,12 @@ twell_status twell_sparse_ffn_fused(const twell_matrix *packed, const void *x, c
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (packed->rows == 0) return hip_check(zero_int(packed->n_ovf, s), "zero n_ovf");
   if ((st = check_ffn_ptrs(x, w_gate, w_up, w_down, gate_bias, y)) != TWELL_OK) return st;
-  const size_t need = ffn_ws_layout(packed->rows, packed->cols, packed->tile, packed->cap, packed->dtype).total;
+  const FfnWs L = ffn_ws_layout(packed->rows, d, packed->cols, packed->tile, packed->cap, packed->dtype);
+  const size_t need = L.total;
   if (workspace == nullptr || ws_bytes < need)
     return fail(TWELL_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : 0);
   if (!aligned(workspace, ALIGN_WS)) return fail(TWELL_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
-  return run_sparse_fused(packed, x, w_gate, w_up, w_down, gate_bias, y, d, workspace, s);
+  return run_sparse_fused(packed, x, w_gate, w_up, w_down, gate_bias, y, d, workspace, L, s);
 }
 
 twell_status twell_ffn_forward(const void *x, const void *w_gate, const void *w_up, const void *w_down,
@@ -393,7 +446,8 @@ twell_status twell_ffn_forward(const void *x, const void *w_gate, const void *w_
   if ((st = check_weight_bytes(packed->cols, d, (int)packed->dtype)) != TWELL_OK) return st;
   if (packed->rows == 0) return hip_check(zero_int(packed->n_ovf, static_cast<hipStream_t>(stream)), "zero n_ovf");
   if ((st = check_ffn_ptrs(x, w_gate, w_up, w_down, gate_bias, y)) != TWELL_OK) return st;
-  const size_t need = ffn_ws_layout(packed->rows, packed->cols, packed->tile, packed->cap, packed->dtype).total;
+  const FfnWs L = ffn_ws_layout(packed->rows, d, packed->cols, packed->tile, packed->cap, packed->dtype);
+  const size_t need = L.total;
   if (workspace == nullptr || ws_bytes < need)
     return fail(TWELL_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : 0);
   if (!aligned(workspace, ALIGN_WS)) return fail(TWELL_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
@@ -403,7 +457,7 @@ twell_status twell_ffn_forward(const void *x, const void *w_gate, const void *w_
   GateArgs ga{to_dt(packed->dtype), packed->tile, x, w_gate, gate_bias, T, d, F, packed->cap,
               packed->cnt, packed->val, packed->idx, nullptr};
   TW_TRY(gate_twell(ga, s), "gate matmul");
-  return run_sparse(packed, x, w_gate, w_up, w_down, gate_bias, y, d, workspace, s);
+  return run_sparse(packed, x, w_gate, w_up, w_down, gate_bias, y, d, workspace, L, s);
 }
 
 }  // extern "C"
@@ -533,8 +587,8 @@ twell_status dense_ffn_forward(const void *x, const void *w_gate, const void *w_
   if (!aligned(workspace, ALIGN_WS)) return fail(TWELL_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
   if (T == 0) return TWELL_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  DenseArgs da{to_dt(dtype), x, w_gate, w_up, w_down, gate_bias, y, T, d, F, nullptr, nullptr, workspace,
-               nullptr, 0};
+  DenseArgs da{to_dt(dtype), x, w_gate, w_up, w_down, gate_bias, y, T, d, F, nullptr, nullptr, 0, workspace,
+               nullptr, 0, nullptr, 0};
   TW_TRY(dense_gate_up(da, s), "dense gate/up matmul");
   TW_TRY(dense_down(da, s), "dense down matmul");
   return TWELL_OK;

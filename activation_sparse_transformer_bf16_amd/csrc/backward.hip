@@ -312,7 +312,8 @@ __global__ __launch_bounds__(SP_THREADS) void k_bw_entries(RowSrc<typename DtT<D
   group_coords(blockIdx.x, n_groups, n_tb, g, tb);
   if (g >= n_groups) return;
   const int j0 = g * upg, j1 = min(s.F, j0 + upg);
-  const __amdgpu_buffer_rsrc_t wur = buffer_rsrc(wu), wdr = buffer_rsrc(wd);
+  const size_t w_bytes = (size_t)s.F * d * sizeof(TT);
+  const __amdgpu_buffer_rsrc_t wur = buffer_rsrc(wu, w_bytes), wdr = buffer_rsrc(wd, w_bytes);
   const uint32_t lane_off = lane * 16;
   const uint32_t row_bytes = (uint32_t)d * sizeof(TT);
   const int my = U == 2 ? lane >> 5 : 0;  // the entry whose u this lane's row holds (storer lanes)
@@ -448,7 +449,9 @@ __global__ __launch_bounds__(SP_THREADS) void k_bw_dx(RowSrc<typename DtT<D>::T>
   int sl, tb;
   group_coords(blockIdx.x, n_slices, n_tb, sl, tb);
   if (sl >= n_slices) return;
-  const __amdgpu_buffer_rsrc_t wur = buffer_rsrc(wu + sl * DX_SLICE), wgr = buffer_rsrc(wg + sl * DX_SLICE);
+  const size_t w_bytes = ((size_t)s.F * d - (size_t)sl * DX_SLICE) * sizeof(TT);
+  const __amdgpu_buffer_rsrc_t wur = buffer_rsrc(wu + sl * DX_SLICE, w_bytes),
+                               wgr = buffer_rsrc(wg + sl * DX_SLICE, w_bytes);
   const uint32_t lane_off = lcol * sizeof(TT);
   const uint32_t row_bytes = (uint32_t)d * sizeof(TT);
   u32x4_t *C = chunk[wave];
@@ -480,8 +483,9 @@ __global__ __launch_bounds__(SP_THREADS) void k_bw_dx(RowSrc<typename DtT<D>::T>
           const u32x4_t en = C[ok ? q : 0];
           cu[u] = ok ? __uint_as_float(en[1]) : 0.f;
           cg[u] = ok ? __uint_as_float(en[2]) : 0.f;
-          a[u] = buffer_load<u32x4_t>(wur, lane_off + en[0], 0u);
-          b[u] = buffer_load<u32x4_t>(wgr, lane_off + en[0], 0u);
+          const uint32_t ro = ok ? en[0] : NO_ROW;  // past the list: loads return zeros
+          a[u] = buffer_load<u32x4_t>(wur, lane_off + ro, 0u);
+          b[u] = buffer_load<u32x4_t>(wgr, lane_off + ro, 0u);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -532,7 +536,8 @@ __global__ __launch_bounds__(SP_THREADS) void k_bw_dw(const int *__restrict__ co
   int sl, ub;
   group_coords(blockIdx.x, n_slices, n_ub, sl, ub);
   if (sl >= n_slices) return;
-  const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(x + sl * DW_SLICE), gr = buffer_rsrc(dy + sl * DW_SLICE);
+  const size_t a_bytes = ((size_t)T * d - (size_t)sl * DW_SLICE) * sizeof(TT);
+  const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(x + sl * DW_SLICE, a_bytes), gr = buffer_rsrc(dy + sl * DW_SLICE, a_bytes);
   const uint32_t lane_off = lcol * sizeof(TT);
   const uint32_t row_bytes = (uint32_t)d * sizeof(TT);
   u32x4_t *C = chunk[wave];
@@ -562,8 +567,9 @@ __global__ __launch_bounds__(SP_THREADS) void k_bw_dw(const int *__restrict__ co
           ca[u] = ok ? __uint_as_float(en[1]) : 0.f;
           cu[u] = ok ? __uint_as_float(en[2]) : 0.f;
           cg[u] = ok ? __uint_as_float(en[3]) : 0.f;
-          a[u] = buffer_load<u32x4_t>(xr, lane_off + en[0], 0u);
-          b[u] = buffer_load<u32x4_t>(gr, lane_off + en[0], 0u);
+          const uint32_t ro = ok ? en[0] : NO_ROW;  // past the list: loads return zeros
+          a[u] = buffer_load<u32x4_t>(xr, lane_off + ro, 0u);
+          b[u] = buffer_load<u32x4_t>(gr, lane_off + ro, 0u);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {

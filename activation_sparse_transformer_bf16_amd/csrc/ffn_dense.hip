@@ -22,20 +22,14 @@
 
 namespace twell {
 
-constexpr int FALLBACK_WGS = 256;       // grid of the fallback kernels
-constexpr int SPLIT_TILE = GEMM_BM * 256;  // floats of one partial tile (256 x 256)
+constexpr int SPLIT_TILE = FALLBACK_SPLIT_TILE;
+static_assert(SPLIT_TILE == GEMM_BM * 256, "a partial tile is one 256 x 256 output tile");
 
-// K ranges per output tile for the fallback: enough to give every workgroup
-// of the grid a work item, at most smax and at most nk (K slabs).  The limits
-// are measured: each K range adds a 256 KB fp32 partial tile written and read
-// back, and past 2 ranges (gate+up, K = d) or 16 (down, K = d_ff) that traffic
-// costs more than the idle workgroups it would fill.
-__device__ __forceinline__ int fallback_split(int tiles, int nk, int smax) {
-  const int s = min(min(FALLBACK_WGS / max(tiles, 1), smax), nk);
-  return max(s, 1);
-}
-constexpr int GATE_UP_SPLIT_MAX = 2;
-constexpr int DOWN_SPLIT_MAX = 16;
+// K ranges per output tile (fallback_split): enough to give every workgroup
+// of the grid a work item, at most GATE_UP_SPLIT_MAX / DOWN_SPLIT_MAX.  The
+// limits are measured: each K range adds a 256 KB fp32 partial tile written
+// and read back, and past 2 ranges (gate+up, K = d) or 16 (down, K = d_ff)
+// that traffic costs more than the idle workgroups it would fill.
 constexpr int REDUCE_BATCH = 8;  // partials loaded together by the reduction kernels (added in K order)
 
 // Partial tiles are stored in the accumulators' own order: register i of
@@ -201,8 +195,9 @@ template <Dt D>
 __global__ __launch_bounds__(DMA_THREADS) void k_gate_up(
     const typename DtT<D>::T *__restrict__ x, const typename DtT<D>::T *__restrict__ wg,
     const typename DtT<D>::T *__restrict__ wu, const float *__restrict__ beta, int M, int K, int F,
-    const int *__restrict__ rows, const int *__restrict__ n_rows_dev, typename DtT<D>::T *__restrict__ a_ws,
-    typename DtT<D>::T *__restrict__ h_out, int h_cap, float *__restrict__ partial) {
+    const int *__restrict__ rows, const int *__restrict__ n_rows_dev, int n_sub,
+    typename DtT<D>::T *__restrict__ a_ws, typename DtT<D>::T *__restrict__ h_out, int h_cap,
+    float *__restrict__ partial, int partial_tiles) {
   using T = typename DtT<D>::T;
   const int nk = (int)((size_t)K * sizeof(T) / SLAB);
   const int mt = (M + GEMM_BM - 1) / GEMM_BM, ntl = F / 128;
@@ -212,9 +207,9 @@ __global__ __launch_bounds__(DMA_THREADS) void k_gate_up(
     gate_up_tile<D>(tm, tn, 0, nk, nullptr, x, wg, wu, beta, M, K, F, rows, M, a_ws, h_out, h_cap);
     return;
   }
-  const int n_eff = min(*n_rows_dev, M);
+  const int n_eff = min(max(*n_rows_dev - n_sub, 0), M);
   const int tiles = (n_eff + GEMM_BM - 1) / GEMM_BM * ntl;
-  const int S = fallback_split(tiles, nk, GATE_UP_SPLIT_MAX);
+  const int S = fallback_split(tiles, nk, GATE_UP_SPLIT_MAX, partial_tiles);
   for (int w = blockIdx.x; w < tiles * S; w += gridDim.x) {
     const int tile = w / S, kc = w - tile * S;
     const int k0 = kc * nk / S, k1 = (kc + 1) * nk / S;
@@ -229,15 +224,16 @@ template <Dt D>
 __global__ __launch_bounds__(256) void k_gate_up_reduce(const float *__restrict__ partial,
                                                         const float *__restrict__ beta, int M, int K, int F,
                                                         const int *__restrict__ rows,
-                                                        const int *__restrict__ n_rows_dev,
+                                                        const int *__restrict__ n_rows_dev, int n_sub,
                                                         typename DtT<D>::T *__restrict__ a_ws,
-                                                        typename DtT<D>::T *__restrict__ h_out, int h_cap) {
+                                                        typename DtT<D>::T *__restrict__ h_out, int h_cap,
+                                                        int partial_tiles) {
   using T = typename DtT<D>::T;
   const int nk = (int)((size_t)K * sizeof(T) / SLAB);
   const int ntl = F / 128;
-  const int n_eff = min(*n_rows_dev, M);
+  const int n_eff = min(max(*n_rows_dev - n_sub, 0), M);
   const int tiles = (n_eff + GEMM_BM - 1) / GEMM_BM * ntl;
-  const int S = fallback_split(tiles, nk, GATE_UP_SPLIT_MAX);
+  const int S = fallback_split(tiles, nk, GATE_UP_SPLIT_MAX, partial_tiles);
   if (S == 1) return;
   const size_t total = (size_t)tiles * GEMM_BM * 128;
   for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (size_t)gridDim.x * 256) {
@@ -282,15 +278,15 @@ __global__ __launch_bounds__(256) void k_gate_up_reduce(const float *__restrict_
 template <Dt D, bool LOOP>
 __global__ __launch_bounds__(GEMM_THREADS) void k_down(
     const typename DtT<D>::T *__restrict__ a_ws, const typename DtT<D>::T *__restrict__ wd, int M, int K,
-    int N, const int *__restrict__ rows, const int *__restrict__ n_rows_dev,
-    typename DtT<D>::T *__restrict__ y, float *__restrict__ partial) {
+    int N, const int *__restrict__ rows, const int *__restrict__ n_rows_dev, int n_sub,
+    typename DtT<D>::T *__restrict__ y, float *__restrict__ partial, int partial_tiles) {
   using T = typename DtT<D>::T;
   const int nk = K / (KCHUNK_BYTES / (int)sizeof(T));
   const int mt = (M + GEMM_BM - 1) / GEMM_BM, ntl = N / 256;
   if constexpr (LOOP) {
-    const int n_eff = min(*n_rows_dev, M);
+    const int n_eff = min(max(*n_rows_dev - n_sub, 0), M);
     const int tiles = (n_eff + GEMM_BM - 1) / GEMM_BM * ntl;
-    const int S = fallback_split(tiles, nk, DOWN_SPLIT_MAX);
+    const int S = fallback_split(tiles, nk, DOWN_SPLIT_MAX, partial_tiles);
     for (int w = blockIdx.x; w < tiles * S; w += gridDim.x) {
       const int tile = w / S, kc = w - tile * S;
       const int k0 = kc * nk / S, k1 = (kc + 1) * nk / S;
@@ -308,14 +304,14 @@ __global__ __launch_bounds__(GEMM_THREADS) void k_down(
 template <Dt D>
 __global__ __launch_bounds__(256) void k_down_reduce(const float *__restrict__ partial, int M, int K, int N,
                                                      const int *__restrict__ rows,
-                                                     const int *__restrict__ n_rows_dev,
-                                                     typename DtT<D>::T *__restrict__ y) {
+                                                     const int *__restrict__ n_rows_dev, int n_sub,
+                                                     typename DtT<D>::T *__restrict__ y, int partial_tiles) {
   using T = typename DtT<D>::T;
   const int nk = K / (KCHUNK_BYTES / (int)sizeof(T));
   const int ntl = N / 256;
-  const int n_eff = min(*n_rows_dev, M);
+  const int n_eff = min(max(*n_rows_dev - n_sub, 0), M);
   const int tiles = (n_eff + GEMM_BM - 1) / GEMM_BM * ntl;
-  const int S = fallback_split(tiles, nk, DOWN_SPLIT_MAX);
+  const int S = fallback_split(tiles, nk, DOWN_SPLIT_MAX, partial_tiles);
   if (S == 1) return;
   const size_t total = (size_t)tiles * SPLIT_TILE;
   for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (size_t)gridDim.x * 256) {
@@ -350,12 +346,13 @@ static hipError_t launch_gate_up(const DenseArgs &a, hipStream_t s) {
   const int mt = (a.M + GEMM_BM - 1) / GEMM_BM, ntl = a.F / 128;
   const int grid = a.n_rows_dev ? FALLBACK_WGS : mt * ntl;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(DMA_THREADS), lds, s, (const T *)a.x, (const T *)a.wg,
-                     (const T *)a.wu, a.beta, a.M, a.d, a.F, a.rows, a.n_rows_dev, (T *)a.a_ws,
-                     (T *)a.h_out, a.h_cap, a.partial);
+                     (const T *)a.wu, a.beta, a.M, a.d, a.F, a.rows, a.n_rows_dev, a.n_sub, (T *)a.a_ws,
+                     (T *)a.h_out, a.h_cap, a.partial, a.partial_tiles);
   e = hipGetLastError();
-  if (e != hipSuccess || a.n_rows_dev == nullptr) return e;
+  // the reduction runs only where a split is possible (it exits when S == 1)
+  if (e != hipSuccess || a.n_rows_dev == nullptr || a.partial_tiles < 2) return e;
   hipLaunchKernelGGL(k_gate_up_reduce<D>, dim3(1024), dim3(256), 0, s, (const float *)a.partial, a.beta, a.M, a.d,
-                     a.F, a.rows, a.n_rows_dev, (T *)a.a_ws, (T *)a.h_out, a.h_cap);
+                     a.F, a.rows, a.n_rows_dev, a.n_sub, (T *)a.a_ws, (T *)a.h_out, a.h_cap, a.partial_tiles);
   return hipGetLastError();
 }
 
@@ -369,11 +366,11 @@ static hipError_t launch_down(const DenseArgs &a, hipStream_t s) {
   const int mt = (a.M + GEMM_BM - 1) / GEMM_BM, ntl = a.d / 256;
   const int grid = a.n_rows_dev ? FALLBACK_WGS : mt * ntl;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(GEMM_THREADS), lds, s, (const T *)a.a_ws, (const T *)a.wd,
-                     a.M, a.F, a.d, a.rows, a.n_rows_dev, (T *)a.y, a.partial);
+                     a.M, a.F, a.d, a.rows, a.n_rows_dev, a.n_sub, (T *)a.y, a.partial, a.partial_tiles);
   e = hipGetLastError();
-  if (e != hipSuccess || a.n_rows_dev == nullptr) return e;
+  if (e != hipSuccess || a.n_rows_dev == nullptr || a.partial_tiles < 2) return e;
   hipLaunchKernelGGL(k_down_reduce<D>, dim3(1024), dim3(256), 0, s, (const float *)a.partial, a.M, a.F, a.d,
-                     a.rows, a.n_rows_dev, (T *)a.y);
+                     a.rows, a.n_rows_dev, a.n_sub, (T *)a.y, a.partial_tiles);
   return hipGetLastError();
 }
 

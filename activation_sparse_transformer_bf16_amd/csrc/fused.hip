@@ -61,7 +61,8 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_fused(
 #pragma unroll
     for (int v = 0; v < EPC; ++v) acc[c][v] = 0.f;
 
-  const __amdgpu_buffer_rsrc_t wur = buffer_rsrc(wu), wdr = buffer_rsrc(wd);
+  const size_t w_bytes = (size_t)nt * tile * d * sizeof(TT);
+  const __amdgpu_buffer_rsrc_t wur = buffer_rsrc(wu, w_bytes), wdr = buffer_rsrc(wd, w_bytes);
   const uint32_t lane_off = lane * 16;
   const uint32_t row_bytes = (uint32_t)d * sizeof(TT);
   u32x2_t *L = lists[wave];
@@ -80,7 +81,7 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_fused(
       const int nq = __shfl(n, kq & 63, 64);
       const int oq = __shfl(incl - n, kq & 63, 64) + sq;
       if (q < kn * cap && sq < nq) {
-        const uint32_t j = (uint32_t)((k0 + kq) * tile + idx[slot0 + q]);
+        const uint32_t j = (uint32_t)((k0 + kq) * tile + (idx[slot0 + q] & (tile - 1)));
         L[oq] = u32x2_t{j * row_bytes, __float_as_uint(to_f32(val[slot0 + q]))};
       }
     }

@@ -53,13 +53,20 @@ __device__ __forceinline__ uint32_t read_lane(uint32_t v, int q) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, q);
 }
 
-// Raw buffer over [p, p + 2 GiB): a load takes a per-lane VGPR offset and a
+// Raw buffer over [p, p + bytes): a load takes a per-lane VGPR offset and a
 // wave-uniform SGPR offset, so a gathered weight row costs no per-lane address
-// arithmetic.  Every offset used here is below 2 GiB (weights are limited to
-// that size).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *p) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, 0x7FFFFFFF, 0x00020000);
+// arithmetic.  The hardware checks the per-lane offset against `bytes`: a lane
+// whose offset lies past the end reads zeros instead of touching memory.
+// Every array addressed this way is below 2 GiB.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *p, size_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, (int)min(bytes, (size_t)0x7FFFFFFF),
+                                           0x00020000);
 }
+
+// Row offset of a list entry that stands for nothing (padding, or a lane past
+// the end of a list): past every buffer above, so its load returns zeros and
+// a non-finite weight elsewhere cannot leak in through a 0 * w product.
+constexpr uint32_t NO_ROW = 0x80000000u;
 template <class V>
 __device__ __forceinline__ V buffer_load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff);
 template <>

@@ -62,7 +62,7 @@ __global__ __launch_bounds__(64 * HY_WAVES) void k_hybrid_rows(
         for (int s = 0; s < n; ++s) {
           if (pos0 + s < width) {
             vrow[pos0 + s] = val[slot0 + s];
-            crow_out[pos0 + s] = k * tile + idx[slot0 + s];
+            crow_out[pos0 + s] = k * tile + (idx[slot0 + s] & (tile - 1));
           }
         }
         before += __builtin_amdgcn_readlane(incl, 63);
@@ -147,8 +147,8 @@ __global__ __launch_bounds__(HY_DENSE_THREADS) void k_hybrid_dense(
       for (int q = threadIdx.x; q < nt * cap; q += HY_DENSE_THREADS) {
         const int k = q / cap, s = q - k * cap;
         const size_t slot = ((size_t)t * nt + k) * cap + s;
-        const int c = idx[slot];
-        if (s < (int)cnt[(size_t)t * nt + k] && c < tile) orow[k * tile + c] = val[slot];
+        const int c = idx[slot] & (tile - 1);  // an index is taken modulo the tile width
+        if (s < (int)cnt[(size_t)t * nt + k]) orow[k * tile + c] = val[slot];
       }
     }
     __syncthreads();

@@ -65,24 +65,44 @@ hipError_t sparse_fused(const SparseArgs &a, hipStream_t s);
 
 // Dense ReGLU FFN on the matrix cores over a (possibly gathered) set of rows:
 // logical row r < n_rows reads x[rows ? rows[r] : r] and writes y at the same
-// physical row.  n_rows_dev (device int) overrides M when non-null; the grid
-// is sized for M and workgroups past the device count exit at once.
+// physical row.  With n_rows_dev (device int) non-null the row count is
+// clamp(*n_rows_dev - n_sub, 0, M): one chunk of M rows of a longer list whose
+// first n_sub rows earlier chunks took; the grid is sized for M and
+// workgroups past the device count exit at once.
 struct DenseArgs {
   Dt dtype;
   const void *x, *wg, *wu, *wd;
   const float *beta;   // indexed by physical row, or null
   void *y;             // [T][d]
-  int M, d, F;         // M = grid rows (T)
+  int M, d, F;         // M = grid rows (T, or the chunk's rows)
   const int *rows;     // [M] or null (identity)
   const int *n_rows_dev;
+  int n_sub;           // rows of *n_rows_dev taken by earlier chunks
   void *a_ws;          // [M][F] storage dtype, logical rows
   void *h_out;         // [h_cap][F] storage dtype (ReLU'd gate rows) or null
   int h_cap;
-  float *partial;      // fallback only: FALLBACK_PARTIAL_FLOATS fp32 of split-K partial tiles
+  float *partial;      // fallback only: split-K partial tiles (partial_tiles of FALLBACK_SPLIT_TILE floats)
+  int partial_tiles;   // capacity of `partial` in tiles; 0 = no split
 };
-// Partial tiles of the fallback's split-K: at most one 256 x 256 fp32 tile per
-// workgroup of its grid (256).
-constexpr size_t FALLBACK_PARTIAL_FLOATS = (size_t)256 * 256 * 256;
+
+// The fallback's split-K.  Its grid has FALLBACK_WGS workgroups; when the
+// rows fill fewer output tiles than that, K is cut into S ranges whose fp32
+// partial tiles (256 x 256) a reduction kernel adds in K order.  S is at most
+// smax, at most the K slabs nk, and S * tiles stays within the capacity of
+// the partial area.
+constexpr int FALLBACK_WGS = 256;
+constexpr int FALLBACK_SPLIT_TILE = 256 * 256;  // floats of one partial tile
+constexpr int GATE_UP_SPLIT_MAX = 2;
+constexpr int DOWN_SPLIT_MAX = 16;
+constexpr int FALLBACK_PARTIAL_TILES_MAX = 128;  // 32 MB of partial tiles at most
+__host__ __device__ inline int fallback_split(int tiles, int nk, int smax, int cap_tiles) {
+  const int t = tiles > 0 ? tiles : 1;
+  int s = FALLBACK_WGS / t;
+  s = s < smax ? s : smax;
+  s = s < nk ? s : nk;
+  s = s < cap_tiles / t ? s : cap_tiles / t;
+  return s > 1 ? s : 1;
+}
 hipError_t dense_gate_up(const DenseArgs &a, hipStream_t s);
 hipError_t dense_down(const DenseArgs &a, hipStream_t s);
 

@@ -216,10 +216,12 @@ constexpr int UP_LIST = 256;  // entries per wave list (tiles per group * cap)
 // Writes, per non-overflow row t, the compact entry list of the row:
 //   list[t * stride + e] = (byte offset of hidden unit j's weight row, v = h * u)
 // for e < list_n[t], in ascending (tile, slot) order, i.e. ascending j, and
-// zero entries up to the next multiple of 8.  A row overflows iff one of its
-// tiles counts more than cap entries; every wave decides that from the row's
-// counts, skips such rows, and the group-0 wave records row_flag[t] (1 for an
-// overflow row) and list_n[t] = -1 for them.
+// padding entries (NO_ROW, 0) up to the next multiple of 8.  A row overflows
+// iff one of its tiles counts more than cap entries; every wave decides that
+// from the row's counts, skips such rows, and the group-0 wave records
+// row_flag[t] (1 for an overflow row) and list_n[t] = -1 for them.  A local
+// column index is taken modulo the tile width, so a malformed index cannot
+// address a row outside its tile.
 
 struct UpEntry {
   uint32_t off;   // byte offset of the unit's row in W_u^T (and in W_d)
@@ -245,7 +247,7 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_up(
   const int k0 = g * tpg;
   const int kn = min(tpg, nt - k0);
   UpEntry *L = lists[wave];
-  const __amdgpu_buffer_rsrc_t wur = buffer_rsrc(wu);
+  const __amdgpu_buffer_rsrc_t wur = buffer_rsrc(wu, (size_t)nt * tile * d * sizeof(TT));
   const uint32_t lane_off = lane * 16;
   const uint32_t row_bytes = (uint32_t)d * sizeof(TT);
   // lanes 16 r (r = 0..3) store the entry whose total their row holds
@@ -281,7 +283,7 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_up(
         row_flag[t] = ovf ? 1 : 0;
         list_n[t] = ovf ? -1 : sum;
       }
-      if (!ovf && lane < ((sum + 7) & ~7) - sum) list[lbase + sum + lane] = u32x2_t{0u, 0u};
+      if (!ovf && lane < ((sum + 7) & ~7) - sum) list[lbase + sum + lane] = u32x2_t{NO_ROW, 0u};
     }
     if (ovf) continue;
     const int before = g == 0 ? 0 : sum;
@@ -300,7 +302,7 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_up(
       const int oq = __shfl(incl - n, kq & 63, 64) + sq;
       if (q < kn * cap && sq < nq) {
         UpEntry en;
-        en.off = (uint32_t)((k0 + kq) * tile + idx[gslot0 + q]) * row_bytes;
+        en.off = (uint32_t)((k0 + kq) * tile + (idx[gslot0 + q] & (tile - 1))) * row_bytes;
         en.dst = (uint32_t)(before + oq);
         en.h = to_f32(val[gslot0 + q]);
         en.pad = 0;
@@ -362,8 +364,8 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_up(
 template <Dt D, int SLICE, int U>
 __global__ __launch_bounds__(SP_THREADS) void k_sparse_down(
     const u32x2_t *__restrict__ list, const int *__restrict__ list_n, int stride,
-    const typename DtT<D>::T *__restrict__ wd, typename DtT<D>::T *__restrict__ y, int T, int d, int n_slices,
-    int tok_per_wg, int n_tb) {
+    const typename DtT<D>::T *__restrict__ wd, typename DtT<D>::T *__restrict__ y, int T, int d, int F,
+    int n_slices, int tok_per_wg, int n_tb) {
   using TT = typename DtT<D>::T;
   constexpr int CPL = 16 / sizeof(TT);      // columns per lane
   constexpr int LPE = SLICE / CPL;          // lanes per entry
@@ -372,9 +374,9 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_down(
   static_assert(EPI == 1 || EPI == 2, "32 or 64 lanes per entry");
   static_assert(STEP <= 64 && 64 % STEP == 0, "a 64-entry chunk holds whole iterations");
   // One iteration consumes STEP list entries and a chunk holds the list's
-  // entries rounded up to a multiple of 8 (the zero padding the up kernel
-  // writes); a larger STEP would read entries past them and load weight rows
-  // at stale offsets.
+  // entries rounded up to a multiple of 8 (the padding the up kernel writes,
+  // whose loads return zeros); a larger STEP would read entries past them and
+  // load weight rows at stale offsets.
   static_assert(8 % STEP == 0, "STEP must divide the list padding of 8 entries");
   __shared__ u32x2_t chunk[SP_WAVES][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -383,7 +385,9 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_down(
   int sl, tb;
   group_coords(blockIdx.x, n_slices, n_tb, sl, tb);
   if (sl >= n_slices) return;
-  const __amdgpu_buffer_rsrc_t wdr = buffer_rsrc(wd + sl * SLICE);  // the slice's columns of row 0
+  // the slice's columns of row 0 onwards, to the end of W_d
+  const __amdgpu_buffer_rsrc_t wdr =
+      buffer_rsrc(wd + sl * SLICE, ((size_t)F * d - (size_t)sl * SLICE) * sizeof(TT));
   const uint32_t lane_off = lcol * sizeof(TT);
   u32x2_t *C = chunk[wave];
   for (int it = wave; it < tok_per_wg; it += SP_WAVES) {
@@ -399,8 +403,9 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_down(
       // 64 entries of the list to LDS with one load; each lane then reads the
       // entry it works on (lanes of a half-wave read the same one), so the
       // row offset and the weight arrive per lane without any selects.  The
-      // list is zero-padded to a multiple of 8 entries; entries beyond that
-      // in the chunk are never read.
+      // list is padded to a multiple of 8 entries with (NO_ROW, 0), whose
+      // loads return zeros, so padding adds exactly 0 whatever the weights
+      // hold; entries beyond that in the chunk are never read.
       const int ne = min(64, (n - e0 + 7) & ~7);
       if (lane < ne) C[lane] = lt[e0 + lane];
       wave_sync_lds();
@@ -509,8 +514,8 @@ static hipError_t launch_down(const SparseArgs &a, hipStream_t s) {
   const int tok = 16;
   const int n_tb = (a.T + tok - 1) / tok;
   hipLaunchKernelGGL((k_sparse_down<D, SLICE, U>), dim3(padded_groups(n_slices) * n_tb), dim3(SP_THREADS), 0, s,
-                     (const u32x2_t *)a.list, a.list_n, a.stride, (const TT *)a.wd, (TT *)a.y, a.T, a.d, n_slices,
-                     tok, n_tb);
+                     (const u32x2_t *)a.list, a.list_n, a.stride, (const TT *)a.wd, (TT *)a.y, a.T, a.d, a.F,
+                     n_slices, tok, n_tb);
   return hipGetLastError();
 }
 

@@ -43,6 +43,13 @@
  *   transposed once at load time so that every hidden unit's down row is
  *   contiguous).  x and y are [T][d] row-major.  gate_bias is one fp32 value
  *   per token ([T]) or NULL for none.
+ * - Inactive units contribute nothing (the pages' exactness argument for
+ *   skipping zeros, gist.science Resumen Técnico §2.B): on the sparse path a
+ *   token's output depends only on the w_up and w_down rows of its active
+ *   units, so a non-finite weight in the row of a unit that is inactive for
+ *   that token does not reach it.  Rows that take the dense fallback (and
+ *   dense_ffn_forward) go through dense matmuls, where such a weight gives
+ *   0 * inf = NaN as in any dense product: there weights must be finite.
  * - Thread safety: every entry point is reentrant; calls on different
  *   streams do not interact.  twell_last_error() is thread-local.
  */
@@ -82,7 +89,9 @@ typedef enum { TWELL_F32 = 0, TWELL_BF16 = 1 } twell_dtype;
  *     val[t][k][s],      for s < min(cnt, cap): the bits of the s-th active
  *     idx[t][k][s]       column in ascending column order, and its offset
  *                        inside the tile (0..tile-1).  Slots s >= cnt hold
- *                        +0 and 0.
+ *                        +0 and 0.  A consumer takes an index modulo the
+ *                        tile width, so a malformed index (>= tile) can
+ *                        only name a column of its own tile.
  *   Row t OVERFLOWS iff cnt[t][k] > cap for some k (cnt == cap still fits).
  *   Its TwELL slots still hold the first min(cnt, cap) entries per tile.
  *     ovf_rows[r]        the overflowing rows in ascending order, r < n_ovf.
@@ -132,8 +141,18 @@ const char *twell_last_error(void);
 twell_status twell_pack(const void *pre, twell_matrix *out, void *stream);
 
 /*
- * Workspace bytes needed by twell_ffn_forward / twell_sparse_ffn for the
- * given shape and format (0 on invalid arguments).
+ * Workspace bytes needed by twell_ffn_forward / twell_sparse_ffn /
+ * twell_sparse_ffn_fused for the given shape and format (0 on invalid
+ * arguments).  The layout (each piece 256-byte aligned): one flag byte and one
+ * int32 entry count per row; a region shared by the per-row entry lists
+ * (F/tile*cap pairs of (weight-row offset, v) per row, 8 bytes each, rounded
+ * up to 8 pairs) and, once the down projection has consumed them, the dense
+ * fallback's activations for one chunk of R overflow rows ([R][F] in the
+ * storage dtype, R = T for T <= 512, else ceil(T/2) rounded up to 256); and
+ * the fp32 partial tiles of the fallback's split-K (256 x 256 floats each, at
+ * most 128, only as many as a split can use for chunks of R rows).  At
+ * T = 8192, d = 2048, F = 8192, tile 256, cap 16, bf16 this is 96 MiB, below
+ * the 128 MiB of the dense activation matrix the format replaces.
  */
 size_t twell_ffn_workspace_size(int T, int d, int F, int tile, int cap, twell_dtype dtype);
 
@@ -159,12 +178,11 @@ size_t twell_ffn_workspace_size(int T, int d, int F, int tile, int cap, twell_dt
  * completes) *packed describes round(pre) exactly as twell_pack would.
  * y: [T][d] in the storage dtype, fully written.
  * workspace: device buffer of at least twell_ffn_workspace_size() bytes,
- * 256-byte aligned; its contents on entry do not matter.  It holds one flag
- * byte per row, per row a list of up to F/tile*cap (weight-row offset, v)
- * pairs of 8 bytes, the fallback's [T][F] activations, and 64 MB of fp32
- * partial tiles for the fallback's split-K (used when the overflowing rows
- * are too few to fill the GPU; their sums are taken in a fixed order, so y
- * stays deterministic).
+ * 256-byte aligned; its contents on entry do not matter (layout above).  The
+ * fallback runs over the overflow list in chunks of R rows, so any number of
+ * overflowing rows, up to all T, is computed; when they are too few to fill
+ * the GPU the first chunk splits K into ranges whose fp32 partial tiles are
+ * added in a fixed order, so y stays deterministic.
  * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP.
  */
 twell_status twell_ffn_forward(const void *x, const void *w_gate, const void *w_up,
@@ -177,7 +195,11 @@ twell_status twell_ffn_forward(const void *x, const void *w_gate, const void *w_
  * twell_gate_pack followed by twell_sparse_ffn on the same arguments.
  *
  * twell_gate_pack: step (1) alone -- one kernel, the gate matmul with the
- * TwELL epilogue.  Writes packed->cnt, val and idx; ovf_rows, n_ovf and dense
+ * TwELL epilogue: the dense matmul whose epilogue materialises the sparse
+ * activations in TwELL with no separate conversion pass and no
+ * synchronisation between thread blocks (gist.science Resumen Técnico §2.A;
+ * the estadored.mx item on the same paper, on the index management and
+ * memory traffic this avoids).  Writes packed->cnt, val and idx; ovf_rows, n_ovf and dense
  * are not touched (twell_overflow_scan completes them).  pre_out, when
  * non-NULL, receives the rounded pre-activations [T][F] in the storage dtype
  * (a debugging dump; the fused path itself never stores them).
@@ -195,7 +217,10 @@ twell_status twell_overflow_scan(twell_matrix *packed, void *stream);
 
 /*
  * twell_sparse_ffn: steps (2)-(5) from the cnt/val/idx written by
- * twell_gate_pack (or by twell_pack of the rounded gate pre-activations).  It
+ * twell_gate_pack (or by twell_pack of the rounded gate pre-activations): the
+ * inference route of gist.science Resumen Técnico §2.B (up and down
+ * projections over the active gate units only) plus the dense backup for
+ * rows with many non-zeros (§2.A; q2bstudio post on TwELL, third paragraph).  It
  * rebuilds the overflow list itself; the overflow rows' gate is recomputed from
  * x, w_gate and gate_bias, and packed->dense is written when non-NULL.
  */
@@ -208,7 +233,10 @@ size_t dense_ffn_workspace_size(int T, int d, int F, twell_dtype dtype);
 
 /*
  * dense_ffn_forward -- the same layer computed densely on the matrix cores
- * (the baseline the sparse path is measured against): a fused gate+up matmul
+ * (the baseline the sparse path is measured against: GPUs are built for
+ * dense products and sparse kernels used to lose to them, gist.science
+ * Resumen Técnico §1 and the q2bstudio post's first paragraph; the forward
+ * speedups of §4 are over dense execution): a fused gate+up matmul
  * whose epilogue forms a = ReLU(round(pre)) * u rounded to the storage dtype,
  * then the down matmul y = a W_d.  Same argument conventions as
  * twell_ffn_forward.  Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP.

@@ -120,9 +120,14 @@ def test_workspace_sizes():
     ws = twell.twell_ffn_workspace_size
     import torch
     n = ws(8192, 2048, 8192, 256, 16, torch.bfloat16)
-    # row flags + fp32 v per slot + bf16 fallback activations, 256-byte aligned pieces
-    assert n >= 8192 + 8192 * 32 * 16 * 4 + 8192 * 8192 * 2
+    # row flags + entry counts + the region the entry lists (8 bytes per TwELL
+    # slot) and one fallback chunk of 4096 bf16 rows share + 128 partial tiles
+    assert n >= 8192 + 8192 * 4 + max(8192 * 32 * 16 * 8, 4096 * 8192 * 2) + 128 * 256 * 256 * 4
     assert n % 256 == 0
+    # smaller than the dense activation matrix [T][F] it stands in for, at the
+    # 1.5B-class and the larger layer shapes
+    assert n < 128 * 2 ** 20 and n < 8192 * 8192 * 2
+    assert ws(16384, 4096, 14336, 256, 16, torch.bfloat16) < 16384 * 14336 * 2
     assert ws(8, 2048, 8192, 100, 16, torch.bfloat16) == 0
     assert ws(8, 300, 8192, 256, 16, torch.bfloat16) == 0
     assert ws(0, 512, 512, 256, 16, torch.bfloat16) >= 256

@@ -31,6 +31,10 @@ SMALL = [
     ("f32", 17, 4096, 256, 256, 16, -0.5),         # widest fp32 rows
     ("bf16", 24, 512, 8448, 256, 16, -2.0),        # many hidden units per output slice
     ("f32", 20, 256, 4352, 128, 8, -1.5),          # fp32, many hidden units per output slice
+    # the fallback in chunks of 768 (bf16, T = 1100) or 512 (fp32, T = 600) rows
+    ("bf16", 1100, 512, 1024, 256, 16, 6.0),       # every row overflows: two chunks
+    ("bf16", 1100, 512, 1024, 256, 16, -1.55),     # ~6% dense: ~890 rows overflow, the second chunk partly
+    ("f32", 600, 256, 512, 128, 8, 3.0),           # every row overflows: two chunks
 ]
 
 
@@ -66,8 +70,10 @@ def test_twell_ffn_forward(dtype, T, d, F, tile, cap, bias):
         assert np.all(np.abs(h - want) <= bound[t] + rel * (np.abs(pre64[t]) + bound[t]))
     if bias == "hot":
         assert host["n_ovf"] > 0
-    if bias == 6.0:
+    if bias in (6.0, 3.0):
         assert host["n_ovf"] == T
+    if bias == -1.55:
+        assert 768 < host["n_ovf"] < T
 
 
 @pytest.mark.parametrize("dtype,T,d,F,tile,cap,bias", SMALL)

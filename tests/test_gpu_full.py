@@ -45,7 +45,7 @@ def test_full_size(name):
         check_y(from_dev(yd, w.dtype), inp, w.dtype, rows=rows)
 
 
-@pytest.mark.parametrize("rho", [0.001, 0.02, 0.10])
+@pytest.mark.parametrize("rho", [0.001, 0.005, 0.02, 0.05, 0.10])
 def test_density_sweep_points(rho):
     w = workload(f"sweep@{rho}")
     print(f"sweep {rho}", flush=True)
