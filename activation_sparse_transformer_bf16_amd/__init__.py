@@ -66,6 +66,7 @@ def _load():
         "twell_pack": (I, [P, M, P]),
         "twell_ffn_workspace_size": (Z, [I, I, I, I, I, I]),
         "twell_ffn_forward": (I, [P, P, P, P, P, P, I, M, P, Z, P]),
+        "twell_ffn_forward_noalloc": (I, [P, P, P, P, P, P, I, M, P]),
         "twell_gate_pack": (I, [P, P, P, I, M, P, P]),
         "twell_overflow_scan": (I, [M, P]),
         "twell_sparse_ffn": (I, [M, P, P, P, P, P, P, I, P, Z, P]),
@@ -108,7 +109,11 @@ EXPORTS = ("twell_abi_version", "twell_status_str", "twell_last_error", "twell_p
            "dense_ffn_workspace_size", "dense_ffn_forward", "twell_to_hybrid",
            "twell_l1_workspace_size", "twell_l1_norm", "twell_l1_grad",
            "twell_ffn_backward_workspace_size", "twell_ffn_backward", "twell_sparse_ffn_fused",
-           "twell_stream_probe", "twell_mfma_probe")
+           "twell_stream_probe", "twell_mfma_probe", "twell_ffn_forward_noalloc")
+
+# Size of the static device scratch behind twell_ffn_forward_noalloc
+# (TWELL_NOALLOC_SCRATCH_BYTES in include/twell.h).
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 def lib():
@@ -457,6 +462,19 @@ def twell_ffn_forward(x, w_gate, w_up, w_down, gate_bias=None, tile: int = 256, 
     _check(_lib.twell_ffn_forward(_ptr(x), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(gate_bias),
                                   _ptr(y), d, ctypes.byref(m), _ptr(ws),
                                   ws.numel(), _stream(device)))
+    return y, packed
+
+
+def twell_ffn_forward_noalloc(x, w_gate, w_up, w_down, packed: TwellMatrix, y, gate_bias=None):
+    """twell_ffn_forward with its workspace in the library's static device
+    scratch: the caller passes the outputs (packed, y) and nothing is
+    allocated.  Calls that overlap on one GPU race (one scratch per GPU)."""
+    device, T, d, F = _ffn_checks(x, w_gate, w_up, w_down, gate_bias)
+    _packed_for(packed, device, T, F, x.dtype)
+    _need(y, "y", device, x.dtype, (T, d))
+    m = packed.c_struct()
+    _check(_lib.twell_ffn_forward_noalloc(_ptr(x), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(gate_bias),
+                                          _ptr(y), d, ctypes.byref(m), _stream(device)))
     return y, packed
 
 

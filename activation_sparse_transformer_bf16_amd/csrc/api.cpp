@@ -7,6 +7,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "launch.hpp"
 #include "twell.h"
@@ -125,8 +126,9 @@ int default_chunk_rows(int T) {
 }
 
 // The largest number of partial tiles the fallback's split-K can use with
-// chunks of R rows (the device picks S with the same fallback_split).
-int fallback_partial_tiles(int R, int d, int F, twell_dtype dt) {
+// chunks of R rows and an area of at most cap_tiles tiles (the device picks S
+// with the same fallback_split, given the area's capacity).
+int fallback_partial_tiles(int R, int d, int F, twell_dtype dt, int cap_tiles) {
   const int s = dt_size(dt);
   const int row_tiles = (R + GEMM_ROWS - 1) / GEMM_ROWS;
   const int nk_gu = d * s / 64, ntl_gu = F / 128;   // gate+up: 64-byte K slabs, 128-unit tiles
@@ -134,20 +136,21 @@ int fallback_partial_tiles(int R, int d, int F, twell_dtype dt) {
   int best = 0;
   for (int rt = 1; rt <= row_tiles; ++rt) {
     const int tg = rt * ntl_gu, td = rt * ntl_dn;
-    const int sg = fallback_split(tg, nk_gu, GATE_UP_SPLIT_MAX, FALLBACK_PARTIAL_TILES_MAX);
-    const int sd = fallback_split(td, nk_dn, DOWN_SPLIT_MAX, FALLBACK_PARTIAL_TILES_MAX);
+    const int sg = fallback_split(tg, nk_gu, GATE_UP_SPLIT_MAX, cap_tiles);
+    const int sd = fallback_split(td, nk_dn, DOWN_SPLIT_MAX, cap_tiles);
     if (sg > 1) best = std::max(best, sg * tg);
     if (sd > 1) best = std::max(best, sd * td);
   }
   return best;
 }
 
-FfnWs ffn_ws_layout(int T, int d, int F, int tile, int cap, twell_dtype dt, int chunk_rows) {
+FfnWs ffn_ws_layout(int T, int d, int F, int tile, int cap, twell_dtype dt, int chunk_rows,
+                    int partial_cap = FALLBACK_PARTIAL_TILES_MAX) {
   FfnWs w;
   const size_t nt = (size_t)F / tile;
   w.stride = (int)((nt * cap + 7) / 8 * 8);
   w.chunk_rows = chunk_rows;
-  w.partial_tiles = T > 0 ? fallback_partial_tiles(chunk_rows, d, F, dt) : 0;
+  w.partial_tiles = T > 0 ? fallback_partial_tiles(chunk_rows, d, F, dt, partial_cap) : 0;
   w.flag = 0;
   w.list_n = align_up((size_t)T, ALIGN_WS);
   w.list = align_up(w.list_n + (size_t)T * 4, ALIGN_WS);
@@ -225,6 +228,65 @@ twell_status run_sparse_fused(const twell_matrix *m, const void *x, const void *
   SparseArgs sa{D, T, d, F, m->tile, m->cap, m->cnt, m->val, m->idx, row_flag, x, wu, wd, nullptr, nullptr, 0, y};
   TW_TRY(sparse_fused(sa, s), "fused sparse up/down projection");
   return run_fallback(m, x, wg, wu, wd, beta, y, d, L, base, row_flag, s);
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Static scratch of twell_ffn_forward_noalloc: the forward's workspace as a
+// file-scope device array, for callers that cannot allocate.  Every GPU the
+// library runs on holds its own copy (TWELL_NOALLOC_SCRATCH_BYTES) until the
+// process ends.  In host code `scratch` only names the symbol: its device
+// address on the current GPU comes from hipGetSymbolAddress, taken once per
+// device and kept in g_scratch_ptr, and only that address is ever passed to
+// a kernel.
+static __device__ __align__(256) char scratch[TWELL_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int SCRATCH_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[SCRATCH_MAX_DEVICES] = {};
+
+// The scratch address on the current device, which must be the stream's.
+twell_status scratch_address(hipStream_t s, void **out) {
+  int dev = -1;
+  TW_TRY(hipGetDevice(&dev), "hipGetDevice");
+  if (s != nullptr) {
+    hipDevice_t sdev = -1;
+    TW_TRY(hipStreamGetDevice(s, &sdev), "hipStreamGetDevice");
+    if ((int)sdev != dev)
+      return fail(TWELL_ERR_INVALID_ARG, "the stream belongs to device %d, the current device is %d", (int)sdev, dev);
+  }
+  if (dev < 0 || dev >= SCRATCH_MAX_DEVICES)
+    return fail(TWELL_ERR_UNSUPPORTED, "device %d: the static scratch is kept for devices 0..%d", dev,
+                SCRATCH_MAX_DEVICES - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *p = nullptr;
+    TW_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (p == nullptr) return fail(TWELL_ERR_HIP, "hipGetSymbolAddress(scratch) returned a null address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return TWELL_OK;
+}
+
+// The forward's workspace layout within the static scratch: the default
+// chunk of fallback rows, or smaller chunks (multiples of 256 rows) until it
+// fits; failing that, a smaller split-K area (fewer K ranges for the
+// fallback's first chunk, down to none).  false when nothing fits.
+bool noalloc_layout(int T, int d, int F, int tile, int cap, twell_dtype dt, FfnWs *out) {
+  for (int pcap = FALLBACK_PARTIAL_TILES_MAX;; pcap /= 2) {
+    for (int R = default_chunk_rows(T); R > 0; R = R > 256 ? (R - 1) / 256 * 256 : 0) {
+      const FfnWs L = ffn_ws_layout(T, d, F, tile, cap, dt, R, pcap < 2 ? 0 : pcap);
+      if (L.total <= TWELL_NOALLOC_SCRATCH_BYTES) {
+        *out = L;
+        return true;
+      }
+    }
+    if (pcap < 2) return false;
+  }
 }
 
 }  // namespace
@@ -458,6 +520,32 @@ twell_status twell_ffn_forward(const void *x, const void *w_gate, const void *w_
               packed->cnt, packed->val, packed->idx, nullptr};
   TW_TRY(gate_twell(ga, s), "gate matmul");
   return run_sparse(packed, x, w_gate, w_up, w_down, gate_bias, y, d, workspace, L, s);
+}
+
+twell_status twell_ffn_forward_noalloc(const void *x, const void *w_gate, const void *w_up, const void *w_down,
+                                       const float *gate_bias, void *y, int d, twell_matrix *packed, void *stream) {
+  g_err[0] = 0;
+  twell_status st = check_matrix(packed, true);
+  if (st != TWELL_OK) return st;
+  if ((st = check_d(d, (int)packed->dtype)) != TWELL_OK) return st;
+  if ((st = check_weight_bytes(packed->cols, d, (int)packed->dtype)) != TWELL_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (packed->rows == 0) return hip_check(zero_int(packed->n_ovf, s), "zero n_ovf");
+  if ((st = check_ffn_ptrs(x, w_gate, w_up, w_down, gate_bias, y)) != TWELL_OK) return st;
+  const int T = packed->rows, F = packed->cols;
+  FfnWs L;
+  if (!noalloc_layout(T, d, F, packed->tile, packed->cap, packed->dtype, &L))
+    return fail(TWELL_ERR_WORKSPACE,
+                "the forward of T=%d, d=%d, F=%d needs %zu bytes of workspace even with 256-row fallback chunks "
+                "and no split-K area; the static scratch holds %zu",
+                T, d, F, ffn_ws_layout(T, d, F, packed->tile, packed->cap, packed->dtype, std::min(T, 256), 0).total,
+                (size_t)TWELL_NOALLOC_SCRATCH_BYTES);
+  void *ws = nullptr;
+  if ((st = scratch_address(s, &ws)) != TWELL_OK) return st;
+  GateArgs ga{to_dt(packed->dtype), packed->tile, x, w_gate, gate_bias, T, d, F, packed->cap,
+              packed->cnt, packed->val, packed->idx, nullptr};
+  TW_TRY(gate_twell(ga, s), "gate matmul");
+  return run_sparse(packed, x, w_gate, w_up, w_down, gate_bias, y, d, ws, L, s);
 }
 
 }  // extern "C"

@@ -191,6 +191,29 @@ twell_status twell_ffn_forward(const void *x, const void *w_gate, const void *w_
                                void *stream);
 
 /*
+ * twell_ffn_forward_noalloc -- twell_ffn_forward for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same computation, kernels and results,
+ * with the workspace taken from a static device array of
+ * TWELL_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends.  The call allocates nothing.  The fallback's row
+ * chunk is the largest (multiple of 256 rows, at most the default) whose
+ * workspace fits; shapes whose workspace does not fit even with 256-row
+ * chunks are rejected with TWELL_ERR_WORKSPACE before any launch (the
+ * 1.5B-class layer, T = 8192, d = 2048, F = 8192, bf16, fits).
+ * The stream must belong to the current device.  Every call on one GPU uses
+ * that GPU's one array: calls that overlap in time on one GPU (different
+ * streams, or different host threads) race and must be serialised by the
+ * caller.  The array's contents between calls do not matter.
+ * Errors: as twell_ffn_forward, WORKSPACE when the shape needs more than the
+ * static scratch, INVALID_ARG when the stream is another device's.
+ */
+#define TWELL_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+twell_status twell_ffn_forward_noalloc(const void *x, const void *w_gate, const void *w_up,
+                                       const void *w_down, const float *gate_bias, void *y, int d,
+                                       twell_matrix *packed, void *stream);
+
+/*
  * Stage entry points (for profiling and parity).  twell_ffn_forward performs
  * twell_gate_pack followed by twell_sparse_ffn on the same arguments.
  *

@@ -236,3 +236,18 @@ def test_mfma_probe_validation():
     assert L.twell_mfma_probe(FAKE, 0, 4, None) == twell.TWELL_ERR_INVALID_ARG
     assert L.twell_mfma_probe(FAKE, 10, 0, None) == twell.TWELL_ERR_INVALID_ARG
     assert L.twell_mfma_probe(FAKE + 2, 10, 4, None) == twell.TWELL_ERR_UNSUPPORTED
+
+
+def test_noalloc_rejects_shapes_beyond_the_static_scratch():
+    # 65536 tokens x 8192 units: the entry lists alone need 256 MiB, more than
+    # the 64 MiB static scratch; rejected before any HIP call
+    m = _matrix(rows=65536, cols=8192)
+    st = L.twell_ffn_forward_noalloc(FAKE, FAKE, FAKE, FAKE, None, FAKE, 2048, ctypes.byref(m), None)
+    assert st == twell.TWELL_ERR_WORKSPACE
+    assert "static scratch" in twell.twell_last_error()
+    assert twell.NOALLOC_SCRATCH_BYTES == 64 << 20
+    assert "((size_t)64 << 20)" in open(HEADER).read()
+    # the validation of the allocating entry point applies as well
+    bad = _matrix(rows=8, cols=500)
+    assert L.twell_ffn_forward_noalloc(FAKE, FAKE, FAKE, FAKE, None, FAKE, 512, ctypes.byref(bad),
+                                       None) == twell.TWELL_ERR_INVALID_ARG
