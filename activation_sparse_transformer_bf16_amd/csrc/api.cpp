@@ -131,15 +131,16 @@ int default_chunk_rows(int T) {
 int fallback_partial_tiles(int R, int d, int F, twell_dtype dt, int cap_tiles) {
   const int s = dt_size(dt);
   const int row_tiles = (R + GEMM_ROWS - 1) / GEMM_ROWS;
-  const int nk_gu = d * s / 64, ntl_gu = F / 128;   // gate+up: 64-byte K slabs, 128-unit tiles
-  const int nk_dn = F * s / 128, ntl_dn = d / 256;  // down: 128-byte K chunks, 256-column tiles
+  const int nk_gu = d * s / 64, ntl_gu = F / 128;                 // gate+up: 64-byte K slabs, 128-unit tiles
+  const int nk_dn = F * s / 128, ntl_dn = d / FALLBACK_DOWN_BN;   // down: 128-byte K chunks
+  const int per = 256 / FALLBACK_DOWN_BN;                         // down partial tiles per 256 x 256 tile
   int best = 0;
   for (int rt = 1; rt <= row_tiles; ++rt) {
     const int tg = rt * ntl_gu, td = rt * ntl_dn;
     const int sg = fallback_split(tg, nk_gu, GATE_UP_SPLIT_MAX, cap_tiles);
-    const int sd = fallback_split(td, nk_dn, DOWN_SPLIT_MAX, cap_tiles);
+    const int sd = fallback_split(td, nk_dn, DOWN_SPLIT_MAX, cap_tiles * per);
     if (sg > 1) best = std::max(best, sg * tg);
-    if (sd > 1) best = std::max(best, sd * td);
+    if (sd > 1) best = std::max(best, (sd * td + per - 1) / per);
   }
   return best;
 }
@@ -176,9 +177,8 @@ twell_status check_ffn_ptrs(const void *x, const void *wg, const void *wu, const
 
 // The overflow-row list, then the dense fallback over it, chunk by chunk.
 // Chunk c takes list positions [c R, c R + R); its kernels read *n_ovf on the
-// device and exit at once when the list is shorter.  Only the first chunk
-// may split K (a later chunk runs only when more than R rows overflow, which
-// fills the grid).
+// device and exit at once when the list is shorter.  Each chunk may split K
+// over the same partial area (the chunks run one after the other).
 twell_status run_fallback(const twell_matrix *m, const void *x, const void *wg, const void *wu, const void *wd,
                           const float *beta, void *y, int d, const FfnWs &L, char *base, const uint8_t *row_flag,
                           hipStream_t s) {
@@ -187,13 +187,12 @@ twell_status run_fallback(const twell_matrix *m, const void *x, const void *wg, 
   TW_TRY(compact_rows(row_flag, T, m->ovf_rows, m->ovf_cap, m->n_ovf, s), "overflow row list");
   for (int c0 = 0; c0 < T; c0 += R) {
     const int rows = std::min(R, T - c0);
-    const bool first = c0 == 0;
     const int h_cap = std::max(0, std::min(m->ovf_cap - c0, rows));
     void *h_out = (m->dense != nullptr && h_cap > 0)
                       ? static_cast<char *>(m->dense) + (size_t)c0 * F * dt_size(m->dtype)
                       : nullptr;
     DenseArgs da{D, x, wg, wu, wd, beta, y, rows, d, F, m->ovf_rows + c0, m->n_ovf, c0, base + L.a, h_out, h_cap,
-                 first ? reinterpret_cast<float *>(base + L.partial) : nullptr, first ? L.partial_tiles : 0};
+                 reinterpret_cast<float *>(base + L.partial), L.partial_tiles};
     TW_TRY(dense_gate_up(da, s), "fallback gate/up matmul");
     TW_TRY(dense_down(da, s), "fallback down matmul");
   }

@@ -42,11 +42,13 @@ __device__ __forceinline__ int gate_up_part_index(int row, int col) {
   const int rr = row & 31, i = 4 * (rr >> 3) + (rr & 3), lane = ((rr & 7) >> 2) * 32 + (col & 31);
   return (((w * 4 + bm) * 2 + bn) * 16 + i) * 64 + lane;
 }
-// down tiles (4 waves of 64 rows, 2 x 8 blocks):
+// down tiles of BN columns (4 waves of 64 rows, 2 x BN/32 blocks):
+template <int BN>
 __device__ __forceinline__ int down_part_index(int row, int col) {
+  constexpr int NB = BN / 32;
   const int w = row >> 6, bm = (row & 63) >> 5, bn = col >> 5;
   const int rr = row & 31, i = 4 * (rr >> 3) + (rr & 3), lane = ((rr & 7) >> 2) * 32 + (col & 31);
-  return (((w * 2 + bm) * 8 + bn) * 16 + i) * 64 + lane;
+  return (((w * 2 + bm) * NB + bn) * 16 + i) * 64 + lane;
 }
 
 // One 256-row x 128-unit tile (tm, tn) of the gate / up matmul over K slabs
@@ -129,15 +131,15 @@ __device__ __forceinline__ void gate_up_tile(
   }
 }
 
-// One 256 x 256 tile (tm, tn) of y = a W_d over K chunks [k0, k0 + nk) of
+// One 256 x BN tile (tm, tn) of y = a W_d over K chunks [k0, k0 + nk) of
 // 128 bytes; part == null: y is written, otherwise the fp32 partial tile.
-template <Dt D>
+template <Dt D, int BN>
 __device__ __forceinline__ void down_tile(
     int tm, int tn, int k0, int nk, float *__restrict__ part, const typename DtT<D>::T *__restrict__ a_ws,
     const typename DtT<D>::T *__restrict__ wd, int M, int K, int N, const int *__restrict__ rows, int n_eff,
     typename DtT<D>::T *__restrict__ y) {
   using T = typename DtT<D>::T;
-  constexpr int BN = 256;
+  constexpr int NB = BN / 32;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int m0 = tm * GEMM_BM, n0 = tn * BN;
   if (m0 >= n_eff) return;
@@ -154,23 +156,23 @@ __device__ __forceinline__ void down_tile(
   lb.init(tid, reinterpret_cast<const char *>(wd) + (size_t)k0 * (KCHUNK_BYTES / sizeof(T)) * N * sizeof(T),
           (size_t)N * sizeof(T), n0);
 
-  f32x16_t acc[2][8];
+  f32x16_t acc[2][NB];
 #pragma unroll
   for (int bm = 0; bm < 2; ++bm)
 #pragma unroll
-    for (int bn = 0; bn < 8; ++bn) acc[bm][bn] = f32x16_t{};
+    for (int bn = 0; bn < NB; ++bn) acc[bm][bn] = f32x16_t{};
 
   gemm_mainloop<D, BN>(acc, la, lb, nk, smem);
 
   const int col = lane & 31;
   if (part != nullptr) {
-    float *q = part + (size_t)wave * (2 * 8 * 16 * 64) + lane;
+    float *q = part + (size_t)wave * (2 * NB * 16 * 64) + lane;
 #pragma unroll
     for (int bm = 0; bm < 2; ++bm)
 #pragma unroll
-      for (int bn = 0; bn < 8; ++bn)
+      for (int bn = 0; bn < NB; ++bn)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) q[((bm * 8 + bn) * 16 + i) * 64] = acc[bm][bn][i];
+        for (int i = 0; i < 16; ++i) q[((bm * NB + bn) * 16 + i) * 64] = acc[bm][bn][i];
     return;
   }
   int row_base = m0 + 64 * wave + 4 * (lane >> 5);  // opaque: keep row math after the mainloop
@@ -183,7 +185,7 @@ __device__ __forceinline__ void down_tile(
       if (lr >= n_eff) continue;
       const size_t prow = rows ? (size_t)rows[lr] : (size_t)lr;
 #pragma unroll
-      for (int bn = 0; bn < 8; ++bn) y[prow * N + n0 + 32 * bn + col] = from_f32<D>(acc[bm][bn][i]);
+      for (int bn = 0; bn < NB; ++bn) y[prow * N + n0 + 32 * bn + col] = from_f32<D>(acc[bm][bn][i]);
     }
   }
 }
@@ -275,64 +277,70 @@ __global__ __launch_bounds__(256) void k_gate_up_reduce(const float *__restrict_
   }
 }
 
-template <Dt D, bool LOOP>
+// Output tiles of BN columns; the fallback uses BN = 128 (twice the tiles of
+// 256-column ones for the same rows, so a chunk of a few thousand overflow
+// rows still fills the grid), the dense baseline BN = 256.  Partial tiles of
+// the split hold 256 x BN floats; the area's capacity, given in 256 x 256
+// tiles, holds 256 / BN times as many.
+template <Dt D, bool LOOP, int BN>
 __global__ __launch_bounds__(GEMM_THREADS) void k_down(
     const typename DtT<D>::T *__restrict__ a_ws, const typename DtT<D>::T *__restrict__ wd, int M, int K,
     int N, const int *__restrict__ rows, const int *__restrict__ n_rows_dev, int n_sub,
     typename DtT<D>::T *__restrict__ y, float *__restrict__ partial, int partial_tiles) {
   using T = typename DtT<D>::T;
   const int nk = K / (KCHUNK_BYTES / (int)sizeof(T));
-  const int mt = (M + GEMM_BM - 1) / GEMM_BM, ntl = N / 256;
+  const int mt = (M + GEMM_BM - 1) / GEMM_BM, ntl = N / BN;
   if constexpr (LOOP) {
     const int n_eff = min(max(*n_rows_dev - n_sub, 0), M);
     const int tiles = (n_eff + GEMM_BM - 1) / GEMM_BM * ntl;
-    const int S = fallback_split(tiles, nk, DOWN_SPLIT_MAX, partial_tiles);
+    const int S = fallback_split(tiles, nk, DOWN_SPLIT_MAX, partial_tiles * (256 / BN));
     for (int w = blockIdx.x; w < tiles * S; w += gridDim.x) {
       const int tile = w / S, kc = w - tile * S;
       const int k0 = kc * nk / S, k1 = (kc + 1) * nk / S;
-      down_tile<D>(tile / ntl, tile % ntl, k0, k1 - k0, S > 1 ? partial + (size_t)w * SPLIT_TILE : nullptr,
-                   a_ws, wd, M, K, N, rows, n_eff, y);
+      down_tile<D, BN>(tile / ntl, tile % ntl, k0, k1 - k0,
+                       S > 1 ? partial + (size_t)w * GEMM_BM * BN : nullptr, a_ws, wd, M, K, N, rows, n_eff, y);
     }
   } else {
     int tm, tn;
     tile_coords(blockIdx.x, mt, ntl, tm, tn);
-    down_tile<D>(tm, tn, 0, nk, nullptr, a_ws, wd, M, K, N, rows, M, y);
+    down_tile<D, BN>(tm, tn, 0, nk, nullptr, a_ws, wd, M, K, N, rows, M, y);
   }
 }
 
 // y rows of the fallback after a split: the S partials added in K order.
-template <Dt D>
+template <Dt D, int BN>
 __global__ __launch_bounds__(256) void k_down_reduce(const float *__restrict__ partial, int M, int K, int N,
                                                      const int *__restrict__ rows,
                                                      const int *__restrict__ n_rows_dev, int n_sub,
                                                      typename DtT<D>::T *__restrict__ y, int partial_tiles) {
   using T = typename DtT<D>::T;
+  constexpr int PT = GEMM_BM * BN;  // floats of one partial tile
   const int nk = K / (KCHUNK_BYTES / (int)sizeof(T));
-  const int ntl = N / 256;
+  const int ntl = N / BN;
   const int n_eff = min(max(*n_rows_dev - n_sub, 0), M);
   const int tiles = (n_eff + GEMM_BM - 1) / GEMM_BM * ntl;
-  const int S = fallback_split(tiles, nk, DOWN_SPLIT_MAX, partial_tiles);
+  const int S = fallback_split(tiles, nk, DOWN_SPLIT_MAX, partial_tiles * (256 / BN));
   if (S == 1) return;
-  const size_t total = (size_t)tiles * SPLIT_TILE;
+  const size_t total = (size_t)tiles * PT;
   for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (size_t)gridDim.x * 256) {
-    const int tile = (int)(e / SPLIT_TILE);
-    const int rem = (int)(e - (size_t)tile * SPLIT_TILE);
-    const int r = rem / 256, c = rem % 256;
+    const int tile = (int)(e / PT);
+    const int rem = (int)(e - (size_t)tile * PT);
+    const int r = rem / BN, c = rem % BN;
     const int lr = (tile / ntl) * GEMM_BM + r;
     if (lr >= n_eff) continue;
-    const float *p = partial + (size_t)tile * S * SPLIT_TILE + down_part_index(r, c);
+    const float *p = partial + (size_t)tile * S * PT + down_part_index<BN>(r, c);
     float v = 0.f;
     int kc = 0;
     for (; kc + REDUCE_BATCH <= S; kc += REDUCE_BATCH) {  // loads of a batch in flight together
       float q[REDUCE_BATCH];
 #pragma unroll
-      for (int i = 0; i < REDUCE_BATCH; ++i) q[i] = p[(size_t)(kc + i) * SPLIT_TILE];
+      for (int i = 0; i < REDUCE_BATCH; ++i) q[i] = p[(size_t)(kc + i) * PT];
 #pragma unroll
       for (int i = 0; i < REDUCE_BATCH; ++i) v += q[i];
     }
-    for (; kc < S; ++kc) v += p[(size_t)kc * SPLIT_TILE];
+    for (; kc < S; ++kc) v += p[(size_t)kc * PT];
     const size_t prow = rows ? (size_t)rows[lr] : (size_t)lr;
-    y[prow * N + (size_t)(tile % ntl) * 256 + c] = from_f32<D>(v);
+    y[prow * N + (size_t)(tile % ntl) * BN + c] = from_f32<D>(v);
   }
 }
 
@@ -359,8 +367,9 @@ static hipError_t launch_gate_up(const DenseArgs &a, hipStream_t s) {
 template <Dt D>
 static hipError_t launch_down(const DenseArgs &a, hipStream_t s) {
   using T = typename DtT<D>::T;
-  auto kern = a.n_rows_dev ? k_down<D, true> : k_down<D, false>;
-  const int lds = gemm_lds_bytes(256);
+  constexpr int BNF = FALLBACK_DOWN_BN;
+  auto kern = a.n_rows_dev ? k_down<D, true, BNF> : k_down<D, false, 256>;
+  const int lds = gemm_lds_bytes(a.n_rows_dev ? BNF : 256);
   hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
   const int mt = (a.M + GEMM_BM - 1) / GEMM_BM, ntl = a.d / 256;
@@ -368,9 +377,9 @@ static hipError_t launch_down(const DenseArgs &a, hipStream_t s) {
   hipLaunchKernelGGL(kern, dim3(grid), dim3(GEMM_THREADS), lds, s, (const T *)a.a_ws, (const T *)a.wd,
                      a.M, a.F, a.d, a.rows, a.n_rows_dev, a.n_sub, (T *)a.y, a.partial, a.partial_tiles);
   e = hipGetLastError();
-  if (e != hipSuccess || a.n_rows_dev == nullptr || a.partial_tiles < 2) return e;
-  hipLaunchKernelGGL(k_down_reduce<D>, dim3(1024), dim3(256), 0, s, (const float *)a.partial, a.M, a.F, a.d,
-                     a.rows, a.n_rows_dev, a.n_sub, (T *)a.y, a.partial_tiles);
+  if (e != hipSuccess || a.n_rows_dev == nullptr || a.partial_tiles < 1) return e;
+  hipLaunchKernelGGL((k_down_reduce<D, BNF>), dim3(1024), dim3(256), 0, s, (const float *)a.partial, a.M, a.F,
+                     a.d, a.rows, a.n_rows_dev, a.n_sub, (T *)a.y, a.partial_tiles);
   return hipGetLastError();
 }
 

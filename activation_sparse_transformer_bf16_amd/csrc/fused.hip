@@ -9,9 +9,10 @@
 // (ascending unit order), holds x_t in registers and y_t as fp32 accumulators
 // (d / 64 per lane, in the same lane layout as x_t), and per entry:
 //   u = x_t . W_u^T[j]   (16-byte loads of the W_u row, dot2, joint reduction)
-//   y_t += (h * u) W_d[j] (16-byte loads of the W_d row, issued with the W_u
-//                          loads, FMA into the accumulators)
-// so v = h u never leaves the registers.  y_t is rounded once at the end.
+//   y_t += v W_d[j]      (v = h * u rounded to the storage dtype; 16-byte
+//                         loads of the W_d row, issued with the W_u loads, FMA
+//                         into the accumulators)
+// so v never leaves the registers.  y_t is rounded once at the end.
 // Unlike the two-kernel route, the weight rows of a token come from the whole
 // of W_u and W_d, so no XCD can keep "its" rows in L2: they stream from the
 // Infinity Cache / HBM.
@@ -117,7 +118,9 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_fused(
         for (int u = 0; u < U; ++u) {
           const float h = __uint_as_float(read_lane(me[1], min(u0 + u, ne - 1)));
           const float uu = __uint_as_float(read_lane(__float_as_uint(tot), reduce_lane<U>(u)));
-          const float v = u0 + u < ne ? h * uu : 0.f;
+          // v = h * u rounded to the storage dtype (the down projection's input
+          // activation, rounded as on every other path)
+          const float v = u0 + u < ne ? to_f32(from_f32<D>(h * uu)) : 0.f;
 #pragma unroll
           for (int c = 0; c < NC; ++c) {
             if constexpr (D == Dt::BF16) {

@@ -74,18 +74,23 @@ struct KRowLoader {
 template <Dt D, int BN> struct NColLoader;
 
 // bf16: 8 (k) x 8 (n) blocks, 16 bytes per k row; 8 x 8 transpose with v_perm.
+// With fewer blocks than threads (BN = 128: 128 blocks) the first BLOCKS
+// threads (whole waves) carry one block each and the others none.
 template <int BN>
 struct NColLoader<Dt::BF16, BN> {
   static constexpr int BLOCKS = BN / 8 * 8;  // (BN/8 n-blocks) x (8 k-blocks of 8)
-  static constexpr int PER_THREAD = BLOCKS / GEMM_THREADS;
+  static constexpr int PER_THREAD = BLOCKS >= GEMM_THREADS ? BLOCKS / GEMM_THREADS : 1;
+  static_assert(BLOCKS % 64 == 0, "whole waves of blocks");
   const char *base;
   size_t ld;  // bytes per k row
   int kb[PER_THREAD], nb[PER_THREAD];
+  bool on;
   u32x4_t reg[PER_THREAD][8];
 
   __device__ __forceinline__ void init(int tid, const void *b, size_t ld_bytes, int n0) {
     ld = ld_bytes;
     base = reinterpret_cast<const char *>(b) + (size_t)n0 * 2;
+    on = tid < BLOCKS;
 #pragma unroll
     for (int p = 0; p < PER_THREAD; ++p) {
       int blk = tid + GEMM_THREADS * p;
@@ -94,6 +99,7 @@ struct NColLoader<Dt::BF16, BN> {
     }
   }
   __device__ __forceinline__ void issue(int kt) {
+    if (!on) return;
 #pragma unroll
     for (int p = 0; p < PER_THREAD; ++p) {
       const char *src = base + (size_t)(kt * 64 + kb[p] * 8) * ld + nb[p] * 16;
@@ -102,6 +108,7 @@ struct NColLoader<Dt::BF16, BN> {
     }
   }
   __device__ __forceinline__ void commit(char *dst) {
+    if (!on) return;
 #pragma unroll
     for (int p = 0; p < PER_THREAD; ++p) {
 #pragma unroll

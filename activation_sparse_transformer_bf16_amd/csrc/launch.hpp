@@ -95,6 +95,7 @@ constexpr int FALLBACK_SPLIT_TILE = 256 * 256;  // floats of one partial tile
 constexpr int GATE_UP_SPLIT_MAX = 2;
 constexpr int DOWN_SPLIT_MAX = 16;
 constexpr int FALLBACK_PARTIAL_TILES_MAX = 128;  // 32 MB of partial tiles at most
+constexpr int FALLBACK_DOWN_BN = 128;            // output columns per tile of the fallback's down matmul
 __host__ __device__ inline int fallback_split(int tiles, int nk, int smax, int cap_tiles) {
   const int t = tiles > 0 ? tiles : 1;
   int s = FALLBACK_WGS / t;

@@ -8,12 +8,15 @@
 //   up:   hidden units are split into groups of TwELL tiles and group g runs on
 //         XCD g % 8; per active entry (t, j) one wave dots x_t (held in
 //         registers) with the W_u^T row j, and writes (row offset of j,
-//         v = h * u in fp32) to row t's compact entry list.
+//         v = h * u rounded to the storage dtype) to row t's compact entry
+//         list.  v is the down projection's input activation, rounded as the
+//         dense layer and the dense fallback round it.
 //   down: the d output columns are split into slices and slice s runs on
 //         XCD s % 8; per token one wave copies the token's entry list to LDS
 //         64 entries at a time, accumulates v * W_d[j][slice] in fp32
-//         registers (two entries per load instruction for bf16) and rounds y
-//         once.
+//         registers (for bf16: the same columns of two entries interleaved
+//         with v_perm, one v_dot2_f32_bf16 per column and entry pair) and
+//         rounds y once.
 // The up kernel also decides which rows overflow (a tile with more than cap
 // entries); those rows are left to the dense fallback.
 #include "gather.hpp"
@@ -214,7 +217,8 @@ constexpr int UP_LIST = 256;  // entries per wave list (tiles per group * cap)
 // in flight per wave (U * NC 16-byte loads per lane outstanding).
 //
 // Writes, per non-overflow row t, the compact entry list of the row:
-//   list[t * stride + e] = (byte offset of hidden unit j's weight row, v = h * u)
+//   list[t * stride + e] = (byte offset of hidden unit j's weight row,
+//                           v = round(h * u): fp32 bits, or bf16 bits in the low half)
 // for e < list_n[t], in ascending (tile, slot) order, i.e. ascending j, and
 // padding entries (NO_ROW, 0) up to the next multiple of 8.  A row overflows
 // iff one of its tiles counts more than cap entries; every wave decides that
@@ -345,7 +349,11 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_up(
           for (int c = 0; c < NC; ++c) p[u] = dot16(xr[c], w[u][c], p[u], TT());
         }
         const float tot = Reduce<U>::run(p);
-        if (storer && u0 + my_u < ne) list[lbase + mine.dst] = u32x2_t{mine.off, __float_as_uint(mine.h * tot)};
+        if (storer && u0 + my_u < ne) {
+          const float v = mine.h * tot;
+          const uint32_t vb = D == Dt::BF16 ? (uint32_t)bf16_rne(v) : __float_as_uint(v);
+          list[lbase + mine.dst] = u32x2_t{mine.off, vb};
+        }
       }
     }
     wave_sync_lds();
@@ -372,6 +380,7 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_down(
   constexpr int EPI = 64 / LPE;             // entries per load instruction
   constexpr int STEP = U * EPI;             // entries per iteration
   static_assert(EPI == 1 || EPI == 2, "32 or 64 lanes per entry");
+  static_assert(D != Dt::BF16 || U % 2 == 0, "bf16 pairs the entries of one lane");
   static_assert(STEP <= 64 && 64 % STEP == 0, "a 64-entry chunk holds whole iterations");
   // One iteration consumes STEP list entries and a chunk holds the list's
   // entries rounded up to a multiple of 8 (the padding the up kernel writes,
@@ -411,28 +420,38 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_down(
       wave_sync_lds();
       for (int e = 0; e < ne; e += STEP) {
         u32x4_t w[U];
-        float sw[U];
+        uint32_t sw[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const u32x2_t en = C[e + EPI * u + part];
-          sw[u] = __uint_as_float(en[1]);
+          sw[u] = en[1];
           w[u] = buffer_load<u32x4_t>(wdr, lane_off + en[0], 0u);
         }
+        if constexpr (D == Dt::BF16) {
+          // entries 2p and 2p+1 of this lane: one dword holds their two v
+          // (bf16), and per weight dword the same column of both rows is
+          // paired, so one dot2 adds both products into that column
+          typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          if constexpr (D == Dt::BF16) {
+          for (int p = 0; p < U / 2; ++p) {
+            const uint32_t vv = __builtin_amdgcn_perm(sw[2 * p + 1], sw[2 * p], 0x05040100u);
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              const uint32_t wv = w[u][v];
-              acc[2 * v] = fmaf(sw[u], bf16lo(wv), acc[2 * v]);
-              acc[2 * v + 1] = fmaf(sw[u], bf16hi(wv), acc[2 * v + 1]);
+            for (int q = 0; q < 4; ++q) {
+              const uint32_t wa = w[2 * p][q], wb = w[2 * p + 1][q];
+              const uint32_t lo = __builtin_amdgcn_perm(wb, wa, 0x05040100u);  // column 2q of both rows
+              const uint32_t hi = __builtin_amdgcn_perm(wb, wa, 0x07060302u);  // column 2q + 1
+              acc[2 * q] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, lo),
+                                                          __builtin_bit_cast(bf16x2_t, vv), acc[2 * q], false);
+              acc[2 * q + 1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, hi),
+                                                              __builtin_bit_cast(bf16x2_t, vv), acc[2 * q + 1],
+                                                              false);
             }
-          } else {
+          }
+        } else {
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              const uint32_t wv = w[u][v];
-              acc[v] = fmaf(sw[u], __uint_as_float(wv), acc[v]);
-            }
+          for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[v] = fmaf(__uint_as_float(sw[u]), __uint_as_float(w[u][v]), acc[v]);
           }
         }
       }

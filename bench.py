@@ -4,23 +4,31 @@
 One step = one call of twell_ffn_forward (gate matmul + TwELL epilogue,
 sparse up projection, which also finds the overflow rows, sparse down
 projection, overflow-row list, dense fallback) over the whole token batch of
-the workload, with inputs resident in HBM.  Before any timed loop the dense
-layer runs untimed for 50 ms, past the clock dip of a freshly loaded GPU; the
-headline loop is W untimed steps then exactly K timed steps.  Prints ONE JSON
-line on stdout:
+the workload, with inputs resident in HBM.
 
-  value        tokens/s of the sparse forward (T * steps / timed seconds)
+Timing protocol (HIP events on the launch stream, W untimed warm-up calls
+first, then exactly K timed calls; median, min and p90 reported beside the
+mean):
+  cold (primary)  a 1 GiB buffer is rewritten before every timed call,
+                  outside its events, so weights and activations come from
+                  HBM (L2 and the 256 MB Infinity Cache evicted), as for a
+                  layer whose weights another layer has just displaced;
+  warm            K calls back to back, everything the previous call left in
+                  the caches.
+Before any timed loop the dense layer runs untimed for 50 ms, past the clock
+dip of a freshly loaded GPU.  Prints ONE JSON line on stdout:
+
+  value        tokens/s of the sparse forward, cold (T * K / sum of the K times)
   roofline     the dominant kernel (the gate matmul with the TwELL epilogue)
-               against the bf16 matrix-core peak
-  cpu_baseline the float64 CPU oracle timed on a bounded sample of the batch
-  speedups     against the library's dense matrix-core FFN and against a
-               torch (hipBLASLt) dense FFN on the same inputs
-  training_formats / backward
-               TwELL -> hybrid, the L1 penalty, a standalone pack, and the
-               backward pass from the hybrid activations, on the same batch
+               against the bf16 matrix-core peak, duration measured live
+  cpu_baseline the float64 CPU oracle, three passes over the batch (median)
+  workloads    the skewed and larger-layer workloads (forward, own dense and
+               torch dense FFN, cold and warm) and the density sweep
+  speedups, stage times, gather byte rates, training formats, backward, the
+               fused up+down kernel, the HBM and matrix-core probes
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload NAME]
-                       [--no-cpu-baseline] [--sweep] [--sweep-out FILE]
+                       [--no-cpu-baseline] [--no-extra] [--no-torch] [--no-cold]
 """
 
 from __future__ import annotations
@@ -54,11 +62,12 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="layer_1p5b_bf16")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work to aim for")
-    p.add_argument("--sweep", action="store_true", help="also run the density sweep (stderr / --sweep-out)")
-    p.add_argument("--sweep-out", default=None)
+    p.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work to aim for per pass")
+    p.add_argument("--cpu-reps", type=int, default=3, help="oracle passes (the median is reported)")
+    p.add_argument("--no-extra", action="store_true",
+                   help="skip the skewed / larger-layer workloads and the density sweep")
     p.add_argument("--no-torch", action="store_true", help="skip the torch (hipBLASLt) dense FFN")
-    p.add_argument("--no-cold", action="store_true", help="skip the cold-cache single-call timings")
+    p.add_argument("--no-cold", action="store_true", help="time warm only (profiling runs)")
     return p.parse_args()
 
 
@@ -111,21 +120,53 @@ def split_time(first, second, steps, warmup):
     return a, b
 
 
-def cold_time(fn, reps, flush_buf):
-    """Median ms of single calls, each after overwriting a 1 GiB buffer (evicts L2 and MALL)."""
+def stats_us(times_ms):
+    """mean / median / min / p90 (microseconds) of a list of per-call times."""
+    t = sorted(times_ms)
+    n = len(t)
+    if n == 0:
+        return None
+    p90 = t[min(n - 1, int(round(0.9 * (n - 1))))]
+    return {"mean_us": 1e3 * sum(t) / n, "median_us": 1e3 * t[n // 2], "min_us": 1e3 * t[0],
+            "p90_us": 1e3 * p90, "n": n}
+
+
+def cold_times(fn, reps, warmup, flush_buf):
+    """Per-call ms of `reps` calls, each after rewriting a 1 GiB buffer (evicts L2
+    and the Infinity Cache) outside its events; `warmup` untimed calls first."""
     import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
     s = torch.cuda.current_stream()
-    times = []
+    ev = []
     for _ in range(reps):
         flush_buf.add_(1)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(s)
         fn()
         e1.record(s)
-        torch.cuda.synchronize()
-        times.append(e0.elapsed_time(e1))
-    times.sort()
-    return times[len(times) // 2]
+        ev.append((e0, e1))
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
+
+
+def warm_times(fn, reps, warmup):
+    """Per-call ms of `reps` back-to-back calls (one event between consecutive
+    calls) and the mean over the whole run (events only at its ends)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record(s)
+    for i in range(reps):
+        fn()
+        ev[i + 1].record(s)
+    torch.cuda.synchronize()
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]
+    return per, ev[0].elapsed_time(ev[reps]) / reps
 
 
 def n_dense_rows_bytes(packed, F, s):
@@ -142,7 +183,94 @@ def gather_bytes(T, d, F, tile, cap, s, nnz_kept, rows_sparse):
             + rows_sparse * nt * (2 + cap * (s + 1)))
 
 
-def measure(w, steps, warmup, want_torch=True, want_cold=True, settle_ms=50.0):
+def settle(fn, settle_ms=50.0):
+    """Run fn untimed for settle_ms: under sustained load the clocks of a fresh
+    GPU dip for some milliseconds before they settle."""
+    import torch
+    t_end = time.perf_counter() + settle_ms * 1e-3
+    while time.perf_counter() < t_end:
+        fn()
+        torch.cuda.synchronize()
+
+
+def forward_timings(w, x, wg, wu, wd, b, steps, warmup, flush, want_torch=True, want_split=True):
+    """The sparse forward, the library's dense FFN and a torch (hipBLASLt) dense
+    FFN on the same device inputs: cold and warm per-call statistics, the gate
+    kernel back to back, and the gate / rest split inside the sequence."""
+    import numpy as np
+    import torch
+    import activation_sparse_transformer_bf16_amd as tw
+
+    dev = x.device
+    T, d, F = w.T, w.d, w.F
+    packed = tw.TwellMatrix.empty(T, F, w.tile, w.cap, x.dtype, dev, T, dense=False)
+    y = torch.empty((T, d), dtype=x.dtype, device=dev)
+    ws = torch.empty((tw.twell_ffn_workspace_size(T, d, F, w.tile, w.cap, x.dtype),), dtype=torch.uint8,
+                     device=dev)
+    yd = torch.empty_like(y)
+    wsd = torch.empty((tw.dense_ffn_workspace_size(T, d, F, x.dtype),), dtype=torch.uint8, device=dev)
+    sparse = lambda: tw.twell_ffn_forward(x, wg, wu, wd, b, packed=packed, y=y, workspace=ws)
+    gate = lambda: tw.twell_gate_pack(x, wg, b, packed=packed, scan=False)
+    rest = lambda: tw.twell_sparse_ffn(packed, x, wg, wu, wd, b, y=y, workspace=ws)
+    dense = lambda: tw.dense_ffn_forward(x, wg, wu, wd, b, y=yd, workspace=wsd)
+    settle(dense)
+
+    r = {"workload": w.name}
+    # the headline protocol: exactly `steps` timed calls after `warmup`
+    if flush is not None:
+        t = cold_times(sparse, steps, warmup, flush)
+        r["sparse_cold"] = stats_us(t)
+        r["sparse_cold_ms_list"] = t
+        r["dense_cold"] = stats_us(cold_times(dense, steps, warmup, flush))
+    per, mean = warm_times(sparse, steps, warmup)
+    r["sparse_warm"] = {**stats_us(per), "back_to_back_mean_us": mean * 1e3}
+    per, mean = warm_times(dense, steps, warmup)
+    r["dense_warm"] = {**stats_us(per), "back_to_back_mean_us": mean * 1e3}
+    # The gate kernel's average launch duration: the same launch back to back,
+    # events only around the whole run, which is what a kernel trace's
+    # per-launch average measures.
+    _, ms_gate_b2b = warm_times(gate, steps, warmup)
+    r["gate_back_to_back_us"] = ms_gate_b2b * 1e3
+    if want_split:
+        ms_gate, ms_rest = split_time(gate, rest, steps, warmup)
+        r["gate_in_sequence_us"], r["rest_in_sequence_us"] = ms_gate * 1e3, ms_rest * 1e3
+    if want_torch:
+        import torch.nn.functional as Fn
+
+        def torch_dense():
+            pre = torch.addmm(b[:, None].to(x.dtype), x, wg.t())  # bias in the activation dtype
+            a = torch.relu(pre) * Fn.linear(x, wu)
+            return a @ wd
+
+        per, mean = warm_times(torch_dense, steps, warmup)
+        r["torch_dense_warm"] = {**stats_us(per), "back_to_back_mean_us": mean * 1e3}
+        if flush is not None:
+            r["torch_dense_cold"] = stats_us(cold_times(torch_dense, steps, warmup, flush))
+    sparse()
+    torch.cuda.synchronize()
+    cnt = packed.cnt.cpu().numpy().view(np.uint16).astype(np.int64)
+    r["n_ovf"] = int(packed.n_ovf.item())
+    r["density"] = float(cnt.sum()) / (T * F)
+    ovf = (cnt > w.cap).any(axis=1)
+    r["nnz"], r["nnz_kept"], r["rows_sparse"] = int(cnt.sum()), int(cnt[~ovf].sum()), int((~ovf).sum())
+    r["gate_tflops"] = 2.0 * T * d * F / (ms_gate_b2b * 1e-3) / 1e12
+    key = "sparse_cold" if flush is not None else "sparse_warm"
+    dkey = "dense_cold" if flush is not None else "dense_warm"
+    r["speedup_vs_dense"] = r[dkey]["mean_us"] / r[key]["mean_us"]
+    if want_torch:
+        tkey = "torch_dense_cold" if flush is not None else "torch_dense_warm"
+        r["speedup_vs_torch_dense"] = r[tkey]["mean_us"] / r[key]["mean_us"]
+    r["tokens_per_s"] = T / (r[key]["mean_us"] * 1e-6)
+    r["tokens_per_s_warm"] = T / (r["sparse_warm"]["back_to_back_mean_us"] * 1e-6)
+    r["speedup_vs_dense_warm"] = r["dense_warm"]["back_to_back_mean_us"] / r["sparse_warm"]["back_to_back_mean_us"]
+    log(f"[bench] {w.name}: forward {r[key]['mean_us']:.1f} us ({key}), warm "
+        f"{r['sparse_warm']['back_to_back_mean_us']:.1f} us; own dense {r[dkey]['mean_us']:.1f} us; gate "
+        f"{r['gate_back_to_back_us']:.1f} us; n_ovf {r['n_ovf']}; speedup {r['speedup_vs_dense']:.2f}x")
+    bufs = (packed, y, ws, yd, wsd)
+    return r, bufs
+
+
+def measure(w, steps, warmup, want_torch=True, want_cold=True):
     import numpy as np
     import torch
     import activation_sparse_transformer_bf16_amd as tw
@@ -155,37 +283,10 @@ def measure(w, steps, warmup, want_torch=True, want_cold=True, settle_ms=50.0):
     b = torch.from_numpy(inp.gate_bias).to(dev)
     T, d, F = w.T, w.d, w.F
     s = 2 if w.dtype == "bf16" else 4
+    flush = torch.empty((1 << 28,), dtype=torch.float32, device=dev) if want_cold else None
 
-    packed = tw.TwellMatrix.empty(T, F, w.tile, w.cap, x.dtype, dev, T, dense=False)
-    y = torch.empty((T, d), dtype=x.dtype, device=dev)
-    ws = torch.empty((tw.twell_ffn_workspace_size(T, d, F, w.tile, w.cap, x.dtype),), dtype=torch.uint8,
-                     device=dev)
-    yd = torch.empty_like(y)
-    wsd = torch.empty((tw.dense_ffn_workspace_size(T, d, F, x.dtype),), dtype=torch.uint8, device=dev)
-
-    sparse = lambda: tw.twell_ffn_forward(x, wg, wu, wd, b, packed=packed, y=y, workspace=ws)
+    fw, (packed, y, ws, yd, wsd) = forward_timings(w, x, wg, wu, wd, b, steps, warmup, flush, want_torch)
     gate = lambda: tw.twell_gate_pack(x, wg, b, packed=packed, scan=False)
-    rest = lambda: tw.twell_sparse_ffn(packed, x, wg, wu, wd, b, y=y, workspace=ws)
-    dense = lambda: tw.dense_ffn_forward(x, wg, wu, wd, b, y=yd, workspace=wsd)
-
-    # Under sustained load the clocks of a fresh GPU dip for some milliseconds
-    # before they settle: run the dense layer untimed for settle_ms first, so
-    # that every loop below is timed in the settled state.
-    t_end = time.perf_counter() + settle_ms * 1e-3
-    while time.perf_counter() < t_end:
-        dense()
-        torch.cuda.synchronize()
-    ms_dense, _ = event_time(dense, steps, warmup)
-    ms_gate, ms_rest = split_time(gate, rest, steps, warmup)
-    log(f"[bench] in sequence: gate {ms_gate * 1e3:.1f} us, up+down+fallback {ms_rest * 1e3:.1f} us; "
-        f"dense {ms_dense * 1e3:.1f} us")
-    # The gate kernel's average launch duration: the same launch back to back,
-    # events around the whole run (no event between launches), which is what a
-    # kernel trace's per-launch average measures.
-    ms_gate_b2b, _ = event_time(gate, steps, warmup)
-    log(f"[bench] gate kernel back to back: {ms_gate_b2b * 1e3:.1f} us per launch")
-    ms_sparse, wall = event_time(sparse, steps, warmup)
-    log(f"[bench] sparse forward: {ms_sparse * 1e3:.1f} us/step ({wall:.2f}s wall for {steps} steps)")
 
     # The fused up+down kernel (one wave per token, both gathers in one flow)
     # in place of the two XCD-placed gather kernels, same gate and fallback.
@@ -193,24 +294,6 @@ def measure(w, steps, warmup, want_torch=True, want_cold=True, settle_ms=50.0):
     _, ms_fused_rest = split_time(gate, fused_rest, steps, warmup)
     ms_fused, _ = event_time(lambda: (gate(), fused_rest()), steps, warmup)
     log(f"[bench] fused up+down: {ms_fused_rest * 1e3:.1f} us in sequence, forward {ms_fused * 1e3:.1f} us")
-
-    ms_torch = None
-    if want_torch:
-        import torch.nn.functional as Fn
-
-        def torch_dense():
-            pre = torch.addmm(b[:, None].to(x.dtype), x, wg.t())  # bias in the activation dtype
-            a = torch.relu(pre) * Fn.linear(x, wu)
-            return a @ wd
-
-        ms_torch, _ = event_time(torch_dense, steps, warmup)
-        log(f"[bench] torch (hipBLASLt) dense {ms_torch * 1e3:.1f} us")
-
-    cold = {}
-    if want_cold:
-        flush = torch.empty((1 << 28,), dtype=torch.float32, device=dev)
-        cold = {"sparse_ms": cold_time(sparse, 7, flush), "dense_ms": cold_time(dense, 7, flush)}
-        del flush
 
     # Training-format kernels on this batch's TwELL matrix (with its dense
     # backup rows): TwELL -> hybrid at an ELL width of 256, the L1 norm and the
@@ -345,42 +428,76 @@ def measure(w, steps, warmup, want_torch=True, want_cold=True, settle_ms=50.0):
     log(f"[bench] stream probe: read {probe['read_GBps']:.0f} GB/s, copy {probe['copy_GBps']:.0f} GB/s")
     del big, lo, hi, sink
 
-    # one more forward to read the statistics of this batch
-    sparse()
-    torch.cuda.synchronize()
-    cnt = packed.cnt.cpu().numpy().view(np.uint16).astype(np.int64)
-    n_ovf = int(packed.n_ovf.item())
-    ovf = (cnt > w.cap).any(axis=1)
-    nnz = int(cnt.sum())
-    nnz_kept = int(cnt[~ovf].sum())
-    rows_sparse = int((~ovf).sum())
-    B_alg = gather_bytes(T, d, F, w.tile, w.cap, s, nnz_kept, rows_sparse)
-    flops_gate = 2.0 * T * d * F
+    B_alg = gather_bytes(T, d, F, w.tile, w.cap, s, fw["nnz_kept"], fw["rows_sparse"])
     peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
     res = {
-        "T": T, "ms_sparse": ms_sparse, "ms_gate": ms_gate, "ms_rest": ms_rest, "ms_dense": ms_dense,
-        "ms_torch": ms_torch, "cold": cold, "n_ovf": n_ovf, "density": nnz / (T * F),
-        "nnz": nnz, "nnz_kept": nnz_kept, "rows_sparse": rows_sparse, "gather_bytes": B_alg,
-        "gate_tflops": flops_gate / (ms_gate_b2b * 1e-3) / 1e12, "peak": peak, "ms_gate_b2b": ms_gate_b2b,
-        "dense_tflops": 3 * flops_gate / (ms_dense * 1e-3) / 1e12,
-        "gather_gbs": B_alg / (ms_rest * 1e-3) / 1e9,
+        "T": T, "forward": fw, "gather_bytes": B_alg, "peak": peak,
         "training": training, "backward": backward, "copy_gbs": copy_gbs, "probe": probe,
         "fused": {"forward_us": ms_fused * 1e3, "up_down_fallback_us": ms_fused_rest * 1e3,
-                  "two_kernel_up_down_fallback_us": ms_rest * 1e3,
-                  "note": "gate then twell_sparse_ffn_fused (up and down in one kernel, one wave per token); "
-                          "the headline uses the two XCD-placed gather kernels"},
+                  "two_kernel_up_down_fallback_us": fw["rest_in_sequence_us"],
+                  "note": "gate then twell_sparse_ffn_fused (up and down in one kernel, one wave per token), "
+                          "warm, back to back; the headline uses the two XCD-placed gather kernels"},
     }
-    del x, wg, wu, wd, b, packed, y, ws, yd, wsd
+    del x, wg, wu, wd, b, packed, y, ws, yd, wsd, flush
     torch.cuda.empty_cache()
     return res, inp
 
 
+def extra_workloads(args, base_inp):
+    """The skewed and larger-layer workloads and the density sweep: forward, own
+    dense FFN and torch dense FFN, cold and warm, with the same protocol."""
+    import numpy as np
+    import torch
+    from workloads import CONFIGS, workload
+    from workloads.configs import SWEEP_DENSITIES
+
+    dev = torch.device("cuda:0")
+    flush = torch.empty((1 << 28,), dtype=torch.float32, device=dev) if not args.no_cold else None
+    out = {}
+    for name in ("skewed_bf16", "large_bf16"):
+        w = CONFIGS[name]
+        t0 = time.perf_counter()
+        inp = w.inputs()
+        log(f"[bench] inputs for {name} generated in {time.perf_counter() - t0:.1f}s")
+        x, wg, wu, wd = (to_dev(a, w.dtype, dev) for a in (inp.x, inp.w_gate, inp.w_up, inp.w_down))
+        b = torch.from_numpy(inp.gate_bias).to(dev)
+        r, bufs = forward_timings(w, x, wg, wu, wd, b, args.steps, args.warmup, flush, not args.no_torch)
+        r.pop("sparse_cold_ms_list", None)
+        r["config"] = w.summary()
+        out[name] = r
+        del x, wg, wu, wd, b, bufs, inp
+        torch.cuda.empty_cache()
+    # the sweep reuses the 1.5B-class x and weights; only the gate bias changes
+    base = CONFIGS["layer_1p5b_bf16"]
+    x, wg, wu, wd = (to_dev(a, base.dtype, dev) for a in (base_inp.x, base_inp.w_gate, base_inp.w_up,
+                                                          base_inp.w_down))
+    sweep = []
+    for rho in SWEEP_DENSITIES:
+        w = workload(f"sweep@{rho}")
+        b = torch.from_numpy(w.bias_vector()).to(dev)
+        r, bufs = forward_timings(w, x, wg, wu, wd, b, args.steps, args.warmup, flush, False, want_split=False)
+        rec = {"density_target": rho, "density": r["density"], "n_ovf": r["n_ovf"],
+               "forward_cold": r.get("sparse_cold"), "dense_cold": r.get("dense_cold"),
+               "forward_warm_us": r["sparse_warm"]["back_to_back_mean_us"],
+               "dense_warm_us": r["dense_warm"]["back_to_back_mean_us"],
+               "sparse_tokens_per_s": r["tokens_per_s"],
+               "dense_tokens_per_s": r["tokens_per_s"] * r["speedup_vs_dense"],
+               "speedup_vs_dense": r["speedup_vs_dense"], "speedup_vs_dense_warm": r["speedup_vs_dense_warm"],
+               "gate_tflops": r["gate_tflops"]}
+        sweep.append(rec)
+        del bufs
+    out["density_sweep"] = sweep
+    del x, wg, wu, wd, flush
+    torch.cuda.empty_cache()
+    return out
+
+
 GATE_SOURCES = ("gate_twell.hip", "gemm.hpp", "common.hpp")
 SPARSE_SOURCES = ("sparse.hip", "gather.hpp", "common.hpp")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_gate_twell.layer_1p5b_bf16.counters.txt")
+COUNTER_FILE = os.path.join(ROOT, "profiles", "forward.layer_1p5b_bf16.counters.txt")
 
 
-def gate_source_hash(files=GATE_SOURCES):
+def source_hash(files):
     """Hash of a kernel's sources with comments and blank space removed (a
     comment edit does not change the kernel the counters were taken on)."""
     import hashlib
@@ -395,46 +512,35 @@ def gate_source_hash(files=GATE_SOURCES):
     return h.hexdigest()[:16]
 
 
-def _counter_summary(workload_name):
-    if workload_name != "layer_1p5b_bf16" or not os.path.exists(TRAFFIC_FILE):
+def counter_summary(workload_name):
+    """Per-kernel figures of the committed rocprofv3 summary for this workload:
+    {'gate': {...}, 'up': {...}, 'down': {...}}, each kept only while the
+    kernel's sources hash to the value recorded with the counters."""
+    if workload_name != "layer_1p5b_bf16" or not os.path.exists(COUNTER_FILE):
         return {}
     kv = {}
-    with open(TRAFFIC_FILE) as f:
+    with open(COUNTER_FILE) as f:
         for line in f:
-            if "=" in line and not line.startswith("#"):
+            if "=" in line and not line.lstrip().startswith(("#", "|")):
                 k, v = line.split("=", 1)
                 kv[k.strip()] = v.strip()
-    return kv
+    out = {}
+    for part, files in (("gate", GATE_SOURCES), ("up", SPARSE_SOURCES), ("down", SPARSE_SOURCES)):
+        rec = {k.split(".", 1)[1]: v for k, v in kv.items() if k.startswith(part + ".")}
+        if rec.get("source_hash") != source_hash(files):
+            continue
+        for k, v in list(rec.items()):
+            try:
+                rec[k] = float(v)
+            except ValueError:
+                pass
+        out[part] = rec
+    return out
 
 
-def counted_traffic(workload_name):
-    """HBM bytes per gate-kernel launch from the committed rocprofv3 counter
-    summary (FETCH_SIZE + WRITE_SIZE, each scaled by the reading of a plain
-    copy of known size); None when there is none for this workload or the
-    kernel sources changed since the counters were taken."""
-    kv = _counter_summary(workload_name)
-    if kv.get("source_hash") != gate_source_hash():
-        return None
-    try:
-        return float(kv["hbm_bytes_per_launch"])
-    except (KeyError, ValueError):
-        return None
-
-
-def counted_gather_traffic(workload_name):
-    """The same counters for one sparse up + one sparse down launch (bytes
-    between L2 and the memory fabric; Infinity Cache hits included), or None."""
-    kv = _counter_summary(workload_name)
-    if kv.get("sparse_source_hash") != gate_source_hash(SPARSE_SOURCES):
-        return None
-    try:
-        return float(kv["sparse_hbm_bytes_per_call"])
-    except (KeyError, ValueError):
-        return None
-
-
-def cpu_baseline(w, inp, budget_s):
-    """The float64 oracle (gate, TwELL pack, dense FFN) on the first n tokens."""
+def cpu_baseline(w, inp, budget_s, reps=3):
+    """The float64 oracle (gate, TwELL pack, dense FFN) on the first n tokens of
+    the batch, `reps` passes; the median pass time is reported."""
     import numpy as np
     from threadpoolctl import threadpool_info, threadpool_limits
 
@@ -460,7 +566,8 @@ def cpu_baseline(w, inp, budget_s):
         # clearly exceed the budget
         n = w.T if t_cal * w.T / n0 <= 3 * budget_s else \
             int(max(n0, n0 * budget_s / max(t_cal, 1e-6)) // 256 * 256)
-        t = run(n)
+        times = sorted(run(n) for _ in range(max(1, reps)))
+    t = times[len(times) // 2]
     cpu_model = None
     try:
         with open("/proc/cpuinfo") as f:
@@ -468,49 +575,48 @@ def cpu_baseline(w, inp, budget_s):
     except OSError:
         pass
     return {"value": n / t, "unit": "tokens/s", "cores": int(used), "kind": "oracle",
-            "cpu_model": cpu_model,
-            "sample": f"first {n} of {w.T} tokens of the same batch, one float64 pass "
-                      f"(gate, TwELL pack, dense FFN) in {t:.1f}s; cpu threads available {cores}"}
-
-
-def sweep(args):
-    from workloads.configs import SWEEP_DENSITIES
-    from workloads import workload
-    out = []
-    for rho in SWEEP_DENSITIES:
-        w = workload(f"sweep@{rho}")
-        r, _ = measure(w, max(5, args.steps // 2), 2, want_torch=False, want_cold=False)
-        rec = {"density_target": rho, "density": r["density"], "n_ovf": r["n_ovf"],
-               "sparse_tokens_per_s": w.T / (r["ms_sparse"] * 1e-3),
-               "dense_tokens_per_s": w.T / (r["ms_dense"] * 1e-3),
-               "speedup_vs_dense": r["ms_dense"] / r["ms_sparse"]}
-        log("[sweep] " + json.dumps(rec))
-        out.append(rec)
-    if args.sweep_out:
-        with open(args.sweep_out, "w") as f:
-            json.dump(out, f, indent=1)
+            "cpu_model": cpu_model, "reps": len(times), "pass_seconds": times,
+            "sample": f"first {n} of {w.T} tokens of the same batch, float64 (gate, TwELL pack, dense FFN); "
+                      f"median of {len(times)} passes, {t:.1f}s; cpu threads available {cores}"}
 
 
 def gather_record(w, r):
-    """Byte rates of the two gather stages (up, down; fallback included in the time)."""
-    t = r["ms_rest"] * 1e-3
+    """Byte rates of the two gather stages (sparse up and down).
+
+    effective_GBps counts the algorithmic bytes (one W_u^T row and one W_d row
+    per active entry, x, y and TwELL) over the in-sequence time of up + down +
+    fallback; most weight rows are served from L2, so it is an effective rate
+    and no roofline fraction.  The physical figures come from the committed
+    rocprofv3 summary of the same kernels: bytes between L2 and the memory
+    fabric per launch (FETCH_SIZE + WRITE_SIZE, Infinity Cache hits included,
+    so an upper bound on HBM bytes) over the kernel-trace duration, against
+    the 8 TB/s HBM spec, and their ratio to the compulsory bytes (each weight
+    row once, x, y and TwELL once)."""
+    fw = r["forward"]
+    t = fw["rest_in_sequence_us"] * 1e-6
     s = 2 if w.dtype == "bf16" else 4
-    # compulsory: every weight row of W_u and W_d once, x read, y written, TwELL read
-    compulsory = 2 * w.F * w.d * s + 2 * w.T * w.d * s + w.T * w.n_tiles * (2 + w.cap * (s + 1))
-    rec = {"bytes_alg": r["gather_bytes"], "achieved_GBps": r["gather_gbs"],
-           "frac_of_hbm_peak": r["gather_gbs"] / HBM_PEAK_GBS,
-           "compulsory_bytes": compulsory, "compulsory_frac_of_hbm_peak": compulsory / t / 1e9 / HBM_PEAK_GBS}
-    rec["compulsory_frac_of_measured_copy"] = compulsory / t / 1e9 / r["copy_gbs"]
-    counted = counted_gather_traffic(w.name)
-    rec["counted_fabric_bytes"] = counted
-    if counted:
-        rec["counted_GBps"] = counted / t / 1e9
-        rec["counted_frac_of_hbm_peak"] = counted / t / 1e9 / HBM_PEAK_GBS
-        rec["reuse_factor"] = r["gather_bytes"] / counted
-    rec["note"] = ("up+down+fallback time within the forward sequence; bytes_alg per active entry = one W_u^T row "
-                   "+ one W_d row; compulsory = each weight row once + x, y and TwELL; counted = rocprofv3 "
-                   "FETCH_SIZE + WRITE_SIZE of one up and one down launch (L2 <-> fabric, Infinity Cache hits "
-                   "included), scaled by a plain copy")
+    twell_bytes = w.T * w.n_tiles * (2 + w.cap * (s + 1))
+    rec = {"bytes_alg": r["gather_bytes"], "effective_GBps": r["gather_bytes"] / t / 1e9,
+           "time_in_sequence_us": t * 1e6,
+           "compulsory_bytes": {"up": w.F * w.d * s + w.T * w.d * s + twell_bytes,
+                                "down": w.F * w.d * s + w.T * w.d * s}}
+    cs = counter_summary(w.name)
+    for part in ("up", "down"):
+        c = cs.get(part)
+        if not c:
+            rec[part] = None
+            continue
+        b, us = c["fabric_bytes"], c["trace_us"]
+        rec[part] = {"kernel": c.get("kernel"), "trace_us": us, "fabric_bytes": b,
+                     "fabric_GBps": b / (us * 1e-6) / 1e9,
+                     "fabric_frac_of_hbm_peak": b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                     "fabric_over_compulsory": b / rec["compulsory_bytes"][part],
+                     "ta_busy": c.get("ta_busy"), "valu_busy": c.get("valu_busy")}
+    rec["note"] = ("effective_GBps: algorithmic bytes / in-sequence time (L2-served re-reads counted; not a "
+                   "roofline fraction). up/down: rocprofv3 FETCH_SIZE + WRITE_SIZE per launch (scaled by a plain "
+                   "copy; Infinity Cache hits included) over the kernel-trace average duration, from the committed "
+                   "summary of these sources; ta_busy / valu_busy: TA_TA_BUSY and SQ_INSTS_VALU x 4 cycles over "
+                   "the elapsed cycles")
     return rec
 
 
@@ -528,49 +634,62 @@ def main():
 
     w = workload(args.workload)
     r, inp = measure(w, args.steps, args.warmup, want_torch=not args.no_torch, want_cold=not args.no_cold)
-    cpu = None if args.no_cpu_baseline else cpu_baseline(w, inp, args.cpu_budget)
-    if args.sweep:
-        sweep(args)
+    fw = r["forward"]
+    extra = None
+    if not args.no_extra and w.name == "layer_1p5b_bf16":
+        extra = extra_workloads(args, inp)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, inp, args.cpu_budget, args.cpu_reps)
 
-    ach = r["gate_tflops"]
+    cold = "sparse_cold" in fw
+    head = fw["sparse_cold"] if cold else fw["sparse_warm"]
+    ms_step = head["mean_us"] * 1e-3
+    ach = fw["gate_tflops"]
+    cs = counter_summary(w.name).get("gate", {})
     record = {
         "metric": METRIC,
-        "value": w.T / (r["ms_sparse"] * 1e-3),
+        "value": w.T / (ms_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": r["ms_sparse"],
+        "ms_per_step": ms_step,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic: seeded Gaussian x and weights (var 1/fan_in), per-token gate bias for the density",
-        "config": {**w.summary(), "parallelism": "single GPU"},
+        "config": {**w.summary(), "parallelism": "single GPU",
+                   "timing": "cold: 1 GiB rewritten before every timed step, outside its HIP events" if cold
+                   else "warm: back-to-back steps"},
         "roofline": {"bound": "mfma", "achieved": ach, "peak": r["peak"], "unit": "TFLOP/s",
-                     "frac": ach / r["peak"], "traffic": counted_traffic(w.name),
+                     "frac": ach / r["peak"], "traffic": cs.get("fabric_bytes"),
                      "measured_peak": r["probe"]["mfma_bf16_TFLOPs"] if w.dtype == "bf16" else None,
                      "frac_of_measured_peak": ach / r["probe"]["mfma_bf16_TFLOPs"] if w.dtype == "bf16" else None,
+                     "mfma_busy_counter": cs.get("mfma_busy"),
                      "kernel": "k_gate_twell (gate matmul + TwELL epilogue)",
-                     "duration_us": r["ms_gate_b2b"] * 1e3,
+                     "duration_us": fw["gate_back_to_back_us"],
                      "timing": "HIP events around back-to-back launches on the launch stream"},
         "cpu_baseline": cpu,
-        "speedup_vs_dense": r["ms_dense"] / r["ms_sparse"],
-        "speedup_vs_torch_dense": (r["ms_torch"] / r["ms_sparse"]) if r["ms_torch"] else None,
-        "stages_us": {"gate_twell_in_sequence": r["ms_gate"] * 1e3, "gate_twell_back_to_back": r["ms_gate_b2b"] * 1e3,
-                      "up_down_fallback_in_sequence": r["ms_rest"] * 1e3,
-                      "forward": r["ms_sparse"] * 1e3, "dense_ffn": r["ms_dense"] * 1e3,
-                      "torch_dense_ffn": r["ms_torch"] * 1e3 if r["ms_torch"] else None},
-        "cold_us": {k: v * 1e3 for k, v in r["cold"].items()},
+        "timing_us": {"forward_cold": fw.get("sparse_cold"), "forward_warm": fw["sparse_warm"],
+                      "dense_cold": fw.get("dense_cold"), "dense_warm": fw["dense_warm"],
+                      "torch_dense_cold": fw.get("torch_dense_cold"), "torch_dense_warm": fw.get("torch_dense_warm")},
+        "speedup_vs_dense": fw["speedup_vs_dense"],
+        "speedup_vs_torch_dense": fw.get("speedup_vs_torch_dense"),
+        "speedup_vs_dense_warm": fw["speedup_vs_dense_warm"],
+        "tokens_per_s_warm": fw["tokens_per_s_warm"],
+        "stages_us": {"gate_twell_in_sequence": fw["gate_in_sequence_us"],
+                      "gate_twell_back_to_back": fw["gate_back_to_back_us"],
+                      "up_down_fallback_in_sequence": fw["rest_in_sequence_us"]},
         "gather": gather_record(w, r),
-        "dense_mfma_tflops": r["dense_tflops"],
+        "dense_mfma_tflops_warm": 3 * 2.0 * w.T * w.d * w.F / (fw["dense_warm"]["back_to_back_mean_us"] * 1e-6) / 1e12,
         "hbm_copy_GBps": r["copy_gbs"],
         "hbm_probe": r["probe"],
+        "workloads": extra,
         "training_formats": r["training"],
         "backward": r["backward"],
         "fused_up_down": r["fused"],
-        "density": r["density"],
-        "n_ovf": r["n_ovf"],
+        "density": fw["density"],
+        "n_ovf": fw["n_ovf"],
     }
     print(json.dumps(record), flush=True)
 
