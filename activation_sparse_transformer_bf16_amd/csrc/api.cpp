@@ -105,7 +105,8 @@ twell_status check_matrix(const twell_matrix *m, bool need_ovf_all) {
 
 // Workspace of the sparse forward:
 //   row flags [T] u8 | entry counts [T] i32 |
-//   region A: the compact entry lists [T][stride] x 8 bytes, and afterwards
+//   region A: the compact entry lists [T][stride] x 8 bytes (16 when the up
+//             projection splits d in two halves, see UpPlan), and afterwards
 //             (the lists are consumed by the down projection before the
 //             fallback starts, in stream order) the fallback's activations
 //             [R][F] in the storage dtype for one chunk of R overflow rows |
@@ -156,7 +157,8 @@ FfnWs ffn_ws_layout(int T, int d, int F, int tile, int cap, twell_dtype dt, int 
   w.list_n = align_up((size_t)T, ALIGN_WS);
   w.list = align_up(w.list_n + (size_t)T * 4, ALIGN_WS);
   w.a = w.list;  // aliases the lists (see above)
-  const size_t region = std::max((size_t)T * w.stride * 8, (size_t)chunk_rows * F * dt_size(dt));
+  const size_t entry = (size_t)up_plan(d, F, tile, cap, to_dt(dt)).entry_bytes();
+  const size_t region = std::max((size_t)T * w.stride * entry, (size_t)chunk_rows * F * dt_size(dt));
   w.partial = align_up(w.list + region, ALIGN_WS);
   w.total = std::max(align_up(w.partial + (size_t)w.partial_tiles * FALLBACK_SPLIT_TILE * 4, ALIGN_WS), ALIGN_WS);
   return w;

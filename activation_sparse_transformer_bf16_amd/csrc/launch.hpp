@@ -41,6 +41,38 @@ hipError_t compact_rows(const uint8_t *row_flag, int T, int *ovf_rows, int ovf_c
 // The same from int32 flags [T], listing the rows over the flag array itself.
 hipError_t compact_rows_in_place(int *flags_then_rows, int T, int *n_ovf, hipStream_t s);
 
+// How the up projection cuts its weights: hidden units in groups of tpg
+// TwELL tiles (about 4 MB of W_u^T rows, one XCD's L2), and, when the groups
+// need more than one round over the 8 XCDs, each W_u^T row in dc = 2 halves
+// of d (a group then holds twice the units, so x is streamed half as often;
+// the halves' partial dot products meet in a 16-byte list entry).
+struct UpPlan {
+  int tpg, n_groups, dc;
+  int entry_bytes() const { return dc == 1 ? 8 : 16; }
+};
+constexpr int UP_LIST = 256;  // entries per wave list (tiles per group * cap)
+inline UpPlan up_plan(int d, int F, int tile, int cap, Dt dt) {
+  const int s = dt == Dt::BF16 ? 2 : 4;
+  const int nt = F / tile;
+  const size_t group_target = (size_t)4 << 20;
+  auto tiles_per_group = [&](int dc) {
+    const size_t tile_bytes = (size_t)tile * (d / dc) * s;
+    int tpg = (int)std::max<size_t>(1, group_target / tile_bytes);
+    tpg = std::min(tpg, std::min(std::min(64, nt), UP_LIST / cap));
+    while (nt % tpg != 0) --tpg;
+    return tpg;
+  };
+  UpPlan p{tiles_per_group(1), 0, 1};
+  p.n_groups = nt / p.tpg;
+  // a half row must still cover whole 16-byte chunks of all 64 lanes
+  if (p.n_groups > 8 && (d / 2) % (64 * (16 / s)) == 0) {
+    p.dc = 2;
+    p.tpg = tiles_per_group(2);
+    p.n_groups = nt / p.tpg;
+  }
+  return p;
+}
+
 // Sparse up / down projections over the TwELL entries of non-overflow rows.
 struct SparseArgs {
   Dt dtype;
@@ -52,7 +84,8 @@ struct SparseArgs {
   const void *x;            // [T][d]
   const void *wu;           // [F][d]
   const void *wd;           // [F][d]
-  void *list;               // [T][stride] entries (uint32 row byte offset, fp32 v = h * u)
+  void *list;               // [T][stride] entries: UpPlan dc == 1: (uint32 row byte offset, v = round(h * u));
+                            // dc == 2: (offset, fp32 partial u of the first half of d, fp32 h, partial of the second)
   int *list_n;              // [T] entries per row
   int stride;               // list entries per row: nt * cap rounded up to a multiple of 8
   void *y;                  // [T][d]

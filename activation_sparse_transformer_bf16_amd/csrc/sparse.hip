@@ -210,17 +210,21 @@ hipError_t zero_int(int *p, hipStream_t s) {
   return hipGetLastError();
 }
 
-constexpr int UP_LIST = 256;  // entries per wave list (tiles per group * cap)
-
 // ---------------------------------------------------------------------------
-// Sparse up projection.  NC = 16-byte chunks per lane covering d; U = entries
-// in flight per wave (U * NC 16-byte loads per lane outstanding).
+// Sparse up projection.  DC = parts of d (1 or 2, UpPlan): the wave of
+// (group, part q, token) dots the part's d / DC columns of x_t and of the
+// W_u^T rows.  NC = 16-byte chunks per lane covering one part; U = entries in
+// flight per wave (U * NC 16-byte loads per lane outstanding).
 //
-// Writes, per non-overflow row t, the compact entry list of the row:
-//   list[t * stride + e] = (byte offset of hidden unit j's weight row,
-//                           v = round(h * u): fp32 bits, or bf16 bits in the low half)
-// for e < list_n[t], in ascending (tile, slot) order, i.e. ascending j, and
-// padding entries (NO_ROW, 0) up to the next multiple of 8.  A row overflows
+// Writes, per non-overflow row t, the compact entry list of the row, in
+// ascending (tile, slot) order, i.e. ascending j:
+//   DC = 1: list[t * stride + e] = (byte offset of hidden unit j's weight row,
+//           v = round(h * u): fp32 bits, or bf16 bits in the low half);
+//   DC = 2: list[t * stride + e] = (offset, u over the first half of d,
+//           h, u over the second half): part 0 writes the first 8 bytes,
+//           part 1 the last 8; the down kernel forms v = round(h * (u0 + u1));
+// for e < list_n[t], and padding entries (NO_ROW, 0...) up to the next
+// multiple of 8.  A row overflows
 // iff one of its tiles counts more than cap entries; every wave decides that
 // from the row's counts, skips such rows, and the group-0 wave records
 // row_flag[t] (1 for an overflow row) and list_n[t] = -1 for them.  A local
@@ -234,24 +238,30 @@ struct UpEntry {
   uint32_t pad;
 };
 
-template <Dt D, int NC, int U>
+template <Dt D, int NC, int U, int DC>
 __global__ __launch_bounds__(SP_THREADS) void k_sparse_up(
     const typename DtT<D>::T *__restrict__ x, const typename DtT<D>::T *__restrict__ wu,
     const uint16_t *__restrict__ cnt, const typename DtT<D>::T *__restrict__ val,
-    const uint8_t *__restrict__ idx, uint8_t *__restrict__ row_flag, u32x2_t *__restrict__ list,
+    const uint8_t *__restrict__ idx, uint8_t *__restrict__ row_flag, void *__restrict__ list_v,
     int *__restrict__ list_n, int stride, int T, int d, int nt, int tile, int cap, int tpg, int n_groups,
     int tok_per_wg, int n_tb) {
   using TT = typename DtT<D>::T;
   constexpr int EPC = 16 / sizeof(TT);  // elements per 16-byte chunk
+  static_assert(DC == 1 || DC == 2, "d whole or in two halves");
   __shared__ UpEntry lists[SP_WAVES][UP_LIST];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  int g, tb;
-  group_coords(blockIdx.x, n_groups, n_tb, g, tb);
-  if (g >= n_groups) return;
+  int vg, tb;
+  group_coords(blockIdx.x, n_groups * DC, n_tb, vg, tb);
+  if (vg >= n_groups * DC) return;
+  const int g = vg / DC, part = vg - g * DC;  // the two parts of a group sit on neighbouring XCDs
   const int k0 = g * tpg;
   const int kn = min(tpg, nt - k0);
   UpEntry *L = lists[wave];
-  const __amdgpu_buffer_rsrc_t wur = buffer_rsrc(wu, (size_t)nt * tile * d * sizeof(TT));
+  const int dp = d / DC;  // columns of one part
+  u32x2_t *list = reinterpret_cast<u32x2_t *>(list_v);  // DC = 2: two u32x2 per entry
+  // W_u^T from the part's first column on, to the end of the array
+  const __amdgpu_buffer_rsrc_t wur =
+      buffer_rsrc(wu + part * dp, ((size_t)nt * tile * d - (size_t)part * dp) * sizeof(TT));
   const uint32_t lane_off = lane * 16;
   const uint32_t row_bytes = (uint32_t)d * sizeof(TT);
   // lanes 16 r (r = 0..3) store the entry whose total their row holds
@@ -261,7 +271,7 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_up(
   for (int it = wave; it < tok_per_wg; it += SP_WAVES) {
     const int t = tb * tok_per_wg + it;
     if (t >= T) break;
-    const TT *xt = x + (size_t)t * d;
+    const TT *xt = x + (size_t)t * d + part * dp;
     u32x4_t xr[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) xr[c] = *reinterpret_cast<const u32x4_t *>(xt + (c * 64 + lane) * EPC);
@@ -282,12 +292,15 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_up(
     }
     const bool ovf = ballot(over) != 0;
     const int sum = __builtin_amdgcn_readlane(wave_incl_scan(partial), 63);
-    if (g == 0) {
+    if (g == 0 && part == 0) {
       if (lane == 0) {
         row_flag[t] = ovf ? 1 : 0;
         list_n[t] = ovf ? -1 : sum;
       }
-      if (!ovf && lane < ((sum + 7) & ~7) - sum) list[lbase + sum + lane] = u32x2_t{NO_ROW, 0u};
+      if (!ovf && lane < ((sum + 7) & ~7) - sum) {
+        list[(lbase + sum + lane) * DC] = u32x2_t{NO_ROW, 0u};
+        if constexpr (DC == 2) list[(lbase + sum + lane) * 2 + 1] = u32x2_t{0u, 0u};
+      }
     }
     if (ovf) continue;
     const int before = g == 0 ? 0 : sum;
@@ -350,9 +363,14 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_up(
         }
         const float tot = Reduce<U>::run(p);
         if (storer && u0 + my_u < ne) {
-          const float v = mine.h * tot;
-          const uint32_t vb = D == Dt::BF16 ? (uint32_t)bf16_rne(v) : __float_as_uint(v);
-          list[lbase + mine.dst] = u32x2_t{mine.off, vb};
+          if constexpr (DC == 1) {
+            const float v = mine.h * tot;
+            const uint32_t vb = D == Dt::BF16 ? (uint32_t)bf16_rne(v) : __float_as_uint(v);
+            list[lbase + mine.dst] = u32x2_t{mine.off, vb};
+          } else {
+            list[(lbase + mine.dst) * 2 + part] =
+                part == 0 ? u32x2_t{mine.off, __float_as_uint(tot)} : u32x2_t{__float_as_uint(mine.h), __float_as_uint(tot)};
+          }
         }
       }
     }
@@ -369,9 +387,9 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_up(
 // takes one.  The token's list goes through LDS, 64 entries per load.
 // U = load instructions in flight per wave.
 
-template <Dt D, int SLICE, int U>
+template <Dt D, int SLICE, int U, int DC>
 __global__ __launch_bounds__(SP_THREADS) void k_sparse_down(
-    const u32x2_t *__restrict__ list, const int *__restrict__ list_n, int stride,
+    const void *__restrict__ list_v, const int *__restrict__ list_n, int stride,
     const typename DtT<D>::T *__restrict__ wd, typename DtT<D>::T *__restrict__ y, int T, int d, int F,
     int n_slices, int tok_per_wg, int n_tb) {
   using TT = typename DtT<D>::T;
@@ -404,7 +422,7 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_down(
     if (t >= T) break;
     const int n = list_n[t];
     if (n < 0) continue;  // overflow row: the dense fallback writes it
-    const u32x2_t *lt = list + (size_t)t * stride;
+    const u32x2_t *lt = reinterpret_cast<const u32x2_t *>(list_v) + (size_t)t * stride * DC;
     float acc[CPL];
 #pragma unroll
     for (int v = 0; v < CPL; ++v) acc[v] = 0.f;
@@ -416,7 +434,17 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_down(
       // loads return zeros, so padding adds exactly 0 whatever the weights
       // hold; entries beyond that in the chunk are never read.
       const int ne = min(64, (n - e0 + 7) & ~7);
-      if (lane < ne) C[lane] = lt[e0 + lane];
+      if (lane < ne) {
+        if constexpr (DC == 1) {
+          C[lane] = lt[e0 + lane];
+        } else {
+          // (offset, u of the first half of d, h, u of the second half):
+          // v = round(h * u), the halves added in a fixed order
+          const u32x4_t q = reinterpret_cast<const u32x4_t *>(lt)[e0 + lane];
+          const float v = __uint_as_float(q[2]) * (__uint_as_float(q[1]) + __uint_as_float(q[3]));
+          C[lane] = u32x2_t{q[0], D == Dt::BF16 ? (uint32_t)bf16_rne(v) : __float_as_uint(v)};
+        }
+      }
       wave_sync_lds();
       for (int e = 0; e < ne; e += STEP) {
         u32x4_t w[U];
@@ -482,36 +510,43 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_down(
 // ---------------------------------------------------------------------------
 // Launchers.
 
-template <Dt D, int NC>
-static hipError_t launch_up(const SparseArgs &a, hipStream_t s) {
+template <Dt D, int NC, int DC>
+static hipError_t launch_up(const SparseArgs &a, const UpPlan &p, hipStream_t s) {
   using TT = typename DtT<D>::T;
   const int nt = a.F / a.tile;
-  // Tiles per group: about 4 MB of W_u^T rows per group (one XCD's L2); at
-  // the 1.5B-class and larger layer shapes this was the fastest setting of a
-  // sweep over 1..8 tiles per group.
-  const size_t group_target = (size_t)4 << 20;
-  const size_t tile_bytes = (size_t)a.tile * a.d * sizeof(TT);
-  int tpg = (int)std::max<size_t>(1, group_target / tile_bytes);
-  tpg = std::min(tpg, std::min(std::min(64, nt), UP_LIST / a.cap));
-  while (nt % tpg != 0) --tpg;
-  const int n_groups = nt / tpg;
   const int tok = 16;
   const int n_tb = (a.T + tok - 1) / tok;
   constexpr int U = NC <= 4 ? 4 : 2;
-  hipLaunchKernelGGL((k_sparse_up<D, NC, U>), dim3(padded_groups(n_groups) * n_tb), dim3(SP_THREADS), 0, s, (const TT *)a.x,
-                     (const TT *)a.wu, a.cnt, (const TT *)a.val, a.idx, a.row_flag, (u32x2_t *)a.list, a.list_n,
-                     a.stride, a.T, a.d, nt, a.tile, a.cap, tpg, n_groups, tok, n_tb);
+  hipLaunchKernelGGL((k_sparse_up<D, NC, U, DC>), dim3(padded_groups(p.n_groups * DC) * n_tb), dim3(SP_THREADS), 0,
+                     s, (const TT *)a.x, (const TT *)a.wu, a.cnt, (const TT *)a.val, a.idx, a.row_flag, a.list,
+                     a.list_n, a.stride, a.T, a.d, nt, a.tile, a.cap, p.tpg, p.n_groups, tok, n_tb);
   return hipGetLastError();
 }
 
 template <Dt D>
 static hipError_t up_dispatch(const SparseArgs &a, hipStream_t s) {
   using TT = typename DtT<D>::T;
-  const int nc = a.d / (64 * (16 / (int)sizeof(TT)));
+  // Tiles per group: about 4 MB of W_u^T rows per group (one XCD's L2); at
+  // the 1.5B-class and larger layer shapes this was the fastest setting of a
+  // sweep over 1..8 tiles per group.
+  const UpPlan p = up_plan(a.d, a.F, a.tile, a.cap, a.dtype);
+  const int nc = a.d / p.dc / (64 * (16 / (int)sizeof(TT)));
+  if (p.dc == 2) {
+    switch (nc) {
+#define TWELL_UP2_CASE(N) \
+  case N:                 \
+    return launch_up<D, N, 2>(a, p, s);
+      TWELL_UP2_CASE(1) TWELL_UP2_CASE(2) TWELL_UP2_CASE(3) TWELL_UP2_CASE(4) TWELL_UP2_CASE(5)
+      TWELL_UP2_CASE(6) TWELL_UP2_CASE(7) TWELL_UP2_CASE(8)
+#undef TWELL_UP2_CASE
+      default:
+        return hipErrorInvalidValue;
+    }
+  }
   switch (nc) {
 #define TWELL_UP_CASE(N) \
   case N:                \
-    return launch_up<D, N>(a, s);
+    return launch_up<D, N, 1>(a, p, s);
     TWELL_UP_CASE(1) TWELL_UP_CASE(2) TWELL_UP_CASE(3) TWELL_UP_CASE(4) TWELL_UP_CASE(5) TWELL_UP_CASE(6)
     TWELL_UP_CASE(7) TWELL_UP_CASE(8) TWELL_UP_CASE(9) TWELL_UP_CASE(10) TWELL_UP_CASE(11) TWELL_UP_CASE(12)
     TWELL_UP_CASE(13) TWELL_UP_CASE(14) TWELL_UP_CASE(15) TWELL_UP_CASE(16)
@@ -526,15 +561,14 @@ hipError_t sparse_up(const SparseArgs &a, hipStream_t s) {
   return a.dtype == Dt::BF16 ? up_dispatch<Dt::BF16>(a, s) : up_dispatch<Dt::F32>(a, s);
 }
 
-template <Dt D, int SLICE, int U>
+template <Dt D, int SLICE, int U, int DC>
 static hipError_t launch_down(const SparseArgs &a, hipStream_t s) {
   using TT = typename DtT<D>::T;
   const int n_slices = a.d / SLICE;
   const int tok = 16;
   const int n_tb = (a.T + tok - 1) / tok;
-  hipLaunchKernelGGL((k_sparse_down<D, SLICE, U>), dim3(padded_groups(n_slices) * n_tb), dim3(SP_THREADS), 0, s,
-                     (const u32x2_t *)a.list, a.list_n, a.stride, (const TT *)a.wd, (TT *)a.y, a.T, a.d, a.F,
-                     n_slices, tok, n_tb);
+  hipLaunchKernelGGL((k_sparse_down<D, SLICE, U, DC>), dim3(padded_groups(n_slices) * n_tb), dim3(SP_THREADS), 0, s,
+                     a.list, a.list_n, a.stride, (const TT *)a.wd, (TT *)a.y, a.T, a.d, a.F, n_slices, tok, n_tb);
   return hipGetLastError();
 }
 
@@ -543,7 +577,10 @@ hipError_t sparse_down(const SparseArgs &a, hipStream_t s) {
   // 256-column output slices, 8 list entries per iteration.  (128-column
   // slices, which would keep F rows of a slice within one XCD's L2 for
   // F > 8192, measured slower at F = 14336.)
-  return a.dtype == Dt::BF16 ? launch_down<Dt::BF16, 256, 4>(a, s) : launch_down<Dt::F32, 256, 8>(a, s);
+  const int dc = up_plan(a.d, a.F, a.tile, a.cap, a.dtype).dc;
+  if (a.dtype == Dt::BF16)
+    return dc == 2 ? launch_down<Dt::BF16, 256, 4, 2>(a, s) : launch_down<Dt::BF16, 256, 4, 1>(a, s);
+  return dc == 2 ? launch_down<Dt::F32, 256, 8, 2>(a, s) : launch_down<Dt::F32, 256, 8, 1>(a, s);
 }
 
 }  // namespace twell
