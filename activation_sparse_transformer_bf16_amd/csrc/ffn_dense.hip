@@ -100,7 +100,7 @@ __device__ __forceinline__ void gate_up_tile(
     }
   };
   f32x16_t acc[NWM][2];
-  gemm_mainloop_dma<D, BN>(acc, rowA, rowB, rowv, init, nk, smem);
+  gemm_mainloop_dma<D, BN, DmaBig>(acc, rowA, rowB, rowv, init, nk, smem);
 
   const int col = lane & 31;
   if (part != nullptr) {

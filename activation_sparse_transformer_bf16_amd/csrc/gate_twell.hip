@@ -25,14 +25,14 @@ namespace twell {
 //   vals   [RPP][VS bytes]         slot values of each row of the pass
 //   idxs   [RPP][IS bytes]         slot column offsets
 //   dummy  [64][4 bytes]           where the lanes that hold no mask word write
-template <Dt D, int BN, int RPP_>
+template <Dt D, int BN, int RPP_, int BM = GEMM_BM>
 struct EpilogueLds {
   using T = typename DtT<D>::T;
   static constexpr int S = (int)sizeof(T);
   static constexpr int MW = BN / 32;
   static constexpr int RPP = RPP_;
   static constexpr int RS = RPP * S + 8;
-  static constexpr int MASKS = GEMM_BM * MW * 4;
+  static constexpr int MASKS = BM * MW * 4;
   static constexpr int TILE_OFF = MASKS;
   static constexpr int TILE = BN * RS;
   __host__ __device__ static constexpr int vs(int cap) { return (cap * S + 15) / 16 * 16; }
@@ -42,7 +42,7 @@ struct EpilogueLds {
   __host__ __device__ static constexpr int dummy_off(int cap) { return idxs_off(cap) + RPP * is(cap); }
   __host__ __device__ static constexpr int bytes(int cap) { return dummy_off(cap) + 64 * 4; }
 };
-constexpr int LDS_MAX = 160 * 1024;
+constexpr int LDS_MAX = 160 * 1024;  // per CU; a DmaHalf workgroup gets half of it
 
 // Four consecutive rows (accumulator registers i0..i0+3) of one column, rounded.
 __device__ __forceinline__ void put4(char *dst, const f32x16_t &a, int i0, uint16_t) {
@@ -84,21 +84,22 @@ __device__ __forceinline__ void copy_chunk(char *__restrict__ g, const char *l, 
     *g = *l;
 }
 
-template <Dt D, int BN, int RPP_, bool DUMP>
-__global__ __launch_bounds__(DMA_THREADS) void k_gate_twell(
+template <Dt D, int BN, int RPP_, bool DUMP, class Cfg>
+__global__ __launch_bounds__(Cfg::THREADS, Cfg::WAVES_PER_SIMD) void k_gate_twell(
     const typename DtT<D>::T *__restrict__ x, const typename DtT<D>::T *__restrict__ wg,
     const float *__restrict__ beta, int M, int K, int N, int cap, uint16_t *__restrict__ cnt,
     typename DtT<D>::T *__restrict__ val, uint8_t *__restrict__ idx,
     typename DtT<D>::T *__restrict__ pre_out) {
   using T = typename DtT<D>::T;
-  using WT = WaveTile<BN>;
+  using WT = WaveTile<BN, Cfg>;
   constexpr int NWM = WT::NWM, NWN = WT::NWN;
+  constexpr int BM = Cfg::BM;
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
-  const int mt = (M + GEMM_BM - 1) / GEMM_BM, ntl = N / BN;
+  const int mt = (M + BM - 1) / BM, ntl = N / BN;
   int tm, tn;
   tile_coords(blockIdx.x, mt, ntl, tm, tn);
-  const int m0 = tm * GEMM_BM, n0 = tn * BN;
+  const int m0 = tm * BM, n0 = tn * BN;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int row0 = WT::row0(wave), col0 = WT::col0(wave);
   const size_t ldk = (size_t)K * sizeof(T);
@@ -122,7 +123,7 @@ __global__ __launch_bounds__(DMA_THREADS) void k_gate_twell(
     }
   };
   f32x16_t acc[NWM][NWN];
-  gemm_mainloop_dma<D, BN>(acc, rowA, rowB, rowv, init, (int)(ldk / SLAB), smem);
+  gemm_mainloop_dma<D, BN, Cfg>(acc, rowA, rowB, rowv, init, (int)(ldk / SLAB), smem);
 
   // ---- TwELL epilogue ----
   // M  every wave compares its accumulators with the activity threshold of the
@@ -136,7 +137,7 @@ __global__ __launch_bounds__(DMA_THREADS) void k_gate_twell(
   //     (value, column) pairs that fall below `cap` in the row's LDS slots;
   //     then the row's count, slots and zero padding go to global memory
   //     with vector stores.
-  using L = EpilogueLds<D, BN, RPP_>;
+  using L = EpilogueLds<D, BN, RPP_, BM>;
   constexpr int MW = L::MW, RPP = L::RPP, RS = L::RS, S = L::S;
   const int ntiles = N / BN;
   const int VS = L::vs(cap), IS = L::is(cap);
@@ -182,10 +183,10 @@ __global__ __launch_bounds__(DMA_THREADS) void k_gate_twell(
     }
   };
   auto clear_slots = [&]() {
-    for (int o = tid * 16; o < RPP * (VS + IS); o += DMA_THREADS * 16)
+    for (int o = tid * 16; o < RPP * (VS + IS); o += Cfg::THREADS * 16)
       *reinterpret_cast<u32x4_t *>(vals + o) = u32x4_t{0u, 0u, 0u, 0u};
   };
-  if constexpr (RPP == GEMM_BM) {
+  if constexpr (RPP == BM) {
     // one pass: masks and values from the same register reads
     clear_slots();
 #pragma unroll
@@ -209,8 +210,8 @@ __global__ __launch_bounds__(DMA_THREADS) void k_gate_twell(
       for (int bn = 0; bn < NWN; ++bn) asm volatile("" : "+a"(acc[bm][bn]));
   }
 #pragma unroll
-  for (int p = 0; p < GEMM_BM / RPP; ++p) {
-    if constexpr (RPP != GEMM_BM) {
+  for (int p = 0; p < BM / RPP; ++p) {
+    if constexpr (RPP != BM) {
       // V: stage the rounded values of this pass and clear the slots
       clear_slots();
 #pragma unroll
@@ -226,7 +227,7 @@ __global__ __launch_bounds__(DMA_THREADS) void k_gate_twell(
     static_assert(MW == 4 || MW == 8, "tile of 128 or 256 columns");
     const int wsub = lane % MW;
     const int nvc = (cap * S) / vunit, nic = cap / iunit;  // chunks of the slot values / indices
-    for (int rl = wave * RPS + lane / MW; rl - lane / MW < RPP; rl += DMA_WAVES * RPS) {
+    for (int rl = wave * RPS + lane / MW; rl - lane / MW < RPP; rl += Cfg::WAVES * RPS) {
       const int rg = p * RPP + rl;  // row within the tile
       const int t = m0 + rg;
       uint32_t m = masks[rg * MW + wsub];
@@ -259,45 +260,49 @@ __global__ __launch_bounds__(DMA_THREADS) void k_gate_twell(
         }
       }
     }
-    if (p + 1 < GEMM_BM / RPP) __syncthreads();
+    if (p + 1 < BM / RPP) __syncthreads();
   }
 }
 
-template <Dt D, int BN, int RPP, bool DUMP>
+template <Dt D, int BN, int RPP, bool DUMP, class Cfg>
 static hipError_t launch_gate(const GateArgs &a, hipStream_t s) {
   using T = typename DtT<D>::T;
-  auto kern = k_gate_twell<D, BN, RPP, DUMP>;
-  const int lds = std::max(gemm_dma_lds_bytes(BN), EpilogueLds<D, BN, RPP>::bytes(a.cap));
+  auto kern = k_gate_twell<D, BN, RPP, DUMP, Cfg>;
+  const int lds = std::max(gemm_dma_lds_bytes<Cfg>(BN), EpilogueLds<D, BN, RPP, Cfg::BM>::bytes(a.cap));
   hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
-  const int mt = (a.M + GEMM_BM - 1) / GEMM_BM, ntl = a.N / BN;
-  hipLaunchKernelGGL(kern, dim3(mt * ntl), dim3(DMA_THREADS), lds, s, (const T *)a.x,
+  const int mt = (a.M + Cfg::BM - 1) / Cfg::BM, ntl = a.N / BN;
+  hipLaunchKernelGGL(kern, dim3(mt * ntl), dim3(Cfg::THREADS), lds, s, (const T *)a.x,
                      (const T *)a.wg, a.beta, a.M, a.K, a.N, a.cap, a.cnt, (T *)a.val, a.idx,
                      (T *)a.pre_out);
   return hipGetLastError();
 }
 
-// The largest rows-per-pass whose epilogue layout fits the LDS for this cap.
-template <Dt D, int BN, bool DUMP>
+// The largest rows-per-pass whose epilogue layout fits the workgroup's share
+// of the LDS for this cap (all of it for DmaBig, half for DmaHalf, which runs
+// two workgroups per CU).
+template <Dt D, int BN, bool DUMP, class Cfg>
 static hipError_t launch_gate_rpp(const GateArgs &a, hipStream_t s) {
-  if (EpilogueLds<D, BN, 256>::bytes(a.cap) <= LDS_MAX) return launch_gate<D, BN, 256, DUMP>(a, s);
-  if (EpilogueLds<D, BN, 128>::bytes(a.cap) <= LDS_MAX) return launch_gate<D, BN, 128, DUMP>(a, s);
-  return launch_gate<D, BN, 64, DUMP>(a, s);
+  constexpr int BM = Cfg::BM;
+  constexpr int budget = BM == 256 ? LDS_MAX : LDS_MAX / 2;
+  if (EpilogueLds<D, BN, BM, BM>::bytes(a.cap) <= budget) return launch_gate<D, BN, BM, DUMP, Cfg>(a, s);
+  if (EpilogueLds<D, BN, 128, BM>::bytes(a.cap) <= budget) return launch_gate<D, BN, 128, DUMP, Cfg>(a, s);
+  return launch_gate<D, BN, 64, DUMP, Cfg>(a, s);
 }
 
-template <Dt D, int BN>
+template <Dt D, int BN, class Cfg>
 static hipError_t launch_gate(const GateArgs &a, hipStream_t s) {
-  return a.pre_out != nullptr ? launch_gate_rpp<D, BN, true>(a, s) : launch_gate_rpp<D, BN, false>(a, s);
+  return a.pre_out != nullptr ? launch_gate_rpp<D, BN, true, Cfg>(a, s) : launch_gate_rpp<D, BN, false, Cfg>(a, s);
 }
 
 hipError_t gate_twell(const GateArgs &a, hipStream_t s) {
   if (a.M <= 0) return hipSuccess;
   if (a.dtype == Dt::BF16) {
-    if (a.tile == 256) return launch_gate<Dt::BF16, 256>(a, s);
-    if (a.tile == 128) return launch_gate<Dt::BF16, 128>(a, s);
+    if (a.tile == 256) return launch_gate<Dt::BF16, 256, DmaBig>(a, s);
+    if (a.tile == 128) return launch_gate<Dt::BF16, 128, DmaBig>(a, s);
   } else {
-    if (a.tile == 256) return launch_gate<Dt::F32, 256>(a, s);
-    if (a.tile == 128) return launch_gate<Dt::F32, 128>(a, s);
+    if (a.tile == 256) return launch_gate<Dt::F32, 256, DmaBig>(a, s);
+    if (a.tile == 128) return launch_gate<Dt::F32, 128, DmaBig>(a, s);
   }
   return hipErrorInvalidValue;
 }

@@ -260,21 +260,42 @@ __device__ __forceinline__ void gemm_mainloop(f32x16_t (&acc)[2][BN / 32], LA &l
 // (16 consecutive rows, one chunk) hit 16 distinct 4-bank groups of the 64-bank
 // LDS.
 
-constexpr int DMA_STAGES = 4;
 constexpr int SLAB = 64;  // K bytes per stage
-constexpr int DMA_WAVES = 8;
-constexpr int DMA_THREADS = 64 * DMA_WAVES;
+
+// Shape of a DMA mainloop: BM rows per workgroup tile, WAVES waves, a ring of
+// STAGES LDS stages.  Every wave owns 64 columns and BM / (WAVES / (BN / 64))
+// rows of the tile.  DmaBig is the one in use: one workgroup per CU, 256 x BN
+// tiles, 8 waves, 4 stages.  DmaHalf (two workgroups per CU, 128 x BN tiles, 4
+// waves, 3 stages, so that one workgroup's epilogue overlaps the other's
+// matrix-core work) gave bit-identical TwELL output but a slower gate matmul
+// (265 against 240 us at the 1.5B-class shape): its smaller tiles move 1.5x
+// the operand bytes per flop.
+template <int BM_, int WAVES_, int STAGES_>
+struct DmaCfg {
+  static constexpr int BM = BM_, WAVES = WAVES_, THREADS = 64 * WAVES_, STAGES = STAGES_;
+  // waves per SIMD the kernel must leave room for (register budget 512 / this)
+  static constexpr int WAVES_PER_SIMD = 2;
+  static_assert(STAGES == 3 || STAGES == 4, "the peeled tail covers 3- and 4-stage rings");
+};
+using DmaBig = DmaCfg<256, 8, 4>;
+using DmaHalf = DmaCfg<128, 4, 3>;
+constexpr int DMA_STAGES = DmaBig::STAGES;
+constexpr int DMA_WAVES = DmaBig::WAVES;
+constexpr int DMA_THREADS = DmaBig::THREADS;
 
 // LDS: the ring, then one fp32 value per tile row (the gate bias, loaded with
 // the first stages so that no separate global round trip delays the tile).
-__host__ __device__ constexpr int gemm_dma_ring_bytes(int bn) { return DMA_STAGES * (GEMM_BM + bn) * SLAB; }
-__host__ __device__ constexpr int gemm_dma_lds_bytes(int bn) { return gemm_dma_ring_bytes(bn) + GEMM_BM * 4; }
+template <class Cfg = DmaBig>
+__host__ __device__ constexpr int gemm_dma_ring_bytes(int bn) { return Cfg::STAGES * (Cfg::BM + bn) * SLAB; }
+template <class Cfg = DmaBig>
+__host__ __device__ constexpr int gemm_dma_lds_bytes(int bn) { return gemm_dma_ring_bytes<Cfg>(bn) + Cfg::BM * 4; }
 
-template <int BN>
+template <int BN, class Cfg = DmaBig>
 struct WaveTile {
-  static constexpr int WPR = BN / 64;                        // waves across the N tile
-  static constexpr int NWN = 2;                              // 32-column blocks per wave
-  static constexpr int NWM = GEMM_BM / 32 / (DMA_WAVES / WPR);  // 32-row blocks per wave
+  static constexpr int WPR = BN / 64;                                  // waves across the N tile
+  static constexpr int NWN = 2;                                        // 32-column blocks per wave
+  static constexpr int NWM = Cfg::BM / 32 / (Cfg::WAVES / WPR);        // 32-row blocks per wave
+  static_assert(NWM >= 1 && Cfg::WAVES % WPR == 0, "whole waves across the tile");
   __device__ __forceinline__ static int row0(int wave) { return (wave / WPR) * 32 * NWM; }
   __device__ __forceinline__ static int col0(int wave) { return (wave % WPR) * 64; }
 };
@@ -319,10 +340,11 @@ __device__ __forceinline__ void wait_stages(int n) {
 }
 
 // Rows of one operand tile loaded by DMA.  NR rows x 4 chunks = NR*4 lane
-// slots = NR/16 wave instructions, spread over the 8 waves.
-template <int NR>
+// slots = NR/16 wave instructions, spread over the WAVES waves.
+template <int NR, int WAVES = DMA_WAVES>
 struct DmaRows {
-  static constexpr int PER_WAVE = NR / 16 / DMA_WAVES;  // instructions per wave per stage
+  static constexpr int PER_WAVE = NR / 16 / WAVES;  // instructions per wave per stage
+  static_assert(PER_WAVE >= 1 && NR % (16 * WAVES) == 0, "whole 1 KB blocks per wave");
   const char *ptr[PER_WAVE];
   uint32_t lds_off[PER_WAVE];  // byte offset of the wave's 1 KB block in the stage
 
@@ -349,11 +371,11 @@ struct Frag {
   u32x4_t a[NWM], b[NWN];
 };
 
-template <int NWM, int NWN>
+template <int BM, int NWM, int NWN>
 __device__ __forceinline__ void read_frag(Frag<NWM, NWN> &f, const char *stage, int row0, int col0, int half,
                                           int lane) {
   const char *As = stage;
-  const char *Bs = stage + GEMM_BM * SLAB;
+  const char *Bs = stage + BM * SLAB;
   const int r = lane & 31, h = lane >> 5;
 #pragma unroll
   for (int i = 0; i < NWM; ++i)
@@ -375,41 +397,46 @@ __device__ __forceinline__ void mfma_frag(f32x16_t (&acc)[NWM][NWN], const Frag<
 // rowv(r) points at one fp32 value per tile row r (or is null for every r);
 // those values are copied to LDS with the first stages, and init(acc, vals)
 // sets the accumulators before the first MFMA, vals being the LDS copy
-// (GEMM_BM floats) or null.
-template <Dt D, int BN, class RA, class RB, class RV, class INIT>
-__device__ __forceinline__ void gemm_mainloop_dma(f32x16_t (&acc)[WaveTile<BN>::NWM][WaveTile<BN>::NWN], RA rowA,
-                                                  RB rowB, RV rowv, INIT init, int nk, char *smem) {
-  using WT = WaveTile<BN>;
+// (Cfg::BM floats) or null.
+// The accumulators of one wave tile.
+template <int BN, class Cfg>
+using AccTile = f32x16_t[WaveTile<BN, Cfg>::NWM][WaveTile<BN, Cfg>::NWN];
+
+template <Dt D, int BN, class Cfg, class RA, class RB, class RV, class INIT>
+__device__ __forceinline__ void gemm_mainloop_dma(AccTile<BN, Cfg> &acc, RA rowA, RB rowB, RV rowv, INIT init,
+                                                  int nk, char *smem) {
+  using WT = WaveTile<BN, Cfg>;
+  constexpr int BM = Cfg::BM, WAVES = Cfg::WAVES, STAGES = Cfg::STAGES;
   constexpr int NWM = WT::NWM, NWN = WT::NWN;
-  constexpr int STAGE = (GEMM_BM + BN) * SLAB;
-  constexpr int OPS = DmaRows<GEMM_BM>::PER_WAVE + DmaRows<BN>::PER_WAVE;  // DMA ops per stage per lane
+  constexpr int STAGE = (BM + BN) * SLAB;
+  constexpr int OPS = DmaRows<BM, WAVES>::PER_WAVE + DmaRows<BN, WAVES>::PER_WAVE;  // DMA ops per stage per lane
   const int lane = threadIdx.x & 63;
   const int wave_u = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row0 = WT::row0(wave_u), col0 = WT::col0(wave_u);
   const uint32_t base = lds_address(smem);
   const bool has_rowv = rowv(0) != nullptr;
-  DmaRows<GEMM_BM> da;
-  DmaRows<BN> db;
+  DmaRows<BM, WAVES> da;
+  DmaRows<BN, WAVES> db;
   da.init(wave_u, lane, 0, rowA);
-  db.init(wave_u, lane, GEMM_BM * SLAB, rowB);
-  // waves 0-3 copy 64 row values each; issued before the stages, so the
+  db.init(wave_u, lane, BM * SLAB, rowB);
+  // BM / 64 waves copy 64 row values each; issued before the stages, so the
   // stage waits below cover them (loads complete in order)
-  if (has_rowv && wave_u < GEMM_BM / 64)
-    dma4(rowv(64 * wave_u + lane), base + gemm_dma_ring_bytes(BN) + 256 * wave_u);
+  if (has_rowv && wave_u < BM / 64)
+    dma4(rowv(64 * wave_u + lane), base + gemm_dma_ring_bytes<Cfg>(BN) + 256 * wave_u);
 #pragma unroll
-  for (int s = 0; s < DMA_STAGES; ++s) {
+  for (int s = 0; s < STAGES; ++s) {
     if (s < nk) {
       da.issue(s, base + s * STAGE);
       db.issue(s, base + s * STAGE);
     }
   }
-  wait_stages<OPS>(min(nk - 1, DMA_STAGES - 1));
+  wait_stages<OPS>(min(nk - 1, STAGES - 1));
   __syncthreads();
-  init(acc, has_rowv ? reinterpret_cast<const float *>(smem + gemm_dma_ring_bytes(BN)) : nullptr);
+  init(acc, has_rowv ? reinterpret_cast<const float *>(smem + gemm_dma_ring_bytes<Cfg>(BN)) : nullptr);
   Frag<NWM, NWN> f0, f1;
-  read_frag(f0, smem, row0, col0, 0, lane);
+  read_frag<BM>(f0, smem, row0, col0, 0, lane);
   // One slab kt < nk - 1 with WAIT stages (of OPS loads) left in flight at its
-  // barrier, issuing the loads of slab kt + DMA_STAGES if ISSUE.  The loop is
+  // barrier, issuing the loads of slab kt + STAGES if ISSUE.  The loop is
   // peeled by these constants (no runtime selection of the wait) and the last
   // slab has a block of its own: a path that joins the steady state with the
   // last slab's makes the compiler wait for the next slab's first-half reads
@@ -417,8 +444,8 @@ __device__ __forceinline__ void gemm_mainloop_dma(f32x16_t (&acc)[WaveTile<BN>::
   auto slab = [&](auto wait_c, auto issue_c, int kt) {
     constexpr int WAIT = decltype(wait_c)::value;
     constexpr bool ISSUE = decltype(issue_c)::value;
-    const int slot = kt % DMA_STAGES;
-    read_frag(f1, smem + slot * STAGE, row0, col0, 1, lane);
+    const int slot = kt % STAGES;
+    read_frag<BM>(f1, smem + slot * STAGE, row0, col0, 1, lane);
     mfma_frag<D>(acc, f0);
     // Scheduling hint: alternate the MFMAs of the first half with the LDS
     // reads of the second, one each, instead of issuing the reads in a block.
@@ -433,10 +460,10 @@ __device__ __forceinline__ void gemm_mainloop_dma(f32x16_t (&acc)[WaveTile<BN>::
     __syncthreads();
     if constexpr (ISSUE) {
       const uint32_t sb = base + slot * STAGE;
-      da.issue(kt + DMA_STAGES, sb);
-      db.issue(kt + DMA_STAGES, sb);
+      da.issue(kt + STAGES, sb);
+      db.issue(kt + STAGES, sb);
     }
-    read_frag(f0, smem + ((kt + 1) % DMA_STAGES) * STAGE, row0, col0, 0, lane);
+    read_frag<BM>(f0, smem + ((kt + 1) % STAGES) * STAGE, row0, col0, 0, lane);
     mfma_frag<D>(acc, f1);
     // the same alternation for the next slab's first-half reads
 #pragma unroll
@@ -448,18 +475,20 @@ __device__ __forceinline__ void gemm_mainloop_dma(f32x16_t (&acc)[WaveTile<BN>::
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
+  using IW = std::integral_constant<int, STAGES - 2>;
   using BT = std::integral_constant<bool, true>;
   using BF = std::integral_constant<bool, false>;
-  static_assert(DMA_STAGES == 4, "the peeled tail below assumes a 4-stage ring");
-  // slab kt waits for slab kt + 1: min(nk - 2 - kt, 2) stages stay in flight;
-  // slab kt + 4 is loaded while kt + 4 < nk
+  // slab kt waits for slab kt + 1: min(nk - 2 - kt, STAGES - 2) stages stay in
+  // flight; slab kt + STAGES is loaded while kt + STAGES < nk
   int kt = 0;
-  for (; kt + DMA_STAGES < nk; ++kt) slab(I2(), BT(), kt);
-  if (kt == nk - 4) slab(I2(), BF(), kt++);
+  for (; kt + STAGES < nk; ++kt) slab(IW(), BT(), kt);
+  if constexpr (STAGES == 4) {
+    if (kt == nk - 4) slab(I2(), BF(), kt++);
+  }
   if (kt == nk - 3) slab(I1(), BF(), kt++);
   if (kt == nk - 2) slab(I0(), BF(), kt++);
   // the last slab: both halves, no loads left
-  read_frag(f1, smem + (kt % DMA_STAGES) * STAGE, row0, col0, 1, lane);
+  read_frag<BM>(f1, smem + (kt % STAGES) * STAGE, row0, col0, 1, lane);
   mfma_frag<D>(acc, f0);
   mfma_frag<D>(acc, f1);
   // no DMA is left in flight; make every wave's last LDS reads complete before
