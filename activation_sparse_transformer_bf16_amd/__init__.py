@@ -71,6 +71,8 @@ def _load():
         "twell_overflow_scan": (I, [M, P]),
         "twell_sparse_ffn": (I, [M, P, P, P, P, P, P, I, P, Z, P]),
         "twell_sparse_ffn_fused": (I, [M, P, P, P, P, P, P, I, P, Z, P]),
+        "twell_sparse_ffn_grouped": (I, [M, P, P, P, P, P, P, I, P, Z, P]),
+        "twell_sparse_ffn_grouped_workspace_size": (Z, [I, I, I, I, I, I]),
         "dense_ffn_workspace_size": (Z, [I, I, I, I]),
         "dense_ffn_forward": (I, [P, P, P, P, P, P, I, I, I, I, P, Z, P]),
         "twell_to_hybrid": (I, [M, ctypes.POINTER(TwellHybridC), P]),
@@ -109,7 +111,8 @@ EXPORTS = ("twell_abi_version", "twell_status_str", "twell_last_error", "twell_p
            "dense_ffn_workspace_size", "dense_ffn_forward", "twell_to_hybrid",
            "twell_l1_workspace_size", "twell_l1_norm", "twell_l1_grad",
            "twell_ffn_backward_workspace_size", "twell_ffn_backward", "twell_sparse_ffn_fused",
-           "twell_stream_probe", "twell_mfma_probe", "twell_ffn_forward_noalloc")
+           "twell_stream_probe", "twell_mfma_probe", "twell_ffn_forward_noalloc", "twell_sparse_ffn_grouped",
+           "twell_sparse_ffn_grouped_workspace_size")
 
 # Size of the static device scratch behind twell_ffn_forward_noalloc
 # (TWELL_NOALLOC_SCRATCH_BYTES in include/twell.h).
@@ -543,6 +546,28 @@ def twell_sparse_ffn_fused(packed: TwellMatrix, x, w_gate, w_up, w_down, gate_bi
     m = packed.c_struct()
     _check(_lib.twell_sparse_ffn_fused(ctypes.byref(m), _ptr(x), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
                                        _ptr(gate_bias), _ptr(y), d, _ptr(ws), ws.numel(), _stream(device)))
+    return y
+
+
+def twell_sparse_ffn_grouped_workspace_size(T: int, d: int, F: int, tile: int, cap: int, dtype) -> int:
+    return int(_lib.twell_sparse_ffn_grouped_workspace_size(T, d, F, tile, cap, _dtype_code(dtype)))
+
+
+def twell_sparse_ffn_grouped(packed: TwellMatrix, x, w_gate, w_up, w_down, gate_bias=None, y=None,
+                             workspace=None):
+    """twell_sparse_ffn with the fused up+down kernel in hidden-group-major order
+    (fp32 partial output rows per group, added in group order); returns y."""
+    torch = _torch()
+    device, T, d, F = _ffn_checks(x, w_gate, w_up, w_down, gate_bias)
+    _packed_for(packed, device, T, F, x.dtype)
+    if y is None:
+        y = torch.empty((T, d), dtype=x.dtype, device=device)
+    _need(y, "y", device, x.dtype, (T, d))
+    ws = _workspace(twell_sparse_ffn_grouped_workspace_size(T, d, F, packed.tile, packed.cap, x.dtype), device,
+                    workspace)
+    m = packed.c_struct()
+    _check(_lib.twell_sparse_ffn_grouped(ctypes.byref(m), _ptr(x), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+                                         _ptr(gate_bias), _ptr(y), d, _ptr(ws), ws.numel(), _stream(device)))
     return y
 
 

@@ -218,16 +218,30 @@ twell_status run_sparse(const twell_matrix *m, const void *x, const void *wg, co
   return run_fallback(m, x, wg, wu, wd, beta, y, d, L, base, row_flag, s);
 }
 
+// The hidden-group-major fused prototype: the forward's workspace followed by
+// the groups' fp32 partial output rows [n_groups][T][d].
+size_t grouped_partial_offset(const FfnWs &L) { return align_up(L.total, ALIGN_WS); }
+size_t grouped_ws_bytes(const FfnWs &L, int T, int d, int F, int tile, twell_dtype dt) {
+  const FusedGroups fg = fused_groups(d, F, tile, to_dt(dt));
+  return grouped_partial_offset(L) + (size_t)fg.n_groups * T * d * 4;
+}
+
 // The same sequence with the fused up+down kernel in place of the two gather
 // kernels (the compact lists are not used).
 twell_status run_sparse_fused(const twell_matrix *m, const void *x, const void *wg, const void *wu, const void *wd,
-                              const float *beta, void *y, int d, void *ws, const FfnWs &L, hipStream_t s) {
+                              const float *beta, void *y, int d, void *ws, const FfnWs &L, hipStream_t s,
+                              bool grouped = false) {
   const int T = m->rows, F = m->cols;
   char *base = static_cast<char *>(ws);
   uint8_t *row_flag = reinterpret_cast<uint8_t *>(base + L.flag);
   const Dt D = to_dt(m->dtype);
   SparseArgs sa{D, T, d, F, m->tile, m->cap, m->cnt, m->val, m->idx, row_flag, x, wu, wd, nullptr, nullptr, 0, y};
-  TW_TRY(sparse_fused(sa, s), "fused sparse up/down projection");
+  if (grouped) {
+    TW_TRY(sparse_fused_grouped(sa, reinterpret_cast<float *>(base + grouped_partial_offset(L)), s),
+           "grouped fused sparse up/down projection");
+  } else {
+    TW_TRY(sparse_fused(sa, s), "fused sparse up/down projection");
+  }
   return run_fallback(m, x, wg, wu, wd, beta, y, d, L, base, row_flag, s);
 }
 
@@ -497,6 +511,34 @@ twell_status twell_sparse_ffn_fused(const twell_matrix *packed, const void *x, c
     return fail(TWELL_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : 0);
   if (!aligned(workspace, ALIGN_WS)) return fail(TWELL_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
   return run_sparse_fused(packed, x, w_gate, w_up, w_down, gate_bias, y, d, workspace, L, s);
+}
+
+size_t twell_sparse_ffn_grouped_workspace_size(int T, int d, int F, int tile, int cap, twell_dtype dtype) {
+  if (T < 0 || check_format(tile, cap, F, (int)dtype) != TWELL_OK || check_d(d, (int)dtype) != TWELL_OK ||
+      check_weight_bytes(F, d, (int)dtype) != TWELL_OK)
+    return 0;
+  return grouped_ws_bytes(ffn_ws_layout(T, d, F, tile, cap, dtype), T, d, F, tile, dtype);
+}
+
+twell_status twell_sparse_ffn_grouped(const twell_matrix *packed, const void *x, const void *w_gate,
+                                      const void *w_up, const void *w_down, const float *gate_bias, void *y, int d,
+                                      void *workspace, size_t ws_bytes, void *stream) {
+  g_err[0] = 0;
+  twell_status st = check_matrix(packed, true);
+  if (st != TWELL_OK) return st;
+  if ((st = check_d(d, (int)packed->dtype)) != TWELL_OK) return st;
+  const int q = packed->dtype == TWELL_BF16 ? 512 : 256;
+  if (d > 8 * q) return fail(TWELL_ERR_UNSUPPORTED, "grouped fused kernel: d %d not built (<= %d)", d, 8 * q);
+  if ((st = check_weight_bytes(packed->cols, d, (int)packed->dtype)) != TWELL_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (packed->rows == 0) return hip_check(zero_int(packed->n_ovf, s), "zero n_ovf");
+  if ((st = check_ffn_ptrs(x, w_gate, w_up, w_down, gate_bias, y)) != TWELL_OK) return st;
+  const FfnWs L = ffn_ws_layout(packed->rows, d, packed->cols, packed->tile, packed->cap, packed->dtype);
+  const size_t need = grouped_ws_bytes(L, packed->rows, d, packed->cols, packed->tile, packed->dtype);
+  if (workspace == nullptr || ws_bytes < need)
+    return fail(TWELL_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : 0);
+  if (!aligned(workspace, ALIGN_WS)) return fail(TWELL_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+  return run_sparse_fused(packed, x, w_gate, w_up, w_down, gate_bias, y, d, workspace, L, s, true);
 }
 
 twell_status twell_ffn_forward(const void *x, const void *w_gate, const void *w_up, const void *w_down,

@@ -19,6 +19,8 @@
 #include "gather.hpp"
 #include "launch.hpp"
 
+#include <algorithm>
+
 namespace twell {
 
 constexpr int FUSED_LIST = 256;  // entries per LDS list pass (tiles per pass * cap)
@@ -30,17 +32,31 @@ __device__ __forceinline__ int reduce_lane(int u) {
   else return u << 5;                                             // entries 0, 1 -> rows 0, 2; U = 1: lane 0
 }
 
-template <Dt D, int NC, int U>
+// GROUPED = false: one wave per token over all of the token's entries, y
+// written.  GROUPED = true: hidden-group-major.  Units are cut into groups of
+// tpg TwELL tiles (W_u and W_d rows of a group about one XCD's 4 MB L2, group
+// g on XCD g % 8 as in the up projection); the wave of (group g, token t)
+// handles t's entries in g only and writes its fp32 partial output row to
+// partial[g][t][:]; k_group_reduce adds the groups' partials in group order.
+template <Dt D, int NC, int U, bool GROUPED>
 __global__ __launch_bounds__(SP_THREADS) void k_sparse_fused(
     const typename DtT<D>::T *__restrict__ x, const typename DtT<D>::T *__restrict__ wu,
     const typename DtT<D>::T *__restrict__ wd, const uint16_t *__restrict__ cnt,
     const typename DtT<D>::T *__restrict__ val, const uint8_t *__restrict__ idx, uint8_t *__restrict__ row_flag,
-    typename DtT<D>::T *__restrict__ y, int T, int d, int nt, int tile, int cap) {
+    typename DtT<D>::T *__restrict__ y, int T, int d, int nt, int tile, int cap, int tpg, int n_groups,
+    int tok_per_wg, int n_tb, float *__restrict__ partial) {
   using TT = typename DtT<D>::T;
   constexpr int EPC = 16 / sizeof(TT);
   __shared__ u32x2_t lists[SP_WAVES][FUSED_LIST];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t = blockIdx.x * SP_WAVES + wave;
+  int g = 0, tb = 0;
+  if constexpr (GROUPED) {
+    group_coords(blockIdx.x, n_groups, n_tb, g, tb);
+    if (g >= n_groups) return;
+  }
+  const int k_begin = GROUPED ? g * tpg : 0, k_end = GROUPED ? min(nt, (g + 1) * tpg) : nt;
+  for (int it = wave; it < (GROUPED ? tok_per_wg : SP_WAVES); it += SP_WAVES) {
+  const int t = GROUPED ? tb * tok_per_wg + it : blockIdx.x * SP_WAVES + wave;
   if (t >= T) return;
   const uint16_t *crow = cnt + (size_t)t * nt;
   bool over = false;
@@ -49,8 +65,8 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_fused(
     over |= k < nt && (int)crow[k] > cap;
   }
   const bool ovf = ballot(over) != 0;
-  if (lane == 0) row_flag[t] = ovf ? 1 : 0;
-  if (ovf) return;
+  if (lane == 0 && g == 0) row_flag[t] = ovf ? 1 : 0;
+  if (ovf) continue;
 
   const TT *xt = x + (size_t)t * d;
   u32x4_t xr[NC];
@@ -68,8 +84,8 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_fused(
   const uint32_t row_bytes = (uint32_t)d * sizeof(TT);
   u32x2_t *L = lists[wave];
   const int tpp = min(64, FUSED_LIST / cap);  // tiles per pass: one lane per tile
-  for (int k0 = 0; k0 < nt; k0 += tpp) {
-    const int kn = min(tpp, nt - k0);
+  for (int k0 = k_begin; k0 < k_end; k0 += tpp) {
+    const int kn = min(tpp, k_end - k0);
     // The pass's entries into the LDS list, one lane per slot (as in the
     // two-kernel up projection): tile k0 + q holds n(q) entries.
     const int n = lane < kn ? min((int)crow[k0 + lane], cap) : 0;
@@ -143,19 +159,68 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_fused(
     }
     wave_sync_lds();
   }
-  TT *yt = y + (size_t)t * d;
+  if constexpr (GROUPED) {
+    float *pt = partial + ((size_t)g * T + t) * d;
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int q = 0; q < EPC; q += 4)
+        *reinterpret_cast<f32x4_t *>(pt + (c * 64 + lane) * EPC + q) =
+            f32x4_t{acc[c][q], acc[c][q + 1], acc[c][q + 2], acc[c][q + 3]};
+  } else {
+    TT *yt = y + (size_t)t * d;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      u32x4_t out;
+      if constexpr (D == Dt::BF16) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          out[q] = (uint32_t)bf16_rne(acc[c][2 * q]) | ((uint32_t)bf16_rne(acc[c][2 * q + 1]) << 16);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) out[q] = __float_as_uint(acc[c][q]);
+      }
+      *reinterpret_cast<u32x4_t *>(yt + (c * 64 + lane) * EPC) = out;
+    }
+  }
+  }
+}
+
+// y of the non-overflow rows from the groups' partial rows, added in group
+// order (deterministic), one rounding.  One thread per 16 bytes of y.
+template <Dt D>
+__global__ __launch_bounds__(256) void k_group_reduce(const float *__restrict__ partial, const uint8_t *__restrict__ row_flag,
+                                                      typename DtT<D>::T *__restrict__ y, int T, int d, int n_groups) {
+  using TT = typename DtT<D>::T;
+  constexpr int EPC = 16 / sizeof(TT);
+  const size_t chunks = (size_t)T * d / EPC;
+  for (size_t q = (size_t)blockIdx.x * 256 + threadIdx.x; q < chunks; q += (size_t)gridDim.x * 256) {
+    const size_t e0 = q * EPC;
+    const int t = (int)(e0 / d);
+    if (row_flag[t] != 0) continue;  // the dense fallback writes it
+    float s[EPC];
+#pragma unroll
+    for (int k = 0; k < EPC; ++k) s[k] = 0.f;
+    for (int g = 0; g < n_groups; ++g) {
+      const float *p = partial + (size_t)g * T * d + e0;
+#pragma unroll
+      for (int k = 0; k < EPC; k += 4) {
+        const f32x4_t v = *reinterpret_cast<const f32x4_t *>(p + k);
+        s[k] += v[0];
+        s[k + 1] += v[1];
+        s[k + 2] += v[2];
+        s[k + 3] += v[3];
+      }
+    }
     u32x4_t out;
     if constexpr (D == Dt::BF16) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        out[q] = (uint32_t)bf16_rne(acc[c][2 * q]) | ((uint32_t)bf16_rne(acc[c][2 * q + 1]) << 16);
+      for (int k = 0; k < 4; ++k) out[k] = (uint32_t)bf16_rne(s[2 * k]) | ((uint32_t)bf16_rne(s[2 * k + 1]) << 16);
     } else {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) out[q] = __float_as_uint(acc[c][q]);
+      for (int k = 0; k < 4; ++k) out[k] = __float_as_uint(s[k]);
     }
-    *reinterpret_cast<u32x4_t *>(yt + (c * 64 + lane) * EPC) = out;
+    *reinterpret_cast<u32x4_t *>(y + e0) = out;
   }
 }
 
@@ -164,20 +229,40 @@ static hipError_t launch_fused(const SparseArgs &a, hipStream_t s) {
   using TT = typename DtT<D>::T;
   constexpr int U = NC <= 4 ? 2 : 1;
   const int blocks = (a.T + SP_WAVES - 1) / SP_WAVES;
-  hipLaunchKernelGGL((k_sparse_fused<D, NC, U>), dim3(blocks), dim3(SP_THREADS), 0, s, (const TT *)a.x,
+  hipLaunchKernelGGL((k_sparse_fused<D, NC, U, false>), dim3(blocks), dim3(SP_THREADS), 0, s, (const TT *)a.x,
                      (const TT *)a.wu, (const TT *)a.wd, a.cnt, (const TT *)a.val, a.idx, a.row_flag, (TT *)a.y, a.T,
-                     a.d, a.F / a.tile, a.tile, a.cap);
+                     a.d, a.F / a.tile, a.tile, a.cap, 0, 1, SP_WAVES, blocks, nullptr);
+  return hipGetLastError();
+}
+
+template <Dt D, int NC>
+static hipError_t launch_grouped(const SparseArgs &a, float *partial, hipStream_t s) {
+  using TT = typename DtT<D>::T;
+  constexpr int U = NC <= 4 ? 2 : 1;
+  const FusedGroups fg = fused_groups(a.d, a.F, a.tile, a.dtype);
+  const int tok = 16;
+  const int n_tb = (a.T + tok - 1) / tok;
+  hipLaunchKernelGGL((k_sparse_fused<D, NC, U, true>), dim3(padded_groups(fg.n_groups) * n_tb), dim3(SP_THREADS), 0,
+                     s, (const TT *)a.x, (const TT *)a.wu, (const TT *)a.wd, a.cnt, (const TT *)a.val, a.idx,
+                     a.row_flag, (TT *)a.y, a.T, a.d, a.F / a.tile, a.tile, a.cap, fg.tpg, fg.n_groups, tok, n_tb,
+                     partial);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t chunks = (size_t)a.T * a.d / (16 / sizeof(TT));
+  const int blocks = (int)std::min<size_t>((chunks + 255) / 256, 4096);
+  hipLaunchKernelGGL(k_group_reduce<D>, dim3(blocks), dim3(256), 0, s, (const float *)partial, a.row_flag, (TT *)a.y,
+                     a.T, a.d, fg.n_groups);
   return hipGetLastError();
 }
 
 template <Dt D>
-static hipError_t fused_dispatch(const SparseArgs &a, hipStream_t s) {
+static hipError_t fused_dispatch(const SparseArgs &a, float *partial, hipStream_t s) {
   using TT = typename DtT<D>::T;
   const int nc = a.d / (64 * (16 / (int)sizeof(TT)));
   switch (nc) {
 #define TWELL_FUSED_CASE(N) \
   case N:                   \
-    return launch_fused<D, N>(a, s);
+    return partial ? launch_grouped<D, N>(a, partial, s) : launch_fused<D, N>(a, s);
     TWELL_FUSED_CASE(1) TWELL_FUSED_CASE(2) TWELL_FUSED_CASE(3) TWELL_FUSED_CASE(4)
     TWELL_FUSED_CASE(5) TWELL_FUSED_CASE(6) TWELL_FUSED_CASE(7) TWELL_FUSED_CASE(8)
 #undef TWELL_FUSED_CASE
@@ -188,7 +273,12 @@ static hipError_t fused_dispatch(const SparseArgs &a, hipStream_t s) {
 
 hipError_t sparse_fused(const SparseArgs &a, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
-  return a.dtype == Dt::BF16 ? fused_dispatch<Dt::BF16>(a, s) : fused_dispatch<Dt::F32>(a, s);
+  return a.dtype == Dt::BF16 ? fused_dispatch<Dt::BF16>(a, nullptr, s) : fused_dispatch<Dt::F32>(a, nullptr, s);
+}
+
+hipError_t sparse_fused_grouped(const SparseArgs &a, float *partial, hipStream_t s) {
+  if (a.T <= 0) return hipSuccess;
+  return a.dtype == Dt::BF16 ? fused_dispatch<Dt::BF16>(a, partial, s) : fused_dispatch<Dt::F32>(a, partial, s);
 }
 
 }  // namespace twell

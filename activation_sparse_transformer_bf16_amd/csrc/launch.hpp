@@ -96,6 +96,23 @@ hipError_t sparse_down(const SparseArgs &a, hipStream_t s);
 // rows of non-overflow tokens; list / list_n / stride are not used.
 hipError_t sparse_fused(const SparseArgs &a, hipStream_t s);
 
+// The hidden-group-major variant: groups of tpg TwELL tiles whose W_u and W_d
+// rows together are about 4 MB (one XCD's L2), at most 16 groups; partial
+// output rows [n_groups][T][d] fp32, added in group order by a second kernel.
+struct FusedGroups {
+  int tpg, n_groups;
+};
+inline FusedGroups fused_groups(int d, int F, int tile, Dt dt) {
+  const int s = dt == Dt::BF16 ? 2 : 4;
+  const int nt = F / tile;
+  const size_t tile_bytes = (size_t)2 * tile * d * s;  // W_u and W_d rows of one tile
+  int tpg = (int)std::max<size_t>(1, ((size_t)4 << 20) / tile_bytes);
+  tpg = std::max(tpg, (nt + 15) / 16);
+  tpg = std::min(tpg, nt);
+  return FusedGroups{tpg, (nt + tpg - 1) / tpg};
+}
+hipError_t sparse_fused_grouped(const SparseArgs &a, float *partial, hipStream_t s);
+
 // Dense ReGLU FFN on the matrix cores over a (possibly gathered) set of rows:
 // logical row r < n_rows reads x[rows ? rows[r] : r] and writes y at the same
 // physical row.  With n_rows_dev (device int) non-null the row count is

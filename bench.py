@@ -294,6 +294,20 @@ def measure(w, steps, warmup, want_torch=True, want_cold=True):
     _, ms_fused_rest = split_time(gate, fused_rest, steps, warmup)
     ms_fused, _ = event_time(lambda: (gate(), fused_rest()), steps, warmup)
     log(f"[bench] fused up+down: {ms_fused_rest * 1e3:.1f} us in sequence, forward {ms_fused * 1e3:.1f} us")
+    # The hidden-group-major fused prototype (fp32 partial output rows per
+    # group, added in group order by a second kernel).
+    grouped = None
+    if w.d <= (4096 if w.dtype == "bf16" else 2048):
+        ws_g = torch.empty((tw.twell_sparse_ffn_grouped_workspace_size(T, d, F, w.tile, w.cap, x.dtype),),
+                           dtype=torch.uint8, device=dev)
+        grouped_rest = lambda: tw.twell_sparse_ffn_grouped(packed, x, wg, wu, wd, b, y=y, workspace=ws_g)
+        _, ms_grouped_rest = split_time(gate, grouped_rest, steps, warmup)
+        ms_grouped, _ = event_time(lambda: (gate(), grouped_rest()), steps, warmup)
+        grouped = {"forward_us": ms_grouped * 1e3, "up_down_fallback_us": ms_grouped_rest * 1e3,
+                   "partial_bytes": ws_g.numel() - tw.twell_ffn_workspace_size(T, d, F, w.tile, w.cap, x.dtype)}
+        log(f"[bench] grouped fused up+down: {ms_grouped_rest * 1e3:.1f} us in sequence, forward "
+            f"{ms_grouped * 1e3:.1f} us")
+        del ws_g
 
     # Training-format kernels on this batch's TwELL matrix (with its dense
     # backup rows): TwELL -> hybrid at an ELL width of 256, the L1 norm and the
@@ -435,8 +449,11 @@ def measure(w, steps, warmup, want_torch=True, want_cold=True):
         "training": training, "backward": backward, "copy_gbs": copy_gbs, "probe": probe,
         "fused": {"forward_us": ms_fused * 1e3, "up_down_fallback_us": ms_fused_rest * 1e3,
                   "two_kernel_up_down_fallback_us": fw["rest_in_sequence_us"],
-                  "note": "gate then twell_sparse_ffn_fused (up and down in one kernel, one wave per token), "
-                          "warm, back to back; the headline uses the two XCD-placed gather kernels"},
+                  "grouped": grouped,
+                  "note": "gate then twell_sparse_ffn_fused (up and down in one kernel, one wave per token), and "
+                          "gate then twell_sparse_ffn_grouped (hidden-group-major fused kernel with per-group fp32 "
+                          "partial output rows), warm, back to back; the headline uses the two XCD-placed "
+                          "gather kernels"},
     }
     del x, wg, wu, wd, b, packed, y, ws, yd, wsd, flush
     torch.cuda.empty_cache()

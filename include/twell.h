@@ -360,6 +360,27 @@ twell_status twell_sparse_ffn_fused(const twell_matrix *packed, const void *x, c
                                     size_t ws_bytes, void *stream);
 
 /*
+ * twell_sparse_ffn_grouped -- the fused inference kernel in hidden-group-major
+ * order (the same summary, §2.B), a measured prototype beside the two-kernel
+ * route.  Hidden units are cut into groups of TwELL tiles whose w_up and
+ * w_down rows together are about 4 MB (one XCD's L2; at most 16 groups), group
+ * g placed on XCD g % 8.  The wave of (group, token) computes v = round(h * u)
+ * for the token's entries in the group and adds v * W_d[j] into fp32
+ * registers, then writes that partial output row; a second kernel adds the
+ * groups' partial rows in group order (deterministic) and rounds y once.
+ * Overflow rows take the dense fallback as in twell_sparse_ffn.  Same
+ * arguments and results (within the same tolerance) as twell_sparse_ffn;
+ * workspace: twell_sparse_ffn_grouped_workspace_size() bytes, which adds
+ * n_groups * T * d fp32 partial rows (1 GiB at T = 8192, d = 2048, 16 groups)
+ * to the forward's workspace; d limited to 4096 (bf16) / 2048 (fp32).
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP.
+ */
+size_t twell_sparse_ffn_grouped_workspace_size(int T, int d, int F, int tile, int cap, twell_dtype dtype);
+twell_status twell_sparse_ffn_grouped(const twell_matrix *packed, const void *x, const void *w_gate,
+                                      const void *w_up, const void *w_down, const float *gate_bias, void *y,
+                                      int d, void *workspace, size_t ws_bytes, void *stream);
+
+/*
  * twell_ffn_backward -- gradients of the ReLU-gated FFN layer from its
  * activations in the hybrid format (gist.science "Sparser, Faster, Lighter
  * Transformer Language Models", Resumen Técnico §2.A: the hybrid format keeps

@@ -150,6 +150,22 @@ def test_fused_up_down(dtype, T, d, F, tile, cap, bias):
     assert np.array_equal(p.ovf_rows[:n_fused].cpu().numpy(), rows_fused)
 
 
+@pytest.mark.parametrize("dtype,T,d,F,tile,cap,bias", FUSED_SMALL)
+def test_grouped_up_down(dtype, T, d, F, tile, cap, bias):
+    """twell_sparse_ffn_grouped (hidden-group-major fused kernel, fp32 partial
+    rows per group added in group order) after the gate: y against the oracle,
+    every row; repeated calls are bitwise equal."""
+    print(f"grouped {dtype} T={T} d={d} F={F} tile={tile} cap={cap}", flush=True)
+    inp = ffn_inputs(T, d, F, dtype, seed=T + 2, gate_bias=_bias(bias, T))
+    x, wg, wu, wd, b = dev_inputs(inp)
+    p, _ = tw.twell_gate_pack(x, wg, b, tile=tile, cap=cap, scan=False)
+    y = tw.twell_sparse_ffn_grouped(p, x, wg, wu, wd, b)
+    yh = from_dev(y, dtype)
+    check_y(yh, inp, dtype)
+    y2 = tw.twell_sparse_ffn_grouped(p, x, wg, wu, wd, b)
+    assert np.array_equal(from_dev(y2, dtype), yh)
+
+
 def test_fused_rejects_wide_rows():
     import torch
     inp = ffn_inputs(4, 8192, 512, "bf16", seed=1, gate_bias=-1.0)

@@ -68,3 +68,15 @@ def test_full_size_fused_up_down(name):
     y = tw.twell_sparse_ffn_fused(p, x, wg, wu, wd, b)
     hot = [t for t in range(w.T) if t % SEQ < 3]
     check_y(from_dev(y, w.dtype), inp, w.dtype, rows=_rows(w.T, hot))
+
+
+def test_full_size_grouped_up_down():
+    """The hidden-group-major fused prototype at the 1.5B-class shape, as the
+    benchmark times it (gate, then twell_sparse_ffn_grouped): y on sampled rows."""
+    w = CONFIGS["layer_1p5b_bf16"]
+    print("full grouped layer_1p5b_bf16", flush=True)
+    inp = w.inputs()
+    x, wg, wu, wd, b = dev_inputs(inp)
+    p, _ = tw.twell_gate_pack(x, wg, b, tile=w.tile, cap=w.cap, scan=False)
+    y = tw.twell_sparse_ffn_grouped(p, x, wg, wu, wd, b)
+    check_y(from_dev(y, w.dtype), inp, w.dtype, rows=_rows(w.T))
