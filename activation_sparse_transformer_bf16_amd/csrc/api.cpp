@@ -618,20 +618,34 @@ twell_status check_backward_shape(int T, int d, int F, int width, int dense_cap,
   return TWELL_OK;
 }
 
+// The dense backup rows go to the matrix-core kernels when the hidden size is
+// a multiple of their 128-unit tiles; otherwise their entries are walked like
+// the others.
+bool bw_dense_mma(int F) { return F % 128 == 0; }
+
 // Workspace of the backward: compacted dense rows | per-entry (du, dpre) |
 // per-entry column-major position | column-major records | per-block column
-// counts | their running offsets | column totals | column starts | row order.
+// counts | their running offsets | column totals | column starts | row order,
+// then the matrix-core dense-row pieces: gathered x and dy rows | du and dpre
+// rows | a, du, dpre transposed | the dx split's partial tiles.  The dense
+// rows' entry slots and compacted columns exist only without the matrix-core
+// path.
 struct BwWs {
-  size_t dcol, dn, ent, pos, csc, blk, boff, tot, colptr, order, total;
+  size_t dcol, dn, ent, pos, csc, blk, boff, tot, colptr, order;
+  size_t xr, dyr, du, dp, at, dut, dpt, part;
+  int part_tiles, as_stride;
+  size_t total;
 };
 
-BwWs bw_ws_layout(int T, int F, int width, int dense_cap) {
+BwWs bw_ws_layout(int T, int d, int F, int width, int dense_cap, twell_dtype dtype) {
   BwWs w;
-  const size_t NE = (size_t)T * width + (size_t)dense_cap * F;
+  const bool mma = bw_dense_mma(F);
+  const size_t NE = (size_t)T * width + (mma ? 0 : (size_t)dense_cap * F);
   const size_t NB = ((size_t)T + 63) / 64;
+  const size_t dcap_lists = mma ? 0 : (size_t)dense_cap;
   w.dcol = 0;
-  w.dn = align_up(w.dcol + (size_t)dense_cap * F * 4, ALIGN_WS);
-  w.ent = align_up(w.dn + (size_t)dense_cap * 4, ALIGN_WS);
+  w.dn = align_up(w.dcol + dcap_lists * F * 4, ALIGN_WS);
+  w.ent = align_up(w.dn + dcap_lists * 4, ALIGN_WS);
   w.pos = align_up(w.ent + NE * 8, ALIGN_WS);
   w.csc = align_up(w.pos + NE * 4, ALIGN_WS);
   w.blk = align_up(w.csc + NE * 16, ALIGN_WS);
@@ -639,7 +653,24 @@ BwWs bw_ws_layout(int T, int F, int width, int dense_cap) {
   w.tot = align_up(w.boff + NB * F * 4, ALIGN_WS);
   w.colptr = align_up(w.tot + (size_t)F * 4, ALIGN_WS);
   w.order = align_up(w.colptr + ((size_t)F + 1) * 4, ALIGN_WS);
-  w.total = align_up(w.order + (size_t)T * 4, ALIGN_WS);
+  size_t end = align_up(w.order + (size_t)T * 4, ALIGN_WS);
+  const size_t s = dt_size(dtype);
+  const bool dense = mma && dense_cap > 0 && T > 0;
+  const int ns = dtype == TWELL_BF16 ? 2 : 1;
+  w.as_stride = dense ? ns * twell::backward_dense_rows_padded(dense_cap, to_dt(dtype)) : 0;
+  w.part_tiles = dense ? twell::backward_dense_partial_tiles(dense_cap, d) : 0;
+  const size_t g = dense ? (size_t)w.as_stride * d * s : 0;            // gathered rows
+  const size_t rm = dense ? (size_t)dense_cap * F * s : 0;             // du / dpre rows
+  const size_t tr = dense ? (size_t)F * w.as_stride * s : 0;           // transposed operands
+  w.xr = end;
+  w.dyr = align_up(w.xr + g, ALIGN_WS);
+  w.du = align_up(w.dyr + g, ALIGN_WS);
+  w.dp = align_up(w.du + rm, ALIGN_WS);
+  w.at = align_up(w.dp + rm, ALIGN_WS);
+  w.dut = align_up(w.at + tr, ALIGN_WS);
+  w.dpt = align_up(w.dut + tr, ALIGN_WS);
+  w.part = align_up(w.dpt + tr, ALIGN_WS);
+  w.total = align_up(w.part + (size_t)w.part_tiles * twell::FALLBACK_SPLIT_TILE * 4, ALIGN_WS);
   return w;
 }
 
@@ -653,7 +684,7 @@ size_t twell_ffn_backward_workspace_size(int T, int d, int F, int width, int den
   const twell_status st = check_backward_shape(T, d, F, width, dense_cap, (int)dtype);
   memcpy(g_err, saved, sizeof(g_err));
   if (st != TWELL_OK) return 0;
-  return bw_ws_layout(T, F, width, dense_cap).total;
+  return bw_ws_layout(T, d, F, width, dense_cap, dtype).total;
 }
 
 twell_status twell_ffn_backward(const twell_hybrid *h, const void *x, const void *w_gate, const void *w_up,
@@ -678,7 +709,9 @@ twell_status twell_ffn_backward(const twell_hybrid *h, const void *x, const void
   if (!aligned(x, 16) || !aligned(dy, 16) || !aligned(dx, 16) || !aligned(w_gate, 16) || !aligned(w_up, 16) ||
       !aligned(w_down, 16) || !aligned(dw_gate, 16) || !aligned(dw_up, 16) || !aligned(dw_down, 16))
     return fail(TWELL_ERR_UNSUPPORTED, "x, dy, dx, weights and weight gradients must be 16-byte aligned");
-  const BwWs L = bw_ws_layout(T, F, h->width, h->dense_cap);
+  if (h->dense_cap > 0 && bw_dense_mma(F) && !aligned(h->dense, 16))
+    return fail(TWELL_ERR_UNSUPPORTED, "the dense backup rows must be 16-byte aligned");
+  const BwWs L = bw_ws_layout(T, d, F, h->width, h->dense_cap, h->dtype);
   if (workspace == nullptr || ws_bytes < L.total)
     return fail(TWELL_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total, workspace ? ws_bytes : 0);
   if (!aligned(workspace, ALIGN_WS)) return fail(TWELL_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
@@ -688,7 +721,9 @@ twell_status twell_ffn_backward(const twell_hybrid *h, const void *x, const void
                   reinterpret_cast<int *>(base + L.dcol), reinterpret_cast<int *>(base + L.dn), base + L.ent,
                   reinterpret_cast<int *>(base + L.pos), base + L.csc, reinterpret_cast<uint8_t *>(base + L.blk),
                   reinterpret_cast<int *>(base + L.boff), reinterpret_cast<int *>(base + L.tot),
-                  reinterpret_cast<int *>(base + L.colptr), reinterpret_cast<int *>(base + L.order)};
+                  reinterpret_cast<int *>(base + L.colptr), reinterpret_cast<int *>(base + L.order),
+                  bw_dense_mma(F), base + L.xr, base + L.dyr, base + L.du, base + L.dp, base + L.at,
+                  base + L.dut, base + L.dpt, reinterpret_cast<float *>(base + L.part), L.part_tiles};
   TW_TRY(ffn_backward(ba, static_cast<hipStream_t>(stream)), "FFN backward");
   return TWELL_OK;
 }

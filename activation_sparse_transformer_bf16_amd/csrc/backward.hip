@@ -27,6 +27,10 @@
 //   k_bw_dx           per (row, column slice of d): dx over the row's entries
 //   k_bw_dw           per (hidden unit, column slice): dW_u, dW_g and dW_d
 //                     rows over the unit's transposed list
+// and, when the hidden size allows it (a multiple of 128), the dense backup
+// rows on the matrix cores (bw_dense.hip) between k_bw_dx and k_bw_dw; their
+// lists are empty here.  Otherwise k_bw_dense_cols lists their active columns
+// first and they are walked like the others.
 // Every sum runs in a fixed order (entry order of a row, ascending rows of a
 // column), so the results are deterministic.  No atomics touch global memory.
 #include "gather.hpp"
@@ -54,11 +58,13 @@ struct RowSrc {
   const int *dcol;        // [dense_cap][F] compacted columns of the dense rows
   const int *dn;          // [dense_cap] their lengths
   int T, F, width;
+  bool dense_mma;         // dense rows go to the matrix-core kernels: empty lists here
 };
 
 // The entry list of row t: the hybrid's ELL slots, or the compacted columns
 // of its dense backup row (r >= 0).  Entry slots are numbered t * width + i
-// for ELL rows and T * width + r * F + i for dense row r.
+// for ELL rows and T * width + r * F + i for dense row r.  With dense_mma the
+// dense rows' lists are empty (the matrix-core kernels take those rows).
 struct RowList {
   const int *col;
   int n, r;
@@ -74,6 +80,11 @@ __device__ __forceinline__ RowList row_list(const RowSrc<TT> &s, int t) {
     L.n = max(c, 0);
     L.r = -1;
     L.slot0 = (size_t)t * s.width;
+  } else if (s.dense_mma) {
+    L.col = s.col;
+    L.n = 0;
+    L.r = -1;
+    L.slot0 = 0;
   } else {
     const int r = find_row(s.dense_rows, min(*s.n_dense, s.dense_cap), t);
     L.r = r;
@@ -510,11 +521,20 @@ __global__ __launch_bounds__(SP_THREADS) void k_bw_dx(RowSrc<typename DtT<D>::T>
   }
 }
 
+// v (+ base) to p.
 template <int CPL>
-__device__ __forceinline__ void store_f32(float *p, const float (&v)[CPL]) {
+__device__ __forceinline__ void store_f32(float *p, const float (&v)[CPL], const f32x4_t (&base)[CPL / 4]) {
 #pragma unroll
   for (int q = 0; q < CPL; q += 4)
-    *reinterpret_cast<f32x4_t *>(p + q) = f32x4_t{v[q], v[q + 1], v[q + 2], v[q + 3]};
+    *reinterpret_cast<f32x4_t *>(p + q) = f32x4_t{v[q], v[q + 1], v[q + 2], v[q + 3]} + base[q / 4];
+}
+// The values a unit's gradient slice already holds (the dense rows' part),
+// loaded when its list starts so that the loads overlap the walk; zero when
+// there is nothing to add or the lane does not store.
+template <int CPL>
+__device__ __forceinline__ void load_base(f32x4_t (&b)[CPL / 4], const float *p, bool on) {
+#pragma unroll
+  for (int q = 0; q < CPL; q += 4) b[q / 4] = on ? *reinterpret_cast<const f32x4_t *>(p + q) : f32x4_t{};
 }
 
 template <Dt D, int U>
@@ -523,7 +543,8 @@ __global__ __launch_bounds__(SP_THREADS) void k_bw_dw(const int *__restrict__ co
                                                      const typename DtT<D>::T *__restrict__ dy,
                                                      float *__restrict__ dwg, float *__restrict__ dwu,
                                                      float *__restrict__ dwd, int T, int F, int d, int n_slices,
-                                                     int units_per_wg, int n_ub) {
+                                                     int units_per_wg, int n_ub, const int *__restrict__ n_dense,
+                                                     int dense_cap, bool dense_mma) {
   using TT = typename DtT<D>::T;
   constexpr int CPL = 16 / sizeof(TT);
   constexpr int LPE = DW_SLICE / CPL;
@@ -536,6 +557,9 @@ __global__ __launch_bounds__(SP_THREADS) void k_bw_dw(const int *__restrict__ co
   int sl, ub;
   group_coords(blockIdx.x, n_slices, n_ub, sl, ub);
   if (sl >= n_slices) return;
+  // dense rows on the matrix cores: their part of the gradients is written
+  // already, and this kernel adds the other rows' sums to it
+  const bool add = dense_mma && T > 0 && dense_cap > 0 && min(*n_dense, dense_cap) > 0;
   const size_t a_bytes = ((size_t)T * d - (size_t)sl * DW_SLICE) * sizeof(TT);
   const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(x + sl * DW_SLICE, a_bytes), gr = buffer_rsrc(dy + sl * DW_SLICE, a_bytes);
   const uint32_t lane_off = lcol * sizeof(TT);
@@ -545,6 +569,11 @@ __global__ __launch_bounds__(SP_THREADS) void k_bw_dw(const int *__restrict__ co
     const int j = ub * units_per_wg + it;
     if (j >= F) break;
     const int c0 = colptr[j], n = colptr[j + 1] - c0;
+    const size_t o = (size_t)j * d + sl * DW_SLICE + lcol;
+    f32x4_t bg[CPL / 4], bu[CPL / 4], bd[CPL / 4];
+    load_base<CPL>(bg, dwg + o, add && part == 0);
+    load_base<CPL>(bu, dwu + o, add && part == 0);
+    load_base<CPL>(bd, dwd + o, add && part == 0);
     float ag[CPL], au[CPL], ad[CPL];
 #pragma unroll
     for (int v = 0; v < CPL; ++v) ag[v] = au[v] = ad[v] = 0.f;
@@ -587,10 +616,9 @@ __global__ __launch_bounds__(SP_THREADS) void k_bw_dw(const int *__restrict__ co
       ad[v] = add_parts<EPI>(ad[v]);
     }
     if (part == 0) {
-      const size_t o = (size_t)j * d + sl * DW_SLICE + lcol;
-      store_f32<CPL>(dwg + o, ag);
-      store_f32<CPL>(dwu + o, au);
-      store_f32<CPL>(dwd + o, ad);
+      store_f32<CPL>(dwg + o, ag, bg);
+      store_f32<CPL>(dwu + o, au, bu);
+      store_f32<CPL>(dwd + o, ad, bd);
     }
   }
 }
@@ -621,12 +649,12 @@ template <Dt D>
 static hipError_t launch_backward(const BackwardArgs &a, hipStream_t st) {
   using TT = typename DtT<D>::T;
   RowSrc<TT> s{a.cnt, (const TT *)a.val, a.col, a.dense_rows, a.n_dense, a.dense_cap, (const TT *)a.dense,
-               a.dcol, a.dn, a.T, a.F, a.width};
+               a.dcol, a.dn, a.T, a.F, a.width, a.dense_mma};
   hipError_t e;
   const int NB = bw_blocks(a.T);
   const int mask_lds = a.F * 8;
   if (a.T > 0) {
-    if (a.dense_cap > 0) {
+    if (a.dense_cap > 0 && !a.dense_mma) {
       const int grid = std::min((a.dense_cap + BW_WAVES - 1) / BW_WAVES, 1024);
       hipLaunchKernelGGL(k_bw_dense_cols<D>, dim3(grid), dim3(BW_THREADS), 0, st, (const TT *)a.dense, a.n_dense,
                          a.dense_cap, a.F, a.dcol, a.dn);
@@ -670,11 +698,18 @@ static hipError_t launch_backward(const BackwardArgs &a, hipStream_t st) {
                        n_tb, a.order);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
+  // the dense rows on the matrix cores: their dx rows (after the entry
+  // kernels' dx), and their part of the weight gradients (before the entry
+  // kernels' weight gradients, which add onto it)
+  if (a.dense_mma) {
+    if ((e = ffn_backward_dense_dx(a, st)) != hipSuccess) return e;
+    if ((e = ffn_backward_dense_dw(a, st)) != hipSuccess) return e;
+  }
   const int upw = 8;  // units per workgroup; 8 loads in flight per lane (fastest in a sweep)
   const int n_ub = (a.F + upw - 1) / upw;
   hipLaunchKernelGGL((k_bw_dw<D, 8>), dim3(padded_groups(n_wslices) * n_ub), dim3(SP_THREADS), 0, st, a.colptr,
                      (const u32x4_t *)a.csc, (const TT *)a.x, (const TT *)a.dy, a.dwg, a.dwu, a.dwd, a.T, a.F, a.d,
-                     n_wslices, upw, n_ub);
+                     n_wslices, upw, n_ub, a.n_dense, a.dense_cap, a.dense_mma);
   return hipGetLastError();
 }
 

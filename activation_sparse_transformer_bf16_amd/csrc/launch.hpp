@@ -250,8 +250,25 @@ struct BackwardArgs {
   uint8_t *blk;
   int *boff, *tot, *colptr;
   int *order;  // [T] row order of the per-row kernels
+  // The dense backup rows on the matrix cores (dense_mma; F a multiple of
+  // 128).  Otherwise their entries are walked like the others (dcol / dn) and
+  // these are null.  rcp = dense_cap rounded up to whole K chunks
+  // (backward_dense_rows_padded), ns = 2 parts per value for bf16, 1 for fp32.
+  bool dense_mma;
+  void *bd_xr, *bd_dyr;            // [ns * rcp][d] gathered x / dy rows
+  void *bd_du, *bd_dp;             // [dense_cap][F] du, dpre (storage dtype)
+  void *bd_at, *bd_dut, *bd_dpt;   // [F][ns * rcp] a, du, dpre transposed (bf16: high, then low parts)
+  float *bd_part;                  // dx split-K partial tiles
+  int bd_part_tiles;               // their capacity in 256 x 256 fp32 tiles
 };
 hipError_t ffn_backward(const BackwardArgs &a, hipStream_t s);
+// The dense rows' part, launched by ffn_backward: their dx rows (U, DA, and
+// the dx matmul) after the entry kernels' dx, their weight-gradient part
+// before the entry kernels' weight gradients, which add onto it.
+hipError_t ffn_backward_dense_dx(const BackwardArgs &a, hipStream_t s);
+hipError_t ffn_backward_dense_dw(const BackwardArgs &a, hipStream_t s);
+int backward_dense_partial_tiles(int dense_cap, int d);
+int backward_dense_rows_padded(int dense_cap, Dt dt);
 
 // *p = 0 with a one-thread kernel (safe under stream capture).
 hipError_t zero_int(int *p, hipStream_t s);

@@ -270,6 +270,63 @@ def forward_timings(w, x, wg, wu, wd, b, steps, warmup, flush, want_torch=True, 
     return r, bufs
 
 
+def backward_timing(w, hy, x, wg, wu, wd, b, nnz_all, steps, warmup, want_torch):
+    """twell_ffn_backward from the hybrid activations hy (every dense row kept):
+    dx and the three weight gradients with the L1 term, for a seeded dy; and
+    torch's dense backward beside it."""
+    import torch
+
+    import activation_sparse_transformer_bf16_amd as tw
+    from workloads.synth import grad_output
+    dev = x.device
+    T, d, F = w.T, w.d, w.F
+    s = 2 if w.dtype == "bf16" else 4
+    n_dense = int(hy.n_dense.item())
+    dy = to_dev(grad_output(T, d, w.dtype, seed=0), w.dtype, dev)
+    bw_ws = torch.empty((tw.twell_ffn_backward_workspace_size(T, d, F, HYBRID_WIDTH, hy.dense_cap, x.dtype),),
+                        dtype=torch.uint8, device=dev)
+    dxb = torch.empty_like(x)
+    dwb = [torch.empty((F, d), dtype=torch.float32, device=dev) for _ in range(3)]
+    bw = lambda: tw.twell_ffn_backward(hy, x, wg, wu, wd, dy, L1_LAMBDA, dxb, *dwb, workspace=bw_ws)
+    ms_bw, _ = event_time(bw, steps, warmup)
+    # gathered per active entry: W_u and W_d rows (entry gradients), W_u and
+    # W_g rows (dx), x and dy rows (weight gradients); plus the weight
+    # gradients written once and the x / dy / dx rows
+    bw_bytes = nnz_all * 6 * d * s + 3 * F * d * 4 + 3 * T * d * s
+    # compulsory: every weight row once, x and dy read, dx and the fp32
+    # weight gradients written once
+    bw_comp = 3 * F * d * s + 3 * T * d * s + 3 * F * d * 4
+    backward = {"us": ms_bw * 1e3, "tokens_per_s": T / (ms_bw * 1e-3), "hybrid_width": HYBRID_WIDTH,
+                "n_dense": n_dense, "entries": nnz_all, "bytes_alg": bw_bytes,
+                "effective_GBps": bw_bytes / (ms_bw * 1e-3) / 1e9,
+                "compulsory_bytes": bw_comp,
+                "compulsory_frac_of_hbm_peak": bw_comp / (ms_bw * 1e-3) / 1e9 / HBM_PEAK_GBS, "lam": L1_LAMBDA,
+                "note": "twell_ffn_backward: dx (activation dtype) and fp32 dW_g, dW_u, dW_d from the hybrid "
+                        "activations; bytes_alg = 6 rows of d per active entry + weight gradients + x, dy, dx "
+                        "(an effective rate: L2-served re-reads counted, not a roofline fraction); "
+                        "compulsory = each weight row, x, dy, dx and the weight gradients once"}
+    log(f"[bench] {w.name} backward {ms_bw * 1e3:.1f} us ({n_dense} dense rows; "
+        f"{backward['effective_GBps']:.0f} GB/s effective)")
+    if want_torch:
+        import torch.nn.functional as Fn
+        hd = torch.relu(torch.addmm(b[:, None].to(x.dtype), x, wg.t()))
+        ud = Fn.linear(x, wu)
+
+        def torch_backward():  # dense, with h and u saved by the forward (bf16 outputs)
+            da = dy @ wd.t()
+            du = da * hd
+            dp = (da * ud + L1_LAMBDA) * (hd > 0)
+            return du @ wu + dp @ wg, du.t() @ x, dp.t() @ x, (hd * ud).t() @ dy
+
+        ms_tbw, _ = event_time(torch_backward, steps, warmup)
+        backward["torch_dense_backward_us"] = ms_tbw * 1e3
+        backward["speedup_vs_torch_dense_backward"] = ms_tbw / ms_bw
+        log(f"[bench] torch (hipBLASLt) dense backward {ms_tbw * 1e3:.1f} us")
+        del hd, ud
+    del dy, bw_ws, dxb, dwb
+    return backward
+
+
 def measure(w, steps, warmup, want_torch=True, want_cold=True):
     import numpy as np
     import torch
@@ -352,42 +409,8 @@ def measure(w, steps, warmup, want_torch=True, want_cold=True):
 
     # Backward from these hybrid activations (every dense row kept): dx and
     # the three weight gradients with the L1 term, for a seeded dy.
-    from workloads.synth import grad_output
-    dy = to_dev(grad_output(T, d, w.dtype, seed=0), w.dtype, dev)
-    bw_ws = torch.empty((tw.twell_ffn_backward_workspace_size(T, d, F, HYBRID_WIDTH, hy.dense_cap, x.dtype),),
-                        dtype=torch.uint8, device=dev)
-    dxb = torch.empty_like(x)
-    dwb = [torch.empty((F, d), dtype=torch.float32, device=dev) for _ in range(3)]
-    bw = lambda: tw.twell_ffn_backward(hy, x, wg, wu, wd, dy, L1_LAMBDA, dxb, *dwb, workspace=bw_ws)
-    ms_bw, _ = event_time(bw, steps, warmup)
-    # gathered per active entry: W_u and W_d rows (entry gradients), W_u and
-    # W_g rows (dx), x and dy rows (weight gradients); plus the weight
-    # gradients written once and the x / dy / dx rows
-    bw_bytes = nnz_all * 6 * d * s + 3 * F * d * 4 + 3 * T * d * s
-    backward = {"us": ms_bw * 1e3, "tokens_per_s": T / (ms_bw * 1e-3), "hybrid_width": HYBRID_WIDTH,
-                "n_dense": n_dense, "entries": nnz_all, "bytes_alg": bw_bytes,
-                "achieved_GBps": bw_bytes / (ms_bw * 1e-3) / 1e9,
-                "frac_of_hbm_peak": bw_bytes / (ms_bw * 1e-3) / 1e9 / HBM_PEAK_GBS, "lam": L1_LAMBDA,
-                "note": "twell_ffn_backward: dx (activation dtype) and fp32 dW_g, dW_u, dW_d from the hybrid "
-                        "activations; bytes_alg = 6 rows of d per active entry + weight gradients + x, dy, dx"}
-    log(f"[bench] backward {ms_bw * 1e3:.1f} us ({backward['achieved_GBps']:.0f} GB/s algorithmic)")
-    if want_torch:
-        import torch.nn.functional as Fn
-        hd = torch.relu(torch.addmm(b[:, None].to(x.dtype), x, wg.t()))
-        ud = Fn.linear(x, wu)
-
-        def torch_backward():  # dense, with h and u saved by the forward (bf16 outputs)
-            da = dy @ wd.t()
-            du = da * hd
-            dp = (da * ud + L1_LAMBDA) * (hd > 0)
-            return du @ wu + dp @ wg, du.t() @ x, dp.t() @ x, (hd * ud).t() @ dy
-
-        ms_tbw, _ = event_time(torch_backward, steps, warmup)
-        backward["torch_dense_backward_us"] = ms_tbw * 1e3
-        backward["speedup_vs_torch_dense_backward"] = ms_tbw / ms_bw
-        log(f"[bench] torch (hipBLASLt) dense backward {ms_tbw * 1e3:.1f} us")
-        del hd, ud
-    del packed_tr, hy, dy, bw_ws, dxb, dwb
+    backward = backward_timing(w, hy, x, wg, wu, wd, b, nnz_all, steps, warmup, want_torch)
+    del packed_tr, hy
 
     # Standalone twell_pack of this batch's rounded gate pre-activations
     # (dumped once by the gate kernel): HBM-bound, T*F*s bytes read plus the
@@ -465,6 +488,8 @@ def extra_workloads(args, base_inp):
     dense FFN and torch dense FFN, cold and warm, with the same protocol."""
     import numpy as np
     import torch
+
+    import activation_sparse_transformer_bf16_amd as tw
     from workloads import CONFIGS, workload
     from workloads.configs import SWEEP_DENSITIES
 
@@ -481,6 +506,19 @@ def extra_workloads(args, base_inp):
         r, bufs = forward_timings(w, x, wg, wu, wd, b, args.steps, args.warmup, flush, not args.no_torch)
         r.pop("sparse_cold_ms_list", None)
         r["config"] = w.summary()
+        if name == "skewed_bf16":
+            # the backward on the skewed batch: its hot rows are the hybrid's
+            # dense backup rows
+            ws = bufs[2]
+            packed_tr = tw.TwellMatrix.empty(w.T, w.F, w.tile, w.cap, x.dtype, dev, w.T, dense=True)
+            tw.twell_ffn_forward(x, wg, wu, wd, b, packed=packed_tr, y=bufs[1], workspace=ws)
+            hy = tw.TwellHybrid.empty(w.T, w.F, HYBRID_WIDTH, x.dtype, dev)
+            tw.twell_to_hybrid(packed_tr, HYBRID_WIDTH, out=hy)
+            torch.cuda.synchronize()
+            nnz_all = int(packed_tr.cnt.cpu().numpy().view(np.uint16).astype(np.int64).sum())
+            r["backward"] = backward_timing(w, hy, x, wg, wu, wd, b, nnz_all, args.steps, args.warmup,
+                                            not args.no_torch)
+            del packed_tr, hy
         out[name] = r
         del x, wg, wu, wd, b, bufs, inp
         torch.cuda.empty_cache()

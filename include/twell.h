@@ -398,7 +398,8 @@ twell_status twell_sparse_ffn_grouped(const twell_matrix *packed, const void *x,
  *
  * h:      the activations (rows T, cols F, width, dtype); every dense row must
  *         be listed and stored: dense_cap >= *n_dense and dense non-NULL when
- *         dense_cap > 0 (a dense row that is not stored contributes nothing).
+ *         dense_cap > 0 (a dense row that is not stored contributes nothing);
+ *         dense 16-byte aligned when F is a multiple of 128.
  * x, dy:  [T][d] dtype;  w_gate, w_up, w_down: [F][d] dtype (as the forward).
  * dx:     [T][d] dtype, overwritten (one rounding of fp32 sums).
  * dw_gate, dw_up, dw_down: [F][d] fp32, overwritten.

@@ -191,9 +191,17 @@ def test_backward_validation_and_workspace():
     import torch
     ws = twell.twell_ffn_backward_workspace_size
     n = ws(8192, 2048, 8192, 256, 8192, torch.bfloat16)
-    # per entry slot: (du, dpre) 8 B + position 4 B + column-major record 16 B
-    slots = 8192 * 256 + 8192 * 8192
-    assert n >= slots * 28 and n % 256 == 0
+    # per entry slot: (du, dpre) 8 B + position 4 B + column-major record 16 B;
+    # F a multiple of 128: the dense rows go to the matrix-core kernels, which
+    # need gathered x / dy rows (two bf16 copies each), du / dpre rows and a,
+    # du, dpre transposed (high and low bf16 parts)
+    slots = 8192 * 256
+    dense = 2 * (2 * 8192 * 2048 * 2) + 2 * (8192 * 8192 * 2) + 3 * (8192 * 2 * 8192 * 2)
+    assert n >= slots * 28 + dense and n % 256 == 0
+    assert n < (slots + 8192 * 8192) * 28  # no entry slots for the dense rows
+    # other hidden sizes: the dense rows' entries are walked like the others
+    n2 = ws(8192, 2048, 8000, 256, 8192, torch.bfloat16)
+    assert n2 >= (8192 * 256 + 8192 * 8000) * 28 and n2 % 256 == 0
     assert ws(8, 8192, 512, 16, 8, torch.bfloat16) == 0      # d above the backward's limit
     assert ws(8, 4096, 512, 16, 8, torch.float32) == 0       # fp32 d above 2048
     assert ws(8, 2048, 32768, 16, 8, torch.bfloat16) == 0    # F above 16384
@@ -213,6 +221,7 @@ def test_backward_validation_and_workspace():
     assert call(_hybrid(cols=20000)) == twell.TWELL_ERR_UNSUPPORTED
     assert call(_hybrid(n_dense=None)) == twell.TWELL_ERR_INVALID_ARG
     assert call(_hybrid(dense=None)) == twell.TWELL_ERR_INVALID_ARG        # dense_cap > 0 needs the rows
+    assert call(_hybrid(dense=FAKE + 2)) == twell.TWELL_ERR_UNSUPPORTED    # matrix-core dense rows: 16-byte aligned
     assert call(_hybrid(col=FAKE + 2)) == twell.TWELL_ERR_UNSUPPORTED
     assert call(h, x=None) == twell.TWELL_ERR_INVALID_ARG
     assert call(h, dwg=None) == twell.TWELL_ERR_INVALID_ARG

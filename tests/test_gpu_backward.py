@@ -108,6 +108,13 @@ CASES = [
     ("bf16", 50, 4096, 1024, 16, 0.02, (7,), 0.0),             # d = 4096: one entry in flight
     ("bf16", 45, 512, 1536, 1, 0.01, (), 0.1),                 # width 1: most rows dense
     ("bf16", 70, 1536, 640, 300, 0.2, (), 0.0),                # wide ELL: no dense row; F not a power of 2
+    # dense rows on the matrix cores: several row tiles, R not a multiple of 64
+    ("bf16", 300, 512, 1024, 2, 0.02, (), 2e-5),               # width 2: nearly every row dense
+    ("f32", 150, 256, 512, 2, 0.03, (), 0.1),
+    ("bf16", 530, 1024, 2048, 20, 0.01, (0, 17, 256, 529), 2e-5),  # about half the rows dense
+    # F not a multiple of 128: the dense rows' entries are walked like the others
+    ("bf16", 61, 512, 320, 4, 0.03, (2, 30), 2e-5),
+    ("f32", 50, 256, 448, 4, 0.05, (1,), 2e-5),
 ]
 
 
@@ -166,20 +173,22 @@ def test_backward_unstored_dense_rows_contribute_nothing():
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("name", ["layer_1p5b_bf16", "skewed_bf16"])
-def test_backward_full_size(name):
+@pytest.mark.parametrize("name,width", [("layer_1p5b_bf16", 256), ("skewed_bf16", 256), ("layer_1p5b_bf16", 64)])
+def test_backward_full_size(name, width):
     """The 1.5B-class layer (and its skewed variant) at full size, hybrid width 256
     as timed by the bench: dx on sampled rows, the weight gradients on sampled
-    hidden units (each depends only on its own row / unit of h)."""
+    hidden units (each depends only on its own row / unit of h).  Width 64
+    makes nearly every row dense (~82 active units per row): the dense-row
+    matmuls then fill the grid without a K split."""
     import torch
     from workloads.configs import workload
     w = workload(name)
     T, d, F, dtype = w.T, w.d, w.F, w.dtype
-    print(f"backward full size {name}", flush=True)
+    print(f"backward full size {name} width {width}", flush=True)
     inp = w.inputs()
     h = relu_storage(round_to_storage(gate_pre(inp.x, inp.w_gate, inp.gate_bias, dtype), dtype), dtype)
     dy = grad_output(T, d, dtype, seed=0)
-    hy = hybrid(h, dtype, 256)
+    hy = hybrid(h, dtype, width)
     lam = float(np.float32(2e-5))
     got_dev = hybrid_to_dev(hy, F, dtype, dense_cap=T)
     x, wg, wu, wd, _ = dev_inputs(inp)
