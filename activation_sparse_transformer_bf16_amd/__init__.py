@@ -15,7 +15,9 @@ from dataclasses import dataclass
 from typing import Optional, Tuple
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libtwell.so")
+# TWELL_LIBRARY names another build of the same library (the host-sanitizer
+# build of build.py); by default the in-tree libtwell.so.
+LIB_PATH = os.environ.get("TWELL_LIBRARY") or os.path.join(_HERE, "libtwell.so")
 
 TWELL_OK, TWELL_ERR_INVALID_ARG, TWELL_ERR_UNSUPPORTED, TWELL_ERR_WORKSPACE, TWELL_ERR_HIP = range(5)
 TWELL_F32, TWELL_BF16 = 0, 1

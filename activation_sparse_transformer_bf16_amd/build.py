@@ -74,5 +74,52 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     return LIB
 
 
+# Host-side sanitizers for the C ABI layer: api.cpp (argument validation,
+# workspace layouts, the launch sequence) is compiled with AddressSanitizer and
+# UndefinedBehaviorSanitizer on its host code only (-Xarch_host: the device
+# code is built as usual) and linked with the other objects of build() into
+# _build/san/libtwell_san.so.  A process loads it through TWELL_LIBRARY with
+# the shared ASan runtime preloaded (asan_runtime()).
+SAN_FLAGS = ["-g", "-fno-omit-frame-pointer",
+             "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined"]
+SAN_LIB = os.path.join(BUILD, "san", "libtwell_san.so")
+
+
+def asan_runtime() -> str:
+    r = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("the compiler's shared ASan runtime was not found")
+    return path
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """libtwell_san.so: api.cpp with host ASan + UBSan, every other source as in build()."""
+    build(verbose)
+    san = os.path.dirname(SAN_LIB)
+    os.makedirs(san, exist_ok=True)
+    api = os.path.join(CSRC, "api.cpp")
+    obj = os.path.join(san, "api.cpp.o")
+    cmd = [hipcc(), "-x", "hip", *COMMON_FLAGS, *SAN_FLAGS, "-c", api, "-o", obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compiling api.cpp with sanitizers failed:\n{r.stdout}\n{r.stderr}")
+    objs = [os.path.join(BUILD, os.path.basename(s) + ".o") for s in sources() if not s.endswith("api.cpp")]
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", SAN_LIB, *objs, obj,
+           "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", "-shared-libasan"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"linking libtwell_san.so failed:\n{r.stdout}\n{r.stderr}")
+    return SAN_LIB
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--sanitize" in sys.argv:
+        print(build_sanitized(verbose="-v" in sys.argv))
+    else:
+        print(build(verbose="-v" in sys.argv))

@@ -65,7 +65,17 @@ extern "C" {
 
 #define TWELL_ABI_VERSION 1
 
-typedef enum {
+/* The enums are int-sized.  Compiled as C++ they have the fixed underlying
+ * type int, so any int a C caller stores in one is a value of the type, which
+ * the library then validates (an unknown dtype is TWELL_ERR_INVALID_ARG, an
+ * unknown status has the string "unknown status"). */
+#ifdef __cplusplus
+#define TWELL_ENUM_BASE : int
+#else
+#define TWELL_ENUM_BASE
+#endif
+
+typedef enum TWELL_ENUM_BASE {
   TWELL_OK = 0,
   TWELL_ERR_INVALID_ARG = 1, /* NULL required pointer, bad enum, negative or inconsistent size */
   TWELL_ERR_UNSUPPORTED = 2, /* valid but not built: tile, cap, d, dtype or alignment */
@@ -73,7 +83,7 @@ typedef enum {
   TWELL_ERR_HIP = 4          /* a HIP call or kernel launch failed; see twell_last_error() */
 } twell_status;
 
-typedef enum { TWELL_F32 = 0, TWELL_BF16 = 1 } twell_dtype;
+typedef enum TWELL_ENUM_BASE { TWELL_F32 = 0, TWELL_BF16 = 1 } twell_dtype;
 
 /*
  * One TwELL matrix [rows][cols] (token-major), described by caller-owned
