@@ -414,9 +414,20 @@ twell_status twell_sparse_ffn_grouped(const twell_matrix *packed, const void *x,
  * dx:     [T][d] dtype, overwritten (one rounding of fp32 sums).
  * dw_gate, dw_up, dw_down: [F][d] fp32, overwritten.
  * workspace: >= twell_ffn_backward_workspace_size(T, d, F, width, dense_cap,
- *         dtype) bytes, 256-byte aligned; about 28 bytes per entry slot, and
- *         there are T*width + dense_cap*F entry slots.
- * Sums run in a fixed order (deterministic); fp32 accumulation.
+ *         dtype) bytes, 256-byte aligned; about 28 bytes per entry slot.  With
+ *         F a multiple of 128 the dense rows are computed with matrix-core
+ *         matmuls (U = x W_u^T and DA = dy W_d^T over the listed rows, then
+ *         dx and the weight gradients), there are T*width entry slots, and
+ *         per dense row (2*s + 12)*F + 2*ns*s*d bytes of matmul operands
+ *         (s = 2 and ns = 2 for bf16, s = 4 and ns = 1 for fp32) plus up to
+ *         32 MB of split-K partial tiles; otherwise the
+ *         dense rows' active entries are walked like the ELL rows', and there
+ *         are T*width + dense_cap*F entry slots.
+ * Sums run in a fixed order (deterministic); fp32 accumulation.  In the
+ * dense rows' matmuls the dx product takes du and dpre rounded to the
+ * storage dtype; the weight-gradient products take a, du and dpre as the sum
+ * of two bf16 parts (high, and the rounded remainder) in bf16, as they are
+ * in fp32.
  * Supported: bf16 d a multiple of 512 up to 4096, fp32 d a multiple of 256 up
  * to 2048; F <= 16384; T*d and F*d elements below 2 GiB of storage;
  * T*width + dense_cap*F < 2^31.
