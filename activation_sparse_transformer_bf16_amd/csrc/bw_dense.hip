@@ -429,7 +429,10 @@ static hipError_t launch_dense_dx(const BackwardArgs &a, hipStream_t st) {
   using K = BwdK<D>;
   hipError_t e;
   const int rcp = pad_to(a.dense_cap, K::KC), as_stride = K::NS * rcp;
-  hipLaunchKernelGGL(k_bwd_gather<D>, dim3(std::min(K::NS * rcp, 2048)), dim3(256), 0, st, (const TT *)a.x,
+  // grids of at most one workgroup per CU for the gather and U/DA kernels,
+  // which loop (when no row is dense they only read the count and exit); the
+  // reduction keeps 1024 workgroups, which it needs to hide its load latency
+  hipLaunchKernelGGL(k_bwd_gather<D>, dim3(std::min(K::NS * rcp, 256)), dim3(256), 0, st, (const TT *)a.x,
                      (const TT *)a.dy, a.dense_rows, a.n_dense, a.dense_cap, a.T, a.d, (TT *)a.bd_xr,
                      (TT *)a.bd_dyr);
   if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -439,7 +442,7 @@ static hipError_t launch_dense_dx(const BackwardArgs &a, hipStream_t st) {
       hipSuccess)
     return e;
   const int ud_items = (a.dense_cap + UD_BM - 1) / UD_BM * (a.F / UD_BN);
-  hipLaunchKernelGGL(k_bwd_ud<D>, dim3(std::min(ud_items, 1024)), dim3(DiagCfg::THREADS), ud_lds, st,
+  hipLaunchKernelGGL(k_bwd_ud<D>, dim3(std::min(ud_items, 256)), dim3(DiagCfg::THREADS), ud_lds, st,
                      (const TT *)a.x, (const TT *)a.dy, (const TT *)a.wu, (const TT *)a.wd, a.dense_rows, a.n_dense,
                      a.dense_cap, (const TT *)a.dense, a.T, a.d, a.F, a.lam, (TT *)a.bd_du, (TT *)a.bd_dp,
                      (TT *)a.bd_at, (TT *)a.bd_dut, (TT *)a.bd_dpt, as_stride);

@@ -45,6 +45,9 @@ if ROOT not in sys.path:
 
 METRIC = "sparse-FFN tokens/s at 99% sparsity; achieved HBM GB/s vs peak; speedup vs dense"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+# L2 read bandwidth from the unit counts: 8 XCDs x 16 L2 channels x 128 bytes
+# per clock at the 2.4 GHz peak clock (the CDNA L2 organisation)
+L2_PEAK_GBS = 8 * 16 * 128 * 2.4
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 MFMA_F32_PEAK_TFLOPS = 157.3
 HYBRID_WIDTH = 256           # ELL slots per row for the TwELL -> hybrid timing
@@ -667,11 +670,18 @@ def gather_record(w, r):
                      "fabric_frac_of_hbm_peak": b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
                      "fabric_over_compulsory": b / rec["compulsory_bytes"][part],
                      "ta_busy": c.get("ta_busy"), "valu_busy": c.get("valu_busy")}
+        # the weight rows the kernel gathers (one d-row per kept entry) all
+        # pass through L2: a lower bound on its L2 bytes, against the L2 peak
+        l2 = fw["nnz_kept"] * w.d * s
+        rec[part].update({"l2_gathered_bytes": l2, "l2_GBps": l2 / (us * 1e-6) / 1e9,
+                          "l2_frac_of_peak": l2 / (us * 1e-6) / 1e9 / L2_PEAK_GBS})
     rec["note"] = ("effective_GBps: algorithmic bytes / in-sequence time (L2-served re-reads counted; not a "
                    "roofline fraction). up/down: rocprofv3 FETCH_SIZE + WRITE_SIZE per launch (scaled by a plain "
                    "copy; Infinity Cache hits included) over the kernel-trace average duration, from the committed "
                    "summary of these sources; ta_busy / valu_busy: TA_TA_BUSY and SQ_INSTS_VALU x 4 cycles over "
-                   "the elapsed cycles")
+                   "the elapsed cycles; l2_*: the gathered weight rows (one d-row per kept entry, a lower bound on "
+                   "the kernel's L2 traffic) over the kernel-trace duration, against the L2 peak of 8 XCDs x 16 "
+                   "channels x 128 B per clock at 2.4 GHz")
     return rec
 
 
