@@ -675,6 +675,21 @@ def gather_record(w, r):
         l2 = fw["nnz_kept"] * w.d * s
         rec[part].update({"l2_gathered_bytes": l2, "l2_GBps": l2 / (us * 1e-6) / 1e9,
                           "l2_frac_of_peak": l2 / (us * 1e-6) / 1e9 / L2_PEAK_GBS})
+    # compulsory bytes (each weight row, x, y and TwELL once) over the same
+    # time, against the spec and the measured streaming read; and the reuse
+    # factor of the algorithmic bytes over the counted fabric bytes
+    comp = rec["compulsory_bytes"]["up"] + rec["compulsory_bytes"]["down"]
+    rec["compulsory_frac_of_hbm_peak"] = comp / t / 1e9 / HBM_PEAK_GBS
+    probe_read = (r.get("probe") or {}).get("read_GBps")
+    rec["compulsory_frac_of_measured_read"] = comp / t / 1e9 / probe_read if probe_read else None
+    if rec.get("up") and rec.get("down"):
+        fab = rec["up"]["fabric_bytes"] + rec["down"]["fabric_bytes"]
+        rec["reuse_factor"] = r["gather_bytes"] / fab
+        # both gather kernels together: counted fabric bytes over their
+        # summed kernel-trace durations (Infinity Cache hits included)
+        both_s = (rec["up"]["trace_us"] + rec["down"]["trace_us"]) * 1e-6
+        rec["fabric_GBps_up_down"] = fab / both_s / 1e9
+        rec["fabric_frac_of_hbm_peak_up_down"] = fab / both_s / 1e9 / HBM_PEAK_GBS
     rec["note"] = ("effective_GBps: algorithmic bytes / in-sequence time (L2-served re-reads counted; not a "
                    "roofline fraction). up/down: rocprofv3 FETCH_SIZE + WRITE_SIZE per launch (scaled by a plain "
                    "copy; Infinity Cache hits included) over the kernel-trace average duration, from the committed "
@@ -747,6 +762,8 @@ def main():
                       "up_down_fallback_in_sequence": fw["rest_in_sequence_us"]},
         "gather": gather_record(w, r),
         "dense_mfma_tflops_warm": 3 * 2.0 * w.T * w.d * w.F / (fw["dense_warm"]["back_to_back_mean_us"] * 1e-6) / 1e12,
+        "dense_mfma_frac_of_peak": 3 * 2.0 * w.T * w.d * w.F / (fw["dense_warm"]["back_to_back_mean_us"] * 1e-6)
+        / 1e12 / MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else None,
         "hbm_copy_GBps": r["copy_gbs"],
         "hbm_probe": r["probe"],
         "workloads": extra,
