@@ -20,6 +20,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("TWELL_LIBRARY") or os.path.join(_HERE, "libtwell.so")
 
 TWELL_OK, TWELL_ERR_INVALID_ARG, TWELL_ERR_UNSUPPORTED, TWELL_ERR_WORKSPACE, TWELL_ERR_HIP = range(5)
+ABI_VERSION = 2  # TWELL_ABI_VERSION of include/twell.h that these mirrors follow
 TWELL_F32, TWELL_BF16 = 0, 1
 
 
@@ -31,6 +32,7 @@ class TwellMatrixC(ctypes.Structure):
         ("cap", ctypes.c_int32), ("dtype", ctypes.c_int), ("cnt", ctypes.c_void_p),
         ("val", ctypes.c_void_p), ("idx", ctypes.c_void_p), ("ovf_rows", ctypes.c_void_p),
         ("n_ovf", ctypes.c_void_p), ("dense", ctypes.c_void_p), ("ovf_cap", ctypes.c_int32),
+        ("u", ctypes.c_void_p),
     ]
 
 
@@ -41,7 +43,7 @@ class TwellHybridC(ctypes.Structure):
         ("rows", ctypes.c_int32), ("cols", ctypes.c_int32), ("width", ctypes.c_int32),
         ("dtype", ctypes.c_int), ("cnt", ctypes.c_void_p), ("val", ctypes.c_void_p),
         ("col", ctypes.c_void_p), ("dense_rows", ctypes.c_void_p), ("n_dense", ctypes.c_void_p),
-        ("dense", ctypes.c_void_p), ("dense_cap", ctypes.c_int32),
+        ("dense", ctypes.c_void_p), ("dense_cap", ctypes.c_int32), ("u", ctypes.c_void_p),
     ]
 
 
@@ -59,6 +61,10 @@ def _load():
         raise ImportError(f"{LIB_PATH} is missing: build it with "
                           "`python activation_sparse_transformer_bf16_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
+    lib.twell_abi_version.restype = ctypes.c_int
+    if lib.twell_abi_version() != ABI_VERSION:
+        raise ImportError(f"{LIB_PATH} has ABI version {lib.twell_abi_version()}, this binding needs {ABI_VERSION}: "
+                          "rebuild it")
     P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     M = ctypes.POINTER(TwellMatrixC)
     sig = {
@@ -197,10 +203,11 @@ class TwellMatrix:
     n_ovf: object        # int32 [1]
     dense: object        # dtype [ovf_cap, cols] or None
     ovf_cap: int
+    u: object = None     # float32 [rows, cols/tile, cap] (u saved by the forward) or None
 
     @classmethod
     def empty(cls, rows: int, cols: int, tile: int, cap: int, dtype, device,
-              ovf_cap: Optional[int] = None, dense: bool = True) -> "TwellMatrix":
+              ovf_cap: Optional[int] = None, dense: bool = True, u: bool = False) -> "TwellMatrix":
         torch = _torch()
         nt = cols // tile
         ovf_cap = rows if ovf_cap is None else ovf_cap
@@ -211,7 +218,8 @@ class TwellMatrix:
                    torch.empty((max(ovf_cap, 1),), dtype=torch.int32, device=device),
                    torch.empty((1,), dtype=torch.int32, device=device),
                    torch.empty((max(ovf_cap, 1), cols), dtype=dtype, device=device) if dense else None,
-                   ovf_cap)
+                   ovf_cap,
+                   torch.empty((rows, nt, cap), dtype=torch.float32, device=device) if u else None)
 
     def validate(self, device=None) -> None:
         """Check every buffer against the matrix's own fields (device, dtype,
@@ -234,11 +242,13 @@ class TwellMatrix:
             if self.dense.dim() != 2 or self.dense.shape[1] != self.cols or self.dense.shape[0] < self.ovf_cap:
                 raise ValueError(f"dense must have shape (>= {self.ovf_cap}, {self.cols}), "
                                  f"got {tuple(self.dense.shape)}")
+        if self.u is not None:
+            _need(self.u, "u", device, torch.float32, (self.rows, nt, self.cap))
 
     def c_struct(self) -> TwellMatrixC:
         return TwellMatrixC(self.rows, self.cols, self.tile, self.cap, _dtype_code(self.dtype),
                             _ptr(self.cnt), _ptr(self.val), _ptr(self.idx), _ptr(self.ovf_rows),
-                            _ptr(self.n_ovf), _ptr(self.dense), self.ovf_cap)
+                            _ptr(self.n_ovf), _ptr(self.dense), self.ovf_cap, _ptr(self.u))
 
     @property
     def device(self):
@@ -260,10 +270,11 @@ class TwellHybrid:
     n_dense: object      # int32 [1]
     dense: object        # dtype [dense_cap, cols] or None
     dense_cap: int
+    u: object = None     # float32 [rows, width] (saved u of the ELL slots) or None
 
     @classmethod
     def empty(cls, rows: int, cols: int, width: int, dtype, device, dense_cap: Optional[int] = None,
-              dense: bool = True) -> "TwellHybrid":
+              dense: bool = True, u: bool = False) -> "TwellHybrid":
         torch = _torch()
         dense_cap = rows if dense_cap is None else dense_cap
         return cls(rows, cols, width, dtype,
@@ -273,7 +284,8 @@ class TwellHybrid:
                    torch.empty((max(dense_cap, 1),), dtype=torch.int32, device=device),
                    torch.empty((1,), dtype=torch.int32, device=device),
                    torch.empty((max(dense_cap, 1), cols), dtype=dtype, device=device) if dense else None,
-                   dense_cap)
+                   dense_cap,
+                   torch.empty((rows, width), dtype=torch.float32, device=device) if u else None)
 
     def validate(self, device=None) -> None:
         """Check every buffer against the hybrid matrix's own fields."""
@@ -294,19 +306,23 @@ class TwellHybrid:
             if self.dense.dim() != 2 or self.dense.shape[1] != self.cols or self.dense.shape[0] < self.dense_cap:
                 raise ValueError(f"dense must have shape (>= {self.dense_cap}, {self.cols}), "
                                  f"got {tuple(self.dense.shape)}")
+        if self.u is not None:
+            _need(self.u, "u", device, torch.float32, (self.rows, self.width))
 
     def c_struct(self) -> TwellHybridC:
         return TwellHybridC(self.rows, self.cols, self.width, _dtype_code(self.dtype), _ptr(self.cnt),
                             _ptr(self.val), _ptr(self.col), _ptr(self.dense_rows), _ptr(self.n_dense),
-                            _ptr(self.dense), self.dense_cap)
+                            _ptr(self.dense), self.dense_cap, _ptr(self.u))
 
 
 def twell_to_hybrid(packed: TwellMatrix, width: int, dense_cap: Optional[int] = None, dense: bool = True,
                     out: Optional[TwellHybrid] = None) -> TwellHybrid:
-    """Convert a TwELL matrix (with its dense backup rows) to the hybrid format."""
+    """Convert a TwELL matrix (with its dense backup rows) to the hybrid format;
+    a new ``out`` carries the saved u when the TwELL matrix has one."""
     packed.validate()
     if out is None:
-        out = TwellHybrid.empty(packed.rows, packed.cols, width, packed.dtype, packed.device, dense_cap, dense)
+        out = TwellHybrid.empty(packed.rows, packed.cols, width, packed.dtype, packed.device, dense_cap, dense,
+                                u=packed.u is not None)
     out.validate(packed.device)
     if (out.rows, out.cols, out.width, out.dtype) != (packed.rows, packed.cols, width, packed.dtype):
         raise ValueError("out must be a hybrid matrix of the TwELL matrix's rows, cols and dtype at this width")

@@ -98,8 +98,14 @@ twell_status check_matrix(const twell_matrix *m, bool need_ovf_all) {
   if (need_ovf_all && m->ovf_cap < m->rows)
     return fail(TWELL_ERR_INVALID_ARG, "ovf_cap (%d) must be >= rows (%d)", m->ovf_cap, m->rows);
   if (!aligned(m->cnt, 2) || !aligned(m->val, dt_size(m->dtype)) || !aligned(m->ovf_rows, 4) ||
-      !aligned(m->n_ovf, 4) || !aligned(m->dense, 16))
+      !aligned(m->n_ovf, 4) || !aligned(m->dense, 16) || !aligned(m->u, 4))
     return fail(TWELL_ERR_UNSUPPORTED, "misaligned twell_matrix buffer");
+  return TWELL_OK;
+}
+
+// Producers of a TwELL matrix that do not compute u take u == NULL.
+twell_status check_no_u(const twell_matrix *m, const char *who) {
+  if (m->u != nullptr) return fail(TWELL_ERR_INVALID_ARG, "%s does not save u: packed->u must be NULL", who);
   return TWELL_OK;
 }
 
@@ -212,7 +218,8 @@ twell_status run_sparse(const twell_matrix *m, const void *x, const void *wg, co
 
   // The up kernel finds the overflow rows itself (row_flag); their list
   // follows, for the dense fallback.
-  SparseArgs sa{D, T, d, F, m->tile, m->cap, m->cnt, m->val, m->idx, row_flag, x, wu, wd, list, list_n, L.stride, y};
+  SparseArgs sa{D, T, d, F, m->tile, m->cap, m->cnt, m->val, m->idx, row_flag, x, wu, wd, list, list_n, L.stride, y,
+                m->u};
   TW_TRY(sparse_up(sa, s), "sparse up projection");
   TW_TRY(sparse_down(sa, s), "sparse down projection");
   return run_fallback(m, x, wg, wu, wd, beta, y, d, L, base, row_flag, s);
@@ -345,6 +352,7 @@ twell_status twell_pack(const void *pre, twell_matrix *out, void *stream) {
   g_err[0] = 0;
   twell_status st = check_matrix(out, false);
   if (st != TWELL_OK) return st;
+  if ((st = check_no_u(out, "twell_pack")) != TWELL_OK) return st;
   if (out->rows > 0 && pre == nullptr) return fail(TWELL_ERR_INVALID_ARG, "null pre");
   if (!aligned(pre, 16)) return fail(TWELL_ERR_UNSUPPORTED, "pre must be 16-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -413,13 +421,17 @@ twell_status twell_to_hybrid(const twell_matrix *packed, twell_hybrid *out, void
   if (T > 0 && packed->dense == nullptr)
     return fail(TWELL_ERR_INVALID_ARG, "the TwELL matrix needs its dense backup rows (packed->dense)");
   if (!aligned(out->cnt, 4) || !aligned(out->val, dt_size(out->dtype)) || !aligned(out->col, 4) ||
-      !aligned(out->dense_rows, 4) || !aligned(out->n_dense, 4) || !aligned(out->dense, dt_size(out->dtype)))
+      !aligned(out->dense_rows, 4) || !aligned(out->n_dense, 4) || !aligned(out->dense, dt_size(out->dtype)) ||
+      !aligned(out->u, 4))
     return fail(TWELL_ERR_UNSUPPORTED, "misaligned twell_hybrid buffer");
+  if (out->u != nullptr && packed->u == nullptr)
+    return fail(TWELL_ERR_INVALID_ARG, "out->u needs the TwELL matrix's saved u (packed->u)");
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (T == 0) return hip_check(zero_int(out->n_dense, s), "zero n_dense");
   HybridArgs ha{to_dt(packed->dtype), T, packed->cols, packed->tile, packed->cap, packed->cnt, packed->val,
                 packed->idx, packed->ovf_rows, packed->n_ovf, packed->ovf_cap, packed->dense, out->width,
-                out->cnt, out->val, out->col, out->dense_rows, out->n_dense, out->dense_cap, out->dense};
+                out->cnt, out->val, out->col, out->dense_rows, out->n_dense, out->dense_cap, out->dense,
+                out->u != nullptr ? packed->u : nullptr, out->u};
   TW_TRY(twell_to_hybrid_launch(ha, s), "TwELL to hybrid");
   return TWELL_OK;
 }
@@ -498,6 +510,7 @@ twell_status twell_sparse_ffn_fused(const twell_matrix *packed, const void *x, c
   g_err[0] = 0;
   twell_status st = check_matrix(packed, true);
   if (st != TWELL_OK) return st;
+  if ((st = check_no_u(packed, "twell_sparse_ffn_fused")) != TWELL_OK) return st;
   if ((st = check_d(d, (int)packed->dtype)) != TWELL_OK) return st;
   const int q = packed->dtype == TWELL_BF16 ? 512 : 256;
   if (d > 8 * q) return fail(TWELL_ERR_UNSUPPORTED, "fused kernel: d %d not built (<= %d)", d, 8 * q);
@@ -526,6 +539,7 @@ twell_status twell_sparse_ffn_grouped(const twell_matrix *packed, const void *x,
   g_err[0] = 0;
   twell_status st = check_matrix(packed, true);
   if (st != TWELL_OK) return st;
+  if ((st = check_no_u(packed, "twell_sparse_ffn_grouped")) != TWELL_OK) return st;
   if ((st = check_d(d, (int)packed->dtype)) != TWELL_OK) return st;
   const int q = packed->dtype == TWELL_BF16 ? 512 : 256;
   if (d > 8 * q) return fail(TWELL_ERR_UNSUPPORTED, "grouped fused kernel: d %d not built (<= %d)", d, 8 * q);
@@ -701,7 +715,8 @@ twell_status twell_ffn_backward(const twell_hybrid *h, const void *x, const void
   if (h->dense_cap > 0 && (h->dense_rows == nullptr || h->dense == nullptr))
     return fail(TWELL_ERR_INVALID_ARG, "dense_cap > 0 needs dense_rows and the dense backup rows");
   if (!aligned(h->cnt, 4) || !aligned(h->val, dt_size(h->dtype)) || !aligned(h->col, 4) ||
-      !aligned(h->dense_rows, 4) || !aligned(h->n_dense, 4) || !aligned(h->dense, dt_size(h->dtype)))
+      !aligned(h->dense_rows, 4) || !aligned(h->n_dense, 4) || !aligned(h->dense, dt_size(h->dtype)) ||
+      !aligned(h->u, 4))
     return fail(TWELL_ERR_UNSUPPORTED, "misaligned twell_hybrid buffer");
   if (!w_gate || !w_up || !w_down || !dw_gate || !dw_up || !dw_down)
     return fail(TWELL_ERR_INVALID_ARG, "null weight or weight-gradient pointer");
@@ -723,7 +738,7 @@ twell_status twell_ffn_backward(const twell_hybrid *h, const void *x, const void
                   reinterpret_cast<int *>(base + L.boff), reinterpret_cast<int *>(base + L.tot),
                   reinterpret_cast<int *>(base + L.colptr), reinterpret_cast<int *>(base + L.order),
                   bw_dense_mma(F), base + L.xr, base + L.dyr, base + L.du, base + L.dp, base + L.at,
-                  base + L.dut, base + L.dpt, reinterpret_cast<float *>(base + L.part), L.part_tiles};
+                  base + L.dut, base + L.dpt, reinterpret_cast<float *>(base + L.part), L.part_tiles, h->u};
   TW_TRY(ffn_backward(ba, static_cast<hipStream_t>(stream)), "FFN backward");
   return TWELL_OK;
 }

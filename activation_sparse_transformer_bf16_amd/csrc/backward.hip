@@ -59,6 +59,7 @@ struct RowSrc {
   const int *dn;          // [dense_cap] their lengths
   int T, F, width;
   bool dense_mma;         // dense rows go to the matrix-core kernels: empty lists here
+  const float *u;         // [T][width] saved u of the ELL slots (NaN in slot 0: not saved), or null
 };
 
 // The entry list of row t: the hybrid's ELL slots, or the compacted columns
@@ -350,6 +351,9 @@ __global__ __launch_bounds__(SP_THREADS) void k_bw_entries(RowSrc<typename DtT<D
       xr[c] = *reinterpret_cast<const u32x4_t *>(xt + (c * 64 + lane) * EPC);
       gr[c] = *reinterpret_cast<const u32x4_t *>(dyt + (c * 64 + lane) * EPC);
     }
+    // the row's u saved by the forward (an ELL row whose first slot holds a
+    // number): only the W_d rows are gathered
+    const bool saved = s.u != nullptr && L.r < 0 && !__builtin_isnan(s.u[(size_t)t * s.width]);
     for (int e0 = eb; e0 < ee; e0 += 64) {
       const int ne = min(64, ee - e0);
       // the lane's entry of this chunk (the last one repeated past the end)
@@ -358,6 +362,43 @@ __global__ __launch_bounds__(SP_THREADS) void k_bw_entries(RowSrc<typename DtT<D
       const uint32_t moff = (uint32_t)j * row_bytes;
       const float hv = L.r < 0 ? to_f32(s.val[(size_t)t * s.width + i]) : to_f32(s.dense[(size_t)L.r * s.F + j]);
       const int pv = pos[L.slot0 + i];
+      if (saved) {
+        const float uv = s.u[(size_t)t * s.width + i];
+        for (int u0 = 0; u0 < ne; u0 += U) {
+          u32x4_t b[U][NC];
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            const uint32_t off = read_lane(moff, min(u0 + u, ne - 1));
+            if (u0 + u < ne) {
+#pragma unroll
+              for (int c = 0; c < NC; ++c) b[u][c] = buffer_load<u32x4_t>(wdr, lane_off + c * 1024, off);
+            } else {
+#pragma unroll
+              for (int c = 0; c < NC; ++c) b[u][c] = u32x4_t{0u, 0u, 0u, 0u};
+            }
+          }
+          float p[U];
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            p[u] = 0.f;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) p[u] = dot16(gr[c], b[u][c], p[u], TT());
+          }
+          // after Reduce<U> the storer lanes hold da of their entry (the same
+          // lanes and entries as below)
+          const float da = Reduce<U>::run(p);
+          const int src = min(u0 + my, ne - 1);
+          const float h = __shfl(hv, src, 64);
+          const int pp = __shfl(pv, src, 64);
+          const float uu = __shfl(uv, src, 64);
+          if (storer && u0 + my < ne) {
+            const float du = da * h, dp = fmaf(da, uu, lam), av = h * uu;
+            ent[L.slot0 + e0 + u0 + my] = f32x2_t{du, dp};
+            csc[pp] = u32x4_t{(uint32_t)t, __float_as_uint(av), __float_as_uint(du), __float_as_uint(dp)};
+          }
+        }
+        continue;
+      }
       for (int u0 = 0; u0 < ne; u0 += U) {
         u32x4_t a[U][NC], b[U][NC];
 #pragma unroll
@@ -649,7 +690,7 @@ template <Dt D>
 static hipError_t launch_backward(const BackwardArgs &a, hipStream_t st) {
   using TT = typename DtT<D>::T;
   RowSrc<TT> s{a.cnt, (const TT *)a.val, a.col, a.dense_rows, a.n_dense, a.dense_cap, (const TT *)a.dense,
-               a.dcol, a.dn, a.T, a.F, a.width, a.dense_mma};
+               a.dcol, a.dn, a.T, a.F, a.width, a.dense_mma, a.u};
   hipError_t e;
   const int NB = bw_blocks(a.T);
   const int mask_lds = a.F * 8;

@@ -9,7 +9,9 @@
 //                   TwELL slots (one lane per tile, positions from a prefix
 //                   count over the tiles), or, when it overflowed TwELL, by a
 //                   ballot compaction of its dense backup row.  Other rows get
-//                   all-padding ELL slots.
+//                   all-padding ELL slots.  With saved u, an ELL row from
+//                   TwELL slots copies the slots' u too; one from the dense
+//                   backup marks its u as not saved (NaN in its first slot).
 //   k_compact_gt:   ascending list of the rows with more than `width` entries.
 //   k_hybrid_dense: one workgroup per listed row: the dense backup row, copied
 //                   from TwELL's dense backup or scattered from the slots.
@@ -27,7 +29,8 @@ __global__ __launch_bounds__(64 * HY_WAVES) void k_hybrid_rows(
     const uint16_t *__restrict__ cnt, const typename DtT<D>::T *__restrict__ val, const uint8_t *__restrict__ idx,
     const int *__restrict__ ovf_rows, const int *__restrict__ n_ovf, int ovf_cap,
     const typename DtT<D>::T *__restrict__ tw_dense, int T, int F, int tile, int cap, int width,
-    int *__restrict__ out_cnt, typename DtT<D>::T *__restrict__ out_val, int *__restrict__ out_col) {
+    int *__restrict__ out_cnt, typename DtT<D>::T *__restrict__ out_val, int *__restrict__ out_col,
+    const float *__restrict__ tw_u, float *__restrict__ out_u) {
   using TT = typename DtT<D>::T;
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * HY_WAVES + (threadIdx.x >> 6);
@@ -63,12 +66,15 @@ __global__ __launch_bounds__(64 * HY_WAVES) void k_hybrid_rows(
           if (pos0 + s < width) {
             vrow[pos0 + s] = val[slot0 + s];
             crow_out[pos0 + s] = k * tile + (idx[slot0 + s] & (tile - 1));
+            if (out_u != nullptr) out_u[(size_t)t * width + pos0 + s] = tw_u[slot0 + s];
           }
         }
         before += __builtin_amdgcn_readlane(incl, 63);
       }
     } else {
       // the TwELL slots lost entries of this row: compact its dense backup row
+      // (its u was not saved)
+      if (out_u != nullptr && lane == 0) out_u[(size_t)t * width] = __builtin_nanf("");
       const int r = find_row(ovf_rows, min(*n_ovf, ovf_cap), t);
       const TT *drow = tw_dense + (size_t)max(r, 0) * F;
       int before = 0;
@@ -160,7 +166,7 @@ static hipError_t launch_hybrid(const HybridArgs &a, hipStream_t s) {
   using TT = typename DtT<D>::T;
   hipLaunchKernelGGL(k_hybrid_rows<D>, dim3((a.T + HY_WAVES - 1) / HY_WAVES), dim3(64 * HY_WAVES), 0, s, a.cnt,
                      (const TT *)a.val, a.idx, a.ovf_rows, a.n_ovf, a.ovf_cap, (const TT *)a.tw_dense, a.T, a.F,
-                     a.tile, a.cap, a.width, a.out_cnt, (TT *)a.out_val, a.out_col);
+                     a.tile, a.cap, a.width, a.out_cnt, (TT *)a.out_val, a.out_col, a.tw_u, a.out_u);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_compact_gt, dim3(1), dim3(HY_COMPACT_THREADS), 0, s, a.out_cnt, a.T, a.width, a.dense_rows,

@@ -89,6 +89,7 @@ struct SparseArgs {
   int *list_n;              // [T] entries per row
   int stride;               // list entries per row: nt * cap rounded up to a multiple of 8
   void *y;                  // [T][d]
+  float *u = nullptr;       // [T][nt][cap] saved u per TwELL slot (NaN for overflow rows), or null
 };
 hipError_t sparse_up(const SparseArgs &a, hipStream_t s);
 hipError_t sparse_down(const SparseArgs &a, hipStream_t s);
@@ -201,6 +202,8 @@ struct HybridArgs {
   int *n_dense;          // [1]
   int dense_cap;
   void *out_dense;       // [dense_cap][F] or null
+  const float *tw_u = nullptr;  // TwELL saved u [T][F/tile][cap], or null
+  float *out_u = nullptr;       // hybrid saved u [T][width], or null
 };
 hipError_t twell_to_hybrid_launch(const HybridArgs &a, hipStream_t s);
 
@@ -260,6 +263,7 @@ struct BackwardArgs {
   void *bd_at, *bd_dut, *bd_dpt;   // [F][ns * rcp] a, du, dpre transposed (bf16: high, then low parts)
   float *bd_part;                  // dx split-K partial tiles
   int bd_part_tiles;               // their capacity in 256 x 256 fp32 tiles
+  const float *u = nullptr;        // hybrid's saved u [T][width] or null
 };
 hipError_t ffn_backward(const BackwardArgs &a, hipStream_t s);
 // The dense rows' part, launched by ffn_backward: their dx rows (U, DA, and

@@ -22,6 +22,7 @@
 #include "gather.hpp"
 #include "launch.hpp"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace twell {
@@ -205,6 +206,9 @@ hipError_t compact_rows_in_place(int *flags_then_rows, int T, int *n_ovf, hipStr
 }
 
 __global__ void k_zero_int(int *p) { *p = 0; }
+__global__ void k_fill_f32(float *p, size_t n, float v) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = v;
+}
 hipError_t zero_int(int *p, hipStream_t s) {
   hipLaunchKernelGGL(k_zero_int, dim3(1), dim3(1), 0, s, p);
   return hipGetLastError();
@@ -224,7 +228,10 @@ hipError_t zero_int(int *p, hipStream_t s) {
 //           h, u over the second half): part 0 writes the first 8 bytes,
 //           part 1 the last 8; the down kernel forms v = round(h * (u0 + u1));
 // for e < list_n[t], and padding entries (NO_ROW, 0...) up to the next
-// multiple of 8.  A row overflows
+// multiple of 8.  With u_out non-null the wave also saves u of every entry at
+// its TwELL slot: DC = 1 stores it, DC = 2 adds each half's partial sum to a
+// slot zeroed beforehand (two fp32 addends: the sum does not depend on their
+// order); the slots of an overflow row get NaN.  A row overflows
 // iff one of its tiles counts more than cap entries; every wave decides that
 // from the row's counts, skips such rows, and the group-0 wave records
 // row_flag[t] (1 for an overflow row) and list_n[t] = -1 for them.  A local
@@ -235,7 +242,7 @@ struct UpEntry {
   uint32_t off;   // byte offset of the unit's row in W_u^T (and in W_d)
   uint32_t dst;   // index of the entry in the compact list
   float h;        // the gate activation
-  uint32_t pad;
+  uint32_t slot;  // the entry's TwELL slot (where u is saved)
 };
 
 template <Dt D, int NC, int U, int DC>
@@ -244,7 +251,7 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_up(
     const uint16_t *__restrict__ cnt, const typename DtT<D>::T *__restrict__ val,
     const uint8_t *__restrict__ idx, uint8_t *__restrict__ row_flag, void *__restrict__ list_v,
     int *__restrict__ list_n, int stride, int T, int d, int nt, int tile, int cap, int tpg, int n_groups,
-    int tok_per_wg, int n_tb) {
+    int tok_per_wg, int n_tb, float *__restrict__ u_out) {
   using TT = typename DtT<D>::T;
   constexpr int EPC = 16 / sizeof(TT);  // elements per 16-byte chunk
   static_assert(DC == 1 || DC == 2, "d whole or in two halves");
@@ -302,7 +309,12 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_up(
         if constexpr (DC == 2) list[(lbase + sum + lane) * 2 + 1] = u32x2_t{0u, 0u};
       }
     }
-    if (ovf) continue;
+    const size_t gslot0 = ((size_t)t * nt + k0) * cap;  // first slot of the group
+    if (ovf) {
+      if (u_out != nullptr && part == 0)
+        for (int q = lane; q < kn * cap; q += 64) u_out[gslot0 + q] = __builtin_nanf("");
+      continue;
+    }
     const int before = g == 0 ? 0 : sum;
     // The group's entries into the wave list.  Tile k0 + q has n(q) entries
     // (lane q, q < kn <= 64); its slots are contiguous after those of tile q-1,
@@ -311,7 +323,6 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_up(
     const int n = lane < kn ? min((int)crow[k0 + lane], cap) : 0;
     const int incl = wave_incl_scan(n);
     const int E = __builtin_amdgcn_readlane(incl, 63);
-    const size_t gslot0 = ((size_t)t * nt + k0) * cap;  // first slot of the group
     for (int q0 = 0; q0 < kn * cap; q0 += 64) {
       const int q = q0 + lane;
       const int kq = q / cap, sq = q - kq * cap;
@@ -322,7 +333,7 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_up(
         en.off = (uint32_t)((k0 + kq) * tile + (idx[gslot0 + q] & (tile - 1))) * row_bytes;
         en.dst = (uint32_t)(before + oq);
         en.h = to_f32(val[gslot0 + q]);
-        en.pad = 0;
+        en.slot = (uint32_t)(gslot0 + q);
         L[oq] = en;
       }
     }
@@ -367,9 +378,11 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_up(
             const float v = mine.h * tot;
             const uint32_t vb = D == Dt::BF16 ? (uint32_t)bf16_rne(v) : __float_as_uint(v);
             list[lbase + mine.dst] = u32x2_t{mine.off, vb};
+            if (u_out != nullptr) u_out[mine.slot] = tot;
           } else {
             list[(lbase + mine.dst) * 2 + part] =
                 part == 0 ? u32x2_t{mine.off, __float_as_uint(tot)} : u32x2_t{__float_as_uint(mine.h), __float_as_uint(tot)};
+            if (u_out != nullptr) atomicAdd(u_out + mine.slot, tot);
           }
         }
       }
@@ -517,9 +530,16 @@ static hipError_t launch_up(const SparseArgs &a, const UpPlan &p, hipStream_t s)
   const int tok = 16;
   const int n_tb = (a.T + tok - 1) / tok;
   constexpr int U = NC <= 4 ? 4 : 2;
+  if (DC == 2 && a.u != nullptr) {  // the halves are added into zeroed slots
+    const size_t n = (size_t)a.T * nt * a.cap;
+    hipLaunchKernelGGL(k_fill_f32, dim3((unsigned)std::min<size_t>((n + 255) / 256, 4096)), dim3(256), 0, s, a.u,
+                       n, 0.0f);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL((k_sparse_up<D, NC, U, DC>), dim3(padded_groups(p.n_groups * DC) * n_tb), dim3(SP_THREADS), 0,
                      s, (const TT *)a.x, (const TT *)a.wu, a.cnt, (const TT *)a.val, a.idx, a.row_flag, a.list,
-                     a.list_n, a.stride, a.T, a.d, nt, a.tile, a.cap, p.tpg, p.n_groups, tok, n_tb);
+                     a.list_n, a.stride, a.T, a.d, nt, a.tile, a.cap, p.tpg, p.n_groups, tok, n_tb, a.u);
   return hipGetLastError();
 }
 

@@ -292,6 +292,13 @@ def backward_timing(w, hy, x, wg, wu, wd, b, nnz_all, steps, warmup, want_torch)
     dwb = [torch.empty((F, d), dtype=torch.float32, device=dev) for _ in range(3)]
     bw = lambda: tw.twell_ffn_backward(hy, x, wg, wu, wd, dy, L1_LAMBDA, dxb, *dwb, workspace=bw_ws)
     ms_bw, _ = event_time(bw, steps, warmup)
+    # the same without the forward's saved u (the backward gathers W_u rows
+    # again to recompute it)
+    ms_bw_recompute = None
+    if hy.u is not None:
+        saved_u, hy.u = hy.u, None
+        ms_bw_recompute, _ = event_time(bw, steps, warmup)
+        hy.u = saved_u
     # gathered per active entry: W_u and W_d rows (entry gradients), W_u and
     # W_g rows (dx), x and dy rows (weight gradients); plus the weight
     # gradients written once and the x / dy / dx rows
@@ -300,6 +307,8 @@ def backward_timing(w, hy, x, wg, wu, wd, b, nnz_all, steps, warmup, want_torch)
     # weight gradients written once
     bw_comp = 3 * F * d * s + 3 * T * d * s + 3 * F * d * 4
     backward = {"us": ms_bw * 1e3, "tokens_per_s": T / (ms_bw * 1e-3), "hybrid_width": HYBRID_WIDTH,
+                "saved_u": hy.u is not None,
+                "us_recomputing_u": ms_bw_recompute * 1e3 if ms_bw_recompute is not None else None,
                 "n_dense": n_dense, "entries": nnz_all, "bytes_alg": bw_bytes,
                 "effective_GBps": bw_bytes / (ms_bw * 1e-3) / 1e9,
                 "compulsory_bytes": bw_comp,
@@ -309,7 +318,8 @@ def backward_timing(w, hy, x, wg, wu, wd, b, nnz_all, steps, warmup, want_torch)
                         "(an effective rate: L2-served re-reads counted, not a roofline fraction); "
                         "compulsory = each weight row, x, dy, dx and the weight gradients once"}
     log(f"[bench] {w.name} backward {ms_bw * 1e3:.1f} us ({n_dense} dense rows; "
-        f"{backward['effective_GBps']:.0f} GB/s effective)")
+        f"{backward['effective_GBps']:.0f} GB/s effective)"
+        + (f"; recomputing u {ms_bw_recompute * 1e3:.1f} us" if ms_bw_recompute is not None else ""))
     if want_torch:
         import torch.nn.functional as Fn
         hd = torch.relu(torch.addmm(b[:, None].to(x.dtype), x, wg.t()))
@@ -372,9 +382,9 @@ def measure(w, steps, warmup, want_torch=True, want_cold=True):
     # Training-format kernels on this batch's TwELL matrix (with its dense
     # backup rows): TwELL -> hybrid at an ELL width of 256, the L1 norm and the
     # L1 gradient.
-    packed_tr = tw.TwellMatrix.empty(T, F, w.tile, w.cap, x.dtype, dev, T, dense=True)
+    packed_tr = tw.TwellMatrix.empty(T, F, w.tile, w.cap, x.dtype, dev, T, dense=True, u=True)
     tw.twell_ffn_forward(x, wg, wu, wd, b, packed=packed_tr, y=y, workspace=ws)
-    hy = tw.TwellHybrid.empty(T, F, HYBRID_WIDTH, x.dtype, dev)
+    hy = tw.TwellHybrid.empty(T, F, HYBRID_WIDTH, x.dtype, dev, u=True)
     l1_out = torch.empty((1,), dtype=torch.float64, device=dev)
     l1_ws = torch.empty((tw.twell_l1_workspace_size(),), dtype=torch.uint8, device=dev)
     gval, gdense = torch.empty_like(packed_tr.val), torch.empty_like(packed_tr.dense)
@@ -393,9 +403,13 @@ def measure(w, steps, warmup, want_torch=True, want_cold=True):
     # matrix (cnt, val, idx and its dense backup rows), and the hybrid
     # format (cnt, ELL values and int32 columns, the dense row list and rows).
     n_ovf_tr = int(packed_tr.n_ovf.item())
+    # The saved u (fp32 per TwELL slot, then per ELL entry) is counted apart:
+    # it trades memory for the backward's W_u gather.
     mem = {"dense_h_bytes": T * F * s,
            "twell_bytes": T * nt * (2 + w.cap * (s + 1)) + n_ovf_tr * (4 + F * s),
-           "hybrid_bytes": T * 4 + T * HYBRID_WIDTH * (s + 4) + n_dense * (4 + F * s)}
+           "hybrid_bytes": T * 4 + T * HYBRID_WIDTH * (s + 4) + n_dense * (4 + F * s),
+           "twell_saved_u_bytes": T * nt * w.cap * 4,
+           "hybrid_saved_u_bytes": T * HYBRID_WIDTH * 4}
     mem["twell_over_dense"] = mem["twell_bytes"] / mem["dense_h_bytes"]
     mem["hybrid_over_dense"] = mem["hybrid_bytes"] / mem["dense_h_bytes"]
     log(f"[bench] activation memory: dense {mem['dense_h_bytes'] / 2**20:.0f} MiB, TwELL "
@@ -513,9 +527,9 @@ def extra_workloads(args, base_inp):
             # the backward on the skewed batch: its hot rows are the hybrid's
             # dense backup rows
             ws = bufs[2]
-            packed_tr = tw.TwellMatrix.empty(w.T, w.F, w.tile, w.cap, x.dtype, dev, w.T, dense=True)
+            packed_tr = tw.TwellMatrix.empty(w.T, w.F, w.tile, w.cap, x.dtype, dev, w.T, dense=True, u=True)
             tw.twell_ffn_forward(x, wg, wu, wd, b, packed=packed_tr, y=bufs[1], workspace=ws)
-            hy = tw.TwellHybrid.empty(w.T, w.F, HYBRID_WIDTH, x.dtype, dev)
+            hy = tw.TwellHybrid.empty(w.T, w.F, HYBRID_WIDTH, x.dtype, dev, u=True)
             tw.twell_to_hybrid(packed_tr, HYBRID_WIDTH, out=hy)
             torch.cuda.synchronize()
             nnz_all = int(packed_tr.cnt.cpu().numpy().view(np.uint16).astype(np.int64).sum())

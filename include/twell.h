@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define TWELL_ABI_VERSION 1
+#define TWELL_ABI_VERSION 2
 
 /* The enums are int-sized.  Compiled as C++ they have the fixed underlying
  * type int, so any int a C caller stores in one is a value of the type, which
@@ -110,6 +110,15 @@ typedef enum TWELL_ENUM_BASE { TWELL_F32 = 0, TWELL_BF16 = 1 } twell_dtype;
  *     dense[r][:]        ReLU of overflow row ovf_rows[r] (active values bit
  *                        for bit, +0 elsewhere), r < min(n_ovf, ovf_cap);
  *                        the dense backup of the hybrid format.
+ *     u[t][k][s]         optional (NULL: none): for a row that did not
+ *                        overflow, the up-projection value x_t . W_u[j] (fp32)
+ *                        of the unit j of each used slot, saved by the forward
+ *                        (twell_ffn_forward, twell_ffn_forward_noalloc,
+ *                        twell_sparse_ffn) so that the backward need not
+ *                        recompute it; every slot of an overflow row holds
+ *                        NaN (not saved).  Slots past the count are not
+ *                        written.  The other producers of a TwELL matrix
+ *                        (twell_pack) and the fused prototypes take u == NULL.
  */
 typedef struct {
   int32_t rows, cols;   /* T, F; cols % tile == 0 */
@@ -123,6 +132,7 @@ typedef struct {
   int32_t *n_ovf;       /* [1] */
   void *dense;          /* [ovf_cap][cols], dtype; may be NULL (not written) */
   int32_t ovf_cap;      /* rows available in ovf_rows (and dense when non-NULL) */
+  float *u;             /* [rows][cols/tile][cap] fp32, or NULL (see above) */
 } twell_matrix;
 
 /* ABI version of the loaded library (TWELL_ABI_VERSION). */
@@ -185,7 +195,10 @@ size_t twell_ffn_workspace_size(int T, int d, int F, int tile, int cap, twell_dt
  * packed: caller-owned TwELL buffers with rows == T, cols == F; tile, cap and
  * dtype select the format and the arithmetic.  packed->ovf_cap must be >= T so
  * that no overflowing row can be dropped.  On return (after the stream
- * completes) *packed describes round(pre) exactly as twell_pack would.
+ * completes) *packed describes round(pre) exactly as twell_pack would.  With
+ * packed->u non-NULL the up projection also saves u = x_t . W_u[j] (fp32) of
+ * every used slot of a non-overflow row, and NaN in every slot of an
+ * overflow row (the training forward: the backward then skips one gather).
  * y: [T][d] in the storage dtype, fully written.
  * workspace: device buffer of at least twell_ffn_workspace_size() bytes,
  * 256-byte aligned; its contents on entry do not matter (layout above).  The
@@ -295,6 +308,11 @@ twell_status dense_ffn_forward(const void *x, const void *w_gate, const void *w_
  *                        true count, only the first dense_cap are listed) and
  *                        dense[r][:] holds ReLU(row dense_rows[r]) when dense
  *                        is non-NULL.
+ *     u[t][s]            optional (NULL: none): for an ELL row, the saved
+ *                        up-projection value of slot s < cnt[t] (fp32), from
+ *                        the TwELL matrix's u; NaN in u[t][0] marks a row whose
+ *                        u was not saved (its TwELL row overflowed).  Other
+ *                        slots are not written.
  */
 typedef struct {
   int32_t rows, cols;    /* T, F: as the TwELL matrix converted */
@@ -307,6 +325,7 @@ typedef struct {
   int32_t *n_dense;      /* [1] */
   void *dense;           /* [dense_cap][cols], dtype; may be NULL (not written) */
   int32_t dense_cap;     /* rows available in dense_rows (and dense) */
+  float *u;              /* [rows][width] fp32, or NULL (see above) */
 } twell_hybrid;
 
 /*
@@ -317,6 +336,8 @@ typedef struct {
  * packed->dense must be non-NULL and packed->ovf_cap >= packed->rows (as
  * written by twell_pack, or by twell_ffn_forward with a dense buffer).
  * out: caller-owned buffers with rows, cols and dtype equal to packed's.
+ * out->u non-NULL: the saved u of the ELL rows is copied from packed->u, which
+ * must then be non-NULL.
  * Errors: INVALID_ARG, UNSUPPORTED (alignment), HIP.
  */
 twell_status twell_to_hybrid(const twell_matrix *packed, twell_hybrid *out, void *stream);
@@ -409,7 +430,9 @@ twell_status twell_sparse_ffn_grouped(const twell_matrix *packed, const void *x,
  * h:      the activations (rows T, cols F, width, dtype); every dense row must
  *         be listed and stored: dense_cap >= *n_dense and dense non-NULL when
  *         dense_cap > 0 (a dense row that is not stored contributes nothing);
- *         dense 16-byte aligned when F is a multiple of 128.
+ *         dense 16-byte aligned when F is a multiple of 128.  h->u non-NULL:
+ *         the ELL rows with a saved u take it from there instead of gathering
+ *         W_u rows again (the others, and the dense rows, recompute it).
  * x, dy:  [T][d] dtype;  w_gate, w_up, w_down: [F][d] dtype (as the forward).
  * dx:     [T][d] dtype, overwritten (one rounding of fp32 sums).
  * dw_gate, dw_up, dw_down: [F][d] fp32, overwritten.

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert twell.twell_abi_version() == 1
+    assert twell.twell_abi_version() == twell.ABI_VERSION == 2
     assert twell.twell_status_str(twell.TWELL_OK) == "ok"
     assert "workspace" in twell.twell_status_str(twell.TWELL_ERR_WORKSPACE)
     assert twell.twell_status_str(99) == "unknown status"
@@ -106,6 +106,23 @@ def test_sparse_ffn_and_gate_pack_validation():
     assert L.twell_gate_pack(None, FAKE, None, 512, ctypes.byref(m), None, None) == twell.TWELL_ERR_INVALID_ARG
     assert L.twell_gate_pack(FAKE, FAKE, None, 512, ctypes.byref(m), FAKE + 8,
                              None) == twell.TWELL_ERR_UNSUPPORTED
+
+
+def test_saved_u_validation():
+    """Only the forward saves u: the other producers of a TwELL matrix reject
+    one, the hybrid conversion needs the TwELL u to fill the hybrid's, and a
+    misaligned u is rejected (all before any launch)."""
+    m = _matrix(u=FAKE)
+    assert L.twell_pack(FAKE, ctypes.byref(m), None) == twell.TWELL_ERR_INVALID_ARG
+    for f in (L.twell_sparse_ffn_fused, L.twell_sparse_ffn_grouped):
+        assert f(ctypes.byref(m), FAKE, FAKE, FAKE, FAKE, None, FAKE, 512, FAKE, 1 << 40,
+                 None) == twell.TWELL_ERR_INVALID_ARG
+    assert L.twell_sparse_ffn(ctypes.byref(_matrix(u=FAKE + 2)), FAKE, FAKE, FAKE, FAKE, None, FAKE, 512, FAKE,
+                              1 << 40, None) == twell.TWELL_ERR_UNSUPPORTED
+    H = L.twell_to_hybrid
+    assert H(ctypes.byref(_matrix(dense=FAKE)), ctypes.byref(_hybrid(u=FAKE)), None) == twell.TWELL_ERR_INVALID_ARG
+    assert H(ctypes.byref(_matrix(dense=FAKE, u=FAKE)), ctypes.byref(_hybrid(u=FAKE + 2)),
+             None) == twell.TWELL_ERR_UNSUPPORTED
 
 
 def test_dense_validation():
