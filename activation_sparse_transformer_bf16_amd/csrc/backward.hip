@@ -343,17 +343,18 @@ __global__ __launch_bounds__(SP_THREADS) void k_bw_entries(RowSrc<typename DtT<D
     const int eb = wave_lower_bound(L.col, L.n, j0);
     const int ee = wave_lower_bound(L.col, L.n, j1);
     if (eb >= ee) continue;
+    // the row's u saved by the forward (an ELL row whose first slot holds a
+    // number): x_t is not needed and only the W_d rows are gathered
+    const bool saved = s.u != nullptr && L.r < 0 && !__builtin_isnan(s.u[(size_t)t * s.width]);
     const TT *xt = x + (size_t)t * d;
     const TT *dyt = dy + (size_t)t * d;
     u32x4_t xr[NC], gr[NC];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      xr[c] = *reinterpret_cast<const u32x4_t *>(xt + (c * 64 + lane) * EPC);
-      gr[c] = *reinterpret_cast<const u32x4_t *>(dyt + (c * 64 + lane) * EPC);
+    for (int c = 0; c < NC; ++c) gr[c] = *reinterpret_cast<const u32x4_t *>(dyt + (c * 64 + lane) * EPC);
+    if (!saved) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) xr[c] = *reinterpret_cast<const u32x4_t *>(xt + (c * 64 + lane) * EPC);
     }
-    // the row's u saved by the forward (an ELL row whose first slot holds a
-    // number): only the W_d rows are gathered
-    const bool saved = s.u != nullptr && L.r < 0 && !__builtin_isnan(s.u[(size_t)t * s.width]);
     for (int e0 = eb; e0 < ee; e0 += 64) {
       const int ne = min(64, ee - e0);
       // the lane's entry of this chunk (the last one repeated past the end)
@@ -673,8 +674,10 @@ template <Dt D, int NC>
 static hipError_t launch_entries(const BackwardArgs &a, const RowSrc<typename DtT<D>::T> &s, hipStream_t st) {
   using TT = typename DtT<D>::T;
   constexpr int U = NC <= 4 ? 2 : 1;
-  // hidden units per group: about 4 MB of W_u and W_d rows (one XCD's L2)
-  const size_t unit_bytes = (size_t)2 * a.d * sizeof(TT);
+  // hidden units per group: about 4 MB of W_u and W_d rows (one XCD's L2);
+  // of W_d rows only when the forward's u is given (rows without a saved u
+  // then gather from twice that)
+  const size_t unit_bytes = (size_t)(a.u != nullptr ? 1 : 2) * a.d * sizeof(TT);
   int upg = (int)std::max<size_t>(64, ((size_t)4 << 20) / unit_bytes);
   upg = std::min(upg, a.F);
   const int n_groups = (a.F + upg - 1) / upg;
