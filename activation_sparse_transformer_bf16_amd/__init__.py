@@ -20,8 +20,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("TWELL_LIBRARY") or os.path.join(_HERE, "libtwell.so")
 
 TWELL_OK, TWELL_ERR_INVALID_ARG, TWELL_ERR_UNSUPPORTED, TWELL_ERR_WORKSPACE, TWELL_ERR_HIP = range(5)
-ABI_VERSION = 2  # TWELL_ABI_VERSION of include/twell.h that these mirrors follow
+ABI_VERSION = 3  # TWELL_ABI_VERSION of include/twell.h that these mirrors follow
 TWELL_F32, TWELL_BF16 = 0, 1
+TWELL_LAYOUT_ROWS, TWELL_LAYOUT_TILES = 0, 1
 
 
 class TwellMatrixC(ctypes.Structure):
@@ -32,8 +33,11 @@ class TwellMatrixC(ctypes.Structure):
         ("cap", ctypes.c_int32), ("dtype", ctypes.c_int), ("cnt", ctypes.c_void_p),
         ("val", ctypes.c_void_p), ("idx", ctypes.c_void_p), ("ovf_rows", ctypes.c_void_p),
         ("n_ovf", ctypes.c_void_p), ("dense", ctypes.c_void_p), ("ovf_cap", ctypes.c_int32),
-        ("u", ctypes.c_void_p),
+        ("u", ctypes.c_void_p), ("layout", ctypes.c_int),
     ]
+
+
+LAYOUTS = {"rows": TWELL_LAYOUT_ROWS, "tiles": TWELL_LAYOUT_TILES}  # twell_layout: record (t, k) at t * nt + k, or at k * rows + t
 
 
 class TwellHybridC(ctypes.Structure):
@@ -196,30 +200,36 @@ class TwellMatrix:
     tile: int
     cap: int
     dtype: object        # torch dtype of the values
-    cnt: object          # int16 [rows, cols/tile] (uint16 bit patterns)
-    val: object          # dtype [rows, cols/tile, cap]
-    idx: object          # uint8 [rows, cols/tile, cap]
+    cnt: object          # int16 [rows, cols/tile] (uint16 bit patterns); tile-major: [cols/tile, rows]
+    val: object          # dtype [rows, cols/tile, cap]; tile-major: [cols/tile, rows, cap]
+    idx: object          # uint8 [rows, cols/tile, cap]; tile-major: [cols/tile, rows, cap]
     ovf_rows: object     # int32 [ovf_cap]
     n_ovf: object        # int32 [1]
     dense: object        # dtype [ovf_cap, cols] or None
     ovf_cap: int
     u: object = None     # float32 [rows, cols/tile, cap] (u saved by the forward) or None
+    layout: str = "rows"  # "rows" (row-major records) or "tiles" (tile-major, see twell_matrix)
 
     @classmethod
     def empty(cls, rows: int, cols: int, tile: int, cap: int, dtype, device,
-              ovf_cap: Optional[int] = None, dense: bool = True, u: bool = False) -> "TwellMatrix":
+              ovf_cap: Optional[int] = None, dense: bool = True, u: bool = False,
+              layout: str = "rows") -> "TwellMatrix":
         torch = _torch()
         nt = cols // tile
         ovf_cap = rows if ovf_cap is None else ovf_cap
+        if layout not in LAYOUTS:
+            raise ValueError(f"layout must be one of {sorted(LAYOUTS)}, got {layout!r}")
+        r2 = (rows, nt) if layout == "rows" else (nt, rows)
         return cls(rows, cols, tile, cap, dtype,
-                   torch.empty((rows, nt), dtype=torch.int16, device=device),
-                   torch.empty((rows, nt, cap), dtype=dtype, device=device),
-                   torch.empty((rows, nt, cap), dtype=torch.uint8, device=device),
+                   torch.empty(r2, dtype=torch.int16, device=device),
+                   torch.empty(r2 + (cap,), dtype=dtype, device=device),
+                   torch.empty(r2 + (cap,), dtype=torch.uint8, device=device),
                    torch.empty((max(ovf_cap, 1),), dtype=torch.int32, device=device),
                    torch.empty((1,), dtype=torch.int32, device=device),
                    torch.empty((max(ovf_cap, 1), cols), dtype=dtype, device=device) if dense else None,
                    ovf_cap,
-                   torch.empty((rows, nt, cap), dtype=torch.float32, device=device) if u else None)
+                   torch.empty(r2 + (cap,), dtype=torch.float32, device=device) if u else None,
+                   layout)
 
     def validate(self, device=None) -> None:
         """Check every buffer against the matrix's own fields (device, dtype,
@@ -230,9 +240,12 @@ class TwellMatrix:
         if self.rows < 0 or self.cols <= 0 or self.tile <= 0 or self.cap <= 0 or self.cols % self.tile:
             raise ValueError(f"bad TwELL shape rows={self.rows} cols={self.cols} tile={self.tile} cap={self.cap}")
         nt = self.cols // self.tile
-        _need(self.cnt, "cnt", device, torch.int16, (self.rows, nt))
-        _need(self.val, "val", device, self.dtype, (self.rows, nt, self.cap))
-        _need(self.idx, "idx", device, torch.uint8, (self.rows, nt, self.cap))
+        if self.layout not in LAYOUTS:
+            raise ValueError(f"layout must be one of {sorted(LAYOUTS)}, got {self.layout!r}")
+        r2 = (self.rows, nt) if self.layout == "rows" else (nt, self.rows)
+        _need(self.cnt, "cnt", device, torch.int16, r2)
+        _need(self.val, "val", device, self.dtype, r2 + (self.cap,))
+        _need(self.idx, "idx", device, torch.uint8, r2 + (self.cap,))
         _need(self.ovf_rows, "ovf_rows", device, torch.int32)
         if self.ovf_rows.numel() < max(self.ovf_cap, 1):
             raise ValueError(f"ovf_rows holds {self.ovf_rows.numel()} entries, ovf_cap is {self.ovf_cap}")
@@ -243,12 +256,13 @@ class TwellMatrix:
                 raise ValueError(f"dense must have shape (>= {self.ovf_cap}, {self.cols}), "
                                  f"got {tuple(self.dense.shape)}")
         if self.u is not None:
-            _need(self.u, "u", device, torch.float32, (self.rows, nt, self.cap))
+            _need(self.u, "u", device, torch.float32, r2 + (self.cap,))
 
     def c_struct(self) -> TwellMatrixC:
         return TwellMatrixC(self.rows, self.cols, self.tile, self.cap, _dtype_code(self.dtype),
                             _ptr(self.cnt), _ptr(self.val), _ptr(self.idx), _ptr(self.ovf_rows),
-                            _ptr(self.n_ovf), _ptr(self.dense), self.ovf_cap, _ptr(self.u))
+                            _ptr(self.n_ovf), _ptr(self.dense), self.ovf_cap, _ptr(self.u),
+                            LAYOUTS.get(self.layout, -1))
 
     @property
     def device(self):

@@ -100,6 +100,17 @@ twell_status check_matrix(const twell_matrix *m, bool need_ovf_all) {
   if (!aligned(m->cnt, 2) || !aligned(m->val, dt_size(m->dtype)) || !aligned(m->ovf_rows, 4) ||
       !aligned(m->n_ovf, 4) || !aligned(m->dense, 16) || !aligned(m->u, 4))
     return fail(TWELL_ERR_UNSUPPORTED, "misaligned twell_matrix buffer");
+  if (m->layout != TWELL_LAYOUT_ROWS && m->layout != TWELL_LAYOUT_TILES)
+    return fail(TWELL_ERR_INVALID_ARG, "unknown layout %d", (int)m->layout);
+  if (m->layout == TWELL_LAYOUT_TILES && m->u != nullptr)
+    return fail(TWELL_ERR_INVALID_ARG, "a tile-major TwELL matrix carries no u (packed->u must be NULL)");
+  return TWELL_OK;
+}
+
+// Entry points that read or write the row-major layout only.
+twell_status check_rows_layout(const twell_matrix *m, const char *who) {
+  if (m->layout != TWELL_LAYOUT_ROWS)
+    return fail(TWELL_ERR_UNSUPPORTED, "%s takes the row-major TwELL layout only", who);
   return TWELL_OK;
 }
 
@@ -242,7 +253,8 @@ twell_status run_sparse_fused(const twell_matrix *m, const void *x, const void *
   char *base = static_cast<char *>(ws);
   uint8_t *row_flag = reinterpret_cast<uint8_t *>(base + L.flag);
   const Dt D = to_dt(m->dtype);
-  SparseArgs sa{D, T, d, F, m->tile, m->cap, m->cnt, m->val, m->idx, row_flag, x, wu, wd, nullptr, nullptr, 0, y};
+  SparseArgs sa{D, T, d, F, m->tile, m->cap, m->cnt, m->val, m->idx, row_flag, x, wu, wd, nullptr, nullptr, 0, y,
+                nullptr, m->layout == TWELL_LAYOUT_TILES};
   if (grouped) {
     TW_TRY(sparse_fused_grouped(sa, reinterpret_cast<float *>(base + grouped_partial_offset(L)), s),
            "grouped fused sparse up/down projection");
@@ -352,6 +364,7 @@ twell_status twell_pack(const void *pre, twell_matrix *out, void *stream) {
   g_err[0] = 0;
   twell_status st = check_matrix(out, false);
   if (st != TWELL_OK) return st;
+  if ((st = check_rows_layout(out, "twell_pack")) != TWELL_OK) return st;
   if ((st = check_no_u(out, "twell_pack")) != TWELL_OK) return st;
   if (out->rows > 0 && pre == nullptr) return fail(TWELL_ERR_INVALID_ARG, "null pre");
   if (!aligned(pre, 16)) return fail(TWELL_ERR_UNSUPPORTED, "pre must be 16-byte aligned");
@@ -398,7 +411,7 @@ twell_status twell_gate_pack(const void *x, const void *w_gate, const float *gat
   const int T = packed->rows, F = packed->cols;
   if (T == 0) return TWELL_OK;
   GateArgs ga{to_dt(packed->dtype), packed->tile, x, w_gate, gate_bias, T, d, F, packed->cap,
-              packed->cnt, packed->val, packed->idx, pre_out};
+              packed->cnt, packed->val, packed->idx, pre_out, packed->layout == TWELL_LAYOUT_TILES};
   TW_TRY(gate_twell(ga, s), "gate matmul");
   return TWELL_OK;
 }
@@ -407,6 +420,7 @@ twell_status twell_to_hybrid(const twell_matrix *packed, twell_hybrid *out, void
   g_err[0] = 0;
   twell_status st = check_matrix(packed, true);
   if (st != TWELL_OK) return st;
+  if ((st = check_rows_layout(packed, "twell_to_hybrid")) != TWELL_OK) return st;
   if (out == nullptr) return fail(TWELL_ERR_INVALID_ARG, "null twell_hybrid");
   if (out->rows != packed->rows || out->cols != packed->cols || out->dtype != packed->dtype)
     return fail(TWELL_ERR_INVALID_ARG, "hybrid rows/cols/dtype must equal the TwELL matrix's");
@@ -443,6 +457,7 @@ twell_status twell_l1_norm(const twell_matrix *packed, double *out, void *worksp
   g_err[0] = 0;
   twell_status st = check_matrix(packed, true);
   if (st != TWELL_OK) return st;
+  if ((st = check_rows_layout(packed, "twell_l1_norm")) != TWELL_OK) return st;
   if (out == nullptr) return fail(TWELL_ERR_INVALID_ARG, "null out");
   if (packed->rows > 0 && packed->dense == nullptr)
     return fail(TWELL_ERR_INVALID_ARG, "the TwELL matrix needs its dense backup rows (packed->dense)");
@@ -461,6 +476,7 @@ twell_status twell_l1_grad(const twell_matrix *packed, float lam, void *grad_val
   g_err[0] = 0;
   twell_status st = check_matrix(packed, false);
   if (st != TWELL_OK) return st;
+  if ((st = check_rows_layout(packed, "twell_l1_grad")) != TWELL_OK) return st;
   if (packed->rows > 0 && grad_val == nullptr) return fail(TWELL_ERR_INVALID_ARG, "null grad_val");
   if (grad_dense != nullptr && packed->dense == nullptr)
     return fail(TWELL_ERR_INVALID_ARG, "grad_dense needs the TwELL matrix's dense backup rows");
@@ -479,7 +495,7 @@ twell_status twell_overflow_scan(twell_matrix *packed, void *stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (packed->rows == 0) return hip_check(zero_int(packed->n_ovf, s), "zero n_ovf");
   ScanArgs sc{packed->cnt, packed->rows, packed->cols / packed->tile, packed->cap, nullptr, packed->ovf_rows,
-              packed->ovf_cap, packed->n_ovf};
+              packed->ovf_cap, packed->n_ovf, packed->layout == TWELL_LAYOUT_TILES};
   TW_TRY(overflow_scan(sc, s), "overflow scan");
   return TWELL_OK;
 }
@@ -490,6 +506,7 @@ twell_status twell_sparse_ffn(const twell_matrix *packed, const void *x, const v
   g_err[0] = 0;
   twell_status st = check_matrix(packed, true);
   if (st != TWELL_OK) return st;
+  if ((st = check_rows_layout(packed, "twell_sparse_ffn")) != TWELL_OK) return st;
   if ((st = check_d(d, (int)packed->dtype)) != TWELL_OK) return st;
   if ((st = check_weight_bytes(packed->cols, d, (int)packed->dtype)) != TWELL_OK) return st;
   if (packed->rows == 0) return hip_check(zero_int(packed->n_ovf, static_cast<hipStream_t>(stream)), "zero n_ovf");
@@ -510,6 +527,7 @@ twell_status twell_sparse_ffn_fused(const twell_matrix *packed, const void *x, c
   g_err[0] = 0;
   twell_status st = check_matrix(packed, true);
   if (st != TWELL_OK) return st;
+  if ((st = check_rows_layout(packed, "twell_sparse_ffn_fused")) != TWELL_OK) return st;
   if ((st = check_no_u(packed, "twell_sparse_ffn_fused")) != TWELL_OK) return st;
   if ((st = check_d(d, (int)packed->dtype)) != TWELL_OK) return st;
   const int q = packed->dtype == TWELL_BF16 ? 512 : 256;
@@ -561,6 +579,7 @@ twell_status twell_ffn_forward(const void *x, const void *w_gate, const void *w_
   g_err[0] = 0;
   twell_status st = check_matrix(packed, true);
   if (st != TWELL_OK) return st;
+  if ((st = check_rows_layout(packed, "twell_ffn_forward")) != TWELL_OK) return st;
   if ((st = check_d(d, (int)packed->dtype)) != TWELL_OK) return st;
   if ((st = check_weight_bytes(packed->cols, d, (int)packed->dtype)) != TWELL_OK) return st;
   if (packed->rows == 0) return hip_check(zero_int(packed->n_ovf, static_cast<hipStream_t>(stream)), "zero n_ovf");
@@ -584,6 +603,7 @@ twell_status twell_ffn_forward_noalloc(const void *x, const void *w_gate, const 
   g_err[0] = 0;
   twell_status st = check_matrix(packed, true);
   if (st != TWELL_OK) return st;
+  if ((st = check_rows_layout(packed, "twell_ffn_forward_noalloc")) != TWELL_OK) return st;
   if ((st = check_d(d, (int)packed->dtype)) != TWELL_OK) return st;
   if ((st = check_weight_bytes(packed->cols, d, (int)packed->dtype)) != TWELL_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);

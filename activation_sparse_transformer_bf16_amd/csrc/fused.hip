@@ -38,7 +38,10 @@ __device__ __forceinline__ int reduce_lane(int u) {
 // g on XCD g % 8 as in the up projection); the wave of (group g, token t)
 // handles t's entries in g only and writes its fp32 partial output row to
 // partial[g][t][:]; k_group_reduce adds the groups' partials in group order.
-template <Dt D, int NC, int U, bool GROUPED>
+// TILE_MAJOR: the TwELL records of (row t, tile k) sit at k * T + t (a tile's
+// records contiguous over the tokens), else at t * nt + k; only where the
+// counts and slots are read from changes.
+template <Dt D, int NC, int U, bool GROUPED, bool TILE_MAJOR = false>
 __global__ __launch_bounds__(SP_THREADS) void k_sparse_fused(
     const typename DtT<D>::T *__restrict__ x, const typename DtT<D>::T *__restrict__ wu,
     const typename DtT<D>::T *__restrict__ wd, const uint16_t *__restrict__ cnt,
@@ -58,11 +61,11 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_fused(
   for (int it = wave; it < (GROUPED ? tok_per_wg : SP_WAVES); it += SP_WAVES) {
   const int t = GROUPED ? tb * tok_per_wg + it : blockIdx.x * SP_WAVES + wave;
   if (t >= T) return;
-  const uint16_t *crow = cnt + (size_t)t * nt;
+  auto rec = [&](int k) { return TILE_MAJOR ? (size_t)k * T + t : (size_t)t * nt + k; };
   bool over = false;
   for (int kb = 0; kb < nt; kb += 64) {
     const int k = kb + lane;
-    over |= k < nt && (int)crow[k] > cap;
+    over |= k < nt && (int)cnt[rec(k)] > cap;
   }
   const bool ovf = ballot(over) != 0;
   if (lane == 0 && g == 0) row_flag[t] = ovf ? 1 : 0;
@@ -88,18 +91,18 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_fused(
     const int kn = min(tpp, k_end - k0);
     // The pass's entries into the LDS list, one lane per slot (as in the
     // two-kernel up projection): tile k0 + q holds n(q) entries.
-    const int n = lane < kn ? min((int)crow[k0 + lane], cap) : 0;
+    const int n = lane < kn ? min((int)cnt[rec(k0 + lane)], cap) : 0;
     const int incl = wave_incl_scan(n);
     const int E = __builtin_amdgcn_readlane(incl, 63);
-    const size_t slot0 = ((size_t)t * nt + k0) * cap;
     for (int q0 = 0; q0 < kn * cap; q0 += 64) {
       const int q = q0 + lane;
       const int kq = q / cap, sq = q - kq * cap;
       const int nq = __shfl(n, kq & 63, 64);
       const int oq = __shfl(incl - n, kq & 63, 64) + sq;
       if (q < kn * cap && sq < nq) {
-        const uint32_t j = (uint32_t)((k0 + kq) * tile + (idx[slot0 + q] & (tile - 1)));
-        L[oq] = u32x2_t{j * row_bytes, __float_as_uint(to_f32(val[slot0 + q]))};
+        const size_t sl = rec(k0 + kq) * cap + sq;  // the slot
+        const uint32_t j = (uint32_t)((k0 + kq) * tile + (idx[sl] & (tile - 1)));
+        L[oq] = u32x2_t{j * row_bytes, __float_as_uint(to_f32(val[sl]))};
       }
     }
     wave_sync_lds();
@@ -242,10 +245,10 @@ static hipError_t launch_grouped(const SparseArgs &a, float *partial, hipStream_
   const FusedGroups fg = fused_groups(a.d, a.F, a.tile, a.dtype);
   const int tok = 16;
   const int n_tb = (a.T + tok - 1) / tok;
-  hipLaunchKernelGGL((k_sparse_fused<D, NC, U, true>), dim3(padded_groups(fg.n_groups) * n_tb), dim3(SP_THREADS), 0,
-                     s, (const TT *)a.x, (const TT *)a.wu, (const TT *)a.wd, a.cnt, (const TT *)a.val, a.idx,
-                     a.row_flag, (TT *)a.y, a.T, a.d, a.F / a.tile, a.tile, a.cap, fg.tpg, fg.n_groups, tok, n_tb,
-                     partial);
+  auto kern = a.tile_major ? k_sparse_fused<D, NC, U, true, true> : k_sparse_fused<D, NC, U, true, false>;
+  hipLaunchKernelGGL(kern, dim3(padded_groups(fg.n_groups) * n_tb), dim3(SP_THREADS), 0, s, (const TT *)a.x,
+                     (const TT *)a.wu, (const TT *)a.wd, a.cnt, (const TT *)a.val, a.idx, a.row_flag, (TT *)a.y, a.T,
+                     a.d, a.F / a.tile, a.tile, a.cap, fg.tpg, fg.n_groups, tok, n_tb, partial);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t chunks = (size_t)a.T * a.d / (16 / sizeof(TT));
@@ -273,6 +276,7 @@ static hipError_t fused_dispatch(const SparseArgs &a, float *partial, hipStream_
 
 hipError_t sparse_fused(const SparseArgs &a, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
+  if (a.tile_major) return hipErrorInvalidValue;  // the token-major kernel reads row-major records only
   return a.dtype == Dt::BF16 ? fused_dispatch<Dt::BF16>(a, nullptr, s) : fused_dispatch<Dt::F32>(a, nullptr, s);
 }
 

@@ -89,7 +89,7 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::WAVES_PER_SIMD) void k_gate_twel
     const typename DtT<D>::T *__restrict__ x, const typename DtT<D>::T *__restrict__ wg,
     const float *__restrict__ beta, int M, int K, int N, int cap, uint16_t *__restrict__ cnt,
     typename DtT<D>::T *__restrict__ val, uint8_t *__restrict__ idx,
-    typename DtT<D>::T *__restrict__ pre_out) {
+    typename DtT<D>::T *__restrict__ pre_out, bool tile_major) {
   using T = typename DtT<D>::T;
   using WT = WaveTile<BN, Cfg>;
   constexpr int NWM = WT::NWM, NWN = WT::NWN;
@@ -249,8 +249,10 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::WAVES_PER_SIMD) void k_gate_twel
       }
       wave_lds_sync();
       if (t < M) {
-        const size_t slot0 = ((size_t)t * ntiles + tn) * cap;
-        if (wsub == MW - 1) cnt[(size_t)t * ntiles + tn] = (uint16_t)incl;
+        // the (row, tile) record: row-major, or tile-major (the tile's rows contiguous)
+        const size_t rec = tile_major ? (size_t)tn * M + t : (size_t)t * ntiles + tn;
+        const size_t slot0 = rec * cap;
+        if (wsub == MW - 1) cnt[rec] = (uint16_t)incl;
         for (int q = wsub; q < nvc + nic; q += MW) {
           if (q < nvc)
             copy_chunk(reinterpret_cast<char *>(val + slot0) + q * vunit, vals + rl * VS + q * vunit, vunit);
@@ -274,7 +276,7 @@ static hipError_t launch_gate(const GateArgs &a, hipStream_t s) {
   const int mt = (a.M + Cfg::BM - 1) / Cfg::BM, ntl = a.N / BN;
   hipLaunchKernelGGL(kern, dim3(mt * ntl), dim3(Cfg::THREADS), lds, s, (const T *)a.x,
                      (const T *)a.wg, a.beta, a.M, a.K, a.N, a.cap, a.cnt, (T *)a.val, a.idx,
-                     (T *)a.pre_out);
+                     (T *)a.pre_out, a.tile_major);
   return hipGetLastError();
 }
 

@@ -22,6 +22,7 @@ struct GateArgs {
   void *val;          // [M][N/tile][cap]
   uint8_t *idx;       // [M][N/tile][cap]
   void *pre_out;      // [M][N] or null
+  bool tile_major = false;  // records at k * M + t instead of t * (N/tile) + k
 };
 hipError_t gate_twell(const GateArgs &a, hipStream_t s);
 
@@ -33,6 +34,7 @@ struct ScanArgs {
   int *ovf_rows;        // [ovf_cap] (may be null when ovf_cap == 0)
   int ovf_cap;
   int *n_ovf;           // [1]
+  bool tile_major = false;  // cnt is [nt][T]
 };
 hipError_t overflow_scan(const ScanArgs &a, hipStream_t s);
 
@@ -90,6 +92,7 @@ struct SparseArgs {
   int stride;               // list entries per row: nt * cap rounded up to a multiple of 8
   void *y;                  // [T][d]
   float *u = nullptr;       // [T][nt][cap] saved u per TwELL slot (NaN for overflow rows), or null
+  bool tile_major = false;  // TwELL records tile-major (read by the grouped fused kernel only)
 };
 hipError_t sparse_up(const SparseArgs &a, hipStream_t s);
 hipError_t sparse_down(const SparseArgs &a, hipStream_t s);

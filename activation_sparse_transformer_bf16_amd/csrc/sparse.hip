@@ -29,10 +29,11 @@ namespace twell {
 
 // ---------------------------------------------------------------------------
 // Overflow scan: row t overflows iff max_k cnt[t][k] > cap.  One workgroup.
-// Rows are taken SCAN_CHUNK at a time: the chunk's counts are read as one flat
-// stream of 16-byte loads (consecutive threads, consecutive bytes), a count
-// above cap sets its row's flag byte in LDS, and the flags are then compacted
-// in ascending row order, so the list is deterministic.
+// Rows are taken SCAN_CHUNK at a time: the chunk's counts are read as flat
+// streams of 16-byte loads (consecutive threads, consecutive bytes; one stream
+// in the row-major layout, one per tile in the tile-major one), a count above
+// cap sets its row's flag byte in LDS, and the flags are then compacted in
+// ascending row order, so the list is deterministic.
 constexpr int SCAN_THREADS = 1024;
 constexpr int SCAN_PER = 8;                         // flag bytes per thread in the compaction
 constexpr int SCAN_CHUNK = SCAN_PER * SCAN_THREADS;  // rows per round
@@ -41,7 +42,7 @@ constexpr int SCAN_LOADS = 16;                       // 16-byte loads per thread
 __global__ __launch_bounds__(SCAN_THREADS) void k_overflow_scan(const uint16_t *__restrict__ cnt, int T, int nt,
                                                                int cap, uint8_t *__restrict__ row_flag,
                                                                int *__restrict__ ovf_rows, int ovf_cap,
-                                                               int *__restrict__ n_ovf) {
+                                                               int *__restrict__ n_ovf, bool tile_major) {
   __shared__ __align__(16) uint32_t flag4[SCAN_CHUNK / 4];
   __shared__ int wcount[SCAN_THREADS / 64];
   uint8_t *flag = reinterpret_cast<uint8_t *>(flag4);
@@ -51,34 +52,44 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_overflow_scan(const uint16_t *
     const int nr = min(SCAN_CHUNK, T - r0);
     for (int i = tid; i < SCAN_CHUNK / 4; i += SCAN_THREADS) flag4[i] = 0u;
     __syncthreads();
-    // counts of rows [r0, r0 + nr): elements [e_begin, e_end) of the flat array
-    const size_t e_begin = (size_t)r0 * nt, e_end = (size_t)(r0 + nr) * nt;
-    const uintptr_t a0 = reinterpret_cast<uintptr_t>(cnt + e_begin);
-    const size_t head = min((size_t)(((16u - (a0 & 15u)) & 15u) / 2u), e_end - e_begin);
-    const size_t v0 = e_begin + head;
-    const size_t nv = (e_end - v0) / 8;  // whole 16-byte chunks
-    const size_t v_end = v0 + nv * 8;
-    for (size_t e = e_begin + tid; e < v0; e += SCAN_THREADS)
-      if (cnt[e] > cap) flag[e / nt - r0] = 1;
-    for (size_t e = v_end + tid; e < e_end; e += SCAN_THREADS)
-      if (cnt[e] > cap) flag[e / nt - r0] = 1;
-    for (size_t c0 = tid; c0 < nv; c0 += (size_t)SCAN_THREADS * SCAN_LOADS) {
-      u32x4_t w[SCAN_LOADS];
+    // counts of rows [r0, r0 + nr): row-major, the elements [r0 nt, (r0 + nr)
+    // nt) of the flat array (one segment, element e of row e / nt);
+    // tile-major, the elements [k T + r0, k T + r0 + nr) of each tile k (nt
+    // segments, element e of row e - k T)
+    const int nseg = tile_major ? nt : 1;
+    for (int sg = 0; sg < nseg; ++sg) {
+      const size_t e_begin = tile_major ? (size_t)sg * T + r0 : (size_t)r0 * nt;
+      const size_t e_end = tile_major ? e_begin + nr : (size_t)(r0 + nr) * nt;
+      const size_t row_base = tile_major ? e_begin : 0;
+      const int rdiv = tile_major ? 1 : nt, rsub = tile_major ? 0 : r0;
+      auto mark = [&](size_t e) { flag[(int)((e - row_base) / rdiv) - rsub] = 1; };
+      const uintptr_t a0 = reinterpret_cast<uintptr_t>(cnt + e_begin);
+      const size_t head = min((size_t)(((16u - (a0 & 15u)) & 15u) / 2u), e_end - e_begin);
+      const size_t v0 = e_begin + head;
+      const size_t nv = (e_end - v0) / 8;  // whole 16-byte chunks
+      const size_t v_end = v0 + nv * 8;
+      for (size_t e = e_begin + tid; e < v0; e += SCAN_THREADS)
+        if (cnt[e] > cap) mark(e);
+      for (size_t e = v_end + tid; e < e_end; e += SCAN_THREADS)
+        if (cnt[e] > cap) mark(e);
+      for (size_t c0 = tid; c0 < nv; c0 += (size_t)SCAN_THREADS * SCAN_LOADS) {
+        u32x4_t w[SCAN_LOADS];
 #pragma unroll
-      for (int q = 0; q < SCAN_LOADS; ++q) {
-        const size_t c = c0 + (size_t)q * SCAN_THREADS;
-        w[q] = c < nv ? *reinterpret_cast<const u32x4_t *>(cnt + v0 + c * 8) : u32x4_t{0u, 0u, 0u, 0u};
-      }
+        for (int q = 0; q < SCAN_LOADS; ++q) {
+          const size_t c = c0 + (size_t)q * SCAN_THREADS;
+          w[q] = c < nv ? *reinterpret_cast<const u32x4_t *>(cnt + v0 + c * 8) : u32x4_t{0u, 0u, 0u, 0u};
+        }
 #pragma unroll
-      for (int q = 0; q < SCAN_LOADS; ++q) {
-        uint32_t mx = 0;
+        for (int q = 0; q < SCAN_LOADS; ++q) {
+          uint32_t mx = 0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) mx = max(mx, max(w[q][j] & 0xFFFFu, w[q][j] >> 16));
-        if (mx > (uint32_t)cap) {
-          const size_t e0 = v0 + (c0 + (size_t)q * SCAN_THREADS) * 8;
+          for (int j = 0; j < 4; ++j) mx = max(mx, max(w[q][j] & 0xFFFFu, w[q][j] >> 16));
+          if (mx > (uint32_t)cap) {
+            const size_t e0 = v0 + (c0 + (size_t)q * SCAN_THREADS) * 8;
 #pragma unroll
-          for (int j = 0; j < 8; ++j)
-            if (((w[q][j / 2] >> (16 * (j & 1))) & 0xFFFFu) > (uint32_t)cap) flag[(e0 + j) / nt - r0] = 1;
+            for (int j = 0; j < 8; ++j)
+              if (((w[q][j / 2] >> (16 * (j & 1))) & 0xFFFFu) > (uint32_t)cap) mark(e0 + j);
+          }
         }
       }
     }
@@ -116,7 +127,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_overflow_scan(const uint16_t *
 
 hipError_t overflow_scan(const ScanArgs &a, hipStream_t s) {
   hipLaunchKernelGGL(k_overflow_scan, dim3(1), dim3(SCAN_THREADS), 0, s, a.cnt, a.T, a.nt, a.cap, a.row_flag,
-                     a.ovf_rows, a.ovf_cap, a.n_ovf);
+                     a.ovf_rows, a.ovf_cap, a.n_ovf, a.tile_major);
   return hipGetLastError();
 }
 

@@ -371,13 +371,24 @@ def measure(w, steps, warmup, want_torch=True, want_cold=True):
         ws_g = torch.empty((tw.twell_sparse_ffn_grouped_workspace_size(T, d, F, w.tile, w.cap, x.dtype),),
                            dtype=torch.uint8, device=dev)
         grouped_rest = lambda: tw.twell_sparse_ffn_grouped(packed, x, wg, wu, wd, b, y=y, workspace=ws_g)
-        _, ms_grouped_rest = split_time(gate, grouped_rest, steps, warmup)
+        ms_gate_r, ms_grouped_rest = split_time(gate, grouped_rest, steps, warmup)
         ms_grouped, _ = event_time(lambda: (gate(), grouped_rest()), steps, warmup)
-        grouped = {"forward_us": ms_grouped * 1e3, "up_down_fallback_us": ms_grouped_rest * 1e3,
+        grouped = {"forward_us": ms_grouped * 1e3, "gate_us": ms_gate_r * 1e3, "up_down_fallback_us": ms_grouped_rest * 1e3,
                    "partial_bytes": ws_g.numel() - tw.twell_ffn_workspace_size(T, d, F, w.tile, w.cap, x.dtype)}
-        log(f"[bench] grouped fused up+down: {ms_grouped_rest * 1e3:.1f} us in sequence, forward "
-            f"{ms_grouped * 1e3:.1f} us")
-        del ws_g
+        log(f"[bench] grouped fused up+down: gate {ms_gate_r * 1e3:.1f} us, {ms_grouped_rest * 1e3:.1f} us in "
+            f"sequence, forward {ms_grouped * 1e3:.1f} us")
+        # the same over the tile-major TwELL layout written by the gate (a
+        # tile's records of consecutive tokens contiguous)
+        packed_t = tw.TwellMatrix.empty(T, F, w.tile, w.cap, x.dtype, dev, T, dense=True, layout="tiles")
+        gate_t = lambda: tw.twell_gate_pack(x, wg, b, packed=packed_t, scan=False)
+        grouped_t_rest = lambda: tw.twell_sparse_ffn_grouped(packed_t, x, wg, wu, wd, b, y=y, workspace=ws_g)
+        ms_gate_t, ms_grouped_t_rest = split_time(gate_t, grouped_t_rest, steps, warmup)
+        ms_grouped_t, _ = event_time(lambda: (gate_t(), grouped_t_rest()), steps, warmup)
+        grouped["tile_major"] = {"forward_us": ms_grouped_t * 1e3, "gate_us": ms_gate_t * 1e3,
+                                 "up_down_fallback_us": ms_grouped_t_rest * 1e3}
+        log(f"[bench] grouped fused up+down over tile-major TwELL: gate {ms_gate_t * 1e3:.1f} us, "
+            f"{ms_grouped_t_rest * 1e3:.1f} us in sequence, forward {ms_grouped_t * 1e3:.1f} us")
+        del ws_g, packed_t
 
     # Training-format kernels on this batch's TwELL matrix (with its dense
     # backup rows): TwELL -> hybrid at an ELL width of 256, the L1 norm and the

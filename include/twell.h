@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define TWELL_ABI_VERSION 2
+#define TWELL_ABI_VERSION 3
 
 /* The enums are int-sized.  Compiled as C++ they have the fixed underlying
  * type int, so any int a C caller stores in one is a value of the type, which
@@ -84,6 +84,9 @@ typedef enum TWELL_ENUM_BASE {
 } twell_status;
 
 typedef enum TWELL_ENUM_BASE { TWELL_F32 = 0, TWELL_BF16 = 1 } twell_dtype;
+
+/* Order of the (row, tile) records of a TwELL matrix (see twell_matrix). */
+typedef enum TWELL_ENUM_BASE { TWELL_LAYOUT_ROWS = 0, TWELL_LAYOUT_TILES = 1 } twell_layout;
 
 /*
  * One TwELL matrix [rows][cols] (token-major), described by caller-owned
@@ -119,20 +122,32 @@ typedef enum TWELL_ENUM_BASE { TWELL_F32 = 0, TWELL_BF16 = 1 } twell_dtype;
  *                        NaN (not saved).  Slots past the count are not
  *                        written.  The other producers of a TwELL matrix
  *                        (twell_pack) and the fused prototypes take u == NULL.
+ *
+ *   Layout.  The record of (row t, tile k) -- its count and its cap slots --
+ *   sits at position r = t * (cols/tile) + k (TWELL_LAYOUT_ROWS, the default:
+ *   a row's records are contiguous) or r = k * rows + t (TWELL_LAYOUT_TILES:
+ *   a tile's records are contiguous, for consumers that walk the hidden units
+ *   tile by tile over all tokens): cnt[r], val[r][s], idx[r][s], u[r][s].
+ *   The tile-major layout is written by twell_gate_pack and read by
+ *   twell_overflow_scan and twell_sparse_ffn_grouped (the hidden-group-major
+ *   fused prototype, gist.science Resumen Técnico §2.B); it carries no u.
+ *   Every other entry point takes TWELL_LAYOUT_ROWS only and returns
+ *   TWELL_ERR_UNSUPPORTED for the other.
  */
 typedef struct {
   int32_t rows, cols;   /* T, F; cols % tile == 0 */
   int32_t tile;         /* W: 128 or 256 */
   int32_t cap;          /* C: 1 <= cap <= min(tile, 64) */
   twell_dtype dtype;    /* value dtype == activation dtype */
-  uint16_t *cnt;        /* [rows][cols/tile] */
-  void *val;            /* [rows][cols/tile][cap], dtype */
-  uint8_t *idx;         /* [rows][cols/tile][cap] */
+  uint16_t *cnt;        /* [rows][cols/tile] ([cols/tile][rows] tile-major) */
+  void *val;            /* [rows][cols/tile][cap], dtype (tile-major: [cols/tile][rows][cap]) */
+  uint8_t *idx;         /* [rows][cols/tile][cap] (tile-major: [cols/tile][rows][cap]) */
   int32_t *ovf_rows;    /* [ovf_cap] */
   int32_t *n_ovf;       /* [1] */
   void *dense;          /* [ovf_cap][cols], dtype; may be NULL (not written) */
   int32_t ovf_cap;      /* rows available in ovf_rows (and dense when non-NULL) */
   float *u;             /* [rows][cols/tile][cap] fp32, or NULL (see above) */
+  twell_layout layout;  /* record order (see above); TWELL_LAYOUT_ROWS unless stated */
 } twell_matrix;
 
 /* ABI version of the loaded library (TWELL_ABI_VERSION). */
@@ -246,7 +261,9 @@ twell_status twell_ffn_forward_noalloc(const void *x, const void *w_gate, const 
  * synchronisation between thread blocks (gist.science Resumen Técnico §2.A;
  * the estadored.mx item on the same paper, on the index management and
  * memory traffic this avoids).  Writes packed->cnt, val and idx; ovf_rows, n_ovf and dense
- * are not touched (twell_overflow_scan completes them).  pre_out, when
+ * are not touched (twell_overflow_scan completes them).  With
+ * packed->layout == TWELL_LAYOUT_TILES the records are written tile-major
+ * (the same values at the other record positions).  pre_out, when
  * non-NULL, receives the rounded pre-activations [T][F] in the storage dtype
  * (a debugging dump; the fused path itself never stores them).
  * Errors: INVALID_ARG, UNSUPPORTED, HIP.
@@ -255,8 +272,9 @@ twell_status twell_gate_pack(const void *x, const void *w_gate, const float *gat
                              twell_matrix *packed, void *pre_out, void *stream);
 
 /*
- * twell_overflow_scan: step (2) alone.  Reads packed->cnt and writes the
- * ascending list of overflowing rows (first ovf_cap of them) and *n_ovf.
+ * twell_overflow_scan: step (2) alone.  Reads packed->cnt (either layout)
+ * and writes the ascending list of overflowing rows (first ovf_cap of them)
+ * and *n_ovf.
  * Errors: INVALID_ARG, UNSUPPORTED, HIP.
  */
 twell_status twell_overflow_scan(twell_matrix *packed, void *stream);
@@ -404,6 +422,10 @@ twell_status twell_sparse_ffn_fused(const twell_matrix *packed, const void *x, c
  * workspace: twell_sparse_ffn_grouped_workspace_size() bytes, which adds
  * n_groups * T * d fp32 partial rows (1 GiB at T = 8192, d = 2048, 16 groups)
  * to the forward's workspace; d limited to 4096 (bf16) / 2048 (fp32).
+ * packed may be in either layout: with TWELL_LAYOUT_TILES (written so by
+ * twell_gate_pack) a group's TwELL records are read tile by tile, each tile's
+ * records of consecutive tokens contiguous.  The layout changes only where the
+ * records are read from: y is bit for bit the same.
  * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP.
  */
 size_t twell_sparse_ffn_grouped_workspace_size(int T, int d, int F, int tile, int cap, twell_dtype dtype);

@@ -51,5 +51,6 @@ from .twell import (  # noqa: F401
     pack_loop,
     relu_storage,
     sparse_ffn,
+    tile_major,
     unpack,
 )

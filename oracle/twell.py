@@ -154,6 +154,18 @@ def unpack(p: Packed) -> np.ndarray:
     return out
 
 
+def tile_major(p: Packed):
+    """The records of ``p`` in the tile-major layout of ``include/twell.h``
+    (``twell_layout``): the record of (row t, tile k) -- count and cap slots --
+    moves from position t * nt + k to k * T + t, so that a tile's records are
+    contiguous over the tokens (the hidden-tile-major walk of the fused
+    inference kernel, gist.science Resumen Técnico §2.B).  A change of order
+    only: every record is kept whole.  Returns (cnt [nt, T], val [nt, T, cap],
+    idx [nt, T, cap])."""
+    return (np.ascontiguousarray(p.cnt.transpose(1, 0)), np.ascontiguousarray(p.val.transpose(1, 0, 2)),
+            np.ascontiguousarray(p.idx.transpose(1, 0, 2)))
+
+
 def sparse_ffn(p: Packed, x: np.ndarray, w_up: np.ndarray, w_down: np.ndarray) -> np.ndarray:
     """y from the packed gate activations, one active entry at a time (float64).
 

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert twell.twell_abi_version() == twell.ABI_VERSION == 2
+    assert twell.twell_abi_version() == twell.ABI_VERSION == 3
     assert twell.twell_status_str(twell.TWELL_OK) == "ok"
     assert "workspace" in twell.twell_status_str(twell.TWELL_ERR_WORKSPACE)
     assert twell.twell_status_str(99) == "unknown status"
@@ -123,6 +123,31 @@ def test_saved_u_validation():
     assert H(ctypes.byref(_matrix(dense=FAKE)), ctypes.byref(_hybrid(u=FAKE)), None) == twell.TWELL_ERR_INVALID_ARG
     assert H(ctypes.byref(_matrix(dense=FAKE, u=FAKE)), ctypes.byref(_hybrid(u=FAKE + 2)),
              None) == twell.TWELL_ERR_UNSUPPORTED
+
+
+def test_layout_validation():
+    """The tile-major layout is written by twell_gate_pack and read by the
+    overflow scan and the grouped fused kernel only; every other entry point
+    rejects it, an unknown layout and a tile-major matrix with u are invalid
+    (all before any launch)."""
+    tiles = twell.TWELL_LAYOUT_TILES
+    for bad in (2, -1):
+        assert L.twell_overflow_scan(ctypes.byref(_matrix(layout=bad)), None) == twell.TWELL_ERR_INVALID_ARG
+    assert L.twell_overflow_scan(ctypes.byref(_matrix(layout=tiles, u=FAKE)), None) == twell.TWELL_ERR_INVALID_ARG
+    m = _matrix(layout=tiles, dense=FAKE)
+    U = twell.TWELL_ERR_UNSUPPORTED
+    assert L.twell_pack(FAKE, ctypes.byref(m), None) == U
+    for f in (L.twell_sparse_ffn, L.twell_sparse_ffn_fused):
+        assert f(ctypes.byref(m), FAKE, FAKE, FAKE, FAKE, None, FAKE, 512, FAKE, 1 << 40, None) == U
+    assert L.twell_ffn_forward(FAKE, FAKE, FAKE, FAKE, None, FAKE, 512, ctypes.byref(m), FAKE, 1 << 40, None) == U
+    assert L.twell_ffn_forward_noalloc(FAKE, FAKE, FAKE, FAKE, None, FAKE, 512, ctypes.byref(m), None) == U
+    assert L.twell_to_hybrid(ctypes.byref(m), ctypes.byref(_hybrid()), None) == U
+    assert L.twell_l1_norm(ctypes.byref(m), FAKE, FAKE, 1 << 20, None) == U
+    assert L.twell_l1_grad(ctypes.byref(m), ctypes.c_float(1.0), FAKE, None, None) == U
+    # accepted by the grouped kernel's validation: it fails only at the
+    # workspace check, after the layout has passed
+    assert L.twell_sparse_ffn_grouped(ctypes.byref(m), FAKE, FAKE, FAKE, FAKE, None, FAKE, 512, FAKE, 10,
+                                      None) == twell.TWELL_ERR_WORKSPACE
 
 
 def test_dense_validation():

@@ -9,7 +9,7 @@ from hypothesis import given, settings, strategies as st
 
 from oracle.ffn import ffn, ffn_from_h, rel_l2
 from oracle.numerics import decode, round_to_storage
-from oracle.twell import active, pack, pack_loop, relu_storage, sparse_ffn, unpack
+from oracle.twell import active, pack, pack_loop, relu_storage, sparse_ffn, tile_major, unpack
 from workloads.synth import ffn_inputs, pre_activations, to_storage
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -172,3 +172,44 @@ def test_pack_rejects_bad_shapes():
         pack(to_storage(np.zeros((2, 8)), "f32"), "f32", 4, 5)
     with pytest.raises(ValueError):
         pack(to_storage(np.zeros((2, 8)), "f32"), "bf16", 4, 2)
+
+
+@settings(max_examples=200, deadline=None)
+@given(_pre_case())
+def test_tile_major_records_rebuild_relu(case):
+    """Tile-major layout (include/twell.h, twell_layout): the record of (row t,
+    tile k) sits at flat position k * T + t.  Walking the flat arrays by that
+    definition alone, one record at a time, must rebuild ReLU(H) bit for bit
+    (overflow rows from the dense backup), independently of ``unpack``."""
+    dtype, tile, cap, pre = case
+    p = pack(pre, dtype, tile, cap)
+    T, F = pre.shape
+    nt = F // tile
+    cnt_t, val_t, idx_t = tile_major(p)
+    assert cnt_t.shape == (nt, T) and val_t.shape == (nt, T, cap) and idx_t.shape == (nt, T, cap)
+    c, v, i = cnt_t.reshape(-1), val_t.reshape(-1, cap), idx_t.reshape(-1, cap)
+    h = np.zeros_like(pre)
+    h[...] = relu_storage(np.zeros_like(pre), dtype)  # +0 of the storage dtype
+    overflow = np.zeros(T, dtype=bool)
+    for t in range(T):
+        for k in range(nt):
+            r = k * T + t
+            overflow[t] |= int(c[r]) > cap
+            for s_ in range(min(int(c[r]), cap)):
+                h[t, k * tile + int(i[r, s_])] = v[r, s_]
+    for r_, t in enumerate(p.ovf_rows):
+        h[t] = p.dense[r_]
+    assert overflow.tolist() == [t in set(p.ovf_rows.tolist()) for t in range(T)]
+    _assert_same(h, relu_storage(pre, dtype))
+
+
+def test_tile_major_hand_example():
+    """The golden example's counts in tile-major order, written out by hand:
+    rows 0 and 1 of tile 0, then rows 0 and 1 of tile 1, ..."""
+    g = _load("twell_pack_example.json")
+    pre = _storage(g["pre"], "f32")
+    p = pack(pre, "f32", g["tile"], g["cap"])
+    cnt_t, _, idx_t = tile_major(p)
+    T = len(g["cnt"])
+    assert cnt_t.reshape(-1).tolist() == [g["cnt"][t][k] for k in range(len(g["cnt"][0])) for t in range(T)]
+    assert idx_t.reshape(-1, g["cap"]).tolist() == [g["idx"][t][k] for k in range(len(g["idx"][0])) for t in range(T)]
