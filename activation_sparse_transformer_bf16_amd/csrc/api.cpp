@@ -167,7 +167,7 @@ FfnWs ffn_ws_layout(int T, int d, int F, int tile, int cap, twell_dtype dt, int 
                     int partial_cap = FALLBACK_PARTIAL_TILES_MAX) {
   FfnWs w;
   const size_t nt = (size_t)F / tile;
-  w.stride = (int)((nt * cap + 7) / 8 * 8);
+  w.stride = (int)((nt * cap + LIST_PAD - 1) / LIST_PAD * LIST_PAD);
   w.chunk_rows = chunk_rows;
   w.partial_tiles = T > 0 ? fallback_partial_tiles(chunk_rows, d, F, dt, partial_cap) : 0;
   w.flag = 0;

@@ -76,6 +76,11 @@ inline UpPlan up_plan(int d, int F, int tile, int cap, Dt dt) {
 }
 
 // Sparse up / down projections over the TwELL entries of non-overflow rows.
+// Each compact entry list is padded to a multiple of LIST_PAD entries (the
+// down projection consumes up to LIST_PAD entries per step without a bound
+// check on the list length).
+constexpr int LIST_PAD = 16;
+
 struct SparseArgs {
   Dt dtype;
   int T, d, F, tile, cap;
@@ -89,7 +94,7 @@ struct SparseArgs {
   void *list;               // [T][stride] entries: UpPlan dc == 1: (uint32 row byte offset, v = round(h * u));
                             // dc == 2: (offset, fp32 partial u of the first half of d, fp32 h, partial of the second)
   int *list_n;              // [T] entries per row
-  int stride;               // list entries per row: nt * cap rounded up to a multiple of 8
+  int stride;               // list entries per row: nt * cap rounded up to a multiple of LIST_PAD
   void *y;                  // [T][d]
   float *u = nullptr;       // [T][nt][cap] saved u per TwELL slot (NaN for overflow rows), or null
   bool tile_major = false;  // TwELL records tile-major (read by the grouped fused kernel only)

@@ -239,7 +239,7 @@ hipError_t zero_int(int *p, hipStream_t s) {
 //           h, u over the second half): part 0 writes the first 8 bytes,
 //           part 1 the last 8; the down kernel forms v = round(h * (u0 + u1));
 // for e < list_n[t], and padding entries (NO_ROW, 0...) up to the next
-// multiple of 8.  With u_out non-null the wave also saves u of every entry at
+// multiple of LIST_PAD.  With u_out non-null the wave also saves u of every entry at
 // its TwELL slot: DC = 1 stores it, DC = 2 adds each half's partial sum to a
 // slot zeroed beforehand (two fp32 addends: the sum does not depend on their
 // order); the slots of an overflow row get NaN.  A row overflows
@@ -315,7 +315,7 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_up(
         row_flag[t] = ovf ? 1 : 0;
         list_n[t] = ovf ? -1 : sum;
       }
-      if (!ovf && lane < ((sum + 7) & ~7) - sum) {
+      if (!ovf && lane < ((sum + LIST_PAD - 1) & ~(LIST_PAD - 1)) - sum) {
         list[(lbase + sum + lane) * DC] = u32x2_t{NO_ROW, 0u};
         if constexpr (DC == 2) list[(lbase + sum + lane) * 2 + 1] = u32x2_t{0u, 0u};
       }
@@ -425,10 +425,10 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_down(
   static_assert(D != Dt::BF16 || U % 2 == 0, "bf16 pairs the entries of one lane");
   static_assert(STEP <= 64 && 64 % STEP == 0, "a 64-entry chunk holds whole iterations");
   // One iteration consumes STEP list entries and a chunk holds the list's
-  // entries rounded up to a multiple of 8 (the padding the up kernel writes,
-  // whose loads return zeros); a larger STEP would read entries past them and
-  // load weight rows at stale offsets.
-  static_assert(8 % STEP == 0, "STEP must divide the list padding of 8 entries");
+  // entries rounded up to a multiple of LIST_PAD (the padding the up kernel
+  // writes, whose loads return zeros); a larger STEP would read entries past
+  // them and load weight rows at stale offsets.
+  static_assert(LIST_PAD % STEP == 0, "STEP must divide the list padding");
   __shared__ u32x2_t chunk[SP_WAVES][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int part = lane / LPE;                 // which of the EPI entries this lane works on
@@ -454,10 +454,10 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_down(
       // 64 entries of the list to LDS with one load; each lane then reads the
       // entry it works on (lanes of a half-wave read the same one), so the
       // row offset and the weight arrive per lane without any selects.  The
-      // list is padded to a multiple of 8 entries with (NO_ROW, 0), whose
+      // list is padded to a multiple of LIST_PAD entries with (NO_ROW, 0), whose
       // loads return zeros, so padding adds exactly 0 whatever the weights
       // hold; entries beyond that in the chunk are never read.
-      const int ne = min(64, (n - e0 + 7) & ~7);
+      const int ne = min(64, (n - e0 + LIST_PAD - 1) & ~(LIST_PAD - 1));
       if (lane < ne) {
         if constexpr (DC == 1) {
           C[lane] = lt[e0 + lane];
@@ -610,7 +610,7 @@ hipError_t sparse_down(const SparseArgs &a, hipStream_t s) {
   // F > 8192, measured slower at F = 14336.)
   const int dc = up_plan(a.d, a.F, a.tile, a.cap, a.dtype).dc;
   if (a.dtype == Dt::BF16)
-    return dc == 2 ? launch_down<Dt::BF16, 256, 4, 2>(a, s) : launch_down<Dt::BF16, 256, 4, 1>(a, s);
+    return dc == 2 ? launch_down<Dt::BF16, 256, 8, 2>(a, s) : launch_down<Dt::BF16, 256, 8, 1>(a, s);
   return dc == 2 ? launch_down<Dt::F32, 256, 8, 2>(a, s) : launch_down<Dt::F32, 256, 8, 1>(a, s);
 }
 
