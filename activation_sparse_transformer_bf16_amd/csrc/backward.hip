@@ -42,6 +42,10 @@ namespace twell {
 
 constexpr int BW_THREADS = 256;
 constexpr int BW_WAVES = BW_THREADS / 64;
+// The row-mask kernels of the transpose walk a block's rows through dependent
+// loads (count, then columns): 16 waves per workgroup, 4 rows each.
+constexpr int TR_THREADS = 1024;
+constexpr int TR_WAVES = TR_THREADS / 64;
 constexpr int BW_RB = 64;     // rows per block of the transpose (one bit each)
 constexpr int DX_SLICE = 128; // columns of d per dx slice
 constexpr int DW_SLICE = 128; // columns of d per dW slice
@@ -129,11 +133,11 @@ __global__ __launch_bounds__(BW_THREADS) void k_bw_dense_cols(const typename DtT
 
 template <class TT>
 __device__ __forceinline__ void block_masks(const RowSrc<TT> &s, int b, unsigned long long *mask) {
-  for (int j = threadIdx.x; j < s.F; j += BW_THREADS) mask[j] = 0ull;
+  for (int j = threadIdx.x; j < s.F; j += TR_THREADS) mask[j] = 0ull;
   __syncthreads();
   const int lane = threadIdx.x & 63;
   const int t_end = min(s.T, (b + 1) * BW_RB);
-  for (int t = b * BW_RB + (threadIdx.x >> 6); t < t_end; t += BW_WAVES) {
+  for (int t = b * BW_RB + (threadIdx.x >> 6); t < t_end; t += TR_WAVES) {
     const RowList L = row_list(s, t);
     const unsigned long long bit = 1ull << (t - b * BW_RB);
     for (int i = lane; i < L.n; i += 64) atomicOr(&mask[clamp_col(L.col[i], s.F)], bit);
@@ -142,11 +146,11 @@ __device__ __forceinline__ void block_masks(const RowSrc<TT> &s, int b, unsigned
 }
 
 template <class TT>
-__global__ __launch_bounds__(BW_THREADS) void k_bw_count(RowSrc<TT> s, uint8_t *__restrict__ blk) {
+__global__ __launch_bounds__(TR_THREADS) void k_bw_count(RowSrc<TT> s, uint8_t *__restrict__ blk) {
   extern __shared__ unsigned long long mask[];
   block_masks(s, blockIdx.x, mask);
   uint8_t *out = blk + (size_t)blockIdx.x * s.F;
-  for (int j = threadIdx.x; j < s.F; j += BW_THREADS) out[j] = (uint8_t)__popcll(mask[j]);
+  for (int j = threadIdx.x; j < s.F; j += TR_THREADS) out[j] = (uint8_t)__popcll(mask[j]);
 }
 
 // boff[b][j] = entries of column j in blocks before b; tot[j] = all of them.
@@ -261,7 +265,7 @@ __device__ __forceinline__ void row_order(const RowSrc<TT> &s, int *__restrict__
 // pos[slot] = colptr[j] + boff[b][j] + (rows of the block before t with an
 // entry in column j).
 template <class TT>
-__global__ __launch_bounds__(BW_THREADS) void k_bw_pos(RowSrc<TT> s, const int *__restrict__ colptr,
+__global__ __launch_bounds__(TR_THREADS) void k_bw_pos(RowSrc<TT> s, const int *__restrict__ colptr,
                                                       const int *__restrict__ boff, int *__restrict__ pos) {
   extern __shared__ unsigned long long mask[];
   const int b = blockIdx.x;
@@ -269,7 +273,7 @@ __global__ __launch_bounds__(BW_THREADS) void k_bw_pos(RowSrc<TT> s, const int *
   const int lane = threadIdx.x & 63;
   const int t_end = min(s.T, (b + 1) * BW_RB);
   const int *bo = boff + (size_t)b * s.F;
-  for (int t = b * BW_RB + (threadIdx.x >> 6); t < t_end; t += BW_WAVES) {
+  for (int t = b * BW_RB + (threadIdx.x >> 6); t < t_end; t += TR_WAVES) {
     const RowList L = row_list(s, t);
     const unsigned long long below = (1ull << (t - b * BW_RB)) - 1ull;
     for (int i = lane; i < L.n; i += 64) {
@@ -333,7 +337,8 @@ __global__ __launch_bounds__(SP_THREADS) void k_bw_entries(RowSrc<typename DtT<D
   const int partner = U == 2 ? 16 : 32;
 
   // the workgroup's rows, one per lane (tok_per_wg <= 64), read once
-  const int my_row = order[min(tb * tok_per_wg + min(lane, tok_per_wg - 1), s.T - 1)];
+  const int r_i = min(tb * tok_per_wg + min(lane, tok_per_wg - 1), s.T - 1);
+  const int my_row = order != nullptr ? order[r_i] : r_i;
   for (int it = wave; it < tok_per_wg; it += SP_WAVES) {
     const int ti = tb * tok_per_wg + it;
     if (ti >= s.T) break;
@@ -509,7 +514,8 @@ __global__ __launch_bounds__(SP_THREADS) void k_bw_dx(RowSrc<typename DtT<D>::T>
   const uint32_t row_bytes = (uint32_t)d * sizeof(TT);
   u32x4_t *C = chunk[wave];
   // the workgroup's rows, one per lane (tok_per_wg <= 64), read once
-  const int my_row = order[min(tb * tok_per_wg + min(lane, tok_per_wg - 1), s.T - 1)];
+  const int r_i = min(tb * tok_per_wg + min(lane, tok_per_wg - 1), s.T - 1);
+  const int my_row = order != nullptr ? order[r_i] : r_i;
   for (int it = wave; it < tok_per_wg; it += SP_WAVES) {
     const int ti = tb * tok_per_wg + it;
     if (ti >= s.T) break;
@@ -671,7 +677,8 @@ __global__ __launch_bounds__(SP_THREADS) void k_bw_dw(const int *__restrict__ co
 static int bw_blocks(int T) { return (T + BW_RB - 1) / BW_RB; }
 
 template <Dt D, int NC>
-static hipError_t launch_entries(const BackwardArgs &a, const RowSrc<typename DtT<D>::T> &s, hipStream_t st) {
+static hipError_t launch_entries(const BackwardArgs &a, const RowSrc<typename DtT<D>::T> &s, const int *order,
+                                 hipStream_t st) {
   using TT = typename DtT<D>::T;
   constexpr int U = NC <= 4 ? 2 : 1;
   // hidden units per group: about 4 MB of W_u and W_d rows (one XCD's L2);
@@ -685,7 +692,7 @@ static hipError_t launch_entries(const BackwardArgs &a, const RowSrc<typename Dt
   const int n_tb = (a.T + tok - 1) / tok;
   hipLaunchKernelGGL((k_bw_entries<D, NC, U>), dim3(padded_groups(n_groups) * n_tb), dim3(SP_THREADS), 0, st, s,
                      (const TT *)a.x, (const TT *)a.dy, (const TT *)a.wu, (const TT *)a.wd, a.lam, a.d, upg,
-                     n_groups, tok, n_tb, a.pos, (f32x2_t *)a.ent, (u32x4_t *)a.csc, a.order);
+                     n_groups, tok, n_tb, a.pos, (f32x2_t *)a.ent, (u32x4_t *)a.csc, order);
   return hipGetLastError();
 }
 
@@ -707,27 +714,31 @@ static hipError_t launch_backward(const BackwardArgs &a, hipStream_t st) {
     if ((e = hipFuncSetAttribute((const void *)k_bw_count<TT>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                  mask_lds)) != hipSuccess)
       return e;
-    hipLaunchKernelGGL(k_bw_count<TT>, dim3(NB), dim3(BW_THREADS), mask_lds, st, s, a.blk);
+    hipLaunchKernelGGL(k_bw_count<TT>, dim3(NB), dim3(TR_THREADS), mask_lds, st, s, a.blk);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   hipLaunchKernelGGL(k_bw_colscan, dim3((a.F + BW_THREADS - 1) / BW_THREADS), dim3(BW_THREADS), 0, st, a.blk, NB,
                      a.F, a.boff, a.tot);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  // the per-row kernels take the long dense rows first only when those rows
+  // are walked entry by entry; with the dense rows on the matrix cores every
+  // list is ELL-short and the rows go in index order (no order array)
+  const int *order = a.T > 0 && !a.dense_mma ? a.order : nullptr;
   hipLaunchKernelGGL(k_bw_colptr<TT>, dim3(1), dim3(COLPTR_THREADS), 0, st, a.tot, a.F, a.colptr, s,
-                     a.T > 0 ? a.order : nullptr);
+                     const_cast<int *>(order));
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int n_slices = a.d / DX_SLICE, n_wslices = a.d / DW_SLICE;
   if (a.T > 0) {
     if ((e = hipFuncSetAttribute((const void *)k_bw_pos<TT>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                  mask_lds)) != hipSuccess)
       return e;
-    hipLaunchKernelGGL(k_bw_pos<TT>, dim3(NB), dim3(BW_THREADS), mask_lds, st, s, a.colptr, a.boff, a.pos);
+    hipLaunchKernelGGL(k_bw_pos<TT>, dim3(NB), dim3(TR_THREADS), mask_lds, st, s, a.colptr, a.boff, a.pos);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int nc = a.d / (64 * (16 / (int)sizeof(TT)));
     switch (nc) {
 #define TWELL_BW_CASE(N)                                            \
   case N:                                                           \
-    if ((e = launch_entries<D, N>(a, s, st)) != hipSuccess) return e; \
+    if ((e = launch_entries<D, N>(a, s, order, st)) != hipSuccess) return e; \
     break;
       TWELL_BW_CASE(1) TWELL_BW_CASE(2) TWELL_BW_CASE(3) TWELL_BW_CASE(4)
       TWELL_BW_CASE(5) TWELL_BW_CASE(6) TWELL_BW_CASE(7) TWELL_BW_CASE(8)
@@ -739,7 +750,7 @@ static hipError_t launch_backward(const BackwardArgs &a, hipStream_t st) {
     const int n_tb = (a.T + tok - 1) / tok;
     hipLaunchKernelGGL((k_bw_dx<D, 4>), dim3(padded_groups(n_slices) * n_tb), dim3(SP_THREADS), 0, st, s,
                        (const f32x2_t *)a.ent, (const TT *)a.wu, (const TT *)a.wg, (TT *)a.dx, a.d, n_slices, tok,
-                       n_tb, a.order);
+                       n_tb, order);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   // the dense rows on the matrix cores: their dx rows (after the entry
