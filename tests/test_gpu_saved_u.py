@@ -212,3 +212,56 @@ def test_forward_saves_u_full_size(name):
     rows = np.unique(np.concatenate([rng.choice(w.T, 24, replace=False), np.arange(0, w.T, 2048)[:4]]))
     host = {"cnt": p.cnt.cpu().numpy().view(np.uint16), "idx": p.idx.cpu().numpy()}
     _check_forward_u(p.u.cpu().numpy(), host, inp, w.tile, w.cap, rows)
+
+
+WALKED_CASES = [
+    # dtype, T, d, F, width, density, hot rows (hidden sizes that are not a
+    # multiple of 128: the dense rows are walked entry by entry beside the
+    # saved-u ELL rows)
+    ("bf16", 61, 512, 320, 8, 0.01, (2, 30)),
+    ("f32", 50, 256, 448, 4, 0.005, (1, 7)),
+]
+
+
+@pytest.mark.parametrize("dtype,T,d,F,width,rho,hot", WALKED_CASES)
+def test_caller_built_hybrid_with_u_and_walked_dense_rows(dtype, T, d, F, width, rho, hot):
+    """A hybrid built by the oracle and uploaded, with the float64 u of every
+    ELL entry rounded to fp32 and every third ELL row marked not saved (NaN
+    in its first slot): the backward takes u from the hybrid where it is
+    saved, recomputes it elsewhere (marked rows, dense rows) and must match the
+    float64 oracle with the tolerances of the other backward tests."""
+    import torch
+    from oracle.hybrid import hybrid
+    from test_gpu_backward import hybrid_to_dev
+    print(f"caller-built hybrid with u {dtype} T={T} d={d} F={F} width={width}", flush=True)
+    inp = ffn_inputs(T, d, F, dtype, seed=5 * T + F, gate_bias=_bias(T, rho, hot, 0.4))
+    pre = round_to_storage(gate_pre(inp.x, inp.w_gate, inp.gate_bias, dtype), dtype)
+    h = relu_storage(pre, dtype)
+    hy = hybrid(h, dtype, width)
+    assert hy.n_dense > 0, "the case must hold dense rows"
+    ell = np.nonzero(hy.cnt <= width)[0]
+    used = np.arange(width)[None, :] < np.minimum(hy.cnt, width)[:, None]
+    units = np.where(used, hy.col, -1)
+    u64, _ = _u64(inp, np.arange(T), units)
+    u32 = np.where(used, u64, 0.0).astype(np.float32)
+    marked = ell[(hy.cnt[ell] > 0)][::3]
+    u32[marked, 0] = np.nan
+    assert marked.size > 0
+    hd = hybrid_to_dev(hy, F, dtype)
+    hd.u = torch.from_numpy(np.ascontiguousarray(u32)).to("cuda:0")
+    dy = grad_output(T, d, dtype, seed=T)
+    lam = float(np.float32(2e-5))
+    ref = ffn_backward(inp.x, inp.w_gate, inp.w_up, inp.w_down, h, dy, lam, dtype)
+    x, wg, wu, wd, _ = dev_inputs(inp)
+    out = tw.twell_ffn_backward(hd, x, wg, wu, wd, to_dev(dy, dtype), lam)
+    torch.cuda.synchronize()
+    got = {"dx": decode(from_dev(out[0], dtype), dtype)}
+    for k, t_ in zip(KEYS[1:], out[1:]):
+        got[k] = t_.cpu().numpy().astype(np.float64)
+    for k in KEYS:
+        tol = DX_TOL[dtype] if k == "dx" else DW_TOL
+        g, r = got[k], ref[k]
+        err = np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-300)
+        assert err <= tol, f"{k}: relative L2 error {err:.3e} > {tol:g}"
+        zero = np.linalg.norm(r, axis=1) == 0
+        assert np.all(g[zero] == 0), f"{k}: rows with no active entry must be exactly zero"
