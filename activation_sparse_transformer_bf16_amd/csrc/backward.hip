@@ -25,8 +25,9 @@
 //                     L2), then du, dpre and a; written per entry and, in
 //                     column order, to the transposed lists
 //   k_bw_dx           per (row, column slice of d): dx over the row's entries
-//   k_bw_dw           per (hidden unit, column slice): dW_u, dW_g and dW_d
-//                     rows over the unit's transposed list
+//   k_bw_dw           per (hidden unit, column slice): dW_u and dW_g rows
+//                     over the unit's transposed list (x rows), then in a
+//                     second launch dW_d (dy rows)
 // and, when the hidden size allows it (a multiple of 128), the dense backup
 // rows on the matrix cores (bw_dense.hip) between k_bw_dx and k_bw_dw; their
 // lists are empty here.  Otherwise k_bw_dense_cols lists their active columns
@@ -48,7 +49,7 @@ constexpr int TR_THREADS = 1024;
 constexpr int TR_WAVES = TR_THREADS / 64;
 constexpr int BW_RB = 64;     // rows per block of the transpose (one bit each)
 constexpr int DX_SLICE = 128; // columns of d per dx slice
-constexpr int DW_SLICE = 128; // columns of d per dW slice
+constexpr int DW_SLICE = 256; // columns of d per dW slice
 
 template <class TT>
 struct RowSrc {
@@ -585,7 +586,8 @@ __device__ __forceinline__ void load_base(f32x4_t (&b)[CPL / 4], const float *p,
   for (int q = 0; q < CPL; q += 4) b[q / 4] = on ? *reinterpret_cast<const f32x4_t *>(p + q) : f32x4_t{};
 }
 
-template <Dt D, int U>
+// PART 0 forms dW_g and dW_u from the x rows, PART 1 dW_d from the dy rows.
+template <Dt D, int U, int PART>
 __global__ __launch_bounds__(SP_THREADS) void k_bw_dw(const int *__restrict__ colptr, const u32x4_t *__restrict__ csc,
                                                      const typename DtT<D>::T *__restrict__ x,
                                                      const typename DtT<D>::T *__restrict__ dy,
@@ -619,9 +621,12 @@ __global__ __launch_bounds__(SP_THREADS) void k_bw_dw(const int *__restrict__ co
     const int c0 = colptr[j], n = colptr[j + 1] - c0;
     const size_t o = (size_t)j * d + sl * DW_SLICE + lcol;
     f32x4_t bg[CPL / 4], bu[CPL / 4], bd[CPL / 4];
-    load_base<CPL>(bg, dwg + o, add && part == 0);
-    load_base<CPL>(bu, dwu + o, add && part == 0);
-    load_base<CPL>(bd, dwd + o, add && part == 0);
+    if (PART == 0) {
+      load_base<CPL>(bg, dwg + o, add && part == 0);
+      load_base<CPL>(bu, dwu + o, add && part == 0);
+    } else {
+      load_base<CPL>(bd, dwd + o, add && part == 0);
+    }
     float ag[CPL], au[CPL], ad[CPL];
 #pragma unroll
     for (int v = 0; v < CPL; ++v) ag[v] = au[v] = ad[v] = 0.f;
@@ -645,14 +650,17 @@ __global__ __launch_bounds__(SP_THREADS) void k_bw_dw(const int *__restrict__ co
           cu[u] = ok ? __uint_as_float(en[2]) : 0.f;
           cg[u] = ok ? __uint_as_float(en[3]) : 0.f;
           const uint32_t ro = ok ? en[0] : NO_ROW;  // past the list: loads return zeros
-          a[u] = buffer_load<u32x4_t>(xr, lane_off + ro, 0u);
-          b[u] = buffer_load<u32x4_t>(gr, lane_off + ro, 0u);
+          if (PART == 0) a[u] = buffer_load<u32x4_t>(xr, lane_off + ro, 0u);
+          else b[u] = buffer_load<u32x4_t>(gr, lane_off + ro, 0u);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          fma16<D>(ag, cg[u], a[u]);
-          fma16<D>(au, cu[u], a[u]);
-          fma16<D>(ad, ca[u], b[u]);
+          if (PART == 0) {
+            fma16<D>(ag, cg[u], a[u]);
+            fma16<D>(au, cu[u], a[u]);
+          } else {
+            fma16<D>(ad, ca[u], b[u]);
+          }
         }
       }
       wave_sync_lds();
@@ -664,9 +672,12 @@ __global__ __launch_bounds__(SP_THREADS) void k_bw_dw(const int *__restrict__ co
       ad[v] = add_parts<EPI>(ad[v]);
     }
     if (part == 0) {
-      store_f32<CPL>(dwg + o, ag, bg);
-      store_f32<CPL>(dwu + o, au, bu);
-      store_f32<CPL>(dwd + o, ad, bd);
+      if (PART == 0) {
+        store_f32<CPL>(dwg + o, ag, bg);
+        store_f32<CPL>(dwu + o, au, bu);
+      } else {
+        store_f32<CPL>(dwd + o, ad, bd);
+      }
     }
   }
 }
@@ -762,7 +773,15 @@ static hipError_t launch_backward(const BackwardArgs &a, hipStream_t st) {
   }
   const int upw = 8;  // units per workgroup; 8 loads in flight per lane (fastest in a sweep)
   const int n_ub = (a.F + upw - 1) / upw;
-  hipLaunchKernelGGL((k_bw_dw<D, 8>), dim3(padded_groups(n_wslices) * n_ub), dim3(SP_THREADS), 0, st, a.colptr,
+  // two passes over the transposed lists: x rows (dW_g, dW_u), then dy rows
+  // (dW_d), so that each pass keeps one 256-column slice of one matrix per
+  // XCD (4 MB at 8192 rows) and its loads cover two rows each
+  constexpr int UDW = 8;
+  hipLaunchKernelGGL((k_bw_dw<D, UDW, 0>), dim3(padded_groups(n_wslices) * n_ub), dim3(SP_THREADS), 0, st, a.colptr,
+                     (const u32x4_t *)a.csc, (const TT *)a.x, (const TT *)a.dy, a.dwg, a.dwu, a.dwd, a.T, a.F, a.d,
+                     n_wslices, upw, n_ub, a.n_dense, a.dense_cap, a.dense_mma);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((k_bw_dw<D, UDW, 1>), dim3(padded_groups(n_wslices) * n_ub), dim3(SP_THREADS), 0, st, a.colptr,
                      (const u32x4_t *)a.csc, (const TT *)a.x, (const TT *)a.dy, a.dwg, a.dwu, a.dwd, a.T, a.F, a.d,
                      n_wslices, upw, n_ub, a.n_dense, a.dense_cap, a.dense_mma);
   return hipGetLastError();
