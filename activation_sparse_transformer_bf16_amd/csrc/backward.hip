@@ -346,8 +346,27 @@ __global__ __launch_bounds__(SP_THREADS) void k_bw_entries(RowSrc<typename DtT<D
     const int t = min(max(__builtin_amdgcn_readlane(my_row, it), 0), s.T - 1);  // a valid hybrid gives a permutation
     const RowList L = row_list(s, t);
     if (L.n == 0) continue;
-    const int eb = wave_lower_bound(L.col, L.n, j0);
-    const int ee = wave_lower_bound(L.col, L.n, j1);
+    // the row's entries in [j0, j1): its (ascending) columns below j0 and j1
+    // counted in one pass of independent loads for an ELL-sized row, a
+    // search otherwise
+    int eb, ee;
+    if (L.n <= 256) {
+      int cb = 0, ce = 0;
+#pragma unroll
+      for (int k = 0; k < 256; k += 64) {
+        if (k < L.n) {
+          const int p = k + lane;
+          const int c = p < L.n ? L.col[p] : 0x7FFFFFFF;
+          cb += popc64(ballot(c < j0));
+          ce += popc64(ballot(c < j1));
+        }
+      }
+      eb = cb;
+      ee = ce;
+    } else {
+      eb = wave_lower_bound(L.col, L.n, j0);
+      ee = wave_lower_bound(L.col, L.n, j1);
+    }
     if (eb >= ee) continue;
     // the row's u saved by the forward (an ELL row whose first slot holds a
     // number): x_t is not needed and only the W_d rows are gathered
