@@ -340,6 +340,58 @@ def backward_timing(w, hy, x, wg, wu, wd, b, nnz_all, steps, warmup, want_torch)
     return backward
 
 
+def training_step_timing(w, x, wg, wu, wd, b, ws, y, packed_tr, hy, steps, warmup, want_torch):
+    """One training step of the layer on this batch, timed as one sequence:
+    the forward that saves u (twell_ffn_forward with packed.u), the TwELL ->
+    hybrid conversion, the L1 norm of h and the backward (dx and the three
+    weight gradients with the L1 term); beside it torch's dense forward and
+    backward of the same layer (bf16 matmuls, h and u kept)."""
+    import torch
+
+    import activation_sparse_transformer_bf16_amd as tw
+    from workloads.synth import grad_output
+    dev = x.device
+    T, d, F = w.T, w.d, w.F
+    dy = to_dev(grad_output(T, d, w.dtype, seed=0), w.dtype, dev)
+    bw_ws = torch.empty((tw.twell_ffn_backward_workspace_size(T, d, F, HYBRID_WIDTH, hy.dense_cap, x.dtype),),
+                        dtype=torch.uint8, device=dev)
+    l1_out = torch.empty((1,), dtype=torch.float64, device=dev)
+    l1_ws = torch.empty((tw.twell_l1_workspace_size(),), dtype=torch.uint8, device=dev)
+    dxb = torch.empty_like(x)
+    dwb = [torch.empty((F, d), dtype=torch.float32, device=dev) for _ in range(3)]
+
+    def step():
+        tw.twell_ffn_forward(x, wg, wu, wd, b, packed=packed_tr, y=y, workspace=ws)
+        tw.twell_to_hybrid(packed_tr, HYBRID_WIDTH, out=hy)
+        tw.twell_l1_norm(packed_tr, out=l1_out, workspace=l1_ws)
+        tw.twell_ffn_backward(hy, x, wg, wu, wd, dy, L1_LAMBDA, dxb, *dwb, workspace=bw_ws)
+
+    ms_step, _ = event_time(step, steps, warmup)
+    out = {"us": ms_step * 1e3, "tokens_per_s": T / (ms_step * 1e-3),
+           "note": "forward saving u + TwELL->hybrid + L1 norm + backward (dx, dW_g, dW_u, dW_d with the L1 term), "
+                   "one sequence on the launch stream, warm"}
+    log(f"[bench] {w.name} training step (forward + hybrid + L1 + backward) {ms_step * 1e3:.1f} us")
+    if want_torch:
+        bcol = b[:, None].to(x.dtype)
+
+        def torch_step():  # dense forward keeping h and u, then the dense backward
+            hd = torch.relu(torch.addmm(bcol, x, wg.t()))
+            ud = x @ wu.t()
+            a = hd * ud
+            yt = a @ wd
+            da = dy @ wd.t()
+            du = da * hd
+            dp = (da * ud + L1_LAMBDA) * (hd > 0)
+            return yt, du @ wu + dp @ wg, du.t() @ x, dp.t() @ x, a.t() @ dy
+
+        ms_t, _ = event_time(torch_step, steps, warmup)
+        out["torch_dense_step_us"] = ms_t * 1e3
+        out["speedup_vs_torch_dense_step"] = ms_t / ms_step
+        log(f"[bench] torch (hipBLASLt) dense training step {ms_t * 1e3:.1f} us")
+    del dy, bw_ws, l1_out, l1_ws, dxb, dwb
+    return out
+
+
 def measure(w, steps, warmup, want_torch=True, want_cold=True):
     import numpy as np
     import torch
@@ -438,6 +490,8 @@ def measure(w, steps, warmup, want_torch=True, want_cold=True):
     # Backward from these hybrid activations (every dense row kept): dx and
     # the three weight gradients with the L1 term, for a seeded dy.
     backward = backward_timing(w, hy, x, wg, wu, wd, b, nnz_all, steps, warmup, want_torch)
+    backward["training_step"] = training_step_timing(w, x, wg, wu, wd, b, ws, y, packed_tr, hy, steps, warmup,
+                                                     want_torch)
     del packed_tr, hy
 
     # Standalone twell_pack of this batch's rounded gate pre-activations
