@@ -1,5 +1,7 @@
-"""GPU parity on seeded random shapes: forward (two-kernel and fused), TwELL ->
-hybrid, and backward, each against the oracle, over shapes, tiles, capacities,
+"""GPU parity on seeded random shapes: forward (two-kernel, fused, and the
+hidden-group-major fused kernel over tile-major records), the training forward
+that saves u, TwELL -> hybrid, and backward (u recomputed, and u carried from
+the TwELL matrix), each against the oracle, over shapes, tiles, capacities,
 densities and ELL widths drawn within the documented limits.
 
 The cases are drawn once from a fixed seed, so every run checks the same
@@ -17,6 +19,7 @@ from oracle.twell import pack, relu_storage
 from workloads.synth import ffn_inputs, gate_bias_for_density, grad_output
 
 from gpu_util import TOL, assert_bitwise, check_y, dev_inputs, from_dev, packed_to_host, to_dev, torch_dtype
+from test_gpu_saved_u import _check_forward_u, _slot_units, _u64
 
 pytestmark = pytest.mark.gpu
 
@@ -64,10 +67,19 @@ def test_random_case(dtype, T, d, F, tile, cap, rho, hot, width):
     packed = tw.TwellMatrix.empty(T, F, tile, cap, x.dtype, x.device, T, dense=True)
     y, packed = tw.twell_ffn_forward(x, wg, wu, wd, b, packed=packed)
     check_y(from_dev(y, dtype), inp, dtype)
-    # forward, fused up+down
+    # forward, fused up+down; the hidden-group-major one also over tile-major records
     if fused_ok:
         p2, _ = tw.twell_gate_pack(x, wg, b, tile=tile, cap=cap, scan=False)
         check_y(from_dev(tw.twell_sparse_ffn_fused(p2, x, wg, wu, wd, b), dtype), inp, dtype)
+        pt = tw.TwellMatrix.empty(T, F, tile, cap, x.dtype, x.device, T, dense=True, layout="tiles")
+        tw.twell_gate_pack(x, wg, b, packed=pt, scan=False)
+        check_y(from_dev(tw.twell_sparse_ffn_grouped(pt, x, wg, wu, wd, b), dtype), inp, dtype)
+    # the training forward saving u: y bit for bit the same, every saved u within
+    # the fp32 bound of its float64 dot product
+    pu = tw.TwellMatrix.empty(T, F, tile, cap, x.dtype, x.device, T, dense=True, u=True)
+    yu, _ = tw.twell_ffn_forward(x, wg, wu, wd, b, packed=pu)
+    assert_bitwise(from_dev(yu, dtype), from_dev(y, dtype), "y with u")
+    _check_forward_u(pu.u.cpu().numpy(), packed_to_host(pu, dtype), inp, tile, cap, np.arange(T))
 
     # TwELL -> hybrid on an oracle-packed matrix, bit for bit
     h = relu_storage(round_to_storage(gate_pre(inp.x, inp.w_gate, inp.gate_bias, dtype), dtype), dtype)
@@ -91,14 +103,23 @@ def test_random_case(dtype, T, d, F, tile, cap, rho, hot, width):
     if hy.n_dense:
         assert_bitwise(from_dev(hy_dev.dense, dtype)[:hy.n_dense], hy.dense, "dense")
 
-    # backward from those hybrid activations
+    # backward from those hybrid activations, then again with the oracle's u
+    # (float64 dot products rounded to fp32, NaN for overflow rows) carried
+    # through the conversion
     if F <= 16384:
         dy = grad_output(T, d, dtype, seed=T + 1)
         lam = float(np.float32(2e-5))
-        dx, dwg, dwu, dwd = tw.twell_ffn_backward(hy_dev, x, wg, wu, wd, to_dev(dy, dtype), lam)
-        torch.cuda.synchronize()
         ref = ffn_backward(inp.x, inp.w_gate, inp.w_up, inp.w_down, h, dy, lam, dtype)
-        assert rel_l2(decode(from_dev(dx, dtype), dtype), ref["dx"]) <= TOL[dtype]
-        for k, g in (("dw_gate", dwg), ("dw_up", dwu), ("dw_down", dwd)):
-            err = rel_l2(g.cpu().numpy().astype(np.float64), ref[k])
-            assert err <= 1e-5, f"{k}: {err:.3e}"
+        units = _slot_units(ref_p.cnt, ref_p.idx, tile, cap).reshape(T, -1)
+        u64, _ = _u64(inp, np.arange(T), units)
+        u32 = np.where(units >= 0, u64, 0.0).astype(np.float32)
+        u32[(ref_p.cnt > cap).any(axis=1)] = np.nan
+        pd.u = torch.from_numpy(np.ascontiguousarray(u32.reshape(ref_p.val.shape))).to(x.device)
+        hy_u = tw.twell_to_hybrid(pd, width)
+        for hy_in in (hy_dev, hy_u):
+            dx, dwg, dwu, dwd = tw.twell_ffn_backward(hy_in, x, wg, wu, wd, to_dev(dy, dtype), lam)
+            torch.cuda.synchronize()
+            assert rel_l2(decode(from_dev(dx, dtype), dtype), ref["dx"]) <= TOL[dtype]
+            for k, g in (("dw_gate", dwg), ("dw_up", dwu), ("dw_down", dwd)):
+                err = rel_l2(g.cpu().numpy().astype(np.float64), ref[k])
+                assert err <= 1e-5, f"{k}: {err:.3e}"
