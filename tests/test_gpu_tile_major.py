@@ -49,8 +49,10 @@ def test_gate_tile_major_exact_inputs_bitwise(dtype, T, d, F, tile, cap, rho):
     print(f"tile-major gate exact {dtype} T={T} d={d} F={F} tile={tile} cap={cap}", flush=True)
     inp = exact_gate_inputs(T, d, F, dtype, seed=T + d, density=rho)
     x, wg, _, _, b = dev_inputs(inp)
-    p, _ = tw.twell_gate_pack(x, wg, b, packed=_tiles(T, F, tile, cap, x))
-    ref = pack(round_to_storage(gate_pre(inp.x, inp.w_gate, inp.gate_bias, dtype), dtype), dtype, tile, cap)
+    p, pre = tw.twell_gate_pack(x, wg, b, packed=_tiles(T, F, tile, cap, x), pre_out=True)
+    want_pre = round_to_storage(gate_pre(inp.x, inp.w_gate, inp.gate_bias, dtype), dtype)
+    assert_bitwise(from_dev(pre, dtype), want_pre, "pre_out (row-major whatever the TwELL layout)")
+    ref = pack(want_pre, dtype, tile, cap)
     cnt_t, val_t, idx_t = tile_major(ref)
     host = packed_to_host(p, dtype)
     assert_bitwise(host["cnt"], cnt_t, "cnt")
@@ -130,3 +132,16 @@ def test_grouped_over_tile_major_full_size(name):
     rng = np.random.default_rng(2)
     rows = np.unique(np.concatenate([rng.choice(w.T, 24, replace=False), pt.ovf_rows[:min(n_ovf, 8)].cpu().numpy()]))
     check_y(yh, inp, w.dtype, rows=rows)
+
+
+def test_tile_major_empty_batch():
+    """T = 0: the gate writes nothing and the grouped kernel returns an empty y
+    with n_ovf = 0."""
+    import torch
+    x = torch.zeros((0, 512), dtype=torch.bfloat16, device="cuda:0")
+    w = torch.zeros((512, 512), dtype=torch.bfloat16, device="cuda:0")
+    pt = tw.TwellMatrix.empty(0, 512, 256, 16, x.dtype, x.device, 0, dense=True, layout="tiles")
+    tw.twell_gate_pack(x, w, None, packed=pt)
+    y = tw.twell_sparse_ffn_grouped(pt, x, w, w, w, None)
+    torch.cuda.synchronize()
+    assert y.shape == (0, 512) and int(pt.n_ovf.item()) == 0
