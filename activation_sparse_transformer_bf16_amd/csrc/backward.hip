@@ -16,14 +16,16 @@
 //                     LDS; writes the per-column entry counts of the block
 //   k_bw_colscan      per column, the running count over the blocks
 //   k_bw_colptr       column starts of the transposed (column-major) lists,
-//                     and the order in which the per-row kernels take the
-//                     rows: the long dense rows first
+//                     and, when the dense rows are walked entry by entry,
+//                     the order in which the per-row kernels take the rows:
+//                     the long dense rows first
 //   k_bw_pos          each entry's place in its column's list: rows in
 //                     ascending order, from the same LDS row masks
 //   k_bw_entries      per (row, group of hidden units): u and da by gathering
 //                     W_u and W_d rows (the group's rows stay in one XCD's
-//                     L2), then du, dpre and a; written per entry and, in
-//                     column order, to the transposed lists
+//                     L2; W_d rows only where the forward saved u), then du,
+//                     dpre and a; written per entry and, in column order, to
+//                     the transposed lists
 //   k_bw_dx           per (row, column slice of d): dx over the row's entries
 //   k_bw_dw           per (hidden unit, column slice): dW_u and dW_g rows
 //                     over the unit's transposed list (x rows), then in a
@@ -184,7 +186,8 @@ constexpr int COLPTR_THREADS = 1024;
 template <class TT>
 __device__ __forceinline__ void row_order(const RowSrc<TT> &s, int *__restrict__ order, int *wcount);
 
-// Also writes the row order of the per-row kernels (row_order, below).
+// With an order array, also writes the row order of the per-row kernels
+// (row_order, below).
 template <class TT>
 __global__ __launch_bounds__(COLPTR_THREADS) void k_bw_colptr(const int *__restrict__ tot, int F,
                                                              int *__restrict__ colptr, RowSrc<TT> s,
