@@ -618,7 +618,7 @@ def extra_workloads(args, base_inp):
                "forward_warm_us": r["sparse_warm"]["back_to_back_mean_us"],
                "dense_warm_us": r["dense_warm"]["back_to_back_mean_us"],
                "sparse_tokens_per_s": r["tokens_per_s"],
-               "dense_tokens_per_s": r["tokens_per_s"] * r["speedup_vs_dense"],
+               "dense_tokens_per_s": r["tokens_per_s"] / r["speedup_vs_dense"],
                "speedup_vs_dense": r["speedup_vs_dense"], "speedup_vs_dense_warm": r["speedup_vs_dense_warm"],
                "gate_tflops": r["gate_tflops"]}
         sweep.append(rec)
