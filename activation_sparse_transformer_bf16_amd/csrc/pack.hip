@@ -3,17 +3,20 @@
 //
 // Format: gist.science "Sparser, Faster, Lighter Transformer Language Models",
 // Resumen Técnico §2.A (column tiles, per-tile non-zeros; rows that overflow
-// go to a dense backup matrix).  One wave packs one row.  Every lane loads 16
-// bytes of the row per load instruction, so one load covers 64 * 16 bytes:
-// one tile (fp32, 256 columns), two or four.  The lanes of a tile form a
-// segment.  Per-element activity ballots counted over the lanes below (mbcnt),
-// less the non-zeros of the earlier segments, give the ascending rank of each
-// non-zero inside its tile.  The first `cap`
-// non-zeros of a tile, their local columns and the tile's count are filed in
-// a per-wave LDS image of the chunk's TwELL output (zero-initialised, so the
-// padding is +0 / 0), which the wave then writes out with 16-byte stores.
-// The pass streams the matrix once from HBM.  With a flag array, the wave also
-// records whether its row overflows (some tile counts more than cap).
+// go to a dense backup matrix).  One wave packs one row, a chunk of
+// PACK_LOADS loads at a time.  Every lane loads 16 bytes of the row per load
+// instruction, so one load covers 64 * 16 bytes: one tile (fp32, 256
+// columns), two or four.  The lanes of a tile form a segment.  Per load, each
+// lane turns its elements into activity bits; a wave prefix sum of the lanes'
+// counts, less the non-zeros of the earlier segments, gives the rank of the
+// lane's first non-zero in its tile, and the segment ends give the tile
+// counts.  After the chunk's loads, each lane walks its own non-zeros (few at
+// high sparsity) in ascending column order and files the first `cap` of each
+// tile, with their local columns, in a per-wave LDS image of the chunk's TwELL
+// output (zero-initialised, so the padding is +0 / 0), which the wave then
+// writes out with 16-byte stores.  The pass streams the matrix once from HBM.
+// With a flag array, the wave also records whether its row overflows (some
+// tile counts more than cap).
 #include "gather.hpp"
 #include "launch.hpp"
 
@@ -26,13 +29,15 @@ constexpr int PACK_LOADS = 8;  // 16-byte loads per lane in flight per chunk
 __host__ __device__ constexpr int pack_align16(int n) { return (n + 15) & ~15; }
 
 // Tiles per chunk (PACK_LOADS loads of 64 x 16 bytes) and the per-wave LDS
-// bytes of one chunk's output image: values | local columns | counts.
+// bytes of one chunk: its output image (values | local columns | counts) and
+// the stash of the loads of lanes that hold a non-zero ([PACK_LOADS][64][16]).
 __host__ __device__ constexpr int pack_chunk_tiles(int tile, int elem_bytes) {
   return PACK_LOADS * (64 / (tile / (16 / elem_bytes)));
 }
 __host__ __device__ constexpr int pack_stage_bytes(int tile, int elem_bytes, int cap) {
   return pack_align16(pack_chunk_tiles(tile, elem_bytes) * cap * elem_bytes) +
-         pack_align16(pack_chunk_tiles(tile, elem_bytes) * cap) + pack_align16(pack_chunk_tiles(tile, elem_bytes) * 2);
+         pack_align16(pack_chunk_tiles(tile, elem_bytes) * cap) + pack_align16(pack_chunk_tiles(tile, elem_bytes) * 2) +
+         PACK_LOADS * 64 * 16;
 }
 
 // Wave-cooperative copy of n bytes from LDS to global memory, with the widest
@@ -53,18 +58,44 @@ __device__ __forceinline__ void pack_copy_out(char *dst, const char *src, int n,
   }
 }
 
+// Activity of the EPL elements of a 16-byte load as bits, element 0 in the
+// highest of the EPL bits (each step doubles and adds one flag).
 template <class TT, int EPL>
-__device__ __forceinline__ void unpack16(const u32x4_t &w, TT (&o)[EPL]) {
-  if constexpr (sizeof(TT) == 2) {
+__device__ __forceinline__ uint32_t active_mask16(const u32x4_t &w);
+template <>
+__device__ __forceinline__ uint32_t active_mask16<uint16_t, 8>(const u32x4_t &w) {
+  typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+  uint32_t bits = 0;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      o[2 * e] = (uint16_t)(w[e] & 0xFFFFu);
-      o[2 * e + 1] = (uint16_t)(w[e] >> 16);
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) o[e] = __uint_as_float(w[e]);
+  for (int k = 0; k < 4; ++k) {
+    // bf16 bits b active iff 1 <= b <= 0x7F80, i.e. (b - 1) mod 2^16 < 0x7F80.
+    // The element goes through a scalar: bit-casting a vector element
+    // expression directly reads the vector's first element with this compiler.
+    const uint32_t wk = w[k];
+    const us2 m = __builtin_bit_cast(us2, wk) - (us2){1, 1};
+    bits = bits + bits + (m.x < 0x7F80 ? 1u : 0u);
+    bits = bits + bits + (m.y < 0x7F80 ? 1u : 0u);
   }
+  return bits;
+}
+template <>
+__device__ __forceinline__ uint32_t active_mask16<float, 4>(const u32x4_t &w) {
+  uint32_t bits = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) bits = bits + bits + (active_bits(__uint_as_float(w[k])) ? 1u : 0u);
+  return bits;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts and
+// row broadcasts (every lane active).
+__device__ __forceinline__ int wave_incl_scan_dpp(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);  // row_shr 1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);  // row_shr 2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);  // row_shr 4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);  // row_shr 8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast15 into rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast31 into rows 2, 3
+  return v;
 }
 
 template <Dt D, int TILE>
@@ -78,6 +109,7 @@ __global__ __launch_bounds__(PACK_THREADS) void k_pack(const typename DtT<D>::T 
   constexpr int TPL = 64 / LPT;         // tiles per load
   constexpr int CH = PACK_LOADS * TPL;  // tiles per chunk
   static_assert(CH == pack_chunk_tiles(TILE, sizeof(TT)), "chunk layout");
+  static_assert(PACK_LOADS * EPL <= 64 && PACK_LOADS <= 8, "a chunk's flags in 64 bits, its rank bases in 8 bytes");
   extern __shared__ __align__(16) char pack_lds[];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t = blockIdx.x * PACK_WAVES + wave;
@@ -88,6 +120,7 @@ __global__ __launch_bounds__(PACK_THREADS) void k_pack(const typename DtT<D>::T 
   TT *sv = reinterpret_cast<TT *>(stage);
   uint8_t *si = reinterpret_cast<uint8_t *>(stage + vbytes);
   uint16_t *sc = reinterpret_cast<uint16_t *>(stage + vbytes + ibytes);
+  char *stash = stage + vbytes + ibytes + pack_align16(CH * 2);  // [PACK_LOADS][64 lanes][16 bytes]
   const int seg = lane / LPT, seg_lo = seg * LPT;
   // The row as a buffer of F * s bytes: loads past its last tile return 0 (the
   // range check covers the per-lane offset, which carries the whole offset).
@@ -104,49 +137,58 @@ __global__ __launch_bounds__(PACK_THREADS) void k_pack(const typename DtT<D>::T 
     for (int q = 0; q < PACK_LOADS; ++q)
       raw[q] = buffer_load<u32x4_t>(rsrc, voff + (uint32_t)((k0 + q * TPL) * TILE * sizeof(TT)), 0u);
     wave_sync_lds();
+    // Per load: the lane's active elements as bits, its rank base in the
+    // tile (kept for the walk below, one byte per load), the tile counts;
+    // lanes with an active element stash their 16 bytes for the walk.
+    uint64_t all = 0;           // load q's bits at [(PACK_LOADS-1-q) * EPL, +EPL), element 0 highest
+    uint32_t r0lo = 0, r0hi = 0;  // rank base of loads 0-3 and 4-7, a byte each
 #pragma unroll
     for (int q = 0; q < PACK_LOADS; ++q) {
       const int kc = q * TPL + seg;  // tile inside the chunk
-      TT v[EPL];
-      unpack16<TT, EPL>(raw[q], v);
-      bool act[EPL];
-      uint32_t below = 0;  // non-zeros of this load in the lanes below (whole wave)
-      int own = 0;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        act[e] = active_bits(v[e]);  // +0 for the lanes past the last tile: inactive
-        const uint64_t m = ballot(act[e]);
-        below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, below));
-        own += act[e] ? 1 : 0;
-      }
+      uint32_t bits = active_mask16<TT, EPL>(raw[q]);  // +0 past the last tile: inactive
+      const int own = __builtin_popcount(bits);
+      const int incl = wave_incl_scan_dpp(own);
       // Non-zeros of the earlier segments (base) and up to the end of this
-      // segment, read from the segments' first and last lanes.
-      const int incl = (int)below + own;
+      // segment, read from the segments' last lanes.
       int base = 0, end = 0;
 #pragma unroll
       for (int sg = 0; sg < TPL; ++sg) {
-        const int b = sg == 0 ? 0 : __builtin_amdgcn_readlane((int)below, sg * LPT);
+        const int b = sg == 0 ? 0 : __builtin_amdgcn_readlane(incl, sg * LPT - 1);
         const int en = __builtin_amdgcn_readlane(incl, sg * LPT + LPT - 1);
         if (seg == sg) {
           base = b;
           end = en;
         }
       }
-      if (own > 0) {
-        int r = (int)below - base;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-          if (act[e]) {
-            if (r < cap) {
-              sv[kc * cap + r] = v[e];
-              si[kc * cap + r] = (uint8_t)((lane - seg_lo) * EPL + e);
-            }
-            ++r;
-          }
-        }
-      }
+      const int r0 = incl - own - base;  // rank of the lane's first non-zero in the tile
+      if (r0 >= cap) bits = 0;            // past the tile's capacity: nothing to file
+      if (bits != 0) *reinterpret_cast<u32x4_t *>(stash + (q * 64 + lane) * 16) = raw[q];
+      all |= (uint64_t)bits << ((PACK_LOADS - 1 - q) * EPL);
+      const uint32_t rb = bits != 0 ? (uint32_t)r0 : 0u;  // < cap <= 64 where it is read back
+      if (q < 4)
+        r0lo |= rb << (q * 8);
+      else
+        r0hi |= rb << ((q - 4) * 8);
       if (lane == seg_lo) sc[kc] = (uint16_t)(end - base);
       ovf |= ballot(lane == seg_lo && end - base > cap) != 0;
+    }
+    // The lane's non-zeros of the chunk in ascending (load, element) order,
+    // i.e. ascending column inside each tile; k counts those of the same load
+    // already filed.
+    int cur = -1, k = 0;
+    while (all != 0) {
+      const int hb = 63 - __builtin_clzll(all);
+      all ^= 1ull << hb;
+      const int pos = PACK_LOADS * EPL - 1 - hb;
+      const int q = pos / EPL, e = pos % EPL;
+      k = q == cur ? k + 1 : 0;
+      cur = q;
+      const int r = (int)(((q < 4 ? r0lo : r0hi) >> ((q & 3) * 8)) & 0xFFu) + k;
+      if (r < cap) {
+        const int kc = q * TPL + seg;
+        sv[kc * cap + r] = *reinterpret_cast<const TT *>(stash + (q * 64 + lane) * 16 + e * (int)sizeof(TT));
+        si[kc * cap + r] = (uint8_t)((lane - seg_lo) * EPL + e);
+      }
     }
     wave_sync_lds();
     const size_t slot0 = ((size_t)t * nt + k0) * cap;
