@@ -28,6 +28,11 @@ CASES = [
     (96, 512, 128, 64, 0.3, (), True),              # cap 64, dense rows
     (50, 768, 256, 16, 0.0, (), False),             # no active unit at all
     (40, 512, 256, 16, 1.0 - 1e-9, (), False),      # (almost) everything active: every row overflows
+    # rows over several chunks of 8 loads, the last one partial (bf16: 16 + 5
+    # tiles; fp32: 8 + 8 + 5), and long per-lane walks with tiles past the cap
+    # in every chunk (bf16: 32 + 13 tiles of 128; fp32: 16 + 16 + 13)
+    (37, 5376, 256, 16, 0.04, (5, 20), True),
+    (29, 5760, 128, 32, 0.2, (), False),
 ]
 
 
