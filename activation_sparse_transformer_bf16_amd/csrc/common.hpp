@@ -101,14 +101,16 @@ __device__ __forceinline__ float wave_sum_to_lane63(float v) {
   return v;
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave (integers).
+// Inclusive prefix sum over the 64 lanes of a wave (integers), with DPP row
+// shifts inside each 16-lane row and row broadcasts across rows; every lane of
+// the wave must be active.
 __device__ __forceinline__ int wave_incl_scan(int v) {
-  const int l = lane_id();
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int t = __shfl_up(v, o, 64);
-    if (l >= o) v += t;
-  }
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);   // row_shr 1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);   // row_shr 2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);   // row_shr 4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);   // row_shr 8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast15 into rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast31 into rows 2, 3
   return v;
 }
 

@@ -86,18 +86,6 @@ __device__ __forceinline__ uint32_t active_mask16<float, 4>(const u32x4_t &w) {
   return bits;
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts and
-// row broadcasts (every lane active).
-__device__ __forceinline__ int wave_incl_scan_dpp(int v) {
-  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);  // row_shr 1
-  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);  // row_shr 2
-  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);  // row_shr 4
-  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);  // row_shr 8
-  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast15 into rows 1, 3
-  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast31 into rows 2, 3
-  return v;
-}
-
 template <Dt D, int TILE>
 __global__ __launch_bounds__(PACK_THREADS) void k_pack(const typename DtT<D>::T *__restrict__ pre, int T, int F,
                                                       int cap, uint16_t *__restrict__ cnt,
@@ -147,7 +135,7 @@ __global__ __launch_bounds__(PACK_THREADS) void k_pack(const typename DtT<D>::T 
       const int kc = q * TPL + seg;  // tile inside the chunk
       uint32_t bits = active_mask16<TT, EPL>(raw[q]);  // +0 past the last tile: inactive
       const int own = __builtin_popcount(bits);
-      const int incl = wave_incl_scan_dpp(own);
+      const int incl = wave_incl_scan(own);
       // Non-zeros of the earlier segments (base) and up to the end of this
       // segment, read from the segments' last lanes.
       int base = 0, end = 0;
