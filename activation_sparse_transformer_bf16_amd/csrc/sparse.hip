@@ -247,11 +247,15 @@ hipError_t zero_int(int *p, hipStream_t s) {
 // from the row's counts, skips such rows, and the group-0 wave records
 // row_flag[t] (1 for an overflow row) and list_n[t] = -1 for them.  A local
 // column index is taken modulo the tile width, so a malformed index cannot
-// address a row outside its tile.
+// address a row outside its tile.  A (row, group) wave keeps the group's
+// entries in LDS while it computes them and then writes them to the row's
+// list with coalesced stores, 64 entries per instruction (the kernel is bound
+// by its vector-memory instruction rate).
 
 struct UpEntry {
   uint32_t off;   // byte offset of the unit's row in W_u^T (and in W_d)
-  uint32_t dst;   // index of the entry in the compact list
+  uint32_t dst;   // the entry's index in the compact list; once computed, the
+                  // entry's second word (v, or its part's partial u)
   float h;        // the gate activation
   uint32_t slot;  // the entry's TwELL slot (where u is saved)
 };
@@ -300,11 +304,12 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_up(
     const uint16_t *crow = cnt + (size_t)t * nt;
     const size_t lbase = (size_t)t * stride;
     const int k_end = g == 0 ? nt : k0;
-    int partial = 0;
+    int partial = 0, c_first = 0;
     bool over = false;
     for (int kb = 0; kb < nt; kb += 64) {
       const int kk = kb + lane;
       const int c = kk < nt ? (int)crow[kk] : 0;
+      if (kb == 0) c_first = c;
       over |= c > cap;
       partial += kk < k_end ? min(c, cap) : 0;
     }
@@ -331,7 +336,10 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_up(
     // (lane q, q < kn <= 64); its slots are contiguous after those of tile q-1,
     // so the wave loads all kn * cap slots with one lane per slot and files
     // the occupied ones at (entries of the tiles before q) + slot.
-    const int n = lane < kn ? min((int)crow[k0 + lane], cap) : 0;
+    // the group's tile counts: from the registers of the pass above when the
+    // row has at most 64 tiles
+    const int cg = nt <= 64 ? __shfl(c_first, min(k0 + lane, 63), 64) : (lane < kn ? (int)crow[k0 + lane] : 0);
+    const int n = lane < kn ? min(cg, cap) : 0;
     const int incl = wave_incl_scan(n);
     const int E = __builtin_amdgcn_readlane(incl, 63);
     for (int q0 = 0; q0 < kn * cap; q0 += 64) {
@@ -385,18 +393,28 @@ __global__ __launch_bounds__(SP_THREADS) void k_sparse_up(
         }
         const float tot = Reduce<U>::run(p);
         if (storer && u0 + my_u < ne) {
+          // the entry's second word goes to its dst field; the list is
+          // written below, 64 entries per store
           if constexpr (DC == 1) {
             const float v = mine.h * tot;
-            const uint32_t vb = D == Dt::BF16 ? (uint32_t)bf16_rne(v) : __float_as_uint(v);
-            list[lbase + mine.dst] = u32x2_t{mine.off, vb};
+            L[e0 + u0 + my_u].dst = D == Dt::BF16 ? (uint32_t)bf16_rne(v) : __float_as_uint(v);
             if (u_out != nullptr) u_out[mine.slot] = tot;
           } else {
-            list[(lbase + mine.dst) * 2 + part] =
-                part == 0 ? u32x2_t{mine.off, __float_as_uint(tot)} : u32x2_t{__float_as_uint(mine.h), __float_as_uint(tot)};
+            L[e0 + u0 + my_u].dst = __float_as_uint(tot);
             if (u_out != nullptr) atomicAdd(u_out + mine.slot, tot);
           }
         }
       }
+    }
+    wave_sync_lds();
+    // the group's entries to the row's list: E consecutive entries from
+    // position `before`
+    for (int e = lane; e < E; e += 64) {
+      const UpEntry en = L[e];
+      if constexpr (DC == 1)
+        list[lbase + before + e] = u32x2_t{en.off, en.dst};
+      else
+        list[(lbase + before + e) * 2 + part] = part == 0 ? u32x2_t{en.off, en.dst} : u32x2_t{__float_as_uint(en.h), en.dst};
     }
     wave_sync_lds();
   }
