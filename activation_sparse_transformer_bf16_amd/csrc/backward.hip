@@ -339,6 +339,8 @@ __global__ __launch_bounds__(SP_THREADS) void k_bw_entries(RowSrc<typename DtT<D
   const int my = U == 2 ? lane >> 5 : 0;  // the entry whose u this lane's row holds (storer lanes)
   const bool storer = U == 2 ? (lane & 31) == 0 : lane == 0;
   const int partner = U == 2 ? 16 : 32;
+  __shared__ f32x2_t stage_e[SP_WAVES][64];
+  f32x2_t *S = stage_e[wave];
 
   // the workgroup's rows, one per lane (tok_per_wg <= 64), read once
   const int r_i = min(tb * tok_per_wg + min(lane, tok_per_wg - 1), s.T - 1);
@@ -391,8 +393,11 @@ __global__ __launch_bounds__(SP_THREADS) void k_bw_entries(RowSrc<typename DtT<D
       const uint32_t moff = (uint32_t)j * row_bytes;
       const float hv = L.r < 0 ? to_f32(s.val[(size_t)t * s.width + i]) : to_f32(s.dense[(size_t)L.r * s.F + j]);
       const int pv = pos[L.slot0 + i];
+      const float uv = saved ? s.u[(size_t)t * s.width + i] : 0.f;
+      // Each entry's u (recomputed rows) and da go to the wave's LDS stage;
+      // the entry's own lane then forms du, dpre and a and writes them, one
+      // store instruction per 64 entries for each output.
       if (saved) {
-        const float uv = s.u[(size_t)t * s.width + i];
         for (int u0 = 0; u0 < ne; u0 += U) {
           u32x4_t b[U][NC];
 #pragma unroll
@@ -413,60 +418,52 @@ __global__ __launch_bounds__(SP_THREADS) void k_bw_entries(RowSrc<typename DtT<D
 #pragma unroll
             for (int c = 0; c < NC; ++c) p[u] = dot16(gr[c], b[u][c], p[u], TT());
           }
-          // after Reduce<U> the storer lanes hold da of their entry (the same
-          // lanes and entries as below)
+          // after Reduce<U> the storer lanes hold da of their entry
           const float da = Reduce<U>::run(p);
-          const int src = min(u0 + my, ne - 1);
-          const float h = __shfl(hv, src, 64);
-          const int pp = __shfl(pv, src, 64);
-          const float uu = __shfl(uv, src, 64);
-          if (storer && u0 + my < ne) {
-            const float du = da * h, dp = fmaf(da, uu, lam), av = h * uu;
-            ent[L.slot0 + e0 + u0 + my] = f32x2_t{du, dp};
-            csc[pp] = u32x4_t{(uint32_t)t, __float_as_uint(av), __float_as_uint(du), __float_as_uint(dp)};
-          }
+          if (storer && u0 + my < ne) S[u0 + my] = f32x2_t{0.f, da};
         }
-        continue;
-      }
-      for (int u0 = 0; u0 < ne; u0 += U) {
-        u32x4_t a[U][NC], b[U][NC];
+      } else {
+        for (int u0 = 0; u0 < ne; u0 += U) {
+          u32x4_t a[U][NC], b[U][NC];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const uint32_t off = read_lane(moff, min(u0 + u, ne - 1));
-          if (u0 + u < ne) {
+          for (int u = 0; u < U; ++u) {
+            const uint32_t off = read_lane(moff, min(u0 + u, ne - 1));
+            if (u0 + u < ne) {
+#pragma unroll
+              for (int c = 0; c < NC; ++c) {
+                a[u][c] = buffer_load<u32x4_t>(wur, lane_off + c * 1024, off);
+                b[u][c] = buffer_load<u32x4_t>(wdr, lane_off + c * 1024, off);
+              }
+            } else {
+#pragma unroll
+              for (int c = 0; c < NC; ++c) a[u][c] = b[u][c] = u32x4_t{0u, 0u, 0u, 0u};
+            }
+          }
+          float p[2 * U];
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            p[u] = 0.f;
+            p[U + u] = 0.f;
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
-              a[u][c] = buffer_load<u32x4_t>(wur, lane_off + c * 1024, off);
-              b[u][c] = buffer_load<u32x4_t>(wdr, lane_off + c * 1024, off);
+              p[u] = dot16(xr[c], a[u][c], p[u], TT());
+              p[U + u] = dot16(gr[c], b[u][c], p[U + u], TT());
             }
-          } else {
-#pragma unroll
-            for (int c = 0; c < NC; ++c) a[u][c] = b[u][c] = u32x4_t{0u, 0u, 0u, 0u};
           }
-        }
-        float p[2 * U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          p[u] = 0.f;
-          p[U + u] = 0.f;
-#pragma unroll
-          for (int c = 0; c < NC; ++c) {
-            p[u] = dot16(xr[c], a[u][c], p[u], TT());
-            p[U + u] = dot16(gr[c], b[u][c], p[U + u], TT());
-          }
-        }
-        const float tot = Reduce<2 * U>::run(p);
-        const float other = __shfl_xor(tot, partner, 64);
-        const int src = min(u0 + my, ne - 1);  // chunk index of the storer's entry
-        const float h = __shfl(hv, src, 64);
-        const int pp = __shfl(pv, src, 64);
-        if (storer && u0 + my < ne) {
-          const float uu = tot, da = other;
-          const float du = da * h, dp = fmaf(da, uu, lam), av = h * uu;
-          ent[L.slot0 + e0 + u0 + my] = f32x2_t{du, dp};
-          csc[pp] = u32x4_t{(uint32_t)t, __float_as_uint(av), __float_as_uint(du), __float_as_uint(dp)};
+          const float tot = Reduce<2 * U>::run(p);
+          const float other = __shfl_xor(tot, partner, 64);
+          if (storer && u0 + my < ne) S[u0 + my] = f32x2_t{tot, other};  // u, da
         }
       }
+      wave_sync_lds();
+      if (lane < ne) {
+        const f32x2_t q = S[lane];
+        const float uu = saved ? uv : q[0], da = q[1];
+        const float du = da * hv, dp = fmaf(da, uu, lam), av = hv * uu;
+        ent[L.slot0 + i] = f32x2_t{du, dp};
+        csc[pv] = u32x4_t{(uint32_t)t, __float_as_uint(av), __float_as_uint(du), __float_as_uint(dp)};
+      }
+      wave_sync_lds();
     }
   }
 }
