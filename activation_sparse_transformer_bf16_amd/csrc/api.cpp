@@ -196,8 +196,10 @@ twell_status check_ffn_ptrs(const void *x, const void *wg, const void *wu, const
 
 // The overflow-row list, then the dense fallback over it, chunk by chunk.
 // Chunk c takes list positions [c R, c R + R); its kernels read *n_ovf on the
-// device and exit at once when the list is shorter.  Each chunk may split K
-// over the same partial area (the chunks run one after the other).
+// device and exit at once when the list is shorter.  Only the first chunk may
+// split K (over the partial area): a later chunk runs only when more than R
+// rows overflow, and without a split it launches no reduction kernels, which
+// would otherwise be two more launches that exit at once in the common case.
 twell_status run_fallback(const twell_matrix *m, const void *x, const void *wg, const void *wu, const void *wd,
                           const float *beta, void *y, int d, const FfnWs &L, char *base, const uint8_t *row_flag,
                           hipStream_t s) {
@@ -211,7 +213,7 @@ twell_status run_fallback(const twell_matrix *m, const void *x, const void *wg, 
                       ? static_cast<char *>(m->dense) + (size_t)c0 * F * dt_size(m->dtype)
                       : nullptr;
     DenseArgs da{D, x, wg, wu, wd, beta, y, rows, d, F, m->ovf_rows + c0, m->n_ovf, c0, base + L.a, h_out, h_cap,
-                 reinterpret_cast<float *>(base + L.partial), L.partial_tiles};
+                 reinterpret_cast<float *>(base + L.partial), c0 == 0 ? L.partial_tiles : 0};
     TW_TRY(dense_gate_up(da, s), "fallback gate/up matmul");
     TW_TRY(dense_down(da, s), "fallback down matmul");
   }
