@@ -6,9 +6,11 @@
 //   k_hybrid_rows:  one wave per row.  The row's TwELL counts give its true
 //                   entry count and whether it overflowed TwELL.  A row with
 //                   at most `width` entries becomes an ELL row: from its
-//                   TwELL slots (one lane per tile, positions from a prefix
-//                   count over the tiles), or, when it overflowed TwELL, by a
-//                   ballot compaction of its dense backup row.  Other rows get
+//                   TwELL slots (with at most 64 tiles one lane per ELL
+//                   position, its tile found by a search over the tiles'
+//                   prefix counts; otherwise one lane per tile), or, when it
+//                   overflowed TwELL, by a ballot compaction of its dense
+//                   backup row.  Other rows get
 //                   all-padding ELL slots.  With saved u, an ELL row from
 //                   TwELL slots copies the slots' u too; one from the dense
 //                   backup marks its u as not saved (NaN in its first slot).
@@ -32,8 +34,9 @@ __global__ __launch_bounds__(64 * HY_WAVES) void k_hybrid_rows(
     int *__restrict__ out_cnt, typename DtT<D>::T *__restrict__ out_val, int *__restrict__ out_col,
     const float *__restrict__ tw_u, float *__restrict__ out_u) {
   using TT = typename DtT<D>::T;
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * HY_WAVES + (threadIdx.x >> 6);
+  __shared__ int tile_incl[HY_WAVES][64];  // inclusive entry counts over a row's tiles
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * HY_WAVES + wave;
   if (t >= T) return;
   const int nt = F / tile;
   const uint16_t *crow = cnt + (size_t)t * nt;
@@ -52,7 +55,30 @@ __global__ __launch_bounds__(64 * HY_WAVES) void k_hybrid_rows(
   int *crow_out = out_col + (size_t)t * width;
   const int n_ell = total <= width ? total : 0;  // ELL entries written below
   if (total <= width) {
-    if (!tw_ovf) {
+    if (!tw_ovf && nt <= 64) {
+      // one lane per output position e < total: its tile is the first whose
+      // inclusive count exceeds e (a search over the row's tile counts in
+      // LDS), its slot e minus the entries of the tiles before
+      const int n = lane < nt ? (int)crow[lane] : 0;
+      int *inc = tile_incl[wave];
+      inc[lane] = wave_incl_scan(n);
+      wave_sync_lds();
+      for (int e = lane; e < total; e += 64) {
+        int lo = 0, hi = nt - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (inc[mid] > e)
+            hi = mid;
+          else
+            lo = mid + 1;
+        }
+        const int s = e - (lo > 0 ? inc[lo - 1] : 0);
+        const size_t slot = ((size_t)t * nt + lo) * cap + s;
+        vrow[e] = val[slot];
+        crow_out[e] = lo * tile + (idx[slot] & (tile - 1));
+        if (out_u != nullptr) out_u[(size_t)t * width + e] = tw_u[slot];
+      }
+    } else if (!tw_ovf) {
       // lanes take tiles (64 at a time); a lane copies its tile's entries to
       // the row position given by a prefix count over the tiles
       int before = 0;  // entries of the tiles before the chunk
