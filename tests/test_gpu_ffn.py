@@ -31,6 +31,7 @@ SMALL = [
     ("f32", 17, 4096, 256, 256, 16, -0.5),         # widest fp32 rows
     ("bf16", 24, 512, 8448, 256, 16, -2.0),        # many hidden units per output slice
     ("f32", 20, 256, 4352, 128, 8, -1.5),          # fp32, many hidden units per output slice
+    ("bf16", 31, 512, 8192, 128, 8, -2.0),         # 64 tiles per row: every lane holds a tile count
     ("bf16", 29, 512, 8960, 128, 8, -2.0),         # 70 tiles per row (more than one lane's worth)
     ("bf16", 37, 512, 4096, 256, 64, -1.0),        # ~16% dense, cap 64: ~160 entries per unit group
     # the fallback in chunks of 768 (bf16, T = 1100) or 512 (fp32, T = 600) rows

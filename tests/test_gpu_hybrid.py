@@ -49,6 +49,8 @@ CASES = [
     (50, 768, 256, 16, 8, 0.0, (), False),               # nothing active
     (40, 512, 256, 16, 600, 1.0 - 1e-9, (), False),      # width > F: every row is an ELL row
     (33, 512, 128, 64, 1, 0.3, (), True),                # width 1: nearly every row is dense
+    (29, 8192, 128, 16, 256, 0.01, (4, 17), True),       # 64 tiles: one lane per ELL position, a full search
+    (23, 8960, 128, 16, 256, 0.01, (), False),           # 70 tiles: one lane per tile, two passes
 ]
 
 
