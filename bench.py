@@ -783,7 +783,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU: --gpus {args.gpus} is not supported "
-              "(the TwELL forward shards by tokens with no exchange; see the design notes)", file=sys.stderr)
+              "(the TwELL forward shards by tokens: each GPU runs the layer on its own rows with its own copy of the weights, with no exchange between GPUs)", file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
